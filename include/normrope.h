@@ -1,0 +1,191 @@
+/*
+ * normrope.h -- C ABI of libnormrope.so: single-pass fused RMSNorm and
+ * LayerNorm (forward and backward) and in-place interleaved RoPE (forward
+ * and inverse) for AMD Instinct MI355X (gfx950).
+ *
+ * The operations follow "Helios 性能优化全解析" (hncyxsy.com), sections
+ * 内核一 FlashNorm and 内核二 FlashRoPE, and the fused LayerNorm example of
+ * "LLM层的优化算子" (apxml.com), section 编写定制融合算子.
+ *
+ * Conventions for every call below
+ *   - Pointers are DEVICE pointers unless stated otherwise.  The caller owns
+ *     every buffer; the library allocates nothing and keeps no pointer after
+ *     the call returns.
+ *   - Tensors are dense and row-major: a norm input is [rows][n] with row
+ *     stride n.  x, y, dy, dx, w, gamma and beta share the dtype `dt`.
+ *     Per-row statistics, dw / dgamma / dbeta and RoPE tables are fp32.
+ *   - All arithmetic is fp32; each stored bf16 value is rounded once, to
+ *     nearest even.
+ *   - Work is queued on `stream` (a hipStream_t; NULL = default stream) and
+ *     the call returns without waiting for it.
+ *   - Arguments are checked on the host before anything is queued.  On any
+ *     error the call returns a non-zero nr_status_t and queues nothing,
+ *     except NR_ERR_HIP, which reports a failed launch (see
+ *     nr_last_hip_error).  rows == 0 (or tokens == 0) is a valid no-op.
+ *   - Any alignment is accepted.  Rows whose start is 16-byte aligned and
+ *     whose byte length is a multiple of 16 take the 128-bit load path;
+ *     other shapes take an element-wise path in the same kernels.
+ *   - An output may be the very same buffer as an input of the same shape
+ *     (in place, e.g. y == x, dx == dy); partial overlap is not allowed.
+ *   - Backward results are bitwise reproducible: for a given shape every
+ *     summation order is fixed (no atomics), whatever the device.
+ *   - Thread safety: calls may be made from several host threads; the only
+ *     shared state is the tuning table set by nr_tune.
+ */
+#ifndef NORMROPE_H
+#define NORMROPE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { NR_F32 = 0, NR_BF16 = 1 } nr_dtype_t;
+
+typedef enum {
+  NR_OK = 0,
+  NR_ERR_NULLPTR = 1,       /* a required pointer is NULL */
+  NR_ERR_SHAPE = 2,         /* negative size, n < 1, odd head_dim, bad grid */
+  NR_ERR_DTYPE = 3,         /* dt is not NR_F32 / NR_BF16 */
+  NR_ERR_UNSUPPORTED_N = 4, /* n (or a head's size) beyond the on-chip limit */
+  NR_ERR_WORKSPACE = 5,     /* workspace missing, too small or not 16-byte aligned */
+  NR_ERR_HIP = 6,           /* the HIP runtime refused a launch */
+  NR_ERR_ALIAS = 7,         /* an output partially overlaps an input */
+  NR_ERR_TUNE = 8           /* unknown tuning key or value */
+} nr_status_t;
+
+/* Largest row length the norm kernels accept: 65536 (bf16), 32768 (fp32). */
+int64_t nr_norm_n_max(nr_dtype_t dt); /* host only */
+
+/*
+ * rmsnorm_fwd -- Helios 性能优化全解析, 内核一 FlashNorm.
+ *   for each row i:  r_i = 1 / sqrt(mean_j x_ij^2 + eps)
+ *                    y_ij = (x_ij * r_i) * w'_j
+ *   with w'_j = w_j, or 1 + w_j when gemma_offset != 0 (the Gemma variant),
+ *   or 1 when w is NULL.  inv_rms[i] = r_i is stored when inv_rms != NULL
+ *   (it is what rmsnorm_bwd reads).
+ *   x [rows][n], y [rows][n] (may be x), w [n] or NULL, inv_rms [rows] fp32
+ *   or NULL.
+ */
+nr_status_t rmsnorm_fwd(nr_dtype_t dt, const void* x, const void* w, void* y,
+                        float* inv_rms, int64_t rows, int64_t n, float eps,
+                        int gemma_offset, void* stream);
+
+/*
+ * rmsnorm_bwd -- backward of rmsnorm_fwd; reads the cached inv_rms instead
+ * of recomputing it (内核一 FlashNorm: the backward reuses the forward's
+ * per-row cache).
+ *   xhat = x * r, g = dy * w', c_i = mean_j g_ij xhat_ij
+ *   dx_ij = r_i (g_ij - xhat_ij c_i)            -> dx [rows][n] (may be dy)
+ *   dw_j  = sum_i dy_ij xhat_ij (fp32)          -> dw [n] or NULL (not formed)
+ *   dw is a two-stage fixed-order reduction through `workspace` (device,
+ *   16-byte aligned, at least nr_bwd_workspace_bytes(rows, n, 0) bytes;
+ *   may be NULL when dw is NULL).  The workspace is scratch: its content on
+ *   entry does not matter and is overwritten.
+ */
+nr_status_t rmsnorm_bwd(nr_dtype_t dt, const void* dy, const void* x,
+                        const void* w, const float* inv_rms, void* dx,
+                        float* dw, int64_t rows, int64_t n, int gemma_offset,
+                        void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * layernorm_fwd -- 内核一 FlashNorm (mean, variance and scale in one read of
+ * the row) with the formula of 编写定制融合算子 (biased variance, eps inside
+ * the root, then weight and bias):
+ *   mu_i = mean_j x_ij, var_i = mean_j (x_ij - mu_i)^2, r_i = 1/sqrt(var_i + eps)
+ *   y_ij = (x_ij - mu_i) r_i gamma_j + beta_j    (gamma NULL -> 1, beta NULL -> 0)
+ *   mean[i] = mu_i and rstd[i] = r_i are stored when non-NULL (fp32 [rows]).
+ */
+nr_status_t layernorm_fwd(nr_dtype_t dt, const void* x, const void* gamma,
+                          const void* beta, void* y, float* mean, float* rstd,
+                          int64_t rows, int64_t n, float eps, void* stream);
+
+/*
+ * layernorm_bwd -- backward of layernorm_fwd from the cached mean and rstd.
+ *   xhat = (x - mu) r, g = dy gamma, a_i = mean_j g, b_i = mean_j g xhat
+ *   dx = r (g - a - xhat b)                      -> dx [rows][n] (may be dy)
+ *   dgamma_j = sum_i dy xhat, dbeta_j = sum_i dy -> fp32 [n] each, or NULL
+ *   workspace: at least nr_bwd_workspace_bytes(rows, n, 1) bytes when
+ *   dgamma or dbeta is wanted (same rules as rmsnorm_bwd).
+ */
+nr_status_t layernorm_bwd(nr_dtype_t dt, const void* dy, const void* x,
+                          const void* gamma, const float* mean,
+                          const float* rstd, void* dx, float* dgamma,
+                          float* dbeta, int64_t rows, int64_t n,
+                          void* workspace, size_t workspace_bytes,
+                          void* stream);
+
+/*
+ * rope_interleaved_apply -- Helios 性能优化全解析, 内核二 FlashRoPE.
+ *   x is [batch][tokens][heads][head_dim] with element strides stride_batch,
+ *   stride_token, stride_head (the head_dim axis is contiguous).  For each
+ *   pair i < head_dim/2 of each head vector, with (a, b) = (x[2i], x[2i+1]),
+ *   c = cos_tab[t][i], s = sin_tab[t][i] and sigma = -1 if inverse else +1:
+ *       x[2i]   = a c - b (sigma s)
+ *       x[2i+1] = a (sigma s) + b c
+ *   written IN PLACE.  The inverse is also the backward (the rotation's
+ *   transpose).  Tables are fp32 [tokens][head_dim/2], shared by all heads
+ *   and batches; build them with rope_table_1d / rope_table_3d or supply
+ *   your own.  head_dim must be even.  Distinct (batch, token, head) vectors
+ *   must not share elements (stride_head >= head_dim when heads > 1, else
+ *   NR_ERR_ALIAS).  A token's heads must span less than 1 GiB
+ *   ((heads-1)*stride_head + head_dim elements), else NR_ERR_UNSUPPORTED_N.
+ */
+nr_status_t rope_interleaved_apply(nr_dtype_t dt, void* x, const float* cos_tab,
+                                   const float* sin_tab, int64_t batch,
+                                   int64_t tokens, int64_t heads,
+                                   int64_t head_dim, int64_t stride_batch,
+                                   int64_t stride_token, int64_t stride_head,
+                                   int inverse, void* stream);
+
+/*
+ * rope_table_1d -- cos/sin table for 1-D positions pos0 .. pos0+tokens-1:
+ *   angle(t, i) = (pos0 + t) * theta^(-2i/head_dim), i < head_dim/2,
+ *   computed in double, cos and sin rounded once to fp32.
+ *   cos_tab, sin_tab: device fp32 [tokens][head_dim/2].
+ */
+nr_status_t rope_table_1d(float* cos_tab, float* sin_tab, int64_t tokens,
+                          int64_t head_dim, int64_t pos0, double theta,
+                          void* stream);
+
+/*
+ * rope_table_3d -- cos/sin table for a frames x height x width token grid,
+ * tokens ordered frame-major, then row, then column.  The head_dim/2 =
+ * pairs_t + pairs_h + pairs_w pairs are split into consecutive blocks that
+ * follow the frame, row and column index; pair j of a block of P pairs uses
+ * frequency theta^(-2j/(2P)).  Device fp32 [frames*height*width][head_dim/2].
+ */
+nr_status_t rope_table_3d(float* cos_tab, float* sin_tab, int64_t frames,
+                          int64_t height, int64_t width, int64_t pairs_t,
+                          int64_t pairs_h, int64_t pairs_w, double theta,
+                          void* stream);
+
+/* Workspace bytes rmsnorm_bwd (is_layernorm = 0) or layernorm_bwd (1) needs
+ * for dw / dgamma / dbeta at this shape.  Host only; pure function of its
+ * arguments and the current tuning table. */
+size_t nr_bwd_workspace_bytes(int64_t rows, int64_t n, int is_layernorm);
+
+/* Static description of a status code.  Host only. */
+const char* nr_status_str(nr_status_t s);
+
+/* hipError_t of the last NR_ERR_HIP seen by the calling thread (0 if none). */
+int nr_last_hip_error(void);
+
+/*
+ * nr_tune -- override one launch-shape choice (for tuning sweeps; results
+ * stay within the same tolerances, but the backward's summation order, and
+ * so its exact bits, depend on the shape).  value 0 restores the automatic
+ * choice.  Keys: "fwd_w", "fwd_k", "fwd_r", "bwd_w", "bwd_k", "bwd_d",
+ * "bwd_p", "bwd_rows_min", "rope_k", "rope_wpb".  A key whose forced value
+ * does not fit a call's shape makes that call return NR_ERR_SHAPE.
+ * Returns NR_ERR_TUNE for an unknown key or a negative value.  Host only.
+ */
+nr_status_t nr_tune(const char* key, int value);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* NORMROPE_H */

@@ -1,0 +1,277 @@
+"""Thin Python binding of libnormrope.so (the C ABI in include/normrope.h).
+
+Every function here only marshals arguments: it checks tensor devices,
+dtypes and shapes, allocates outputs the caller did not pass, and hands raw
+device pointers plus PyTorch's current HIP stream to the C function of the
+same name.  All arithmetic happens in the library's HIP kernels; there is no
+CPU or PyTorch fallback -- if the library is missing this module raises.
+
+The operations follow "Helios 性能优化全解析" (sections 内核一 FlashNorm and
+内核二 FlashRoPE); see include/normrope.h for the exact definitions.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+__all__ = [
+    "NormRopeError", "rmsnorm_fwd", "rmsnorm_bwd", "layernorm_fwd", "layernorm_bwd",
+    "rope_interleaved_apply", "rope_table_1d", "rope_table_3d", "nr_bwd_workspace_bytes",
+    "nr_status_str", "nr_tune", "nr_norm_n_max", "library_path",
+]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libnormrope.so")
+
+NR_F32, NR_BF16 = 0, 1
+_DT = {torch.float32: NR_F32, torch.bfloat16: NR_BF16}
+
+
+class NormRopeError(RuntimeError):
+    """A non-zero nr_status_t from the library."""
+
+    def __init__(self, fn: str, status: int):
+        msg = _lib().nr_status_str(status).decode()
+        if status == 6:  # NR_ERR_HIP
+            msg += f" (hipError {_lib().nr_last_hip_error()})"
+        super().__init__(f"{fn}: {msg} (status {status})")
+        self.status = status
+
+
+_L = None
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def _lib():
+    global _L
+    if _L is None:
+        if not os.path.exists(_LIB_PATH):
+            raise ImportError(
+                f"{_LIB_PATH} is not built; run `python -m rmsnorm_layernorm_fwd_amd.build` "
+                "(or __graft_entry__.build()) first")
+        L = ctypes.CDLL(_LIB_PATH)
+        vp, i32, i64, f32, f64, sz = (ctypes.c_void_p, ctypes.c_int, ctypes.c_int64,
+                                      ctypes.c_float, ctypes.c_double, ctypes.c_size_t)
+        sig = {
+            "rmsnorm_fwd": [i32, vp, vp, vp, vp, i64, i64, f32, i32, vp],
+            "rmsnorm_bwd": [i32, vp, vp, vp, vp, vp, vp, i64, i64, i32, vp, sz, vp],
+            "layernorm_fwd": [i32, vp, vp, vp, vp, vp, vp, i64, i64, f32, vp],
+            "layernorm_bwd": [i32, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, vp, sz, vp],
+            "rope_interleaved_apply": [i32, vp, vp, vp, i64, i64, i64, i64, i64, i64, i64, i32, vp],
+            "rope_table_1d": [vp, vp, i64, i64, i64, f64, vp],
+            "rope_table_3d": [vp, vp, i64, i64, i64, i64, i64, i64, f64, vp],
+            "nr_bwd_workspace_bytes": [i64, i64, i32],
+            "nr_status_str": [i32],
+            "nr_last_hip_error": [],
+            "nr_tune": [ctypes.c_char_p, i32],
+            "nr_norm_n_max": [i32],
+        }
+        for name, args in sig.items():
+            fn = getattr(L, name)
+            fn.argtypes = args
+            fn.restype = i32
+        L.nr_bwd_workspace_bytes.restype = sz
+        L.nr_status_str.restype = ctypes.c_char_p
+        L.nr_norm_n_max.restype = i64
+        _L = L
+    return _L
+
+
+def _check(fn: str, status: int):
+    if status != 0:
+        raise NormRopeError(fn, status)
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _stream(t: torch.Tensor):
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _dev(name: str, t: torch.Tensor, dtype=None, shape=None):
+    if t is None:
+        return
+    if not isinstance(t, torch.Tensor) or t.device.type != "cuda":
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
+def _rows_n(x: torch.Tensor):
+    n = x.shape[-1]
+    return x.numel() // n if n else 0, n
+
+
+def _dtype_code(x: torch.Tensor) -> int:
+    if x.dtype not in _DT:
+        raise ValueError(f"unsupported dtype {x.dtype} (fp32 or bf16)")
+    return _DT[x.dtype]
+
+
+def _workspace(rows, n, ln, ws, device):
+    need = nr_bwd_workspace_bytes(rows, n, ln)
+    if ws is None:
+        ws = torch.empty(max(need, 16), dtype=torch.uint8, device=device)
+    return ws, ws.numel() * ws.element_size()
+
+
+# ---------------------------------------------------------------- norms
+
+def rmsnorm_fwd(x, w=None, eps=1e-6, gemma_offset=False, y=None, inv_rms=None, want_stats=True):
+    """y = (x * r) * w' per row, r = 1/sqrt(mean(x^2) + eps); returns (y, inv_rms)."""
+    _dev("x", x)
+    dt = _dtype_code(x)
+    rows, n = _rows_n(x)
+    _dev("w", w, x.dtype, (n,))
+    if y is None:
+        y = torch.empty_like(x)
+    _dev("y", y, x.dtype, x.shape)
+    if inv_rms is None and want_stats:
+        inv_rms = torch.empty(x.shape[:-1], dtype=torch.float32, device=x.device)
+    _dev("inv_rms", inv_rms, torch.float32)
+    _check("rmsnorm_fwd", _lib().rmsnorm_fwd(dt, _ptr(x), _ptr(w), _ptr(y), _ptr(inv_rms), rows, n,
+                                             float(eps), int(bool(gemma_offset)), _stream(x)))
+    return y, inv_rms
+
+
+def rmsnorm_bwd(dy, x, w, inv_rms, gemma_offset=False, dx=None, want_dw=True, dw=None,
+                workspace=None):
+    """Backward of rmsnorm_fwd from the cached inv_rms; returns (dx, dw)."""
+    _dev("x", x)
+    dt = _dtype_code(x)
+    rows, n = _rows_n(x)
+    _dev("dy", dy, x.dtype, x.shape)
+    _dev("w", w, x.dtype, (n,))
+    _dev("inv_rms", inv_rms, torch.float32, x.shape[:-1])
+    if dx is None:
+        dx = torch.empty_like(x)
+    _dev("dx", dx, x.dtype, x.shape)
+    if dw is None and want_dw:
+        dw = torch.empty(n, dtype=torch.float32, device=x.device)
+    _dev("dw", dw, torch.float32, (n,))
+    ws, wsb = (None, 0)
+    if dw is not None:
+        ws, wsb = _workspace(rows, n, 0, workspace, x.device)
+    _check("rmsnorm_bwd", _lib().rmsnorm_bwd(dt, _ptr(dy), _ptr(x), _ptr(w), _ptr(inv_rms),
+                                             _ptr(dx), _ptr(dw), rows, n, int(bool(gemma_offset)),
+                                             _ptr(ws), wsb, _stream(x)))
+    return dx, dw
+
+
+def layernorm_fwd(x, gamma=None, beta=None, eps=1e-5, y=None, mean=None, rstd=None,
+                  want_stats=True):
+    """y = (x - mu) r gamma + beta per row; returns (y, mean, rstd)."""
+    _dev("x", x)
+    dt = _dtype_code(x)
+    rows, n = _rows_n(x)
+    _dev("gamma", gamma, x.dtype, (n,))
+    _dev("beta", beta, x.dtype, (n,))
+    if y is None:
+        y = torch.empty_like(x)
+    _dev("y", y, x.dtype, x.shape)
+    if want_stats:
+        if mean is None:
+            mean = torch.empty(x.shape[:-1], dtype=torch.float32, device=x.device)
+        if rstd is None:
+            rstd = torch.empty(x.shape[:-1], dtype=torch.float32, device=x.device)
+    _dev("mean", mean, torch.float32)
+    _dev("rstd", rstd, torch.float32)
+    _check("layernorm_fwd", _lib().layernorm_fwd(dt, _ptr(x), _ptr(gamma), _ptr(beta), _ptr(y),
+                                                 _ptr(mean), _ptr(rstd), rows, n, float(eps),
+                                                 _stream(x)))
+    return y, mean, rstd
+
+
+def layernorm_bwd(dy, x, gamma, mean, rstd, dx=None, want_dgamma=True, want_dbeta=True,
+                  dgamma=None, dbeta=None, workspace=None):
+    """Backward of layernorm_fwd from the cached mean / rstd; returns (dx, dgamma, dbeta)."""
+    _dev("x", x)
+    dt = _dtype_code(x)
+    rows, n = _rows_n(x)
+    _dev("dy", dy, x.dtype, x.shape)
+    _dev("gamma", gamma, x.dtype, (n,))
+    _dev("mean", mean, torch.float32, x.shape[:-1])
+    _dev("rstd", rstd, torch.float32, x.shape[:-1])
+    if dx is None:
+        dx = torch.empty_like(x)
+    _dev("dx", dx, x.dtype, x.shape)
+    if dgamma is None and want_dgamma:
+        dgamma = torch.empty(n, dtype=torch.float32, device=x.device)
+    if dbeta is None and want_dbeta:
+        dbeta = torch.empty(n, dtype=torch.float32, device=x.device)
+    _dev("dgamma", dgamma, torch.float32, (n,))
+    _dev("dbeta", dbeta, torch.float32, (n,))
+    ws, wsb = (None, 0)
+    if dgamma is not None or dbeta is not None:
+        ws, wsb = _workspace(rows, n, 1, workspace, x.device)
+    _check("layernorm_bwd", _lib().layernorm_bwd(dt, _ptr(dy), _ptr(x), _ptr(gamma), _ptr(mean),
+                                                 _ptr(rstd), _ptr(dx), _ptr(dgamma), _ptr(dbeta),
+                                                 rows, n, _ptr(ws), wsb, _stream(x)))
+    return dx, dgamma, dbeta
+
+
+# ---------------------------------------------------------------- RoPE
+
+def rope_interleaved_apply(x, cos_tab, sin_tab, inverse=False):
+    """Rotate interleaved pairs of x [B, T, H, D] in place (strides taken from x)."""
+    if x.dim() != 4:
+        raise ValueError("x must be [batch, tokens, heads, head_dim]")
+    if x.device.type != "cuda" or x.stride(3) != 1:
+        raise ValueError("x must be a GPU tensor with a contiguous last axis")
+    dt = _dtype_code(x)
+    b, t, h, d = x.shape
+    _dev("cos_tab", cos_tab, torch.float32, (t, d // 2))
+    _dev("sin_tab", sin_tab, torch.float32, (t, d // 2))
+    _check("rope_interleaved_apply", _lib().rope_interleaved_apply(
+        dt, _ptr(x), _ptr(cos_tab), _ptr(sin_tab), b, t, h, d, x.stride(0), x.stride(1),
+        x.stride(2), int(bool(inverse)), _stream(x)))
+    return x
+
+
+def rope_table_1d(tokens, head_dim, pos0=0, theta=10000.0, device="cuda"):
+    """fp32 cos/sin tables [tokens, head_dim/2] for positions pos0.."""
+    c = torch.empty((tokens, head_dim // 2), dtype=torch.float32, device=device)
+    s = torch.empty_like(c)
+    _check("rope_table_1d", _lib().rope_table_1d(_ptr(c), _ptr(s), tokens, head_dim, pos0,
+                                                 float(theta), _stream(c)))
+    return c, s
+
+
+def rope_table_3d(grid, pairs, theta=10000.0, device="cuda"):
+    """fp32 cos/sin tables [F*H*W, sum(pairs)] for a frames x height x width grid."""
+    f, h, w = grid
+    pt, ph, pw = pairs
+    c = torch.empty((f * h * w, pt + ph + pw), dtype=torch.float32, device=device)
+    s = torch.empty_like(c)
+    _check("rope_table_3d", _lib().rope_table_3d(_ptr(c), _ptr(s), f, h, w, pt, ph, pw,
+                                                 float(theta), _stream(c)))
+    return c, s
+
+
+# ---------------------------------------------------------------- helpers
+
+def nr_bwd_workspace_bytes(rows, n, is_layernorm) -> int:
+    return int(_lib().nr_bwd_workspace_bytes(rows, n, int(bool(is_layernorm))))
+
+
+def nr_status_str(status: int) -> str:
+    return _lib().nr_status_str(status).decode()
+
+
+def nr_tune(key: str, value: int):
+    _check("nr_tune", _lib().nr_tune(key.encode(), int(value)))
+
+
+def nr_norm_n_max(dtype) -> int:
+    return int(_lib().nr_norm_n_max(_DT[dtype]))

@@ -1,0 +1,365 @@
+// api.hip -- the C ABI of libnormrope.so (declared in include/normrope.h):
+// host-side argument checks, launch-shape selection and kernel dispatch.
+//
+// Launch-shape selection plays the part of the pages' block-size heuristic
+// (Helios 性能优化全解析, 内核一 FlashNorm: the row length is rounded up and
+// the thread count grows with it, few threads for short rows, a full block
+// for long ones), re-derived for 64-wide wavefronts: a row that fits in one
+// wave's registers (up to 640 16-byte chunks, i.e. 5120 bf16) gets one
+// wavefront and no barrier; longer rows get W waves.  Every check runs before
+// any HIP call, so a rejected call touches neither the device nor the stream.
+#include <atomic>
+#include <cstdint>
+#include <cstring>
+
+#include "../../include/normrope.h"
+#include "nr_internal.hpp"
+
+namespace {
+
+using nr::BwdPlan;
+using nr::FwdPlan;
+using nr::RopePlan;
+
+// ---- tuning overrides ---------------------------------------------------
+
+enum TuneKey { FWD_W, FWD_K, FWD_R, BWD_W, BWD_K, BWD_D, BWD_P, BWD_ROWS_MIN, ROPE_K, ROPE_WPB, NKEYS };
+const char* const kTuneNames[NKEYS] = {"fwd_w", "fwd_k", "fwd_r", "bwd_w", "bwd_k",
+                                       "bwd_d", "bwd_p", "bwd_rows_min", "rope_k", "rope_wpb"};
+std::atomic<int> g_tune[NKEYS];
+
+int tune(TuneKey k) { return g_tune[k].load(std::memory_order_relaxed); }
+
+thread_local int t_last_hip = 0;
+
+nr_status_t hip_status(hipError_t e) {
+  if (e == hipSuccess) return NR_OK;
+  t_last_hip = static_cast<int>(e);
+  return NR_ERR_HIP;
+}
+
+constexpr int64_t kMaxChunksPerRow = 16 * 64 * 8;  // 16 waves x 64 lanes x 8 chunks
+
+int elem_bytes(nr_dtype_t dt) { return dt == NR_F32 ? 4 : 2; }
+int vec_elems(nr_dtype_t dt) { return dt == NR_F32 ? 4 : 8; }
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool in_set(int v, const int* set, int n) {
+  for (int i = 0; i < n; ++i)
+    if (set[i] == v) return true;
+  return false;
+}
+
+// smallest member of the (ascending) set that is >= need, or 0
+int pick_at_least(int64_t need, const int* set, int n) {
+  for (int i = 0; i < n; ++i)
+    if (set[i] >= need) return set[i];
+  return 0;
+}
+
+const int kFwdK[] = {1, 2, 4, 6, 8, 10};
+const int kBwdK[] = {1, 2, 4, 8};
+const int kBwdD[] = {1, 2, 4, 8};
+const int kRopeK[] = {1, 2, 4, 6, 8, 10};
+
+// Two byte ranges either coincide exactly or are disjoint.
+bool bad_overlap(const void* a, size_t na, const void* b, size_t nb) {
+  if (a == nullptr || b == nullptr || na == 0 || nb == 0) return false;
+  const uintptr_t a0 = reinterpret_cast<uintptr_t>(a), b0 = reinterpret_cast<uintptr_t>(b);
+  if (a0 == b0 && na == nb) return false;
+  return a0 < b0 + nb && b0 < a0 + na;
+}
+
+nr_status_t check_dtype(nr_dtype_t dt) {
+  return (dt == NR_F32 || dt == NR_BF16) ? NR_OK : NR_ERR_DTYPE;
+}
+
+nr_status_t check_norm_shape(nr_dtype_t dt, int64_t rows, int64_t n) {
+  if (rows < 0 || n < 1) return NR_ERR_SHAPE;
+  if (n > nr_norm_n_max(dt)) return NR_ERR_UNSUPPORTED_N;
+  if (rows > INT64_MAX / 8 / n) return NR_ERR_SHAPE;
+  return NR_OK;
+}
+
+nr_status_t plan_fwd(nr_dtype_t dt, int64_t n, bool aligned, FwdPlan* pl) {
+  const int64_t nchunk = (n + vec_elems(dt) - 1) / vec_elems(dt);
+  const int64_t need = (nchunk + 63) / 64;
+  int W, K;
+  if (need <= 10) {
+    W = 1;
+    K = pick_at_least(need, kFwdK, 6);
+  } else {
+    W = static_cast<int>((need + 7) / 8);
+    K = pick_at_least((need + W - 1) / W, kFwdK, 5);  // K <= 8 when W > 1
+  }
+  if (tune(FWD_W) > 0) W = tune(FWD_W);
+  if (tune(FWD_K) > 0) K = tune(FWD_K);
+  int R = W == 1 ? 4 : (W == 2 ? 2 : 1);
+  if (tune(FWD_R) > 0) R = tune(FWD_R);
+  if (W < 1 || W > 16 || !in_set(K, kFwdK, 6) || (W > 1 && K > 8)) return NR_ERR_SHAPE;
+  if (static_cast<int64_t>(64) * W * K < nchunk) return NR_ERR_SHAPE;
+  if (R < 1 || (W == 1 && R > 4) || 64 * W * R > 1024) return NR_ERR_SHAPE;
+  *pl = FwdPlan{W, K, R, aligned};
+  return NR_OK;
+}
+
+// Backward workgroups: each takes rows_per_block consecutive rows.  Enough
+// rows per workgroup (16 by default) keep the fp32 partial rows small next to
+// the row traffic; at most 1024 workgroups.  Depends on rows only, so the
+// summation order, and the workspace size, are the same on every device.
+void bwd_grid(int64_t rows, int64_t* P_out, int64_t* rpb_out) {
+  const int64_t rows_min = tune(BWD_ROWS_MIN) > 0 ? tune(BWD_ROWS_MIN) : 16;
+  const int64_t pcap = tune(BWD_P) > 0 ? tune(BWD_P) : 1024;
+  int64_t P = tune(BWD_P) > 0 ? pcap : (rows + rows_min - 1) / rows_min;
+  if (P > pcap) P = pcap;
+  if (P > rows) P = rows;
+  if (P < 1) P = 1;
+  const int64_t rpb = rows > 0 ? (rows + P - 1) / P : 1;
+  *P_out = rows > 0 ? (rows + rpb - 1) / rpb : 1;  // no empty workgroups
+  *rpb_out = rpb;
+}
+
+nr_status_t plan_bwd(nr_dtype_t dt, int64_t rows, int64_t n, bool aligned, BwdPlan* pl) {
+  const int E = vec_elems(dt);
+  const int64_t nchunk = (n + E - 1) / E;
+  const int64_t need = (nchunk + 63) / 64;
+  int K = 0, W = 0;
+  for (int k : kBwdK) {
+    if ((need + k - 1) / k <= 16) {
+      K = k;
+      break;
+    }
+  }
+  if (tune(BWD_K) > 0) K = tune(BWD_K);
+  if (K > 0) W = static_cast<int>((need + K - 1) / K);
+  if (tune(BWD_W) > 0) W = tune(BWD_W);
+  int D = 1;
+  for (int d : kBwdD)
+    if (d * K * E <= 16) D = d;
+  if (tune(BWD_D) > 0) D = tune(BWD_D);
+  if (!in_set(K, kBwdK, 4) || !in_set(D, kBwdD, 4) || K * D > 8 || W < 1 || W > 16)
+    return NR_ERR_SHAPE;
+  if (static_cast<int64_t>(64) * W * K < nchunk) return NR_ERR_SHAPE;
+  int64_t P, rpb;
+  bwd_grid(rows, &P, &rpb);
+  *pl = BwdPlan{W, K, D, static_cast<int>(P), rpb, aligned};
+  return NR_OK;
+}
+
+nr_status_t plan_rope(nr_dtype_t dt, int64_t heads, int64_t head_dim, bool aligned,
+                      RopePlan* pl) {
+  const int E = aligned ? vec_elems(dt) : 2;
+  const int64_t cph = head_dim / E;
+  const int64_t nchunk = heads * cph;
+  int K = pick_at_least((nchunk + 63) / 64, kRopeK, 6);
+  if (K == 0) K = 10;  // several passes over the heads
+  if (tune(ROPE_K) > 0) K = tune(ROPE_K);
+  int wpb = tune(ROPE_WPB) > 0 ? tune(ROPE_WPB) : 4;
+  if (!in_set(K, kRopeK, 6) || wpb < 1 || wpb > 4) return NR_ERR_SHAPE;
+  *pl = RopePlan{K, wpb, aligned, (64 % cph) == 0};
+  return NR_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int64_t nr_norm_n_max(nr_dtype_t dt) {
+  return kMaxChunksPerRow * (dt == NR_F32 ? 4 : 8);
+}
+
+const char* nr_status_str(nr_status_t s) {
+  switch (s) {
+    case NR_OK: return "ok";
+    case NR_ERR_NULLPTR: return "required pointer is NULL";
+    case NR_ERR_SHAPE: return "invalid shape or launch shape";
+    case NR_ERR_DTYPE: return "unsupported dtype";
+    case NR_ERR_UNSUPPORTED_N: return "row length beyond the supported maximum";
+    case NR_ERR_WORKSPACE: return "workspace missing, too small or misaligned";
+    case NR_ERR_HIP: return "HIP launch failed";
+    case NR_ERR_ALIAS: return "output partially overlaps an input";
+    case NR_ERR_TUNE: return "unknown tuning key or value";
+  }
+  return "unknown status";
+}
+
+int nr_last_hip_error(void) { return t_last_hip; }
+
+nr_status_t nr_tune(const char* key, int value) {
+  if (key == nullptr || value < 0) return NR_ERR_TUNE;
+  for (int i = 0; i < NKEYS; ++i) {
+    if (std::strcmp(key, kTuneNames[i]) == 0) {
+      g_tune[i].store(value, std::memory_order_relaxed);
+      return NR_OK;
+    }
+  }
+  return NR_ERR_TUNE;
+}
+
+size_t nr_bwd_workspace_bytes(int64_t rows, int64_t n, int is_layernorm) {
+  if (rows <= 0 || n < 1) return 0;
+  int64_t P, rpb;
+  bwd_grid(rows, &P, &rpb);
+  return static_cast<size_t>(P) * static_cast<size_t>(n) * sizeof(float) *
+         (is_layernorm ? 2u : 1u);
+}
+
+nr_status_t rmsnorm_fwd(nr_dtype_t dt, const void* x, const void* w, void* y, float* inv_rms,
+                        int64_t rows, int64_t n, float eps, int gemma_offset, void* stream) {
+  nr_status_t s;
+  if ((s = check_dtype(dt)) != NR_OK) return s;
+  if ((s = check_norm_shape(dt, rows, n)) != NR_OK) return s;
+  if (rows == 0) return NR_OK;
+  if (x == nullptr || y == nullptr) return NR_ERR_NULLPTR;
+  const size_t bytes = static_cast<size_t>(rows * n) * elem_bytes(dt);
+  if (bad_overlap(y, bytes, x, bytes)) return NR_ERR_ALIAS;
+  const bool aligned = (n % vec_elems(dt)) == 0 && aligned16(x) && aligned16(y) &&
+                       (w == nullptr || aligned16(w));
+  FwdPlan pl;
+  if ((s = plan_fwd(dt, n, aligned, &pl)) != NR_OK) return s;
+  return hip_status(nr::launch_norm_fwd(false, dt, pl, x, w, nullptr, y, inv_rms, nullptr, rows,
+                                        static_cast<int>(n), eps, gemma_offset ? 1.0f : 0.0f,
+                                        static_cast<hipStream_t>(stream)));
+}
+
+nr_status_t layernorm_fwd(nr_dtype_t dt, const void* x, const void* gamma, const void* beta,
+                          void* y, float* mean, float* rstd, int64_t rows, int64_t n, float eps,
+                          void* stream) {
+  nr_status_t s;
+  if ((s = check_dtype(dt)) != NR_OK) return s;
+  if ((s = check_norm_shape(dt, rows, n)) != NR_OK) return s;
+  if (rows == 0) return NR_OK;
+  if (x == nullptr || y == nullptr) return NR_ERR_NULLPTR;
+  const size_t bytes = static_cast<size_t>(rows * n) * elem_bytes(dt);
+  if (bad_overlap(y, bytes, x, bytes)) return NR_ERR_ALIAS;
+  const bool aligned = (n % vec_elems(dt)) == 0 && aligned16(x) && aligned16(y) &&
+                       (gamma == nullptr || aligned16(gamma)) &&
+                       (beta == nullptr || aligned16(beta));
+  FwdPlan pl;
+  if ((s = plan_fwd(dt, n, aligned, &pl)) != NR_OK) return s;
+  return hip_status(nr::launch_norm_fwd(true, dt, pl, x, gamma, beta, y, mean, rstd, rows,
+                                        static_cast<int>(n), eps, 0.0f,
+                                        static_cast<hipStream_t>(stream)));
+}
+
+namespace {
+
+nr_status_t norm_bwd_common(bool ln, nr_dtype_t dt, const void* dy, const void* x, const void* w,
+                            const float* mean, const float* rstat, void* dx, float* o0, float* o1,
+                            int64_t rows, int64_t n, float w_add, void* workspace,
+                            size_t workspace_bytes, void* stream) {
+  nr_status_t s;
+  if ((s = check_dtype(dt)) != NR_OK) return s;
+  if ((s = check_norm_shape(dt, rows, n)) != NR_OK) return s;
+  const bool want_cols = o0 != nullptr || o1 != nullptr;
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  if (rows == 0) {
+    // empty batch: the column gradients are sums over no rows.  The column
+    // reduction over zero partials writes the zeros (a kernel, not a memset,
+    // so the call stays safe to record into a graph).
+    if (!want_cols) return NR_OK;
+    return hip_status(nr::launch_colreduce(nullptr, 0, 0, static_cast<int>(n), o0, o1, st));
+  }
+  if (dy == nullptr || x == nullptr || dx == nullptr || rstat == nullptr ||
+      (ln && mean == nullptr))
+    return NR_ERR_NULLPTR;
+  const size_t bytes = static_cast<size_t>(rows * n) * elem_bytes(dt);
+  if (bad_overlap(dx, bytes, dy, bytes) || bad_overlap(dx, bytes, x, bytes)) return NR_ERR_ALIAS;
+  const bool aligned = (n % vec_elems(dt)) == 0 && aligned16(dy) && aligned16(x) &&
+                       aligned16(dx) && (w == nullptr || aligned16(w));
+  BwdPlan pl;
+  if ((s = plan_bwd(dt, rows, n, aligned, &pl)) != NR_OK) return s;
+  float* part = nullptr;
+  if (want_cols) {
+    const size_t need = static_cast<size_t>(pl.P) * n * sizeof(float) * (ln ? 2 : 1);
+    if (workspace == nullptr || workspace_bytes < need || !aligned16(workspace))
+      return NR_ERR_WORKSPACE;
+    part = static_cast<float*>(workspace);
+  }
+  if ((s = hip_status(nr::launch_norm_bwd(ln, dt, pl, dy, x, w, mean, rstat, dx, part, rows,
+                                          static_cast<int>(n), w_add, st))) != NR_OK)
+    return s;
+  if (want_cols)
+    return hip_status(nr::launch_colreduce(part, static_cast<int64_t>(pl.P) * n, pl.P,
+                                           static_cast<int>(n), o0, o1, st));
+  return NR_OK;
+}
+
+}  // namespace
+
+nr_status_t rmsnorm_bwd(nr_dtype_t dt, const void* dy, const void* x, const void* w,
+                        const float* inv_rms, void* dx, float* dw, int64_t rows, int64_t n,
+                        int gemma_offset, void* workspace, size_t workspace_bytes, void* stream) {
+  return norm_bwd_common(false, dt, dy, x, w, nullptr, inv_rms, dx, dw, nullptr, rows, n,
+                         gemma_offset ? 1.0f : 0.0f, workspace, workspace_bytes, stream);
+}
+
+nr_status_t layernorm_bwd(nr_dtype_t dt, const void* dy, const void* x, const void* gamma,
+                          const float* mean, const float* rstd, void* dx, float* dgamma,
+                          float* dbeta, int64_t rows, int64_t n, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+  return norm_bwd_common(true, dt, dy, x, gamma, mean, rstd, dx, dgamma, dbeta, rows, n, 0.0f,
+                         workspace, workspace_bytes, stream);
+}
+
+nr_status_t rope_interleaved_apply(nr_dtype_t dt, void* x, const float* cos_tab,
+                                   const float* sin_tab, int64_t batch, int64_t tokens,
+                                   int64_t heads, int64_t head_dim, int64_t stride_batch,
+                                   int64_t stride_token, int64_t stride_head, int inverse,
+                                   void* stream) {
+  nr_status_t s;
+  if ((s = check_dtype(dt)) != NR_OK) return s;
+  if (batch < 0 || tokens < 0 || heads < 0 || head_dim < 2 || (head_dim & 1)) return NR_ERR_SHAPE;
+  if (stride_batch < 0 || stride_token < 0 || stride_head < 0) return NR_ERR_SHAPE;
+  if (heads > (int64_t{1} << 20) || head_dim > (int64_t{1} << 20) ||
+      heads * head_dim > (int64_t{1} << 30))
+    return NR_ERR_UNSUPPORTED_N;
+  if (batch == 0 || tokens == 0 || heads == 0) return NR_OK;
+  if (tokens > INT64_MAX / head_dim || batch > INT64_MAX / tokens) return NR_ERR_SHAPE;
+  if (x == nullptr || cos_tab == nullptr || sin_tab == nullptr) return NR_ERR_NULLPTR;
+  if (heads > 1 && stride_head < head_dim) return NR_ERR_ALIAS;  // head vectors overlap
+  // a token's heads are addressed with 32-bit byte offsets from the token start
+  const int64_t span = ((heads - 1) * stride_head + head_dim) * elem_bytes(dt);
+  if (stride_head > (int64_t{1} << 30) || span >= (int64_t{1} << 30)) return NR_ERR_UNSUPPORTED_N;
+  const int v = vec_elems(dt);
+  const bool aligned = head_dim % v == 0 && stride_batch % v == 0 && stride_token % v == 0 &&
+                       stride_head % v == 0 && aligned16(x) && aligned16(cos_tab) &&
+                       aligned16(sin_tab);
+  RopePlan pl;
+  if ((s = plan_rope(dt, heads, head_dim, aligned, &pl)) != NR_OK) return s;
+  return hip_status(nr::launch_rope(dt, pl, x, cos_tab, sin_tab, batch, tokens,
+                                    static_cast<int>(heads), static_cast<int>(head_dim),
+                                    stride_batch, stride_token, stride_head,
+                                    inverse ? -1.0f : 1.0f, static_cast<hipStream_t>(stream)));
+}
+
+nr_status_t rope_table_1d(float* cos_tab, float* sin_tab, int64_t tokens, int64_t head_dim,
+                          int64_t pos0, double theta, void* stream) {
+  if (tokens < 0 || head_dim < 2 || (head_dim & 1) || head_dim > (int64_t{1} << 20))
+    return NR_ERR_SHAPE;
+  if (!(theta > 0.0)) return NR_ERR_SHAPE;
+  if (tokens == 0) return NR_OK;
+  if (tokens > INT64_MAX / head_dim) return NR_ERR_SHAPE;
+  if (cos_tab == nullptr || sin_tab == nullptr) return NR_ERR_NULLPTR;
+  return hip_status(nr::launch_rope_table_1d(cos_tab, sin_tab, tokens, static_cast<int>(head_dim),
+                                             pos0, theta, static_cast<hipStream_t>(stream)));
+}
+
+nr_status_t rope_table_3d(float* cos_tab, float* sin_tab, int64_t frames, int64_t height,
+                          int64_t width, int64_t pairs_t, int64_t pairs_h, int64_t pairs_w,
+                          double theta, void* stream) {
+  if (frames < 0 || height < 0 || width < 0) return NR_ERR_SHAPE;
+  if (pairs_t < 1 || pairs_h < 1 || pairs_w < 1 || pairs_t + pairs_h + pairs_w > (1 << 19))
+    return NR_ERR_SHAPE;
+  if (!(theta > 0.0)) return NR_ERR_SHAPE;
+  if (frames == 0 || height == 0 || width == 0) return NR_OK;
+  if (height > INT64_MAX / width || frames > INT64_MAX / (height * width) / (1 << 20))
+    return NR_ERR_SHAPE;
+  if (cos_tab == nullptr || sin_tab == nullptr) return NR_ERR_NULLPTR;
+  return hip_status(nr::launch_rope_table_3d(
+      cos_tab, sin_tab, frames, height, width, static_cast<int>(pairs_t),
+      static_cast<int>(pairs_h), static_cast<int>(pairs_w), theta,
+      static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

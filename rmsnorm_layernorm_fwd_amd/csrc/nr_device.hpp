@@ -1,0 +1,220 @@
+// nr_device.hpp -- device-side building blocks shared by the norm and RoPE
+// kernels: 16-byte chunk I/O, bf16 <-> fp32 conversion and wave64 / workgroup
+// reductions for gfx950 (CDNA4).
+//
+// Data model: a row (norms) or a token (RoPE) is cut into 16-byte chunks,
+// 8 bf16 or 4 fp32 elements each.  Lane t of a row group owns chunks
+// t, t + 64W, t + 128W, ... so that every wave-wide load instruction touches
+// 1 KiB of contiguous memory (fully coalesced global_load_dwordx4).  Chunks
+// are kept in VGPRs as raw 32-bit words and widened to fp32 where used; every
+// result is rounded to the storage type exactly once, when it is stored.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace nr {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// bfloat16 storage tag: the top 16 bits of an IEEE single.
+struct bf16 {
+  uint16_t bits;
+};
+
+template <typename T> struct Vec;
+template <> struct Vec<float> { static constexpr int N = 4; };
+template <> struct Vec<bf16> { static constexpr int N = 8; };
+
+// ---- conversions ---------------------------------------------------------
+
+// fp32 pair -> packed bf16 pair, round to nearest even
+// (gfx950 has a native instruction for this: v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  f32x2 f = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2));
+}
+
+// ---- 16-byte chunk <-> fp32 --------------------------------------------
+
+template <typename T>
+__device__ __forceinline__ void unpack(const u32x4 c, float (&v)[Vec<T>::N]);
+template <>
+__device__ __forceinline__ void unpack<float>(const u32x4 c, float (&v)[4]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) v[i] = __uint_as_float(c[i]);
+}
+template <>
+__device__ __forceinline__ void unpack<bf16>(const u32x4 c, float (&v)[8]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    v[2 * i] = __uint_as_float(c[i] << 16);
+    v[2 * i + 1] = __uint_as_float(c[i] & 0xffff0000u);
+  }
+}
+
+template <typename T>
+__device__ __forceinline__ u32x4 pack(const float (&v)[Vec<T>::N]);
+template <>
+__device__ __forceinline__ u32x4 pack<float>(const float (&v)[4]) {
+  u32x4 c;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) c[i] = __float_as_uint(v[i]);
+  return c;
+}
+template <>
+__device__ __forceinline__ u32x4 pack<bf16>(const float (&v)[8]) {
+  u32x4 c;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) c[i] = pack_bf16x2(v[2 * i], v[2 * i + 1]);
+  return c;
+}
+
+// ---- buffer resources --------------------------------------------------
+//
+// Rows and tokens are read and written through buffer resources: a
+// wave-uniform descriptor (base address, size in bytes) held in SGPRs plus a
+// 32-bit per-lane byte offset.  The hardware range-checks every access
+// against the size: a load past the end returns 0 and a store past the end
+// is dropped.  So lanes that own no chunk of a short row, or a whole row
+// group past the last row, need no branch, and no lane carries a 64-bit
+// pointer.  Word 3 (0x00020000) is the gfx9-family setting for raw
+// (unswizzled, stride 0) 32-bit buffer access.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0),
+                                           static_cast<int>(bytes), 0x00020000);
+}
+
+// Chunk c (elements [cE, cE + E)) of a buffer.  VEC: one 128-bit access (the
+// buffer starts 16-byte aligned and holds whole chunks).  Otherwise element
+// by element, each access naturally aligned and range-checked on its own;
+// that path serves odd shapes and alignments, not speed.
+template <typename T, bool VEC>
+__device__ __forceinline__ u32x4 ld_chunk(rsrc_t r, int c) {
+  if constexpr (VEC) {
+    return __builtin_amdgcn_raw_buffer_load_b128(r, c * 16, 0, 0);
+  } else if constexpr (Vec<T>::N == 8) {
+    u32x4 v;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t lo = __builtin_amdgcn_raw_buffer_load_b16(r, (c * 8 + 2 * i) * 2, 0, 0);
+      const uint32_t hi = __builtin_amdgcn_raw_buffer_load_b16(r, (c * 8 + 2 * i + 1) * 2, 0, 0);
+      v[i] = lo | (hi << 16);
+    }
+    return v;
+  } else {
+    u32x4 v;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = __builtin_amdgcn_raw_buffer_load_b32(r, (c * 4 + i) * 4, 0, 0);
+    return v;
+  }
+}
+
+template <typename T, bool VEC>
+__device__ __forceinline__ void st_chunk(rsrc_t r, int c, const u32x4 v) {
+  if constexpr (VEC) {
+    __builtin_amdgcn_raw_buffer_store_b128(v, r, c * 16, 0, 0);
+  } else if constexpr (Vec<T>::N == 8) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      __builtin_amdgcn_raw_buffer_store_b16(static_cast<uint16_t>(v[i] & 0xffffu), r,
+                                            (c * 8 + 2 * i) * 2, 0, 0);
+      __builtin_amdgcn_raw_buffer_store_b16(static_cast<uint16_t>(v[i] >> 16), r,
+                                            (c * 8 + 2 * i + 1) * 2, 0, 0);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) __builtin_amdgcn_raw_buffer_store_b32(v[i], r, (c * 4 + i) * 4, 0, 0);
+  }
+}
+
+// single fp32 / element access through a buffer
+__device__ __forceinline__ float ld_f32(rsrc_t r, int byte_off) {
+  return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, byte_off, 0, 0));
+}
+__device__ __forceinline__ void st_f32(rsrc_t r, int byte_off, float v) {
+  __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, byte_off, 0, 0);
+}
+template <typename T> __device__ __forceinline__ float ld_elem(rsrc_t r, int byte_off);
+template <> __device__ __forceinline__ float ld_elem<float>(rsrc_t r, int byte_off) {
+  return ld_f32(r, byte_off);
+}
+template <> __device__ __forceinline__ float ld_elem<bf16>(rsrc_t r, int byte_off) {
+  return __uint_as_float(static_cast<uint32_t>(__builtin_amdgcn_raw_buffer_load_b16(r, byte_off, 0, 0)) << 16);
+}
+template <typename T> __device__ __forceinline__ void st_elem(rsrc_t r, int byte_off, float v);
+template <> __device__ __forceinline__ void st_elem<float>(rsrc_t r, int byte_off, float v) {
+  st_f32(r, byte_off, v);
+}
+template <> __device__ __forceinline__ void st_elem<bf16>(rsrc_t r, int byte_off, float v) {
+  __builtin_amdgcn_raw_buffer_store_b16(static_cast<uint16_t>(pack_bf16x2(v, 0.0f) & 0xffffu), r,
+                                        byte_off, 0, 0);
+}
+
+// index of the calling wave within its workgroup, as a scalar (SGPR) value
+__device__ __forceinline__ int wave_id() {
+  return __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
+}
+
+// ---- reductions ----------------------------------------------------------
+
+// lane i reads lane (pattern) of the same 16-lane DPP row
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __int_as_float(
+      __builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+
+// Sum over the 64 lanes of a wave; every lane gets the same bits.
+// Within a 16-lane row: butterfly over quad_perm [1,0,3,2], quad_perm
+// [2,3,0,1], row_half_mirror and row_mirror (each lane adds a partner that
+// holds a disjoint partial sum, so all lanes of the row end up equal).
+// Across rows: gfx950's v_permlane16_swap / v_permlane32_swap exchange
+// whole rows in VALU, with no LDS round trip.
+__device__ __forceinline__ float wave_sum(float v) {
+  v += dpp<0xB1>(v);   // quad_perm [1,0,3,2]
+  v += dpp<0x4E>(v);   // quad_perm [2,3,0,1]
+  v += dpp<0x141>(v);  // row_half_mirror
+  v += dpp<0x140>(v);  // row_mirror
+  {
+    const uint32_t u = __float_as_uint(v);
+    auto p = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    v = __uint_as_float(p[0]) + __uint_as_float(p[1]);
+  }
+  {
+    const uint32_t u = __float_as_uint(v);
+    auto p = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    v = __uint_as_float(p[0]) + __uint_as_float(p[1]);
+  }
+  return v;
+}
+
+// Sum of v over the W waves of a row group (W == 1: a pure wave reduction).
+// red: LDS scratch of at least blockDim/64 floats, used once per call site;
+// wave sums meet there and are added in wave order.
+__device__ __forceinline__ float group_sum(float v, int W, int wave, int g, float* red) {
+  v = wave_sum(v);
+  if (W == 1) return v;
+  if ((threadIdx.x & 63) == 0) red[wave] = v;
+  __syncthreads();
+  float s = 0.0f;
+  for (int i = 0; i < W; ++i) s += red[g * W + i];
+  return s;
+}
+
+// Make the compiler treat these registers as freshly written, so values it
+// derived from them earlier (widened fp32 copies, products) are recomputed
+// rather than kept alive across a reduction.  Only the packed 16-byte chunks
+// stay resident, which halves the VGPRs a bf16 row needs.
+template <int N>
+__device__ __forceinline__ void reload_barrier(u32x4 (&a)[N]) {
+#pragma unroll
+  for (int i = 0; i < N; ++i) asm volatile("" : "+v"(a[i]));
+}
+
+}  // namespace nr

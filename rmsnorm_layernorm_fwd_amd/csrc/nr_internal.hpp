@@ -1,0 +1,54 @@
+// nr_internal.hpp -- launch plans and launcher entry points shared between
+// the kernel translation units and the C-ABI layer (api.hip).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace nr {
+
+constexpr int kF32 = 0;   // matches NR_F32
+constexpr int kBF16 = 1;  // matches NR_BF16
+
+// Forward row kernel: W waves per row, K 16-byte chunks per lane, R rows
+// per workgroup.  aligned: 128-bit loads/stores on every row.
+struct FwdPlan {
+  int W, K, R;
+  bool aligned;
+};
+
+// Backward stage 1: P workgroups of W waves, each over rows_per_block
+// consecutive rows, D rows per batch, K chunks per lane.
+struct BwdPlan {
+  int W, K, D, P;
+  int64_t rows_per_block;
+  bool aligned;
+};
+
+// RoPE: one wave per token, K chunks per lane per pass over the heads,
+// waves_per_block tokens per workgroup.  aligned: 128-bit path; fast: the
+// table slice a lane needs is the same for every chunk it owns.
+struct RopePlan {
+  int K, waves_per_block;
+  bool aligned, fast;
+};
+
+hipError_t launch_norm_fwd(bool ln, int dt, const FwdPlan& pl, const void* x, const void* w,
+                           const void* b, void* y, float* s0, float* s1, int64_t rows, int n,
+                           float eps, float w_add, hipStream_t st);
+hipError_t launch_norm_bwd(bool ln, int dt, const BwdPlan& pl, const void* dy, const void* x,
+                           const void* w, const float* mean, const float* rstat, void* dx,
+                           float* part, int64_t rows, int n, float w_add, hipStream_t st);
+hipError_t launch_colreduce(const float* part, int64_t part_stride, int P, int n, float* out0,
+                            float* out1, hipStream_t st);
+hipError_t launch_rope(int dt, const RopePlan& pl, void* x, const float* cos_tab,
+                       const float* sin_tab, int64_t batch, int64_t tokens, int heads,
+                       int head_dim, int64_t sb, int64_t st_, int64_t sh, float sign,
+                       hipStream_t st);
+hipError_t launch_rope_table_1d(float* cos_tab, float* sin_tab, int64_t tokens, int head_dim,
+                                int64_t pos0, double theta, hipStream_t st);
+hipError_t launch_rope_table_3d(float* cos_tab, float* sin_tab, int64_t frames, int64_t height,
+                                int64_t width, int pt, int ph, int pw, double theta,
+                                hipStream_t st);
+
+}  // namespace nr

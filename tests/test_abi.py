@@ -1,0 +1,149 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+include/normrope.h declares, and its host-side logic (argument checks, status
+strings, workspace sizing, tuning keys) behaves as documented.  No call here
+reaches a kernel launch: each either is host-only or fails validation first.
+"""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import rmsnorm_layernorm_fwd_amd as nr
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "normrope.h")
+
+NR_OK, NR_ERR_NULLPTR, NR_ERR_SHAPE, NR_ERR_DTYPE, NR_ERR_UNSUPPORTED_N = 0, 1, 2, 3, 4
+NR_ERR_WORKSPACE, NR_ERR_HIP, NR_ERR_ALIAS, NR_ERR_TUNE = 5, 6, 7, 8
+F32, BF16 = 0, 1
+FAKE = 0x10000  # never dereferenced: every call below fails validation first
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*[A-Za-z_][\w\s\*]*?\b([a-z_][a-z0-9_]*)\s*\(", text, re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return nr._lib()
+
+
+def test_header_functions_exported(lib):
+    names = declared_functions()
+    expected = {"rmsnorm_fwd", "rmsnorm_bwd", "layernorm_fwd", "layernorm_bwd",
+                "rope_interleaved_apply", "rope_table_1d", "rope_table_3d",
+                "nr_bwd_workspace_bytes", "nr_status_str", "nr_last_hip_error", "nr_tune",
+                "nr_norm_n_max"}
+    assert expected <= set(names), names
+    out = subprocess.run(["nm", "-D", "--defined-only", nr.library_path()],
+                         capture_output=True, text=True, check=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
+    for n in names:
+        assert n in exported, f"{n} declared in normrope.h but not exported"
+        assert getattr(lib, n) is not None
+
+
+def test_status_strings(lib):
+    for code in range(9):
+        s = nr.nr_status_str(code)
+        assert s and s != "unknown status"
+    assert nr.nr_status_str(99) == "unknown status"
+    assert nr.nr_status_str(0) == "ok"
+
+
+def test_norm_n_max():
+    import torch
+    assert nr.nr_norm_n_max(torch.bfloat16) == 65536
+    assert nr.nr_norm_n_max(torch.float32) == 32768
+
+
+def test_workspace_bytes():
+    # one fp32 partial row per backward workgroup; workgroups take >= 16 rows,
+    # at most 1024 of them, none empty
+    assert nr.nr_bwd_workspace_bytes(3840, 5120, 0) == 240 * 5120 * 4
+    assert nr.nr_bwd_workspace_bytes(3840, 5120, 1) == 2 * 240 * 5120 * 4
+    assert nr.nr_bwd_workspace_bytes(65536, 5120, 0) == 1024 * 5120 * 4
+    assert nr.nr_bwd_workspace_bytes(15360, 5120, 1) == 2 * 960 * 5120 * 4
+    assert nr.nr_bwd_workspace_bytes(1, 7, 0) == 7 * 4
+    assert nr.nr_bwd_workspace_bytes(0, 7, 0) == 0
+    assert nr.nr_bwd_workspace_bytes(17, 8, 0) == 2 * 8 * 4
+
+
+def test_tune_keys(lib):
+    assert lib.nr_tune(b"bwd_d", 0) == NR_OK
+    assert lib.nr_tune(b"no_such_key", 1) == NR_ERR_TUNE
+    assert lib.nr_tune(b"fwd_w", -1) == NR_ERR_TUNE
+    assert lib.nr_tune(None, 1) == NR_ERR_TUNE
+    # a forced workgroup count changes the workspace size, 0 restores it
+    assert lib.nr_tune(b"bwd_p", 120) == NR_OK
+    try:
+        assert nr.nr_bwd_workspace_bytes(3840, 5120, 0) == 120 * 5120 * 4
+    finally:
+        assert lib.nr_tune(b"bwd_p", 0) == NR_OK
+    assert nr.nr_bwd_workspace_bytes(3840, 5120, 0) == 240 * 5120 * 4
+
+
+def test_rejected_calls_return_status(lib):
+    L = lib
+    # dtype
+    assert L.rmsnorm_fwd(7, FAKE, None, FAKE, None, 4, 8, 1e-6, 0, None) == NR_ERR_DTYPE
+    assert L.rope_interleaved_apply(2, FAKE, FAKE, FAKE, 1, 1, 1, 8, 8, 8, 8, 0, None) == NR_ERR_DTYPE
+    # null required pointers
+    assert L.rmsnorm_fwd(BF16, None, None, FAKE, None, 4, 8, 1e-6, 0, None) == NR_ERR_NULLPTR
+    assert L.rmsnorm_fwd(BF16, FAKE, None, None, None, 4, 8, 1e-6, 0, None) == NR_ERR_NULLPTR
+    assert L.rmsnorm_bwd(BF16, FAKE, FAKE, None, None, FAKE, None, 4, 8, 0, None, 0, None) == NR_ERR_NULLPTR
+    assert L.layernorm_bwd(F32, FAKE, FAKE, None, None, FAKE, FAKE, None, None, 4, 8, None, 0, None) == NR_ERR_NULLPTR
+    assert L.rope_interleaved_apply(F32, FAKE, None, FAKE, 1, 1, 1, 8, 8, 8, 8, 0, None) == NR_ERR_NULLPTR
+    assert L.rope_table_1d(None, FAKE, 4, 8, 0, 1e4, None) == NR_ERR_NULLPTR
+    # shapes
+    assert L.rmsnorm_fwd(BF16, FAKE, None, FAKE, None, 4, 0, 1e-6, 0, None) == NR_ERR_SHAPE
+    assert L.rmsnorm_fwd(BF16, FAKE, None, FAKE, None, -1, 8, 1e-6, 0, None) == NR_ERR_SHAPE
+    assert L.layernorm_fwd(F32, FAKE, None, None, FAKE, None, None, 4, -3, 1e-5, None) == NR_ERR_SHAPE
+    assert L.rope_interleaved_apply(F32, FAKE, FAKE, FAKE, 1, 4, 2, 7, 14, 7, 7, 0, None) == NR_ERR_SHAPE
+    assert L.rope_interleaved_apply(F32, FAKE, FAKE, FAKE, 1, 4, 2, 8, -1, 16, 8, 0, None) == NR_ERR_SHAPE
+    assert L.rope_table_1d(FAKE, FAKE, 4, 7, 0, 1e4, None) == NR_ERR_SHAPE
+    assert L.rope_table_1d(FAKE, FAKE, 4, 8, 0, -1.0, None) == NR_ERR_SHAPE
+    assert L.rope_table_3d(FAKE, FAKE, 2, 3, 4, 0, 2, 2, 1e4, None) == NR_ERR_SHAPE
+    # row length beyond the on-chip limit
+    assert L.rmsnorm_fwd(BF16, FAKE, None, FAKE, None, 4, 65537, 1e-6, 0, None) == NR_ERR_UNSUPPORTED_N
+    assert L.rmsnorm_fwd(F32, FAKE, None, FAKE, None, 4, 32769, 1e-6, 0, None) == NR_ERR_UNSUPPORTED_N
+    assert L.layernorm_bwd(BF16, FAKE, FAKE, None, FAKE, FAKE, FAKE, None, None, 4, 70000, None, 0, None) == NR_ERR_UNSUPPORTED_N
+    # partial overlap of an output with an input
+    assert L.rmsnorm_fwd(BF16, FAKE, None, FAKE + 2, None, 4, 8, 1e-6, 0, None) == NR_ERR_ALIAS
+    assert L.rmsnorm_bwd(BF16, FAKE, 0x90000, None, FAKE, FAKE + 16, None, 4, 8, 0, None, 0, None) == NR_ERR_ALIAS
+    assert L.rope_interleaved_apply(BF16, FAKE, FAKE, FAKE, 1, 4, 2, 8, 64, 16, 4, 0, None) == NR_ERR_ALIAS
+    # workspace missing, short or misaligned when a column gradient is wanted
+    need = nr.nr_bwd_workspace_bytes(64, 256, 0)
+    assert L.rmsnorm_bwd(F32, FAKE, 0x90000, None, FAKE, 0xA0000, FAKE, 64, 256, 0, None, 0, None) == NR_ERR_WORKSPACE
+    assert L.rmsnorm_bwd(F32, FAKE, 0x90000, None, FAKE, 0xA0000, FAKE, 64, 256, 0, 0xB0000, need - 4, None) == NR_ERR_WORKSPACE
+    assert L.rmsnorm_bwd(F32, FAKE, 0x90000, None, FAKE, 0xA0000, FAKE, 64, 256, 0, 0xB0004, need, None) == NR_ERR_WORKSPACE
+    need_ln = nr.nr_bwd_workspace_bytes(64, 256, 1)
+    assert L.layernorm_bwd(F32, FAKE, 0x90000, None, FAKE, FAKE, 0xA0000, None, FAKE, 64, 256, 0xB0000, need_ln - 1, None) == NR_ERR_WORKSPACE
+    # a forced launch shape that cannot cover the row
+    assert L.nr_tune(b"fwd_k", 1) == NR_OK
+    try:
+        assert L.rmsnorm_fwd(BF16, FAKE, None, FAKE, None, 4, 5120, 1e-6, 0, None) == NR_ERR_SHAPE
+    finally:
+        L.nr_tune(b"fwd_k", 0)
+
+
+def test_empty_forward_is_a_noop(lib):
+    # rows == 0 / tokens == 0 return before touching the device
+    assert lib.rmsnorm_fwd(BF16, None, None, None, None, 0, 8, 1e-6, 0, None) == NR_OK
+    assert lib.layernorm_fwd(F32, None, None, None, None, None, None, 0, 8, 1e-5, None) == NR_OK
+    assert lib.rope_interleaved_apply(BF16, None, None, None, 1, 0, 4, 8, 0, 0, 0, 0, None) == NR_OK
+    assert lib.rope_table_1d(None, None, 0, 8, 0, 1e4, None) == NR_OK
+    assert lib.rmsnorm_bwd(BF16, None, None, None, None, None, None, 0, 8, 0, None, 0, None) == NR_OK
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    import importlib
+    import sys
+    monkeypatch.setattr(nr, "_L", None)
+    monkeypatch.setattr(nr, "_LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(ImportError):
+        nr._lib()

@@ -1,0 +1,403 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle.
+
+Every test feeds both sides the same seeded input bytes; the oracle never
+sees a GPU output (chained checks compare against the oracle's own fp64
+chain, with a bound derived from the one extra rounding in between).  The
+bounds are written out in tests/tolerance.py.  The full-size workloads run
+in the launch configuration the benchmark times (the library's automatic
+choice).
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import rmsnorm_layernorm_fwd_amd as nr
+import workloads
+from tolerance import check, out_kind, to64, ulp_bf16
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def say(msg):
+    print(f"[case] {msg}", flush=True)
+
+
+def g(t):
+    return None if t is None else t.to(DEV)
+
+
+def sample_rows(m, k, seed, must=()):
+    rng = np.random.default_rng(seed)
+    rows = set(rng.choice(m, size=min(k, m), replace=False).tolist())
+    rows |= {0, m - 1, *[int(r) for r in must]}
+    return np.array(sorted(rows), dtype=np.int64)
+
+
+def ulp32(c):
+    a = np.abs(c)
+    _, e = np.frexp(a)
+    return np.where(a > 0, np.ldexp(1.0, e - 24), 2.0 ** -149)
+
+
+def check_table(name, cos_t, sin_t, angle):
+    c, s = to64(cos_t), to64(sin_t)
+    rc, rs = np.cos(angle), np.sin(angle)
+    assert np.all(np.abs(c - rc) <= ulp32(rc)), f"{name} cos: max err {np.max(np.abs(c - rc))}"
+    assert np.all(np.abs(s - rs) <= ulp32(rs)), f"{name} sin: max err {np.max(np.abs(s - rs))}"
+
+
+# ---------------------------------------------------------------- RMSNorm
+
+def run_rms(x, w, dy, eps, gemma, want_dw=True):
+    y, r = nr.rmsnorm_fwd(g(x), g(w), eps=eps, gemma_offset=gemma)
+    dx, dw = nr.rmsnorm_bwd(g(dy), g(x), g(w), r, gemma_offset=gemma, want_dw=want_dw)
+    torch.cuda.synchronize()
+    return y, r, dx, dw
+
+
+def check_rms_full(tag, x, w, dy, eps, gemma):
+    say(f"{tag}: rmsnorm fwd+bwd {tuple(x.shape)} {x.dtype} gemma={gemma} w={'yes' if w is not None else 'none'}")
+    y, r, dx, dw = run_rms(x, w, dy, eps, gemma, want_dw=w is not None)
+    ry, rr = oracle.rmsnorm_fwd(x, w, eps, gemma)
+    rdx, rdw = oracle.rmsnorm_bwd(dy, x, w, eps, gemma, want_dw=w is not None)
+    k = out_kind(x.dtype)
+    n = x.shape[-1]
+    check(f"{tag} y", y.reshape(-1, n), ry, k)
+    check(f"{tag} inv_rms", r.reshape(-1), rr, "stat", s=0.0)
+    check(f"{tag} dx", dx.reshape(-1, n), rdx, k)
+    if w is not None:
+        check(f"{tag} dw", dw, rdw, "col")
+
+
+def test_tiny_f32_rmsnorm():
+    inp = workloads.norm_inputs("tiny_f32")
+    check_rms_full("tiny_f32", inp["x"], inp["w"], inp["dy"], inp["eps"], inp["gemma"])
+
+
+def test_rms_gemma_3840x5120():
+    inp = workloads.norm_inputs("rms_gemma_3840x5120")
+    check_rms_full("rms_gemma_3840x5120", inp["x"], inp["w"], inp["dy"], inp["eps"], True)
+
+
+# ---------------------------------------------------------------- LayerNorm
+
+def check_ln_full(tag, x, gm, bt, dy, eps):
+    say(f"{tag}: layernorm fwd+bwd {tuple(x.shape)} {x.dtype} gamma={gm is not None} beta={bt is not None}")
+    y, mu, rs = nr.layernorm_fwd(g(x), g(gm), g(bt), eps=eps)
+    dx, dg, db = nr.layernorm_bwd(g(dy), g(x), g(gm), mu, rs)
+    torch.cuda.synchronize()
+    ry, rmu, rrs = oracle.layernorm_fwd(x, gm, bt, eps)
+    rdx, rdg, rdb = oracle.layernorm_bwd(dy, x, gm, eps)
+    k = out_kind(x.dtype)
+    n = x.shape[-1]
+    x64 = to64(x).reshape(-1, n)
+    check(f"{tag} y", y.reshape(-1, n), ry, k)
+    check(f"{tag} mean", mu.reshape(-1), rmu, "stat", s=np.sqrt(np.mean(x64 * x64, axis=1)))
+    check(f"{tag} rstd", rs.reshape(-1), rrs, "stat", s=0.0)
+    check(f"{tag} dx", dx.reshape(-1, n), rdx, k)
+    check(f"{tag} dgamma", dg, rdg, "col")
+    check(f"{tag} dbeta", db, rdb, "col")
+
+
+def test_ln_affine_15360x5120():
+    inp = workloads.norm_inputs("ln_affine_15360x5120")
+    check_ln_full("ln_affine_15360x5120", inp["x"], inp["w"], inp["b"], inp["dy"], inp["eps"])
+
+
+# ---------------------------------------------------------------- RoPE
+
+def gpu_table(spec, tokens, head_dim):
+    if spec["kind"] == "1d":
+        return nr.rope_table_1d(tokens, head_dim, spec.get("pos0", 0), spec["theta"])
+    return nr.rope_table_3d(spec["grid"], spec["pairs"], spec["theta"])
+
+
+def check_rope_full(tag, x, spec):
+    b, t, h, d = x.shape
+    say(f"{tag}: rope table + fwd/inverse {tuple(x.shape)} {x.dtype} table={spec['kind']}")
+    ct, st = gpu_table(spec, t, d)
+    ang = oracle.rope_angles(spec, t, d)
+    torch.cuda.synchronize()
+    check_table(tag, ct, st, ang)
+    k = out_kind(x.dtype)
+    for inv in (False, True):
+        xg = g(x).clone()
+        nr.rope_interleaved_apply(xg, ct, st, inverse=inv)
+        torch.cuda.synchronize()
+        ref = oracle.rope_apply(x, ang, inv)
+        check(f"{tag} {'inverse' if inv else 'forward'}", xg.reshape(-1, d), ref.reshape(-1, d), k)
+    # forward then inverse returns the input; the bound allows the rounding of
+    # the intermediate (half an ulp of each element of the rotated pair)
+    xg = g(x).clone()
+    nr.rope_interleaved_apply(xg, ct, st)
+    nr.rope_interleaved_apply(xg, ct, st, inverse=True)
+    torch.cuda.synchronize()
+    x64 = to64(x).reshape(-1, 2)
+    pair = np.repeat(np.sqrt((x64 ** 2).sum(axis=1)), 2)
+    extra = 0.0 if x.dtype == torch.float32 else (2 ** -8) * math.sqrt(2) * 1.01 * pair
+    check(f"{tag} round trip", xg.reshape(-1), to64(x).reshape(-1), k, s=0.0,
+          extra=extra if x.dtype == torch.bfloat16 else 1e-6 * pair)
+
+
+def test_tiny_f32_rope():
+    inp = workloads.rope_inputs("tiny_f32")
+    check_rope_full("tiny_f32", inp["q"], inp["table"])
+
+
+@pytest.mark.parametrize("which", ["q", "k"])
+def test_rope3d_15360x40x128(which):
+    inp = workloads.rope_inputs("rope3d_15360x40x128")
+    check_rope_full(f"rope3d_15360x40x128 {which}", inp[which], inp["table"])
+
+
+# ---------------------------------------------------------------- long sequence
+
+@pytest.fixture(scope="module")
+def longseq():
+    inp = workloads.norm_inputs("longseq_65536x5120")
+    spec = workloads.WORKLOADS["longseq_65536x5120"]["rope"]
+    rows = sample_rows(65536, 48, 5, must=inp["outlier_rows"][:16].tolist())
+    return inp, spec, rows
+
+
+def test_longseq_rmsnorm(longseq):
+    inp, _, rows = longseq
+    x, w, dy, eps = inp["x"], inp["w"], inp["dy"], inp["eps"]
+    say("longseq_65536x5120: rmsnorm fwd+bwd, sampled rows + full dw")
+    y, r, dx, dw = run_rms(x, w, dy, eps, False)
+    ry, rr = oracle.rmsnorm_fwd(x[rows], w, eps)
+    rdx, _ = oracle.rmsnorm_bwd(dy[rows], x[rows], w, eps, want_dw=False)
+    _, rdw = oracle.rmsnorm_bwd(dy, x, w, eps, want_dx=False)
+    idx = torch.from_numpy(rows).to(DEV)
+    check("longseq y", y[idx], ry, "bf16")
+    check("longseq inv_rms", r[idx], rr, "stat", s=0.0)
+    check("longseq dx", dx[idx], rdx, "bf16")
+    check("longseq dw", dw, rdw, "col")
+
+
+def test_longseq_rope(longseq):
+    inp, spec, rows = longseq
+    d, h = 128, 40
+    ang = oracle.rope_angles(spec["table"], 65536, d)
+    say("longseq_65536x5120: rope table 1-D 65536 tokens")
+    ct, st = gpu_table(spec["table"], 65536, d)
+    torch.cuda.synchronize()
+    check_table("longseq", ct, st, ang)
+    for name, src, inv in (("x forward", inp["x"], False), ("dout inverse", inp["dy"], True)):
+        say(f"longseq_65536x5120: rope {name}")
+        xg = g(src).view(1, 65536, h, d).clone()
+        nr.rope_interleaved_apply(xg, ct, st, inverse=inv)
+        torch.cuda.synchronize()
+        idx = torch.from_numpy(rows).to(DEV)
+        sub = src[rows].view(1, len(rows), h, d)
+        ref = oracle.rope_apply(sub, ang[rows], inv)
+        check(f"longseq rope {name}", xg[0, idx].reshape(-1, d), ref.reshape(-1, d), "bf16")
+
+
+def test_longseq_chain(longseq):
+    """norm -> RoPE forward, and RoPE inverse -> norm backward, against the
+    oracle's fp64 chain.  The GPU rounds the intermediate to bf16 once; the
+    bound adds what that rounding can move the final value by."""
+    inp, spec, rows = longseq
+    x, w, dout, eps = inp["x"], inp["w"], inp["dy"], inp["eps"]
+    d, h = 128, 40
+    idx = torch.from_numpy(rows).to(DEV)
+    ang = oracle.rope_angles(spec["table"], 65536, d)[rows]
+    say("longseq_65536x5120: chain rmsnorm -> rope")
+    ct, st = gpu_table(spec["table"], 65536, d)
+    y, r = nr.rmsnorm_fwd(g(x), g(w), eps=eps)
+    nr.rope_interleaved_apply(y.view(1, 65536, h, d), ct, st)
+    torch.cuda.synchronize()
+    ry, _ = oracle.rmsnorm_fwd(x[rows], w, eps)
+    ref = oracle.rope_apply(torch.from_numpy(ry).view(1, len(rows), h, d), ang)
+    pair = np.abs(ry).reshape(-1, 2).sum(axis=1)
+    extra = (2 ** -8) * 1.01 * np.repeat(pair, 2).reshape(len(rows), -1)
+    check("chain fwd", y[idx], ref.reshape(len(rows), -1), "bf16", extra=extra)
+
+    say("longseq_65536x5120: chain rope inverse -> rmsnorm bwd")
+    dyg = g(dout).view(1, 65536, h, d).clone()
+    nr.rope_interleaved_apply(dyg, ct, st, inverse=True)
+    dx, _ = nr.rmsnorm_bwd(dyg.view(65536, -1), g(x), g(w), r, want_dw=False)
+    torch.cuda.synchronize()
+    dy64 = oracle.rope_apply(dout[rows].view(1, len(rows), h, d), ang, inverse=True).reshape(len(rows), -1)
+    xs = x[rows].double()
+    rdx, _ = oracle.rmsnorm_bwd(torch.from_numpy(dy64), xs, w, eps, want_dw=False)
+    _, rr = oracle.rmsnorm_fwd(xs, None, eps)
+    gg = np.abs(dy64 * to64(w)[None, :])
+    xh = np.abs(to64(xs) * rr[:, None])
+    extra = (2 ** -8) * 1.01 * rr[:, None] * (gg + xh * np.mean(gg * xh, axis=1, keepdims=True))
+    check("chain bwd dx", dx[idx], rdx, "bf16", extra=extra)
+
+
+# ---------------------------------------------------------------- edge cases
+
+NORM_EDGES = [
+    # (rows, n, dtype)
+    (1, 1, torch.float32), (3, 7, torch.bfloat16), (257, 64, torch.float32),
+    (5, 255, torch.bfloat16), (64, 256, torch.bfloat16), (33, 1000, torch.float32),
+    (17, 5128, torch.bfloat16), (9, 8191, torch.bfloat16), (4, 12288, torch.float32),
+    (3, 32768, torch.float32), (3, 65536, torch.bfloat16), (1000, 40, torch.bfloat16),
+]
+
+
+@pytest.mark.parametrize("rows,n,dtype", NORM_EDGES)
+@pytest.mark.parametrize("gemma", [False, True])
+def test_rms_edges(rows, n, dtype, gemma):
+    seed = 2000 + rows * 7 + n
+    x = workloads.normal((rows, n), seed, dtype)
+    w = workloads.normal((n,), seed + 1, dtype, std=0.1, mean=0.0 if gemma else 1.0)
+    dy = workloads.normal((rows, n), seed + 2, dtype)
+    check_rms_full(f"rms edge {rows}x{n}", x, w, dy, 1e-6, gemma)
+
+
+@pytest.mark.parametrize("rows,n,dtype", NORM_EDGES)
+def test_ln_edges(rows, n, dtype):
+    seed = 3000 + rows * 7 + n
+    x = workloads.normal((rows, n), seed, dtype, mean=0.5, std=2.0)
+    gm = workloads.normal((n,), seed + 1, dtype, mean=1.0, std=0.1)
+    bt = workloads.normal((n,), seed + 2, dtype, std=0.1)
+    dy = workloads.normal((rows, n), seed + 3, dtype)
+    check_ln_full(f"ln edge {rows}x{n}", x, gm, bt, dy, 1e-5)
+
+
+def test_non_affine_and_constant_rows():
+    x = workloads.normal((40, 96), 4001, torch.bfloat16)
+    dy = workloads.normal((40, 96), 4002, torch.bfloat16)
+    check_rms_full("rms no weight", x, None, dy, 1e-6, False)
+    x[3] = 1.5  # constant row: LayerNorm gives beta (zero deviation)
+    check_ln_full("ln no gamma/beta", x, None, None, dy, 1e-5)
+    bt = workloads.normal((96,), 4003, torch.bfloat16)
+    say("ln constant row")
+    y, _, _ = nr.layernorm_fwd(g(x), None, g(bt), eps=1e-5)
+    torch.cuda.synchronize()
+    assert torch.equal(y[3].cpu(), bt)
+
+
+def test_in_place_and_unaligned():
+    rows, n = 70, 520
+    x = workloads.normal((rows, n), 4100, torch.bfloat16)
+    w = workloads.normal((n,), 4101, torch.bfloat16, mean=1.0, std=0.1)
+    dy = workloads.normal((rows, n), 4102, torch.bfloat16)
+    ry, _ = oracle.rmsnorm_fwd(x, w, 1e-6)
+    rdx, rdw = oracle.rmsnorm_bwd(dy, x, w, 1e-6)
+    say("rms in place y == x, dx == dy")
+    xg = g(x)
+    _, r = nr.rmsnorm_fwd(g(x), g(w), eps=1e-6)
+    dyg = g(dy)
+    nr.rmsnorm_bwd(dyg, xg, g(w), r, dx=dyg)
+    nr.rmsnorm_fwd(xg, g(w), eps=1e-6, y=xg)
+    torch.cuda.synchronize()
+    check("in-place y", xg, ry, "bf16")
+    check("in-place dx", dyg, rdx, "bf16")
+    say("rms unaligned rows (element-wise path)")
+    buf = torch.empty(rows * n + 1, dtype=torch.bfloat16, device=DEV)
+    xu = buf[1:].view(rows, n)
+    xu.copy_(g(x))
+    buf2 = torch.empty(rows * n + 3, dtype=torch.bfloat16, device=DEV)
+    yu = buf2[3:].view(rows, n)
+    _, ru = nr.rmsnorm_fwd(xu, g(w), eps=1e-6, y=yu)
+    dbuf = torch.empty(rows * n + 1, dtype=torch.bfloat16, device=DEV)
+    dyu = dbuf[1:].view(rows, n)
+    dyu.copy_(g(dy))
+    dxu, dwu = nr.rmsnorm_bwd(dyu, xu, g(w), ru)
+    torch.cuda.synchronize()
+    check("unaligned y", yu, ry, "bf16")
+    check("unaligned dx", dxu, rdx, "bf16")
+    check("unaligned dw", dwu, rdw, "col")
+
+
+def test_empty_batch():
+    say("rows == 0")
+    x = torch.empty((0, 64), dtype=torch.bfloat16, device=DEV)
+    w = torch.ones(64, dtype=torch.bfloat16, device=DEV)
+    y, r = nr.rmsnorm_fwd(x, w)
+    dw = torch.full((64,), 7.0, device=DEV)
+    nr.rmsnorm_bwd(x, x, w, r, dw=dw)
+    dg = torch.full((64,), 7.0, device=DEV)
+    db = torch.full((64,), 7.0, device=DEV)
+    _, mu, rs = nr.layernorm_fwd(x, w, w)
+    nr.layernorm_bwd(x, x, w, mu, rs, dgamma=dg, dbeta=db)
+    torch.cuda.synchronize()
+    assert y.shape == (0, 64)
+    assert torch.all(dw == 0) and torch.all(dg == 0) and torch.all(db == 0)
+
+
+@pytest.mark.parametrize("kind", ["rms", "ln"])
+def test_backward_bitwise_deterministic(kind):
+    inp = workloads.norm_inputs("rms_gemma_3840x5120")
+    x, w, dy = g(inp["x"]), g(inp["w"]), g(inp["dy"])
+    say(f"{kind} bwd determinism 3840x5120")
+    outs = []
+    for _ in range(2):
+        if kind == "rms":
+            _, r = nr.rmsnorm_fwd(x, w, gemma_offset=True)
+            outs.append(nr.rmsnorm_bwd(dy, x, w, r, gemma_offset=True))
+        else:
+            _, mu, rs = nr.layernorm_fwd(x, w, w)
+            outs.append(nr.layernorm_bwd(dy, x, w, mu, rs))
+    torch.cuda.synchronize()
+    for a, b in zip(outs[0], outs[1]):
+        assert torch.equal(a, b)
+
+
+ROPE_EDGES = [
+    # (batch, tokens, heads, head_dim, dtype, layout)
+    (1, 5, 1, 2, torch.float32, "packed"),
+    (2, 9, 3, 6, torch.bfloat16, "packed"),
+    (1, 33, 40, 128, torch.bfloat16, "packed"),
+    (2, 17, 8, 64, torch.float32, "packed"),
+    (1, 12, 5, 256, torch.bfloat16, "packed"),
+    (1, 7, 96, 128, torch.bfloat16, "packed"),       # several passes over the heads
+    (2, 10, 4, 64, torch.bfloat16, "bhtd"),          # heads-major storage, strided view
+    (1, 11, 3, 32, torch.float32, "unaligned"),      # element-wise path
+    (1, 13, 2, 10, torch.bfloat16, "padded"),        # head stride > head_dim
+]
+
+
+@pytest.mark.parametrize("b,t,h,d,dtype,layout", ROPE_EDGES)
+def test_rope_edges(b, t, h, d, dtype, layout):
+    x = workloads.normal((b, t, h, d), 5000 + t * h + d, dtype)
+    pos0 = 1000 if layout == "padded" else 0
+    ang = oracle.rope_angles_1d(t, d, pos0, 10000.0)
+    say(f"rope edge {b}x{t}x{h}x{d} {dtype} {layout}")
+    ct, st = nr.rope_table_1d(t, d, pos0, 10000.0)
+    for inv in (False, True):
+        if layout == "packed":
+            xg = g(x).clone()
+        elif layout == "bhtd":
+            xg = g(x).permute(0, 2, 1, 3).contiguous().permute(0, 2, 1, 3)
+        elif layout == "unaligned":
+            buf = torch.empty(x.numel() + 1, dtype=dtype, device=DEV)
+            xg = buf[1:].view(x.shape)
+            xg.copy_(g(x))
+        else:
+            buf = torch.zeros((b, t, h, d + 6), dtype=dtype, device=DEV)
+            xg = buf[..., :d]
+            xg.copy_(g(x))
+        nr.rope_interleaved_apply(xg, ct, st, inverse=inv)
+        torch.cuda.synchronize()
+        if layout == "padded":
+            assert torch.all(buf[..., d:] == 0), "rope wrote outside the head vectors"
+        ref = oracle.rope_apply(x, ang, inv)
+        check(f"rope edge {layout} inv={inv}", xg.reshape(-1, d), ref.reshape(-1, d), out_kind(dtype))
+
+
+def test_rope_table_3d_small():
+    spec = dict(kind="3d", grid=(3, 4, 5), pairs=(5, 4, 3), theta=10000.0)
+    say("rope 3-D table 3x4x5 pairs 5/4/3")
+    ct, st = gpu_table(spec, 60, 24)
+    torch.cuda.synchronize()
+    check_table("3d small", ct, st, oracle.rope_angles(spec, 60, 24))
+
+
+def test_errors_raise():
+    x = torch.zeros((2, 3, 4, 7), dtype=torch.bfloat16, device=DEV)
+    c = torch.zeros((3, 3), device=DEV)
+    with pytest.raises((nr.NormRopeError, ValueError)):
+        nr.rope_interleaved_apply(x, c, c)
+    with pytest.raises(nr.NormRopeError):
+        nr.rmsnorm_fwd(torch.zeros((2, 70000), dtype=torch.bfloat16, device=DEV))
