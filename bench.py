@@ -1,0 +1,336 @@
+"""Benchmark: achieved HBM bandwidth of the fused norm fwd+bwd and RoPE path.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+One step runs every operation of the path once over one batch that is
+already resident in HBM, by default on the long-sequence workload
+(x [65536, 5120] bf16, viewed as 65536 tokens x 40 heads x 128 for RoPE):
+
+  rmsnorm_fwd(x) -> y, inv_rms        rope forward on y (in place)
+  rope inverse on dout (in place)     rmsnorm_bwd(dout, x) -> dx, dw
+  layernorm_fwd(x) -> y2, mean, rstd  layernorm_bwd(dout, x) -> dx2, dgamma, dbeta
+
+The cos/sin table is built once per shape, outside the steps.  `value` is
+the algorithmic bytes of one step (each tensor read or written once; weights
+once per call; statistics and column gradients in fp32; no workspace) divided
+by the measured time per step.  The other workloads (--workload) time their
+own operations the same way.  One JSON line goes to stdout.
+
+--copy-probe runs only a plain device copy of known size: the reference the
+HBM byte counters are scaled by.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "achieved HBM GB/s (and % of peak) for fused norm fwd+bwd and RoPE"
+PEAK_GBS = 8000.0  # MI355X HBM3E
+PROFILES = os.path.join(ROOT, "profiles")
+KERNEL_SOURCES = ["rmsnorm_layernorm_fwd_amd/csrc/" + f for f in
+                  ("nr_device.hpp", "norm_fwd.hip", "norm_bwd.hip", "rope_kernels.hip", "api.hip")]
+
+
+# ---------------------------------------------------------------- bytes
+
+def rms_fwd_bytes(m, n, e=2):
+    return 2 * e * m * n + e * n + 4 * m
+
+
+def rms_bwd_bytes(m, n, e=2):
+    return 3 * e * m * n + e * n + 4 * m + 4 * n
+
+
+def ln_fwd_bytes(m, n, e=2):
+    return 2 * e * m * n + 2 * e * n + 8 * m
+
+
+def ln_bwd_bytes(m, n, e=2):
+    return 3 * e * m * n + e * n + 8 * m + 8 * n
+
+
+def rope_bytes(t, h, d, e=2):
+    return 2 * e * t * h * d + 2 * 4 * t * (d // 2)
+
+
+def source_hash():
+    hsh = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            hsh.update(fh.read())
+    return hsh.hexdigest()[:16]
+
+
+# ---------------------------------------------------------------- workloads
+
+def build_ops(name, dev):
+    """Returns (ops, description): ops = [(label, kernel_name, fn, bytes)]."""
+    import torch
+
+    import rmsnorm_layernorm_fwd_amd as nr
+    import workloads
+
+    g = lambda t: None if t is None else t.to(dev)
+    ops = []
+    if name == "longseq_65536x5120":
+        inp = workloads.norm_inputs(name)
+        ln_params = workloads.norm_inputs("ln_affine_15360x5120")
+        m, n = inp["x"].shape
+        h, d = 40, 128
+        x, w, dout = g(inp["x"]), g(inp["w"]), g(inp["dy"])
+        gm, bt = g(ln_params["w"]), g(ln_params["b"])
+        y, dx, y2, dx2 = (torch.empty_like(x) for _ in range(4))
+        r = torch.empty(m, dtype=torch.float32, device=dev)
+        mu, rs = torch.empty_like(r), torch.empty_like(r)
+        dw, dg, db = (torch.empty(n, dtype=torch.float32, device=dev) for _ in range(3))
+        ws = torch.empty(max(nr.nr_bwd_workspace_bytes(m, n, 1), 16), dtype=torch.uint8, device=dev)
+        ct, st = nr.rope_table_1d(m, d, 0, 10000.0, device=dev)
+        yv, gv = y.view(1, m, h, d), dout.view(1, m, h, d)
+        ops = [
+            ("rmsnorm_fwd", "norm_fwd[rms]", lambda: nr.rmsnorm_fwd(x, w, 1e-6, y=y, inv_rms=r),
+             rms_fwd_bytes(m, n)),
+            ("rope_fwd", "rope_apply_kernel", lambda: nr.rope_interleaved_apply(yv, ct, st),
+             rope_bytes(m, h, d)),
+            ("rope_inverse", "rope_apply_kernel",
+             lambda: nr.rope_interleaved_apply(gv, ct, st, inverse=True), rope_bytes(m, h, d)),
+            ("rmsnorm_bwd", "norm_bwd_rows[rms]+colreduce",
+             lambda: nr.rmsnorm_bwd(dout, x, w, r, dx=dx, dw=dw, workspace=ws), rms_bwd_bytes(m, n)),
+            ("layernorm_fwd", "norm_fwd[ln]",
+             lambda: nr.layernorm_fwd(x, gm, bt, 1e-5, y=y2, mean=mu, rstd=rs), ln_fwd_bytes(m, n)),
+            ("layernorm_bwd", "norm_bwd_rows[ln]+colreduce",
+             lambda: nr.layernorm_bwd(dout, x, gm, mu, rs, dx=dx2, dgamma=dg, dbeta=db, workspace=ws),
+             ln_bwd_bytes(m, n)),
+        ]
+        desc = dict(workload=name, rows=m, hidden=n, heads=h, head_dim=d, io_dtype="bf16",
+                    positions="1-D 0..65535, theta 1e4", rms_eps=1e-6, ln_eps=1e-5,
+                    outlier_rows=int(len(inp["outlier_rows"])))
+    elif name == "rms_gemma_3840x5120":
+        inp = workloads.norm_inputs(name)
+        m, n = inp["x"].shape
+        x, w, dy = g(inp["x"]), g(inp["w"]), g(inp["dy"])
+        y, dx = torch.empty_like(x), torch.empty_like(x)
+        r = torch.empty(m, dtype=torch.float32, device=dev)
+        dw = torch.empty(n, dtype=torch.float32, device=dev)
+        ws = torch.empty(max(nr.nr_bwd_workspace_bytes(m, n, 0), 16), dtype=torch.uint8, device=dev)
+        ops = [
+            ("rmsnorm_fwd", "norm_fwd[rms]",
+             lambda: nr.rmsnorm_fwd(x, w, 1e-6, True, y=y, inv_rms=r), rms_fwd_bytes(m, n)),
+            ("rmsnorm_bwd", "norm_bwd_rows[rms]+colreduce",
+             lambda: nr.rmsnorm_bwd(dy, x, w, r, True, dx=dx, dw=dw, workspace=ws), rms_bwd_bytes(m, n)),
+        ]
+        desc = dict(workload=name, rows=m, hidden=n, io_dtype="bf16", gemma_offset=True)
+    elif name == "ln_affine_15360x5120":
+        inp = workloads.norm_inputs(name)
+        m, n = inp["x"].shape
+        x, gm, bt, dy = g(inp["x"]), g(inp["w"]), g(inp["b"]), g(inp["dy"])
+        y, dx = torch.empty_like(x), torch.empty_like(x)
+        mu = torch.empty(m, dtype=torch.float32, device=dev)
+        rs = torch.empty_like(mu)
+        dg, db = (torch.empty(n, dtype=torch.float32, device=dev) for _ in range(2))
+        ws = torch.empty(max(nr.nr_bwd_workspace_bytes(m, n, 1), 16), dtype=torch.uint8, device=dev)
+        ops = [
+            ("layernorm_fwd", "norm_fwd[ln]",
+             lambda: nr.layernorm_fwd(x, gm, bt, 1e-5, y=y, mean=mu, rstd=rs), ln_fwd_bytes(m, n)),
+            ("layernorm_bwd", "norm_bwd_rows[ln]+colreduce",
+             lambda: nr.layernorm_bwd(dy, x, gm, mu, rs, dx=dx, dgamma=dg, dbeta=db, workspace=ws),
+             ln_bwd_bytes(m, n)),
+        ]
+        desc = dict(workload=name, rows=m, hidden=n, io_dtype="bf16")
+    elif name == "rope3d_15360x40x128":
+        inp = workloads.rope_inputs(name)
+        b, t, h, d = inp["shape"]
+        q, k = g(inp["q"]), g(inp["k"])
+        ct, st = nr.rope_table_3d(inp["table"]["grid"], inp["table"]["pairs"], 10000.0, device=dev)
+        ops = [
+            ("rope_fwd_q", "rope_apply_kernel", lambda: nr.rope_interleaved_apply(q, ct, st), rope_bytes(t, h, d)),
+            ("rope_fwd_k", "rope_apply_kernel", lambda: nr.rope_interleaved_apply(k, ct, st), rope_bytes(t, h, d)),
+            ("rope_inverse_q", "rope_apply_kernel",
+             lambda: nr.rope_interleaved_apply(q, ct, st, inverse=True), rope_bytes(t, h, d)),
+            ("rope_inverse_k", "rope_apply_kernel",
+             lambda: nr.rope_interleaved_apply(k, ct, st, inverse=True), rope_bytes(t, h, d)),
+        ]
+        desc = dict(workload=name, tokens=t, heads=h, head_dim=d, io_dtype="bf16",
+                    positions="3-D 16x24x40, pairs 22/21/21, theta 1e4")
+    else:
+        raise SystemExit(f"unknown workload {name}")
+    return ops, desc
+
+
+# ---------------------------------------------------------------- traffic
+
+def read_traffic(kernel_label, workload):
+    """HBM bytes per launch from the committed counter summary, or None when
+    missing or taken on different kernel sources."""
+    path = os.path.join(PROFILES, f"traffic_{workload}.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    with open(path) as fh:
+        for line in fh:
+            if "=" in line and not line.startswith("#"):
+                k, v = line.split("=", 1)
+                kv[k.strip()] = v.strip()
+    if kv.get("source_hash") != source_hash():
+        return None
+    v = kv.get(f"bytes_per_launch.{kernel_label}")
+    return float(v) if v else None
+
+
+# ---------------------------------------------------------------- CPU baseline
+
+def cpu_baseline(seconds):
+    """The fp64 oracle, as it stands, on the host cores: the same step on the
+    first rows of the long-sequence workload, repeated for about `seconds`."""
+    import torch
+
+    import oracle
+    import workloads
+
+    rows = 1024
+    inp = workloads.norm_inputs("longseq_65536x5120")
+    lnp = workloads.norm_inputs("ln_affine_15360x5120")
+    x, w, dy = inp["x"][:rows].clone(), inp["w"], inp["dy"][:rows].clone()
+    gm, bt = lnp["w"], lnp["b"]
+    n, h, d = x.shape[1], 40, 128
+    ang = oracle.rope_angles_1d(rows, d, 0, 10000.0)
+    per_pass = (rms_fwd_bytes(rows, n) + 2 * rope_bytes(rows, h, d) + rms_bwd_bytes(rows, n)
+                + ln_fwd_bytes(rows, n) + ln_bwd_bytes(rows, n))
+    oracle.lib()
+    passes, t0 = 0, time.perf_counter()
+    while True:
+        y, _ = oracle.rmsnorm_fwd(x, w, 1e-6)
+        oracle.rope_apply(torch.from_numpy(y).view(1, rows, h, d), ang)
+        oracle.rope_apply(dy.view(1, rows, h, d), ang, inverse=True)
+        oracle.rmsnorm_bwd(dy, x, w, 1e-6)
+        oracle.layernorm_fwd(x, gm, bt, 1e-5)
+        oracle.layernorm_bwd(dy, x, gm, 1e-5)
+        passes += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    cores = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    return dict(value=round(per_pass * passes / el / 1e9, 4), unit="GB/s", cores=cores, kind="oracle",
+                sample=(f"the long-sequence step (rmsnorm fwd, rope fwd, rope inverse, rmsnorm bwd, "
+                        f"layernorm fwd, layernorm bwd) on rows 0..{rows - 1} of 65536, {passes} passes "
+                        f"in {el:.1f} s, fp64, OpenMP over rows; bytes counted as for the GPU"))
+
+
+# ---------------------------------------------------------------- main
+
+def copy_probe(dev):
+    import torch
+    nbytes = 1 << 30
+    a = torch.empty(nbytes // 2, dtype=torch.bfloat16, device=dev).fill_(1.0)
+    b = torch.empty_like(a)
+    for _ in range(5):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes_read": nbytes, "copy_probe_bytes_written": nbytes, "launches": 5}))
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="longseq_65536x5120",
+                    choices=["longseq_65536x5120", "rms_gemma_3840x5120", "ln_affine_15360x5120",
+                             "rope3d_15360x40x128"])
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(the path shards by tokens; see the sharding note in the design document)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    if args.copy_probe:
+        copy_probe(dev)
+        return
+
+    ops, desc = build_ops(args.workload, dev)
+    stream = torch.cuda.current_stream(dev)
+    step_bytes = sum(b for _, _, _, b in ops)
+
+    for _ in range(args.warmup):
+        for _, _, fn, _ in ops:
+            fn()
+    torch.cuda.synchronize()
+
+    # per-op events on the stream the kernels are launched on
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in ops] for _ in range(args.steps)]
+    t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record(stream)
+    for s in range(args.steps):
+        for i, (_, _, fn, _) in enumerate(ops):
+            ev[s][i][0].record(stream)
+            fn()
+            ev[s][i][1].record(stream)
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    total_ms = t_start.elapsed_time(t_end)
+    ms_per_step = total_ms / args.steps
+
+    per_op = {}
+    for i, (label, kname, _, b) in enumerate(ops):
+        times = [ev[s][i][0].elapsed_time(ev[s][i][1]) for s in range(args.steps)]
+        mean = sum(times) / len(times)
+        per_op[label] = dict(kernel=kname, bytes=b, ms_mean=round(mean, 5), ms_min=round(min(times), 5),
+                             gbs=round(b / (mean * 1e-3) / 1e9, 1),
+                             frac_of_peak=round(b / (mean * 1e-3) / 1e9 / PEAK_GBS, 4))
+    # dominant kernel: of the single-kernel operations, the kernel (one
+    # instantiation, one shape) with the largest share of the step's time;
+    # its per-launch figures average over all its launches in the step
+    kern = {}
+    for i, (label, kname, _, b) in enumerate(ops):
+        if "+" in kname:
+            continue
+        k = kern.setdefault(kname, dict(launches=0, bytes=0, ms=0.0, ops=[]))
+        k["launches"] += 1
+        k["bytes"] += b
+        k["ms"] += per_op[label]["ms_mean"]
+        k["ops"].append(label)
+    dname = max(kern, key=lambda k: kern[k]["ms"])
+    dk = kern[dname]
+    bpl, mspl = dk["bytes"] / dk["launches"], dk["ms"] / dk["launches"]
+    achieved = bpl / (mspl * 1e-3) / 1e9
+    roofline = dict(bound="hbm", achieved=round(achieved, 1), peak=PEAK_GBS, unit="GB/s",
+                    frac=round(achieved / PEAK_GBS, 4), traffic=read_traffic(dname, args.workload),
+                    kernel=dname, ops=dk["ops"], bytes_per_launch=int(bpl),
+                    ms_per_launch=round(mspl, 5), share_of_step=round(dk["ms"] / ms_per_step, 3))
+
+    value = step_bytes / (ms_per_step * 1e-3) / 1e9
+    out = {
+        "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic (seeded normal draws shaped like the Helios 14B activations; no model weights)",
+        "config": dict(desc, step_bytes=step_bytes, frac_of_peak=round(value / PEAK_GBS, 4)),
+        "roofline": roofline,
+        "ops": per_op,
+    }
+    if not args.no_cpu_baseline and args.workload == "longseq_65536x5120":
+        out["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

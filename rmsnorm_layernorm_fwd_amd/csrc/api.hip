@@ -57,7 +57,7 @@ int pick_at_least(int64_t need, const int* set, int n) {
   return 0;
 }
 
-const int kFwdK[] = {1, 2, 4, 6, 8, 10};
+const int kFwdK[] = {1, 2, 4, 5, 6, 8, 10};
 const int kBwdK[] = {1, 2, 4, 8};
 const int kBwdD[] = {1, 2, 4, 8};
 const int kRopeK[] = {1, 2, 4, 6, 8, 10};
@@ -84,32 +84,43 @@ nr_status_t check_norm_shape(nr_dtype_t dt, int64_t rows, int64_t n) {
 nr_status_t plan_fwd(nr_dtype_t dt, int64_t n, bool aligned, FwdPlan* pl) {
   const int64_t nchunk = (n + vec_elems(dt) - 1) / vec_elems(dt);
   const int64_t need = (nchunk + 63) / 64;
+  // Short rows: a wavefront per row, no barrier.  Rows of 6..16 chunk slots
+  // (up to 8192 bf16 / 4096 fp32): two waves per row and about 5 chunks per
+  // lane, which keeps the row resident in fewer VGPRs (LayerNorm holds x,
+  // gamma and beta) and measured fastest at 5120 bf16.  Longer rows: up to 8
+  // chunks per lane and as many waves as needed.
   int W, K;
-  if (need <= 10) {
+  if (need <= 4) {
     W = 1;
-    K = pick_at_least(need, kFwdK, 6);
+    K = pick_at_least(need, kFwdK, 7);
+  } else if (need <= 16) {
+    W = 2;
+    K = pick_at_least((need + 1) / 2, kFwdK, 6);
   } else {
     W = static_cast<int>((need + 7) / 8);
-    K = pick_at_least((need + W - 1) / W, kFwdK, 5);  // K <= 8 when W > 1
+    K = pick_at_least((need + W - 1) / W, kFwdK, 6);  // K <= 8 when W > 1
   }
   if (tune(FWD_W) > 0) W = tune(FWD_W);
   if (tune(FWD_K) > 0) K = tune(FWD_K);
   int R = W == 1 ? 4 : (W == 2 ? 2 : 1);
   if (tune(FWD_R) > 0) R = tune(FWD_R);
-  if (W < 1 || W > 16 || !in_set(K, kFwdK, 6) || (W > 1 && K > 8)) return NR_ERR_SHAPE;
+  if (W < 1 || W > 16 || !in_set(K, kFwdK, 7) || (W > 1 && K > 8)) return NR_ERR_SHAPE;
   if (static_cast<int64_t>(64) * W * K < nchunk) return NR_ERR_SHAPE;
   if (R < 1 || (W == 1 && R > 4) || 64 * W * R > 1024) return NR_ERR_SHAPE;
   *pl = FwdPlan{W, K, R, aligned};
   return NR_OK;
 }
 
-// Backward workgroups: each takes rows_per_block consecutive rows.  Enough
-// rows per workgroup (16 by default) keep the fp32 partial rows small next to
-// the row traffic; at most 1024 workgroups.  Depends on rows only, so the
-// summation order, and the workspace size, are the same on every device.
+// Backward workgroups.  Each handles about rows/P rows (dealt out round
+// robin in batches of D).  At least 16 rows per workgroup keep the fp32
+// partial rows small next to the row traffic; at most 512 workgroups, i.e.
+// two resident 10-wave workgroups on each of MI355X's 256 CUs for 5120-wide
+// bf16 rows (more gave a second, partial round of workgroups and measured
+// slower).  Depends on rows only, so the summation order and the workspace
+// size are the same on every device.
 void bwd_grid(int64_t rows, int64_t* P_out, int64_t* rpb_out) {
   const int64_t rows_min = tune(BWD_ROWS_MIN) > 0 ? tune(BWD_ROWS_MIN) : 16;
-  const int64_t pcap = tune(BWD_P) > 0 ? tune(BWD_P) : 1024;
+  const int64_t pcap = tune(BWD_P) > 0 ? tune(BWD_P) : 512;
   int64_t P = tune(BWD_P) > 0 ? pcap : (rows + rows_min - 1) / rows_min;
   if (P > pcap) P = pcap;
   if (P > rows) P = rows;
@@ -135,7 +146,7 @@ nr_status_t plan_bwd(nr_dtype_t dt, int64_t rows, int64_t n, bool aligned, BwdPl
   if (tune(BWD_W) > 0) W = tune(BWD_W);
   int D = 1;
   for (int d : kBwdD)
-    if (d * K * E <= 16) D = d;
+    if (d * K * E <= 8) D = d;
   if (tune(BWD_D) > 0) D = tune(BWD_D);
   if (!in_set(K, kBwdK, 4) || !in_set(D, kBwdD, 4) || K * D > 8 || W < 1 || W > 16)
     return NR_ERR_SHAPE;

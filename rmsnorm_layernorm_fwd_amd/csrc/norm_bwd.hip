@@ -6,16 +6,22 @@
 // FlashNorm: the forward stores each row's inverse statistic and the backward
 // uses it directly).  x and dy are each read once, dx written once.
 //
-// Mapping (stage 1): a workgroup of W waves walks a fixed contiguous range of
-// rows, D rows per batch, all W waves on every row.  A lane therefore owns
-// the same columns for the whole range and adds dy * xhat (and dy) for them
-// into fp32 registers: the column gradients need no atomics and no extra
-// pass.  The D row sums of a batch are wave-reduced together and meet in one
-// LDS round with one barrier (LDS double-buffered by batch parity, so there
-// is no second barrier).  At the end each workgroup writes its fp32 partial
-// row.  Stage 2 adds the partial rows column by column in workgroup order.
-// Every summation order is fixed by the shape, so the results are bitwise
-// reproducible run to run.
+// Mapping (stage 1): a workgroup of W waves works on D rows at a time, all W
+// waves on every row, so a lane owns the same columns throughout and adds
+// dy * xhat (and dy) for them into fp32 registers: the column gradients need
+// no atomics and no extra pass over the rows.  Batches are dealt out
+// round-robin -- workgroup b takes rows b*D.., then b*D + P*D.., ... -- so at
+// any moment the whole grid streams one contiguous window of the tensor,
+// which keeps DRAM pages open (contiguous per-workgroup ranges would spread
+// P concurrent streams over the whole tensor).  The next batch is loaded
+// before the current one is reduced (two register buffers used in turn, so
+// no copy forces a wait on the prefetch), which keeps loads in flight across
+// the reduction's barrier.  A batch's D row sums are wave-reduced together
+// and meet in one LDS round with one barrier (LDS double-buffered by batch
+// parity, so there is no second barrier).  At the end each workgroup writes
+// its fp32 partial row; stage 2 adds the partial rows column by column in
+// workgroup order.  Every summation order is fixed by the shape, so the
+// results are bitwise reproducible run to run.
 #include "nr_device.hpp"
 #include "nr_internal.hpp"
 
@@ -27,21 +33,137 @@ namespace nr {
 //        dx = r (g - a - xhat bb), partial dgamma += dy xhat, dbeta += dy
 // part: [2][P][n] fp32 (second matrix, at part + part_stride, for dbeta);
 // null when no column gradient is wanted.
+template <typename T, int K, int D>
+struct RowBatch {
+  u32x4 x[D * K], g[D * K];
+  float rs[D], mu[D];
+};
+
+template <typename T, int K, int D, bool VEC, bool LN>
+__device__ __forceinline__ void load_batch(RowBatch<T, K, D>& b, int64_t base, int64_t rows,
+                                           const T* x, const T* dy, const float* mean,
+                                           const float* rstat, int n, int t, int nthr) {
+  const uint32_t rbytes = static_cast<uint32_t>(n) * sizeof(T);
+#pragma unroll
+  for (int d = 0; d < D; ++d) {
+    const int64_t row = base + d;
+    const bool okr = row < rows;
+    const int64_t off = (okr ? row : 0) * static_cast<int64_t>(n);
+    const uint32_t nb = okr ? rbytes : 0u;  // rows past the end read as 0, move no data
+    const rsrc_t xr = make_rsrc(x + off, nb);
+    const rsrc_t gr = make_rsrc(dy + off, nb);
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+      b.x[d * K + k] = ld_chunk<T, VEC, kStream>(xr, t + k * nthr);
+      b.g[d * K + k] = ld_chunk<T, VEC, kStream>(gr, t + k * nthr);
+    }
+    b.rs[d] = okr ? rstat[row] : 0.0f;
+    b.mu[d] = (LN && okr) ? mean[row] : 0.0f;
+  }
+}
+
+template <typename T, int K, int D, bool VEC, bool LN>
+__device__ __forceinline__ void process_batch(RowBatch<T, K, D>& b, int64_t base, int64_t rows,
+                                              T* dx, int n, int t, int nthr, int W, int wave,
+                                              int lane, float inv_n, const float (&wv)[K][Vec<T>::N],
+                                              float (&acc1)[K][Vec<T>::N],
+                                              float (&acc2)[K][Vec<T>::N],
+                                              float (*red)[16], int& parity) {
+  constexpr int E = Vec<T>::N;
+  constexpr int NS = LN ? 2 : 1;  // row sums per row
+  // per-lane partial row sums, and the column partials.  Elements past n
+  // were read as 0 (x and dy), so they add nothing; only LayerNorm's
+  // centred xhat needs the explicit mask.
+  float s[NS * D];
+#pragma unroll
+  for (int d = 0; d < D; ++d) {
+    float s1 = 0.0f, s2 = 0.0f;
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+      const int c = t + k * nthr;
+      float xv[E], dv[E];
+      unpack<T>(b.x[d * K + k], xv);
+      unpack<T>(b.g[d * K + k], dv);
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        float xh = (xv[e] - b.mu[d]) * b.rs[d];
+        if constexpr (LN) xh = (c * E + e < n) ? xh : 0.0f;
+        const float gg = dv[e] * wv[k][e];
+        if constexpr (LN) {
+          s1 += gg;
+          s2 = fmaf(gg, xh, s2);
+          acc2[k][e] += dv[e];
+        } else {
+          s1 = fmaf(gg, xh, s1);
+        }
+        acc1[k][e] = fmaf(dv[e], xh, acc1[k][e]);
+      }
+    }
+    s[NS * d] = s1;
+    if constexpr (LN) s[NS * d + 1] = s2;
+  }
+  reload_barrier<D * K>(b.x);
+  reload_barrier<D * K>(b.g);
+
+  // reduce the batch's NS*D sums across the workgroup
+#pragma unroll
+  for (int i = 0; i < NS * D; ++i) s[i] = wave_sum(s[i]);
+  if (W > 1) {
+    float(*rp)[16] = red + parity * (NS * D);
+    if (lane == 0) {
+#pragma unroll
+      for (int i = 0; i < NS * D; ++i) rp[i][wave] = s[i];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < NS * D; ++i) {
+      float tot = 0.0f;
+      for (int q = 0; q < W; ++q) tot += rp[i][q];
+      s[i] = tot;
+    }
+    parity ^= 1;  // the other buffer next batch: no second barrier needed
+  }
+
+  const uint32_t rbytes = static_cast<uint32_t>(n) * sizeof(T);
+#pragma unroll
+  for (int d = 0; d < D; ++d) {
+    const int64_t row = base + d;
+    const bool okr = row < rows;
+    const rsrc_t dr = make_rsrc(dx + (okr ? row : 0) * static_cast<int64_t>(n), okr ? rbytes : 0u);
+    const float c1 = s[NS * d] * inv_n;
+    const float c2 = LN ? s[NS * d + 1] * inv_n : 0.0f;
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+      float xv[E], dv[E], o[E];
+      unpack<T>(b.x[d * K + k], xv);
+      unpack<T>(b.g[d * K + k], dv);
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        const float xh = (xv[e] - b.mu[d]) * b.rs[d];
+        const float gg = dv[e] * wv[k][e];
+        if constexpr (LN) {
+          o[e] = b.rs[d] * (gg - c1 - xh * c2);
+        } else {
+          o[e] = b.rs[d] * (gg - xh * c1);
+        }
+      }
+      st_chunk<T, VEC, kStream>(dr, t + k * nthr, pack<T>(o));
+    }
+  }
+}
+
 template <typename T, int K, int D, bool VEC, bool LN>
 __global__ void __launch_bounds__(1024)
 norm_bwd_rows(const T* dy, const T* x, const T* w, const float* mean, const float* rstat,
-              T* dx, float* part, int64_t part_stride, int64_t rows, int n,
-              int64_t rows_per_block, float w_add) {
+              T* dx, float* part, int64_t part_stride, int64_t rows, int n, float w_add) {
   constexpr int E = Vec<T>::N;
-  constexpr int NS = LN ? 2 : 1;  // row sums per row
-  __shared__ float red[2][NS * D][16];
+  constexpr int NS = LN ? 2 : 1;
+  __shared__ float red[2 * NS * D][16];
   const int t = threadIdx.x;
   const int nthr = blockDim.x;
   const int W = nthr >> 6;
   const int wave = wave_id();
   const int lane = t & 63;
-  const int64_t start = static_cast<int64_t>(blockIdx.x) * rows_per_block;
-  const int64_t end = start + rows_per_block < rows ? start + rows_per_block : rows;
   const float inv_n = 1.0f / static_cast<float>(n);
   const uint32_t rbytes = static_cast<uint32_t>(n) * sizeof(T);
 
@@ -66,103 +188,20 @@ norm_bwd_rows(const T* dy, const T* x, const T* w, const float* mean, const floa
     }
 
   int parity = 0;
-  for (int64_t r0 = start; r0 < end; r0 += D) {
-    u32x4 xa[D * K], ga[D * K];
-    float rs[D], mu[D];
-#pragma unroll
-    for (int d = 0; d < D; ++d) {
-      const int64_t row = r0 + d;
-      const bool okr = row < end;
-      const int64_t off = (okr ? row : 0) * static_cast<int64_t>(n);
-      const uint32_t nb = okr ? rbytes : 0u;  // rows past the range read as 0
-      const rsrc_t xr = make_rsrc(x + off, nb);
-      const rsrc_t gr = make_rsrc(dy + off, nb);
-#pragma unroll
-      for (int k = 0; k < K; ++k) {
-        xa[d * K + k] = ld_chunk<T, VEC>(xr, t + k * nthr);
-        ga[d * K + k] = ld_chunk<T, VEC>(gr, t + k * nthr);
-      }
-      rs[d] = okr ? rstat[row] : 0.0f;
-      mu[d] = (LN && okr) ? mean[row] : 0.0f;
-    }
-
-    // per-lane partial row sums, and the column partials.  Elements past n
-    // were read as 0 (x and dy), so they add nothing; only LayerNorm's
-    // centred xhat needs the explicit mask.
-    float s[NS * D];
-#pragma unroll
-    for (int d = 0; d < D; ++d) {
-      float s1 = 0.0f, s2 = 0.0f;
-#pragma unroll
-      for (int k = 0; k < K; ++k) {
-        const int c = t + k * nthr;
-        float xv[E], dv[E];
-        unpack<T>(xa[d * K + k], xv);
-        unpack<T>(ga[d * K + k], dv);
-#pragma unroll
-        for (int e = 0; e < E; ++e) {
-          float xh = (xv[e] - mu[d]) * rs[d];
-          if constexpr (LN) xh = (c * E + e < n) ? xh : 0.0f;
-          const float gg = dv[e] * wv[k][e];
-          if constexpr (LN) {
-            s1 += gg;
-            s2 = fmaf(gg, xh, s2);
-            acc2[k][e] += dv[e];
-          } else {
-            s1 = fmaf(gg, xh, s1);
-          }
-          acc1[k][e] = fmaf(dv[e], xh, acc1[k][e]);
-        }
-      }
-      s[NS * d] = s1;
-      if constexpr (LN) s[NS * d + 1] = s2;
-    }
-    reload_barrier<D * K>(xa);
-    reload_barrier<D * K>(ga);
-
-    // reduce the batch's NS*D sums across the workgroup
-#pragma unroll
-    for (int i = 0; i < NS * D; ++i) s[i] = wave_sum(s[i]);
-    if (W > 1) {
-      if (lane == 0) {
-#pragma unroll
-        for (int i = 0; i < NS * D; ++i) red[parity][i][wave] = s[i];
-      }
-      __syncthreads();
-#pragma unroll
-      for (int i = 0; i < NS * D; ++i) {
-        float tot = 0.0f;
-        for (int q = 0; q < W; ++q) tot += red[parity][i][q];
-        s[i] = tot;
-      }
-      parity ^= 1;  // the other buffer next batch: no second barrier needed
-    }
-
-#pragma unroll
-    for (int d = 0; d < D; ++d) {
-      const int64_t row = r0 + d;
-      const bool okr = row < end;
-      const rsrc_t dr = make_rsrc(dx + (okr ? row : 0) * static_cast<int64_t>(n), okr ? rbytes : 0u);
-      const float c1 = s[NS * d] * inv_n;
-      const float c2 = LN ? s[NS * d + 1] * inv_n : 0.0f;
-#pragma unroll
-      for (int k = 0; k < K; ++k) {
-        float xv[E], dv[E], o[E];
-        unpack<T>(xa[d * K + k], xv);
-        unpack<T>(ga[d * K + k], dv);
-#pragma unroll
-        for (int e = 0; e < E; ++e) {
-          const float xh = (xv[e] - mu[d]) * rs[d];
-          const float gg = dv[e] * wv[k][e];
-          if constexpr (LN) {
-            o[e] = rs[d] * (gg - c1 - xh * c2);
-          } else {
-            o[e] = rs[d] * (gg - xh * c1);
-          }
-        }
-        st_chunk<T, VEC>(dr, t + k * nthr, pack<T>(o));
-      }
-    }
+  const int64_t step = static_cast<int64_t>(gridDim.x) * D;
+  int64_t base = static_cast<int64_t>(blockIdx.x) * D;
+  RowBatch<T, K, D> A, B;
+  load_batch<T, K, D, VEC, LN>(A, base, rows, x, dy, mean, rstat, n, t, nthr);
+  while (base < rows) {
+    load_batch<T, K, D, VEC, LN>(B, base + step, rows, x, dy, mean, rstat, n, t, nthr);
+    process_batch<T, K, D, VEC, LN>(A, base, rows, dx, n, t, nthr, W, wave, lane, inv_n, wv, acc1,
+                                    acc2, red, parity);
+    base += step;
+    if (base >= rows) break;
+    load_batch<T, K, D, VEC, LN>(A, base + step, rows, x, dy, mean, rstat, n, t, nthr);
+    process_batch<T, K, D, VEC, LN>(B, base, rows, dx, n, t, nthr, W, wave, lane, inv_n, wv, acc1,
+                                    acc2, red, parity);
+    base += step;
   }
 
   // this workgroup's fp32 partial row(s) of the column gradients
@@ -198,57 +237,41 @@ norm_bwd_rows(const T* dy, const T* x, const T* w, const float* mean, const floa
   }
 }
 
-// Stage 2: out[j] = sum over p of part[p][j], p in increasing order within
-// each of nw fixed slices, then the slices in order.  blockIdx.y selects the
-// matrix (dW / dgamma, or dbeta).  Each lane covers 4 adjacent columns.
-template <bool V4>
+// Stage 2: out[j] = sum over p of part[p][j].  One column per lane, 64
+// columns per workgroup; wave q of the 16 adds the fixed slice
+// [qP/16, (q+1)P/16) in order, 16 loads in flight, and the 16 slice sums
+// meet in LDS and are added in wave order.  blockIdx.y selects the matrix
+// (dW / dgamma, or dbeta).
 __global__ void __launch_bounds__(1024)
 colreduce(const float* part, int64_t part_stride, int P, int n, float* out0, float* out1) {
   float* out = blockIdx.y == 0 ? out0 : out1;
   if (out == nullptr) return;  // uniform over the workgroup
   const float* src = part + blockIdx.y * part_stride;
-  __shared__ f32x4 acc_lds[16][64];
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  __shared__ float acc_lds[16][64];
+  const int wave = wave_id(), lane = threadIdx.x & 63;
   const int nw = blockDim.x >> 6;
-  const int col = (blockIdx.x * 64 + lane) * 4;
+  const int col = blockIdx.x * 64 + lane;
   const int p0 = static_cast<int>((static_cast<int64_t>(P) * wave) / nw);
   const int p1 = static_cast<int>((static_cast<int64_t>(P) * (wave + 1)) / nw);
-  f32x4 s = {0.0f, 0.0f, 0.0f, 0.0f};
+  float s = 0.0f;
   if (col < n) {
-    if constexpr (V4) {
-      int p = p0;
-      for (; p + 4 <= p1; p += 4) {
-        const f32x4 a = *reinterpret_cast<const f32x4*>(src + static_cast<int64_t>(p) * n + col);
-        const f32x4 b = *reinterpret_cast<const f32x4*>(src + static_cast<int64_t>(p + 1) * n + col);
-        const f32x4 c = *reinterpret_cast<const f32x4*>(src + static_cast<int64_t>(p + 2) * n + col);
-        const f32x4 d = *reinterpret_cast<const f32x4*>(src + static_cast<int64_t>(p + 3) * n + col);
-        s += a;
-        s += b;
-        s += c;
-        s += d;
-      }
-      for (; p < p1; ++p) s += *reinterpret_cast<const f32x4*>(src + static_cast<int64_t>(p) * n + col);
-    } else {
-      for (int p = p0; p < p1; ++p) {
-        const float* r = src + static_cast<int64_t>(p) * n + col;
+    const float* c = src + col;
+    int p = p0;
+    for (; p + 16 <= p1; p += 16) {
+      float v[16];
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          if (col + i < n) s[i] += r[i];
-      }
+      for (int i = 0; i < 16; ++i) v[i] = c[static_cast<int64_t>(p + i) * n];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) s += v[i];
     }
+    for (; p < p1; ++p) s += c[static_cast<int64_t>(p) * n];
   }
   acc_lds[wave][lane] = s;
   __syncthreads();
   if (wave == 0 && col < n) {
-    f32x4 tot = acc_lds[0][lane];
+    float tot = acc_lds[0][lane];
     for (int i = 1; i < nw; ++i) tot += acc_lds[i][lane];
-    if constexpr (V4) {
-      *reinterpret_cast<f32x4*>(out + col) = tot;
-    } else {
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        if (col + i < n) out[col + i] = tot[i];
-    }
+    out[col] = tot;
   }
 }
 
@@ -262,7 +285,7 @@ hipError_t launch_bwd_kd(const BwdPlan& pl, const void* dy, const void* x, const
   hipLaunchKernelGGL((norm_bwd_rows<T, K, D, A, LN>), dim3(pl.P), dim3(64 * pl.W), 0, st,
                      static_cast<const T*>(dy), static_cast<const T*>(x),
                      static_cast<const T*>(w), mean, rstat, static_cast<T*>(dx), part,
-                     part_stride, rows, n, pl.rows_per_block, w_add);
+                     part_stride, rows, n, w_add);
   return hipGetLastError();
 }
 
@@ -308,15 +331,8 @@ hipError_t launch_norm_bwd(bool ln, int dt, const BwdPlan& pl, const void* dy, c
 
 hipError_t launch_colreduce(const float* part, int64_t part_stride, int P, int n, float* out0,
                             float* out1, hipStream_t st) {
-  const dim3 grid(static_cast<unsigned>((n + 255) / 256), out1 != nullptr ? 2u : 1u);
-  const dim3 block(1024);
-  const bool v4 = (n % 4 == 0) && ((reinterpret_cast<uintptr_t>(part) & 15) == 0) &&
-                  ((reinterpret_cast<uintptr_t>(out0) & 15) == 0) &&
-                  ((reinterpret_cast<uintptr_t>(out1) & 15) == 0);
-  if (v4)
-    hipLaunchKernelGGL((colreduce<true>), grid, block, 0, st, part, part_stride, P, n, out0, out1);
-  else
-    hipLaunchKernelGGL((colreduce<false>), grid, block, 0, st, part, part_stride, P, n, out0, out1);
+  const dim3 grid(static_cast<unsigned>((n + 63) / 64), out1 != nullptr ? 2u : 1u);
+  hipLaunchKernelGGL(colreduce, grid, dim3(1024), 0, st, part, part_stride, P, n, out0, out1);
   return hipGetLastError();
 }
 

@@ -45,7 +45,7 @@ __device__ __forceinline__ void norm_fwd_body(const T* x, const T* w, const T* b
 #pragma unroll
   for (int k = 0; k < K; ++k) {
     const int c = t + k * nthr;
-    xa[k] = ld_chunk<T, VEC>(xr, c);
+    xa[k] = ld_chunk<T, VEC, kStream>(xr, c);
     wa[k] = ld_chunk<T, VEC>(wr, c);
     if constexpr (LN) ba[k] = ld_chunk<T, VEC>(br, c);
   }
@@ -105,7 +105,7 @@ __device__ __forceinline__ void norm_fwd_body(const T* x, const T* w, const T* b
         o[e] = (v[e] * r) * ww;
       }
     }
-    st_chunk<T, VEC>(yr, c, pack<T>(o));
+    st_chunk<T, VEC, kStream>(yr, c, pack<T>(o));
   }
   if (active && t == 0) {
     if constexpr (LN) {
@@ -164,7 +164,7 @@ hipError_t launch_fwd_a(const FwdPlan& pl, const void* x, const void* w, const v
   switch (pl.K) {
 #define NR_CASE(KK) \
   case KK: return launch_fwd_k<T, KK, A, LN>(pl, x, w, b, y, s0, s1, rows, n, eps, w_add, st);
-    NR_CASE(1) NR_CASE(2) NR_CASE(4) NR_CASE(6) NR_CASE(8) NR_CASE(10)
+    NR_CASE(1) NR_CASE(2) NR_CASE(4) NR_CASE(5) NR_CASE(6) NR_CASE(8) NR_CASE(10)
 #undef NR_CASE
     default: return hipErrorInvalidValue;
   }

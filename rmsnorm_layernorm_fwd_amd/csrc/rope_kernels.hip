@@ -80,7 +80,7 @@ rope_apply_kernel(T* x, const float* cos_tab, const float* sin_tab, int64_t ntok
       off[k] = idx < nchunk ? static_cast<int>((h * sh + c * E) * static_cast<int64_t>(sizeof(T)))
                             : kNoChunk;
       if constexpr (VEC) {
-        unpack<T>(__builtin_amdgcn_raw_buffer_load_b128(xr, off[k], 0, 0), v[k]);
+        unpack<T>(__builtin_amdgcn_raw_buffer_load_b128(xr, off[k], 0, kStream), v[k]);
       } else {
         v[k][0] = ld_elem<T>(xr, off[k]);
         v[k][1] = ld_elem<T>(xr, off[k] + static_cast<int>(sizeof(T)));
@@ -102,7 +102,7 @@ rope_apply_kernel(T* x, const float* cos_tab, const float* sin_tab, int64_t ntok
         o[2 * p + 1] = fmaf(a, sn, b * c);
       }
       if constexpr (VEC) {
-        __builtin_amdgcn_raw_buffer_store_b128(pack<T>(o), xr, off[k], 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b128(pack<T>(o), xr, off[k], 0, kStream);
       } else {
         st_elem<T>(xr, off[k], o[0]);
         st_elem<T>(xr, off[k] + static_cast<int>(sizeof(T)), o[1]);

@@ -44,10 +44,28 @@ def ulp32(c):
 
 
 def check_table(name, cos_t, sin_t, angle):
+    """fp32 tables against cos/sin of the oracle's fp64 angles: one fp32 ulp,
+    plus what the two sides' double-precision angles (each within a few
+    2^-53 relative of the true angle) can differ by: 4e-15 |angle|."""
     c, s = to64(cos_t), to64(sin_t)
     rc, rs = np.cos(angle), np.sin(angle)
-    assert np.all(np.abs(c - rc) <= ulp32(rc)), f"{name} cos: max err {np.max(np.abs(c - rc))}"
-    assert np.all(np.abs(s - rs) <= ulp32(rs)), f"{name} sin: max err {np.max(np.abs(s - rs))}"
+    slack = 4e-15 * np.abs(angle)
+    for nm, o, r in (("cos", c, rc), ("sin", s, rs)):
+        err = np.abs(o - r)
+        tol = ulp32(r) + slack
+        i = np.unravel_index(np.argmax(err - tol), err.shape)
+        assert np.all(err <= tol), (f"{name} {nm}: worst at {i}: angle={angle[i]!r} gpu={o[i]!r} "
+                                    f"oracle={r[i]!r} err={err[i]:.3e} bound={tol[i]:.3e}")
+
+
+def grad_scale(r, dy, w, gemma=False):
+    """Row scale for dx: RMS over the row of r * dy * w' (the terms dx is a
+    difference of).  dx can cancel to far below this (a one-column row, where
+    RMSNorm's dx is ~eps-sized and LayerNorm's is exactly 0), and fp32 is only
+    accurate relative to the terms, so the bound is scaled by them."""
+    wp = np.ones(dy.shape[-1]) if w is None else to64(w) + (1.0 if gemma else 0.0)
+    t = to64(r)[:, None] * to64(dy).reshape(len(r), -1) * wp[None, :]
+    return np.sqrt(np.mean(t * t, axis=1, keepdims=True))
 
 
 # ---------------------------------------------------------------- RMSNorm
@@ -68,7 +86,7 @@ def check_rms_full(tag, x, w, dy, eps, gemma):
     n = x.shape[-1]
     check(f"{tag} y", y.reshape(-1, n), ry, k)
     check(f"{tag} inv_rms", r.reshape(-1), rr, "stat", s=0.0)
-    check(f"{tag} dx", dx.reshape(-1, n), rdx, k)
+    check(f"{tag} dx", dx.reshape(-1, n), rdx, k, s=grad_scale(rr, dy, w, gemma))
     if w is not None:
         check(f"{tag} dw", dw, rdw, "col")
 
@@ -98,7 +116,7 @@ def check_ln_full(tag, x, gm, bt, dy, eps):
     check(f"{tag} y", y.reshape(-1, n), ry, k)
     check(f"{tag} mean", mu.reshape(-1), rmu, "stat", s=np.sqrt(np.mean(x64 * x64, axis=1)))
     check(f"{tag} rstd", rs.reshape(-1), rrs, "stat", s=0.0)
-    check(f"{tag} dx", dx.reshape(-1, n), rdx, k)
+    check(f"{tag} dx", dx.reshape(-1, n), rdx, k, s=grad_scale(rrs, dy, gm))
     check(f"{tag} dgamma", dg, rdg, "col")
     check(f"{tag} dbeta", db, rdb, "col")
 
@@ -175,7 +193,7 @@ def test_longseq_rmsnorm(longseq):
     idx = torch.from_numpy(rows).to(DEV)
     check("longseq y", y[idx], ry, "bf16")
     check("longseq inv_rms", r[idx], rr, "stat", s=0.0)
-    check("longseq dx", dx[idx], rdx, "bf16")
+    check("longseq dx", dx[idx], rdx, "bf16", s=grad_scale(rr, dy[rows], w))
     check("longseq dw", dw, rdw, "col")
 
 
@@ -230,7 +248,7 @@ def test_longseq_chain(longseq):
     gg = np.abs(dy64 * to64(w)[None, :])
     xh = np.abs(to64(xs) * rr[:, None])
     extra = (2 ** -8) * 1.01 * rr[:, None] * (gg + xh * np.mean(gg * xh, axis=1, keepdims=True))
-    check("chain bwd dx", dx[idx], rdx, "bf16", extra=extra)
+    check("chain bwd dx", dx[idx], rdx, "bf16", extra=extra, s=grad_scale(rr, dy64, w))
 
 
 # ---------------------------------------------------------------- edge cases

@@ -8,8 +8,14 @@ for a column-gradient vector, the RMS of the whole vector).
   fp32 outputs              |O - R| <= 1e-5 (|R| + s)
   column gradients (fp32)   |O - R| <= 1e-4 (|R| + s)
   bf16 outputs              |O - R| <= ulp_bf16(R) + 1e-5 s      ("1 bf16 ulp")
+
   per-row statistics        |O - R| <= 1e-5 (|R| + s), s = 0 except for the
                             LayerNorm mean, whose s is the RMS of the x row
+
+For an input gradient dx the row scale s is the RMS of r * dy * w' over the
+row (the terms dx is the difference of) rather than the RMS of dx itself:
+dx can cancel far below its terms, and fp32 arithmetic is accurate relative
+to the terms only.  On ordinary rows the two scales are of the same size.
 
 ulp_bf16(R) = 2^(floor(log2 |R|) - 7): bf16 keeps 8 significant bits, so this
 is the spacing of bf16 numbers in R's binade (2^-7 ~ 7.8e-3 relative at its
