@@ -23,9 +23,11 @@ using nr::RopePlan;
 
 // ---- tuning overrides ---------------------------------------------------
 
-enum TuneKey { FWD_W, FWD_K, FWD_R, BWD_W, BWD_K, BWD_D, BWD_P, BWD_ROWS_MIN, ROPE_K, ROPE_WPB, NKEYS };
-const char* const kTuneNames[NKEYS] = {"fwd_w", "fwd_k", "fwd_r", "bwd_w", "bwd_k",
-                                       "bwd_d", "bwd_p", "bwd_rows_min", "rope_k", "rope_wpb"};
+enum TuneKey { FWD_W, FWD_K, FWD_R, FWD_J, BWD_W, BWD_K, BWD_D, BWD_P, BWD_ROWS_MIN, BWD_PF,
+               ROPE_K, ROPE_WPB, NKEYS };
+const char* const kTuneNames[NKEYS] = {"fwd_w", "fwd_k", "fwd_r", "fwd_j", "bwd_w", "bwd_k",
+                                       "bwd_d", "bwd_p", "bwd_rows_min", "bwd_pf", "rope_k",
+                                       "rope_wpb"};
 std::atomic<int> g_tune[NKEYS];
 
 int tune(TuneKey k) { return g_tune[k].load(std::memory_order_relaxed); }
@@ -87,40 +89,51 @@ nr_status_t plan_fwd(nr_dtype_t dt, int64_t n, bool aligned, FwdPlan* pl) {
   // Short rows: a wavefront per row, no barrier.  Rows of 6..16 chunk slots
   // (up to 8192 bf16 / 4096 fp32): two waves per row and about 5 chunks per
   // lane, which keeps the row resident in fewer VGPRs (LayerNorm holds x,
-  // gamma and beta) and measured fastest at 5120 bf16.  Longer rows: up to 8
-  // chunks per lane and as many waves as needed.
-  int W, K;
+  // gamma and beta), and two rows per row group so that each weight chunk
+  // loaded serves both; that measured fastest at 5120 bf16.  Longer rows: up
+  // to 8 chunks per lane and as many waves as needed.
+  int W, K, J = 1;
   if (need <= 4) {
     W = 1;
     K = pick_at_least(need, kFwdK, 7);
   } else if (need <= 16) {
     W = 2;
     K = pick_at_least((need + 1) / 2, kFwdK, 6);
+    if (K <= 5) J = 2;  // one weight load serves two rows
   } else {
     W = static_cast<int>((need + 7) / 8);
     K = pick_at_least((need + W - 1) / W, kFwdK, 6);  // K <= 8 when W > 1
   }
   if (tune(FWD_W) > 0) W = tune(FWD_W);
   if (tune(FWD_K) > 0) K = tune(FWD_K);
-  int R = W == 1 ? 4 : (W == 2 ? 2 : 1);
+  int R = W == 1 ? 4 : (W == 2 && J == 1 ? 2 : 1);
   if (tune(FWD_R) > 0) R = tune(FWD_R);
+  if (tune(FWD_J) > 0) J = tune(FWD_J);
   if (W < 1 || W > 16 || !in_set(K, kFwdK, 7) || (W > 1 && K > 8)) return NR_ERR_SHAPE;
+  if (J < 1 || J > 2 || (J == 2 && K > 5)) return NR_ERR_SHAPE;
   if (static_cast<int64_t>(64) * W * K < nchunk) return NR_ERR_SHAPE;
   if (R < 1 || (W == 1 && R > 4) || 64 * W * R > 1024) return NR_ERR_SHAPE;
-  *pl = FwdPlan{W, K, R, aligned};
+  *pl = FwdPlan{W, K, R, J, aligned};
   return NR_OK;
 }
 
-// Backward workgroups.  Each handles about rows/P rows (dealt out round
-// robin in batches of D).  At least 16 rows per workgroup keep the fp32
-// partial rows small next to the row traffic; at most 512 workgroups, i.e.
-// two resident 10-wave workgroups on each of MI355X's 256 CUs for 5120-wide
-// bf16 rows (more gave a second, partial round of workgroups and measured
-// slower).  Depends on rows only, so the summation order and the workspace
-// size are the same on every device.
-void bwd_grid(int64_t rows, int64_t* P_out, int64_t* rpb_out) {
+// Backward launch shape.
+//   K, W: as few chunks per lane as lets at most 16 waves cover the row
+//     (5120 bf16: K = 1, W = 10).
+//   D (rows per batch) and PF (batches loaded ahead): the largest that fit
+//     the 128-VGPR budget of a 1024-thread workgroup without spilling.
+//     RMSNorm with one chunk per lane takes D = 2, PF = 2; LayerNorm, which
+//     also carries the dbeta accumulators, D = 1, PF = 1.
+//   P (workgroups): each handles about rows/P rows, dealt out round robin.
+//     At least 16 rows per workgroup keep the fp32 partial rows small next
+//     to the row traffic.  At most 256 (RMSNorm, D = 2) or 512 (LayerNorm):
+//     on MI355X's 256 CUs that is one or two resident workgroups per CU;
+//     more gave a second, partial round of workgroups and measured slower.
+//   P depends on the row count and the operator only, so the summation order
+//   and the workspace size are the same on every device.
+void bwd_grid(int64_t rows, bool ln, int64_t* P_out, int64_t* rpb_out) {
   const int64_t rows_min = tune(BWD_ROWS_MIN) > 0 ? tune(BWD_ROWS_MIN) : 16;
-  const int64_t pcap = tune(BWD_P) > 0 ? tune(BWD_P) : 512;
+  const int64_t pcap = tune(BWD_P) > 0 ? tune(BWD_P) : (ln ? 512 : 256);
   int64_t P = tune(BWD_P) > 0 ? pcap : (rows + rows_min - 1) / rows_min;
   if (P > pcap) P = pcap;
   if (P > rows) P = rows;
@@ -130,7 +143,7 @@ void bwd_grid(int64_t rows, int64_t* P_out, int64_t* rpb_out) {
   *rpb_out = rpb;
 }
 
-nr_status_t plan_bwd(nr_dtype_t dt, int64_t rows, int64_t n, bool aligned, BwdPlan* pl) {
+nr_status_t plan_bwd(nr_dtype_t dt, bool ln, int64_t rows, int64_t n, bool aligned, BwdPlan* pl) {
   const int E = vec_elems(dt);
   const int64_t nchunk = (n + E - 1) / E;
   const int64_t need = (nchunk + 63) / 64;
@@ -144,16 +157,17 @@ nr_status_t plan_bwd(nr_dtype_t dt, int64_t rows, int64_t n, bool aligned, BwdPl
   if (tune(BWD_K) > 0) K = tune(BWD_K);
   if (K > 0) W = static_cast<int>((need + K - 1) / K);
   if (tune(BWD_W) > 0) W = tune(BWD_W);
-  int D = 1;
-  for (int d : kBwdD)
-    if (d * K * E <= 8) D = d;
+  int D = (!ln && K == 1) ? 2 : 1;
+  int PF = (!ln && K == 1) ? 2 : 1;
   if (tune(BWD_D) > 0) D = tune(BWD_D);
+  if (tune(BWD_PF) > 0) PF = tune(BWD_PF);
   if (!in_set(K, kBwdK, 4) || !in_set(D, kBwdD, 4) || K * D > 8 || W < 1 || W > 16)
     return NR_ERR_SHAPE;
+  if (PF < 1 || PF > 2) return NR_ERR_SHAPE;
   if (static_cast<int64_t>(64) * W * K < nchunk) return NR_ERR_SHAPE;
   int64_t P, rpb;
-  bwd_grid(rows, &P, &rpb);
-  *pl = BwdPlan{W, K, D, static_cast<int>(P), rpb, aligned};
+  bwd_grid(rows, ln, &P, &rpb);
+  *pl = BwdPlan{W, K, D, static_cast<int>(P), PF, rpb, aligned};
   return NR_OK;
 }
 
@@ -210,7 +224,7 @@ nr_status_t nr_tune(const char* key, int value) {
 size_t nr_bwd_workspace_bytes(int64_t rows, int64_t n, int is_layernorm) {
   if (rows <= 0 || n < 1) return 0;
   int64_t P, rpb;
-  bwd_grid(rows, &P, &rpb);
+  bwd_grid(rows, is_layernorm != 0, &P, &rpb);
   return static_cast<size_t>(P) * static_cast<size_t>(n) * sizeof(float) *
          (is_layernorm ? 2u : 1u);
 }
@@ -279,7 +293,7 @@ nr_status_t norm_bwd_common(bool ln, nr_dtype_t dt, const void* dy, const void* 
   const bool aligned = (n % vec_elems(dt)) == 0 && aligned16(dy) && aligned16(x) &&
                        aligned16(dx) && (w == nullptr || aligned16(w));
   BwdPlan pl;
-  if ((s = plan_bwd(dt, rows, n, aligned, &pl)) != NR_OK) return s;
+  if ((s = plan_bwd(dt, ln, rows, n, aligned, &pl)) != NR_OK) return s;
   float* part = nullptr;
   if (want_cols) {
     const size_t need = static_cast<size_t>(pl.P) * n * sizeof(float) * (ln ? 2 : 1);

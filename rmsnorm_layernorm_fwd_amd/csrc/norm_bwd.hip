@@ -152,7 +152,7 @@ __device__ __forceinline__ void process_batch(RowBatch<T, K, D>& b, int64_t base
   }
 }
 
-template <typename T, int K, int D, bool VEC, bool LN>
+template <typename T, int K, int D, int PF, bool VEC, bool LN>
 __global__ void __launch_bounds__(1024)
 norm_bwd_rows(const T* dy, const T* x, const T* w, const float* mean, const float* rstat,
               T* dx, float* part, int64_t part_stride, int64_t rows, int n, float w_add) {
@@ -190,19 +190,25 @@ norm_bwd_rows(const T* dy, const T* x, const T* w, const float* mean, const floa
   int parity = 0;
   const int64_t step = static_cast<int64_t>(gridDim.x) * D;
   int64_t base = static_cast<int64_t>(blockIdx.x) * D;
-  RowBatch<T, K, D> A, B;
-  load_batch<T, K, D, VEC, LN>(A, base, rows, x, dy, mean, rstat, n, t, nthr);
-  while (base < rows) {
-    load_batch<T, K, D, VEC, LN>(B, base + step, rows, x, dy, mean, rstat, n, t, nthr);
-    process_batch<T, K, D, VEC, LN>(A, base, rows, dx, n, t, nthr, W, wave, lane, inv_n, wv, acc1,
-                                    acc2, red, parity);
-    base += step;
-    if (base >= rows) break;
-    load_batch<T, K, D, VEC, LN>(A, base + step, rows, x, dy, mean, rstat, n, t, nthr);
-    process_batch<T, K, D, VEC, LN>(B, base, rows, dx, n, t, nthr, W, wave, lane, inv_n, wv, acc1,
-                                    acc2, red, parity);
-    base += step;
+  // PF batches are loaded ahead of the one being reduced; PF + 1 register
+  // buffers are used in turn (the loop is unrolled over them, so no register
+  // copy ever waits on a load in flight).
+  RowBatch<T, K, D> buf[PF + 1];
+#pragma unroll
+  for (int i = 0; i < PF; ++i)
+    load_batch<T, K, D, VEC, LN>(buf[i], base + i * step, rows, x, dy, mean, rstat, n, t, nthr);
+  while (true) {
+#pragma unroll
+    for (int i = 0; i <= PF; ++i) {
+      if (base >= rows) goto done;
+      load_batch<T, K, D, VEC, LN>(buf[(i + PF) % (PF + 1)], base + PF * step, rows, x, dy, mean,
+                                   rstat, n, t, nthr);
+      process_batch<T, K, D, VEC, LN>(buf[i], base, rows, dx, n, t, nthr, W, wave, lane, inv_n, wv,
+                                      acc1, acc2, red, parity);
+      base += step;
+    }
   }
+done:
 
   // this workgroup's fp32 partial row(s) of the column gradients
   if (part != nullptr) {
@@ -282,7 +288,8 @@ hipError_t launch_bwd_kd(const BwdPlan& pl, const void* dy, const void* x, const
                          const float* mean, const float* rstat, void* dx, float* part,
                          int64_t rows, int n, float w_add, hipStream_t st) {
   const int64_t part_stride = static_cast<int64_t>(pl.P) * n;
-  hipLaunchKernelGGL((norm_bwd_rows<T, K, D, A, LN>), dim3(pl.P), dim3(64 * pl.W), 0, st,
+  auto kern = pl.PF == 2 ? norm_bwd_rows<T, K, D, 2, A, LN> : norm_bwd_rows<T, K, D, 1, A, LN>;
+  hipLaunchKernelGGL(kern, dim3(pl.P), dim3(64 * pl.W), 0, st,
                      static_cast<const T*>(dy), static_cast<const T*>(x),
                      static_cast<const T*>(w), mean, rstat, static_cast<T*>(dx), part,
                      part_stride, rows, n, w_add);

@@ -20,141 +20,207 @@
 
 namespace nr {
 
-template <typename T, int K, bool VEC, bool LN>
+// Sum each of the J values over the W waves of a row group (W == 1: pure
+// wave reductions).  red: LDS scratch [J][16] used once per call site.
+template <int J>
+__device__ __forceinline__ void group_sum_n(float (&v)[J], int W, int wave, int g, float (*red)[16]) {
+#pragma unroll
+  for (int j = 0; j < J; ++j) v[j] = wave_sum(v[j]);
+  if (W == 1) return;
+  if ((threadIdx.x & 63) == 0) {
+#pragma unroll
+    for (int j = 0; j < J; ++j) red[j][wave] = v[j];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < J; ++j) {
+    float s = 0.0f;
+    for (int i = 0; i < W; ++i) s += red[j][g * W + i];
+    v[j] = s;
+  }
+}
+
+// A row group (W waves) normalises J consecutive rows; the weight chunks it
+// loads serve all J of them.
+template <typename T, int K, int J, bool VEC, bool LN>
 __device__ __forceinline__ void norm_fwd_body(const T* x, const T* w, const T* b, T* y,
                                               float* stat0, float* stat1, int64_t rows, int n,
                                               float eps, float w_add, int W) {
   constexpr int E = Vec<T>::N;
-  __shared__ float red0[16], red1[16];
+  __shared__ float red0[J][16], red1[J][16];
   const int lane = threadIdx.x & 63;
   const int wave = wave_id();
   const int g = wave / W;
   const int t = (wave - g * W) * 64 + lane;
   const int nthr = 64 * W;
   const int R = blockDim.x / nthr;
-  const int64_t row = static_cast<int64_t>(blockIdx.x) * R + g;
-  const bool active = row < rows;
+  const int64_t row0 = (static_cast<int64_t>(blockIdx.x) * R + g) * J;
   const uint32_t rbytes = static_cast<uint32_t>(n) * sizeof(T);
-  // a row group past the last row sees an empty buffer: loads give 0, stores vanish
-  const rsrc_t xr = make_rsrc(x + (active ? row : 0) * static_cast<int64_t>(n), active ? rbytes : 0u);
-  const rsrc_t yr = make_rsrc(y + (active ? row : 0) * static_cast<int64_t>(n), active ? rbytes : 0u);
   const rsrc_t wr = make_rsrc(w, w != nullptr ? rbytes : 0u);
   const rsrc_t br = make_rsrc(b, b != nullptr ? rbytes : 0u);
 
-  u32x4 xa[K], wa[K], ba[K];
+  // rows past the last one see an empty buffer: loads give 0, stores vanish
+  u32x4 xa[J * K], wa[K], ba[K];
+#pragma unroll
+  for (int j = 0; j < J; ++j) {
+    const int64_t row = row0 + j;
+    const bool active = row < rows;
+    const rsrc_t xr = make_rsrc(x + (active ? row : 0) * static_cast<int64_t>(n), active ? rbytes : 0u);
+#pragma unroll
+    for (int k = 0; k < K; ++k) xa[j * K + k] = ld_chunk<T, VEC, kStream>(xr, t + k * nthr);
+  }
 #pragma unroll
   for (int k = 0; k < K; ++k) {
-    const int c = t + k * nthr;
-    xa[k] = ld_chunk<T, VEC, kStream>(xr, c);
-    wa[k] = ld_chunk<T, VEC>(wr, c);
-    if constexpr (LN) ba[k] = ld_chunk<T, VEC>(br, c);
+    wa[k] = ld_chunk<T, VEC>(wr, t + k * nthr);
+    if constexpr (LN) ba[k] = ld_chunk<T, VEC>(br, t + k * nthr);
   }
 
   const float fn = static_cast<float>(n);
-  float mean = 0.0f, r;
+  float mean[J], r[J];
   if constexpr (LN) {
-    float s = 0.0f;
+    float s[J];
 #pragma unroll
-    for (int k = 0; k < K; ++k) {
-      float v[E];
-      unpack<T>(xa[k], v);
+    for (int j = 0; j < J; ++j) {
+      s[j] = 0.0f;
 #pragma unroll
-      for (int e = 0; e < E; ++e) s += v[e];
-    }
-    mean = group_sum(s, W, wave, g, red0) / fn;
-    // second pass over the registers, not over HBM: squared deviations
-    float q = 0.0f;
+      for (int k = 0; k < K; ++k) {
+        float v[E];
+        unpack<T>(xa[j * K + k], v);
 #pragma unroll
-    for (int k = 0; k < K; ++k) {
-      const int c = t + k * nthr;
-      float v[E];
-      unpack<T>(xa[k], v);
-#pragma unroll
-      for (int e = 0; e < E; ++e) {
-        const float d = (c * E + e < n) ? v[e] - mean : 0.0f;
-        q = fmaf(d, d, q);
+        for (int e = 0; e < E; ++e) s[j] += v[e];
       }
     }
-    r = rsqrtf(group_sum(q, W, wave, g, red1) / fn + eps);
-  } else {
-    float ss = 0.0f;
+    group_sum_n<J>(s, W, wave, g, red0);
+    reload_barrier<J * K>(xa);
+    // second pass over the registers, not over HBM: squared deviations
+    float q[J];
 #pragma unroll
-    for (int k = 0; k < K; ++k) {
-      float v[E];
-      unpack<T>(xa[k], v);
+    for (int j = 0; j < J; ++j) {
+      mean[j] = s[j] / fn;
+      q[j] = 0.0f;
 #pragma unroll
-      for (int e = 0; e < E; ++e) ss = fmaf(v[e], v[e], ss);
+      for (int k = 0; k < K; ++k) {
+        const int c = t + k * nthr;
+        float v[E];
+        unpack<T>(xa[j * K + k], v);
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          const float d = (c * E + e < n) ? v[e] - mean[j] : 0.0f;
+          q[j] = fmaf(d, d, q[j]);
+        }
+      }
     }
-    r = rsqrtf(group_sum(ss, W, wave, g, red0) / fn + eps);
+    group_sum_n<J>(q, W, wave, g, red1);
+#pragma unroll
+    for (int j = 0; j < J; ++j) r[j] = rsqrtf(q[j] / fn + eps);
+  } else {
+    float ss[J];
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+      ss[j] = 0.0f;
+#pragma unroll
+      for (int k = 0; k < K; ++k) {
+        float v[E];
+        unpack<T>(xa[j * K + k], v);
+#pragma unroll
+        for (int e = 0; e < E; ++e) ss[j] = fmaf(v[e], v[e], ss[j]);
+      }
+    }
+    group_sum_n<J>(ss, W, wave, g, red0);
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+      mean[j] = 0.0f;
+      r[j] = rsqrtf(ss[j] / fn + eps);
+    }
   }
-  reload_barrier<K>(xa);
+  reload_barrier<J * K>(xa);
+  // the weights too: widen them where they are used, not when they arrive
+  reload_barrier<K>(wa);
+  if constexpr (LN) reload_barrier<K>(ba);
 
 #pragma unroll
-  for (int k = 0; k < K; ++k) {
-    const int c = t + k * nthr;
-    float v[E], wv[E], bv[E], o[E];
-    unpack<T>(xa[k], v);
-    unpack<T>(wa[k], wv);
-    if constexpr (LN) unpack<T>(ba[k], bv);
+  for (int j = 0; j < J; ++j) {
+    const int64_t row = row0 + j;
+    const bool active = row < rows;
+    const rsrc_t yr = make_rsrc(y + (active ? row : 0) * static_cast<int64_t>(n), active ? rbytes : 0u);
 #pragma unroll
-    for (int e = 0; e < E; ++e) {
-      const float ww = (w != nullptr) ? wv[e] + w_add : 1.0f;
-      if constexpr (LN) {
-        o[e] = fmaf((v[e] - mean) * r, ww, bv[e]);
-      } else {
-        o[e] = (v[e] * r) * ww;
+    for (int k = 0; k < K; ++k) {
+      float v[E], wv[E], bv[E], o[E];
+      unpack<T>(xa[j * K + k], v);
+      unpack<T>(wa[k], wv);
+      if constexpr (LN) unpack<T>(ba[k], bv);
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        const float ww = (w != nullptr) ? wv[e] + w_add : 1.0f;
+        if constexpr (LN) {
+          o[e] = fmaf((v[e] - mean[j]) * r[j], ww, bv[e]);
+        } else {
+          o[e] = (v[e] * r[j]) * ww;
+        }
       }
+      st_chunk<T, VEC, kStream>(yr, t + k * nthr, pack<T>(o));
     }
-    st_chunk<T, VEC, kStream>(yr, c, pack<T>(o));
-  }
-  if (active && t == 0) {
-    if constexpr (LN) {
-      if (stat0) stat0[row] = mean;
-      if (stat1) stat1[row] = r;
-    } else {
-      if (stat0) stat0[row] = r;
+    if (active && t == 0) {
+      if constexpr (LN) {
+        if (stat0) stat0[row] = mean[j];
+        if (stat1) stat1[row] = r[j];
+      } else {
+        if (stat0) stat0[row] = r[j];
+      }
     }
   }
 }
 
-// One wavefront per row (W == 1), at most 4 rows (256 threads) per workgroup,
-// so the compiler may spend up to 128 VGPRs per lane keeping a row resident.
-template <typename T, int K, bool VEC, bool LN>
+// One wavefront per row group (W == 1), at most 4 row groups (256 threads)
+// per workgroup.
+template <typename T, int K, int J, bool VEC, bool LN>
 __global__ void __launch_bounds__(256)
 norm_fwd_wave(const T* x, const T* w, const T* b, T* y, float* stat0, float* stat1,
               int64_t rows, int n, float eps, float w_add) {
-  norm_fwd_body<T, K, VEC, LN>(x, w, b, y, stat0, stat1, rows, n, eps, w_add, 1);
+  norm_fwd_body<T, K, J, VEC, LN>(x, w, b, y, stat0, stat1, rows, n, eps, w_add, 1);
 }
 
-// Several waves per row (W > 1), up to 16 waves per workgroup.
-template <typename T, int K, bool VEC, bool LN>
+// Several waves per row group (W > 1), up to 16 waves per workgroup.
+template <typename T, int K, int J, bool VEC, bool LN>
 __global__ void __launch_bounds__(1024)
 norm_fwd_group(const T* x, const T* w, const T* b, T* y, float* stat0, float* stat1,
                int64_t rows, int n, float eps, float w_add, int W) {
-  norm_fwd_body<T, K, VEC, LN>(x, w, b, y, stat0, stat1, rows, n, eps, w_add, W);
+  norm_fwd_body<T, K, J, VEC, LN>(x, w, b, y, stat0, stat1, rows, n, eps, w_add, W);
 }
 
 namespace {
+
+template <typename T, int K, int J, bool A, bool LN>
+hipError_t launch_fwd_kj(const FwdPlan& pl, const void* x, const void* w, const void* b, void* y,
+                         float* s0, float* s1, int64_t rows, int n, float eps, float w_add,
+                         hipStream_t st) {
+  const int64_t per_block = static_cast<int64_t>(pl.R) * J;
+  const dim3 grid(static_cast<unsigned>((rows + per_block - 1) / per_block));
+  const dim3 block(64 * pl.W * pl.R);
+  if (pl.W == 1) {
+    hipLaunchKernelGGL((norm_fwd_wave<T, K, J, A, LN>), grid, block, 0, st,
+                       static_cast<const T*>(x), static_cast<const T*>(w),
+                       static_cast<const T*>(b), static_cast<T*>(y), s0, s1, rows, n, eps, w_add);
+  } else if constexpr (K * J <= 10 && K <= 8) {
+    hipLaunchKernelGGL((norm_fwd_group<T, K, J, A, LN>), grid, block, 0, st,
+                       static_cast<const T*>(x), static_cast<const T*>(w),
+                       static_cast<const T*>(b), static_cast<T*>(y), s0, s1, rows, n, eps, w_add,
+                       pl.W);
+  } else {
+    return hipErrorInvalidValue;  // the planner keeps K <= 8 and K * J <= 10 when W > 1
+  }
+  return hipGetLastError();
+}
 
 template <typename T, int K, bool A, bool LN>
 hipError_t launch_fwd_k(const FwdPlan& pl, const void* x, const void* w, const void* b, void* y,
                         float* s0, float* s1, int64_t rows, int n, float eps, float w_add,
                         hipStream_t st) {
-  const dim3 grid(static_cast<unsigned>((rows + pl.R - 1) / pl.R));
-  const dim3 block(64 * pl.W * pl.R);
-  if (pl.W == 1) {
-    hipLaunchKernelGGL((norm_fwd_wave<T, K, A, LN>), grid, block, 0, st,
-                       static_cast<const T*>(x), static_cast<const T*>(w),
-                       static_cast<const T*>(b), static_cast<T*>(y), s0, s1, rows, n, eps, w_add);
-  } else if constexpr (K <= 8) {
-    hipLaunchKernelGGL((norm_fwd_group<T, K, A, LN>), grid, block, 0, st,
-                       static_cast<const T*>(x), static_cast<const T*>(w),
-                       static_cast<const T*>(b), static_cast<T*>(y), s0, s1, rows, n, eps, w_add,
-                       pl.W);
-  } else {
-    return hipErrorInvalidValue;  // the planner never pairs W > 1 with K > 8
+  if constexpr (K <= 5) {
+    if (pl.J == 2) return launch_fwd_kj<T, K, 2, A, LN>(pl, x, w, b, y, s0, s1, rows, n, eps, w_add, st);
   }
-  return hipGetLastError();
+  if (pl.J != 1) return hipErrorInvalidValue;
+  return launch_fwd_kj<T, K, 1, A, LN>(pl, x, w, b, y, s0, s1, rows, n, eps, w_add, st);
 }
 
 template <typename T, bool A, bool LN>

@@ -10,17 +10,18 @@ namespace nr {
 constexpr int kF32 = 0;   // matches NR_F32
 constexpr int kBF16 = 1;  // matches NR_BF16
 
-// Forward row kernel: W waves per row, K 16-byte chunks per lane, R rows
-// per workgroup.  aligned: 128-bit loads/stores on every row.
+// Forward row kernel: W waves per row group, K 16-byte chunks per lane, J
+// rows per row group, R row groups per workgroup.  aligned: 128-bit
+// loads/stores on every row.
 struct FwdPlan {
-  int W, K, R;
+  int W, K, R, J;
   bool aligned;
 };
 
-// Backward stage 1: P workgroups of W waves, each over rows_per_block
-// consecutive rows, D rows per batch, K chunks per lane.
+// Backward stage 1: P workgroups of W waves, D rows per batch, K chunks per
+// lane, PF batches loaded ahead.
 struct BwdPlan {
-  int W, K, D, P;
+  int W, K, D, P, PF;
   int64_t rows_per_block;
   bool aligned;
 };

@@ -63,10 +63,11 @@ def test_norm_n_max():
 
 def test_workspace_bytes():
     # one fp32 partial row per backward workgroup; workgroups take >= 16 rows,
-    # at most 512 of them, none empty
+    # at most 256 (RMSNorm) or 512 (LayerNorm) of them, none empty
     assert nr.nr_bwd_workspace_bytes(3840, 5120, 0) == 240 * 5120 * 4
     assert nr.nr_bwd_workspace_bytes(3840, 5120, 1) == 2 * 240 * 5120 * 4
-    assert nr.nr_bwd_workspace_bytes(65536, 5120, 0) == 512 * 5120 * 4
+    assert nr.nr_bwd_workspace_bytes(65536, 5120, 0) == 256 * 5120 * 4
+    assert nr.nr_bwd_workspace_bytes(65536, 5120, 1) == 2 * 512 * 5120 * 4
     assert nr.nr_bwd_workspace_bytes(15360, 5120, 1) == 2 * 512 * 5120 * 4
     assert nr.nr_bwd_workspace_bytes(1, 7, 0) == 7 * 4
     assert nr.nr_bwd_workspace_bytes(0, 7, 0) == 0
