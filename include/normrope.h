@@ -162,6 +162,39 @@ nr_status_t rope_table_3d(float* cos_tab, float* sin_tab, int64_t frames,
                           int64_t pairs_h, int64_t pairs_w, double theta,
                           void* stream);
 
+/*
+ * rmsnorm_rope_fwd -- rmsnorm_fwd followed by interleaved RoPE on its output,
+ * fused into one pass: each row is read once and written once, rotated
+ * before its single rounding (the two operations of Helios 性能优化全解析,
+ * 内核一 FlashNorm and 内核二 FlashRoPE, which the write-up measures
+ * together).  A row of n = (heads in the row) x head_dim elements is
+ * normalised as in rmsnorm_fwd, then each head vector's pair i is rotated by
+ * cos_tab[tok][i], sin_tab[tok][i], tok = row / rows_per_token (1 when a row
+ * is a whole token; heads when each head is normalised on its own).  Tables
+ * are fp32 [rows / rows_per_token][head_dim / 2].  y may be x; inv_rms as in
+ * rmsnorm_fwd.
+ */
+nr_status_t rmsnorm_rope_fwd(nr_dtype_t dt, const void* x, const void* w,
+                             void* y, float* inv_rms, const float* cos_tab,
+                             const float* sin_tab, int64_t rows, int64_t n,
+                             int64_t head_dim, int64_t rows_per_token,
+                             float eps, int gemma_offset, void* stream);
+
+/*
+ * rmsnorm_rope_bwd -- backward of rmsnorm_rope_fwd: dout (the gradient of
+ * the rotated output) is rotated back by the same angles (sin negated) in
+ * registers and fed to the rmsnorm_bwd arithmetic; dx [rows][n] (may be
+ * dout), dw [n] fp32 or NULL.  Workspace as for rmsnorm_bwd
+ * (nr_bwd_workspace_bytes(rows, n, 0)).
+ */
+nr_status_t rmsnorm_rope_bwd(nr_dtype_t dt, const void* dout, const void* x,
+                             const void* w, const float* inv_rms,
+                             const float* cos_tab, const float* sin_tab,
+                             void* dx, float* dw, int64_t rows, int64_t n,
+                             int64_t head_dim, int64_t rows_per_token,
+                             int gemma_offset, void* workspace,
+                             size_t workspace_bytes, void* stream);
+
 /* Workspace bytes rmsnorm_bwd (is_layernorm = 0) or layernorm_bwd (1) needs
  * for dw / dgamma / dbeta at this shape.  Host only; pure function of its
  * arguments and the current tuning table. */
@@ -177,8 +210,8 @@ int nr_last_hip_error(void);
  * nr_tune -- override one launch-shape choice (for tuning sweeps; results
  * stay within the same tolerances, but the backward's summation order, and
  * so its exact bits, depend on the shape).  value 0 restores the automatic
- * choice.  Keys: "fwd_w", "fwd_k", "fwd_r", "bwd_w", "bwd_k", "bwd_d",
- * "bwd_p", "bwd_rows_min", "rope_k", "rope_wpb".  A key whose forced value
+ * choice.  Keys: "fwd_w", "fwd_k", "fwd_r", "fwd_j", "bwd_w", "bwd_k",
+ * "bwd_d", "bwd_p", "bwd_rows_min", "bwd_pf", "rope_k", "rope_wpb".  A key whose forced value
  * does not fit a call's shape makes that call return NR_ERR_SHAPE.
  * Returns NR_ERR_TUNE for an unknown key or a negative value.  Host only.
  */

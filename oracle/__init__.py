@@ -173,3 +173,31 @@ def rope_apply(x, angle, inverse=False):
     out = _out(b, t, h, d)
     lib().oracle_rope_apply(X.p, X.dt, b, t, h, d, _ptr(ang), int(bool(inverse)), _ptr(out))
     return out
+
+
+def _token_angles(angle, rows, rows_per_token):
+    ang = np.ascontiguousarray(angle, dtype=np.float64)
+    return ang[np.arange(rows) // rows_per_token]
+
+
+def rmsnorm_rope_fwd(x, w, angle, head_dim, rows_per_token=1, eps=1e-6, gemma=False):
+    """D1 then D6 on its output, in fp64 with no rounding in between.
+
+    x: [rows, n], n a multiple of head_dim; row i uses the angle row
+    i // rows_per_token.  Returns (out [rows, n], inv_rms [rows])."""
+    y, r = rmsnorm_fwd(x, w, eps, gemma)
+    rows, n = y.shape
+    ang = _token_angles(angle, rows, rows_per_token)
+    out = rope_apply(torch.from_numpy(y).view(1, rows, n // head_dim, head_dim), ang)
+    return out.reshape(rows, n), r
+
+
+def rmsnorm_rope_bwd(dout, x, w, angle, head_dim, rows_per_token=1, eps=1e-6, gemma=False,
+                     want_dx=True, want_dw=True):
+    """Backward of rmsnorm_rope_fwd: D6 inverse on dout, then D2.  Returns (dx, dw)."""
+    rows, n = x.shape
+    ang = _token_angles(angle, rows, rows_per_token)
+    dy = rope_apply(dout.reshape(1, rows, n // head_dim, head_dim), ang, inverse=True)
+    xd = x.detach().cpu().double() if isinstance(x, torch.Tensor) else torch.from_numpy(x)
+    return rmsnorm_bwd(torch.from_numpy(dy.reshape(rows, n)), xd, w, eps, gemma,
+                       want_dx=want_dx, want_dw=want_dw)

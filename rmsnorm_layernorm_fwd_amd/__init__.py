@@ -18,6 +18,7 @@ import torch
 
 __all__ = [
     "NormRopeError", "rmsnorm_fwd", "rmsnorm_bwd", "layernorm_fwd", "layernorm_bwd",
+    "rmsnorm_rope_fwd", "rmsnorm_rope_bwd",
     "rope_interleaved_apply", "rope_table_1d", "rope_table_3d", "nr_bwd_workspace_bytes",
     "nr_status_str", "nr_tune", "nr_norm_n_max", "library_path",
 ]
@@ -63,6 +64,8 @@ def _lib():
             "layernorm_fwd": [i32, vp, vp, vp, vp, vp, vp, i64, i64, f32, vp],
             "layernorm_bwd": [i32, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, vp, sz, vp],
             "rope_interleaved_apply": [i32, vp, vp, vp, i64, i64, i64, i64, i64, i64, i64, i32, vp],
+            "rmsnorm_rope_fwd": [i32, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, f32, i32, vp],
+            "rmsnorm_rope_bwd": [i32, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i32, vp, sz, vp],
             "rope_table_1d": [vp, vp, i64, i64, i64, f64, vp],
             "rope_table_3d": [vp, vp, i64, i64, i64, i64, i64, i64, f64, vp],
             "nr_bwd_workspace_bytes": [i64, i64, i32],
@@ -219,6 +222,62 @@ def layernorm_bwd(dy, x, gamma, mean, rstd, dx=None, want_dgamma=True, want_dbet
                                                  _ptr(rstd), _ptr(dx), _ptr(dgamma), _ptr(dbeta),
                                                  rows, n, _ptr(ws), wsb, _stream(x)))
     return dx, dgamma, dbeta
+
+
+# ---------------------------------------------------------------- fused RMSNorm + RoPE
+
+def _rope_rows(x, cos_tab, sin_tab, head_dim, rows_per_token):
+    rows, n = _rows_n(x)
+    if head_dim <= 0 or n % head_dim:
+        raise ValueError("the row length must be a whole number of head vectors")
+    tokens = -(-rows // rows_per_token) if rows else 0
+    _dev("cos_tab", cos_tab, torch.float32, (tokens, head_dim // 2))
+    _dev("sin_tab", sin_tab, torch.float32, (tokens, head_dim // 2))
+    return rows, n
+
+
+def rmsnorm_rope_fwd(x, w, cos_tab, sin_tab, head_dim, rows_per_token=1, eps=1e-6,
+                     gemma_offset=False, y=None, inv_rms=None, want_stats=True):
+    """rope(rmsnorm(x)) in one pass; rows of n = heads x head_dim; returns (y, inv_rms)."""
+    _dev("x", x)
+    dt = _dtype_code(x)
+    rows, n = _rope_rows(x, cos_tab, sin_tab, head_dim, rows_per_token)
+    _dev("w", w, x.dtype, (n,))
+    if y is None:
+        y = torch.empty_like(x)
+    _dev("y", y, x.dtype, x.shape)
+    if inv_rms is None and want_stats:
+        inv_rms = torch.empty(x.shape[:-1], dtype=torch.float32, device=x.device)
+    _dev("inv_rms", inv_rms, torch.float32)
+    _check("rmsnorm_rope_fwd", _lib().rmsnorm_rope_fwd(
+        dt, _ptr(x), _ptr(w), _ptr(y), _ptr(inv_rms), _ptr(cos_tab), _ptr(sin_tab), rows, n,
+        head_dim, rows_per_token, float(eps), int(bool(gemma_offset)), _stream(x)))
+    return y, inv_rms
+
+
+def rmsnorm_rope_bwd(dout, x, w, inv_rms, cos_tab, sin_tab, head_dim, rows_per_token=1,
+                     gemma_offset=False, dx=None, want_dw=True, dw=None, workspace=None):
+    """Backward of rmsnorm_rope_fwd; returns (dx, dw)."""
+    _dev("x", x)
+    dt = _dtype_code(x)
+    rows, n = _rope_rows(x, cos_tab, sin_tab, head_dim, rows_per_token)
+    _dev("dout", dout, x.dtype, x.shape)
+    _dev("w", w, x.dtype, (n,))
+    _dev("inv_rms", inv_rms, torch.float32, x.shape[:-1])
+    if dx is None:
+        dx = torch.empty_like(x)
+    _dev("dx", dx, x.dtype, x.shape)
+    if dw is None and want_dw:
+        dw = torch.empty(n, dtype=torch.float32, device=x.device)
+    _dev("dw", dw, torch.float32, (n,))
+    ws, wsb = (None, 0)
+    if dw is not None:
+        ws, wsb = _workspace(rows, n, 0, workspace, x.device)
+    _check("rmsnorm_rope_bwd", _lib().rmsnorm_rope_bwd(
+        dt, _ptr(dout), _ptr(x), _ptr(w), _ptr(inv_rms), _ptr(cos_tab), _ptr(sin_tab), _ptr(dx),
+        _ptr(dw), rows, n, head_dim, rows_per_token, int(bool(gemma_offset)), _ptr(ws), wsb,
+        _stream(x)))
+    return dx, dw
 
 
 # ---------------------------------------------------------------- RoPE

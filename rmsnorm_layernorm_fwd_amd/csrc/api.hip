@@ -143,7 +143,8 @@ void bwd_grid(int64_t rows, bool ln, int64_t* P_out, int64_t* rpb_out) {
   *rpb_out = rpb;
 }
 
-nr_status_t plan_bwd(nr_dtype_t dt, bool ln, int64_t rows, int64_t n, bool aligned, BwdPlan* pl) {
+nr_status_t plan_bwd(nr_dtype_t dt, bool ln, int64_t rows, int64_t n, bool aligned, BwdPlan* pl,
+                     bool rope = false) {
   const int E = vec_elems(dt);
   const int64_t nchunk = (n + E - 1) / E;
   const int64_t need = (nchunk + 63) / 64;
@@ -157,7 +158,9 @@ nr_status_t plan_bwd(nr_dtype_t dt, bool ln, int64_t rows, int64_t n, bool align
   if (tune(BWD_K) > 0) K = tune(BWD_K);
   if (K > 0) W = static_cast<int>((need + K - 1) / K);
   if (tune(BWD_W) > 0) W = tune(BWD_W);
-  int D = (!ln && K == 1) ? 2 : 1;
+  // (the fused RMSNorm + RoPE backward also holds each chunk's cos/sin: one
+  // row per batch, two batches ahead)
+  int D = (!ln && !rope && K == 1) ? 2 : 1;
   int PF = (!ln && K == 1) ? 2 : 1;
   if (tune(BWD_D) > 0) D = tune(BWD_D);
   if (tune(BWD_PF) > 0) PF = tune(BWD_PF);
@@ -325,6 +328,91 @@ nr_status_t layernorm_bwd(nr_dtype_t dt, const void* dy, const void* x, const vo
                           size_t workspace_bytes, void* stream) {
   return norm_bwd_common(true, dt, dy, x, gamma, mean, rstd, dx, dgamma, dbeta, rows, n, 0.0f,
                          workspace, workspace_bytes, stream);
+}
+
+namespace {
+
+// Checks shared by the fused RMSNorm + RoPE calls: whole heads per row, an
+// even head size, a token index per row; reports whether the 128-bit path
+// applies to the tables.
+nr_status_t check_rope_rows(nr_dtype_t dt, const float* cos_tab, const float* sin_tab,
+                            int64_t n, int64_t head_dim, int64_t rows_per_token, bool* vec_ok) {
+  if (head_dim < 2 || (head_dim & 1) || n % head_dim != 0 || rows_per_token < 1)
+    return NR_ERR_SHAPE;
+  if (cos_tab == nullptr || sin_tab == nullptr) return NR_ERR_NULLPTR;
+  *vec_ok = head_dim % vec_elems(dt) == 0 && aligned16(cos_tab) && aligned16(sin_tab);
+  return NR_OK;
+}
+
+}  // namespace
+
+nr_status_t rmsnorm_rope_fwd(nr_dtype_t dt, const void* x, const void* w, void* y, float* inv_rms,
+                             const float* cos_tab, const float* sin_tab, int64_t rows, int64_t n,
+                             int64_t head_dim, int64_t rows_per_token, float eps,
+                             int gemma_offset, void* stream) {
+  nr_status_t s;
+  if ((s = check_dtype(dt)) != NR_OK) return s;
+  if ((s = check_norm_shape(dt, rows, n)) != NR_OK) return s;
+  if (head_dim < 2 || (head_dim & 1) || n % head_dim != 0 || rows_per_token < 1)
+    return NR_ERR_SHAPE;
+  if (rows == 0) return NR_OK;
+  if (x == nullptr || y == nullptr) return NR_ERR_NULLPTR;
+  bool vec_tab;
+  if ((s = check_rope_rows(dt, cos_tab, sin_tab, n, head_dim, rows_per_token, &vec_tab)) != NR_OK)
+    return s;
+  const size_t bytes = static_cast<size_t>(rows * n) * elem_bytes(dt);
+  if (bad_overlap(y, bytes, x, bytes)) return NR_ERR_ALIAS;
+  const bool aligned = vec_tab && (n % vec_elems(dt)) == 0 && aligned16(x) && aligned16(y) &&
+                       (w == nullptr || aligned16(w));
+  FwdPlan pl;
+  if ((s = plan_fwd(dt, n, aligned, &pl)) != NR_OK) return s;
+  const nr::RopeArgs ra{cos_tab, sin_tab, static_cast<int>(head_dim), rows_per_token};
+  return hip_status(nr::launch_rms_rope_fwd(dt, pl, x, w, y, inv_rms, ra, rows, static_cast<int>(n),
+                                            eps, gemma_offset ? 1.0f : 0.0f,
+                                            static_cast<hipStream_t>(stream)));
+}
+
+nr_status_t rmsnorm_rope_bwd(nr_dtype_t dt, const void* dout, const void* x, const void* w,
+                             const float* inv_rms, const float* cos_tab, const float* sin_tab,
+                             void* dx, float* dw, int64_t rows, int64_t n, int64_t head_dim,
+                             int64_t rows_per_token, int gemma_offset, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+  nr_status_t s;
+  if ((s = check_dtype(dt)) != NR_OK) return s;
+  if ((s = check_norm_shape(dt, rows, n)) != NR_OK) return s;
+  if (head_dim < 2 || (head_dim & 1) || n % head_dim != 0 || rows_per_token < 1)
+    return NR_ERR_SHAPE;
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  if (rows == 0) {
+    if (dw == nullptr) return NR_OK;
+    return hip_status(nr::launch_colreduce(nullptr, 0, 0, static_cast<int>(n), dw, nullptr, st));
+  }
+  if (dout == nullptr || x == nullptr || dx == nullptr || inv_rms == nullptr) return NR_ERR_NULLPTR;
+  bool vec_tab;
+  if ((s = check_rope_rows(dt, cos_tab, sin_tab, n, head_dim, rows_per_token, &vec_tab)) != NR_OK)
+    return s;
+  const size_t bytes = static_cast<size_t>(rows * n) * elem_bytes(dt);
+  if (bad_overlap(dx, bytes, dout, bytes) || bad_overlap(dx, bytes, x, bytes)) return NR_ERR_ALIAS;
+  const bool aligned = vec_tab && (n % vec_elems(dt)) == 0 && aligned16(dout) && aligned16(x) &&
+                       aligned16(dx) && (w == nullptr || aligned16(w));
+  BwdPlan pl;
+  if ((s = plan_bwd(dt, false, rows, n, aligned, &pl, true)) != NR_OK) return s;
+  float* part = nullptr;
+  if (dw != nullptr) {
+    const size_t need = static_cast<size_t>(pl.P) * n * sizeof(float);
+    if (workspace == nullptr || workspace_bytes < need || !aligned16(workspace))
+      return NR_ERR_WORKSPACE;
+    part = static_cast<float*>(workspace);
+  }
+  const nr::RopeArgs ra{cos_tab, sin_tab, static_cast<int>(head_dim), rows_per_token};
+  if ((s = hip_status(nr::launch_rms_rope_bwd(dt, pl, dout, x, w, inv_rms, ra, dx, part, rows,
+                                              static_cast<int>(n), gemma_offset ? 1.0f : 0.0f,
+                                              st))) != NR_OK)
+    return s;
+  if (dw != nullptr)
+    return hip_status(nr::launch_colreduce(part, static_cast<int64_t>(pl.P) * n, pl.P,
+                                           static_cast<int>(n), dw, nullptr, st));
+  return NR_OK;
 }
 
 nr_status_t rope_interleaved_apply(nr_dtype_t dt, void* x, const float* cos_tab,

@@ -33,16 +33,21 @@ namespace nr {
 //        dx = r (g - a - xhat bb), partial dgamma += dy xhat, dbeta += dy
 // part: [2][P][n] fp32 (second matrix, at part + part_stride, for dbeta);
 // null when no column gradient is wanted.
-template <typename T, int K, int D>
+// D rows of x and dy as loaded (packed), their statistics and, for the fused
+// RMSNorm + RoPE backward, each chunk's cos/sin (R = 1 when unused).
+template <typename T, int K, int D, int R = 1>
 struct RowBatch {
   u32x4 x[D * K], g[D * K];
   float rs[D], mu[D];
+  float tc[R * D * K][Vec<T>::N / 2], ts[R * D * K][Vec<T>::N / 2];
 };
 
-template <typename T, int K, int D, bool VEC, bool LN>
-__device__ __forceinline__ void load_batch(RowBatch<T, K, D>& b, int64_t base, int64_t rows,
-                                           const T* x, const T* dy, const float* mean,
-                                           const float* rstat, int n, int t, int nthr) {
+template <typename T, int K, int D, bool VEC, bool LN, bool ROPE>
+__device__ __forceinline__ void load_batch(RowBatch<T, K, D, ROPE ? 1 : 0>& b, int64_t base,
+                                           int64_t rows, const T* x, const T* dy,
+                                           const float* mean, const float* rstat, int n, int t,
+                                           int nthr, const RopeArgs& ra) {
+  constexpr int E = Vec<T>::N;
   const uint32_t rbytes = static_cast<uint32_t>(n) * sizeof(T);
 #pragma unroll
   for (int d = 0; d < D; ++d) {
@@ -59,13 +64,51 @@ __device__ __forceinline__ void load_batch(RowBatch<T, K, D>& b, int64_t base, i
     }
     b.rs[d] = okr ? rstat[row] : 0.0f;
     b.mu[d] = (LN && okr) ? mean[row] : 0.0f;
+    if constexpr (ROPE) {
+      // the token's table rows; this lane's chunks sit at fixed offsets in
+      // their heads (see the forward)
+      constexpr int PP = E / 2;
+      const int half = ra.head_dim >> 1;
+      const int64_t tok = (okr ? row : 0) / ra.rows_per_token;
+      const uint32_t tb = okr ? static_cast<uint32_t>(half) * 4u : 0u;
+      const rsrc_t cr = make_rsrc(ra.cos_tab + tok * half, tb);
+      const rsrc_t sr = make_rsrc(ra.sin_tab + tok * half, tb);
+      int hoff = (t * E) % ra.head_dim;
+      const int hstep = (nthr * E) % ra.head_dim;
+#pragma unroll
+      for (int k = 0; k < K; ++k) {
+        if constexpr (VEC) {
+          load_tab<PP>(cr, hoff >> 1, b.tc[d * K + k]);
+          load_tab<PP>(sr, hoff >> 1, b.ts[d * K + k]);
+        } else {
+#pragma unroll
+          for (int p = 0; p < PP; ++p) {
+            const int ho = (hoff + 2 * p) % ra.head_dim;
+            b.tc[d * K + k][p] = ld_f32(cr, (ho >> 1) * 4);
+            b.ts[d * K + k][p] = ld_f32(sr, (ho >> 1) * 4);
+          }
+        }
+        hoff += hstep;
+        if (hoff >= ra.head_dim) hoff -= ra.head_dim;
+      }
+    }
   }
 }
 
-template <typename T, int K, int D, bool VEC, bool LN>
-__device__ __forceinline__ void process_batch(RowBatch<T, K, D>& b, int64_t base, int64_t rows,
-                                              T* dx, int n, int t, int nthr, int W, int wave,
-                                              int lane, float inv_n, const float (&wv)[K][Vec<T>::N],
+// dy of chunk i as fp32: the loaded values, rotated back by the token's
+// angles when the upstream gradient is that of a RoPE output
+template <typename T, int K, int D, bool ROPE>
+__device__ __forceinline__ void dy_chunk(const RowBatch<T, K, D, ROPE ? 1 : 0>& b, int i,
+                                         float (&dv)[Vec<T>::N]) {
+  unpack<T>(b.g[i], dv);
+  if constexpr (ROPE) rotate_pairs<Vec<T>::N / 2>(dv, b.tc[i], b.ts[i], -1.0f);
+}
+
+template <typename T, int K, int D, bool VEC, bool LN, bool ROPE>
+__device__ __forceinline__ void process_batch(RowBatch<T, K, D, ROPE ? 1 : 0>& b, int64_t base,
+                                              int64_t rows, T* dx, int n, int t, int nthr, int W,
+                                              int wave, int lane, float inv_n,
+                                              const float (&wv)[K][Vec<T>::N],
                                               float (&acc1)[K][Vec<T>::N],
                                               float (&acc2)[K][Vec<T>::N],
                                               float (*red)[16], int& parity) {
@@ -83,7 +126,7 @@ __device__ __forceinline__ void process_batch(RowBatch<T, K, D>& b, int64_t base
       const int c = t + k * nthr;
       float xv[E], dv[E];
       unpack<T>(b.x[d * K + k], xv);
-      unpack<T>(b.g[d * K + k], dv);
+      dy_chunk<T, K, D, ROPE>(b, d * K + k, dv);
 #pragma unroll
       for (int e = 0; e < E; ++e) {
         float xh = (xv[e] - b.mu[d]) * b.rs[d];
@@ -136,7 +179,7 @@ __device__ __forceinline__ void process_batch(RowBatch<T, K, D>& b, int64_t base
     for (int k = 0; k < K; ++k) {
       float xv[E], dv[E], o[E];
       unpack<T>(b.x[d * K + k], xv);
-      unpack<T>(b.g[d * K + k], dv);
+      dy_chunk<T, K, D, ROPE>(b, d * K + k, dv);
 #pragma unroll
       for (int e = 0; e < E; ++e) {
         const float xh = (xv[e] - b.mu[d]) * b.rs[d];
@@ -152,10 +195,11 @@ __device__ __forceinline__ void process_batch(RowBatch<T, K, D>& b, int64_t base
   }
 }
 
-template <typename T, int K, int D, int PF, bool VEC, bool LN>
+template <typename T, int K, int D, int PF, bool VEC, bool LN, bool ROPE>
 __global__ void __launch_bounds__(1024)
 norm_bwd_rows(const T* dy, const T* x, const T* w, const float* mean, const float* rstat,
-              T* dx, float* part, int64_t part_stride, int64_t rows, int n, float w_add) {
+              T* dx, float* part, int64_t part_stride, int64_t rows, int n, float w_add,
+              RopeArgs ra) {
   constexpr int E = Vec<T>::N;
   constexpr int NS = LN ? 2 : 1;
   __shared__ float red[2 * NS * D][16];
@@ -193,18 +237,19 @@ norm_bwd_rows(const T* dy, const T* x, const T* w, const float* mean, const floa
   // PF batches are loaded ahead of the one being reduced; PF + 1 register
   // buffers are used in turn (the loop is unrolled over them, so no register
   // copy ever waits on a load in flight).
-  RowBatch<T, K, D> buf[PF + 1];
+  RowBatch<T, K, D, ROPE ? 1 : 0> buf[PF + 1];
 #pragma unroll
   for (int i = 0; i < PF; ++i)
-    load_batch<T, K, D, VEC, LN>(buf[i], base + i * step, rows, x, dy, mean, rstat, n, t, nthr);
+    load_batch<T, K, D, VEC, LN, ROPE>(buf[i], base + i * step, rows, x, dy, mean, rstat, n, t,
+                                       nthr, ra);
   while (true) {
 #pragma unroll
     for (int i = 0; i <= PF; ++i) {
       if (base >= rows) goto done;
-      load_batch<T, K, D, VEC, LN>(buf[(i + PF) % (PF + 1)], base + PF * step, rows, x, dy, mean,
-                                   rstat, n, t, nthr);
-      process_batch<T, K, D, VEC, LN>(buf[i], base, rows, dx, n, t, nthr, W, wave, lane, inv_n, wv,
-                                      acc1, acc2, red, parity);
+      load_batch<T, K, D, VEC, LN, ROPE>(buf[(i + PF) % (PF + 1)], base + PF * step, rows, x, dy,
+                                         mean, rstat, n, t, nthr, ra);
+      process_batch<T, K, D, VEC, LN, ROPE>(buf[i], base, rows, dx, n, t, nthr, W, wave, lane,
+                                            inv_n, wv, acc1, acc2, red, parity);
       base += step;
     }
   }
@@ -283,30 +328,30 @@ colreduce(const float* part, int64_t part_stride, int P, int n, float* out0, flo
 
 namespace {
 
-template <typename T, int K, int D, bool A, bool LN>
+template <typename T, int K, int D, bool A, bool LN, bool RP>
 hipError_t launch_bwd_kd(const BwdPlan& pl, const void* dy, const void* x, const void* w,
                          const float* mean, const float* rstat, void* dx, float* part,
-                         int64_t rows, int n, float w_add, hipStream_t st) {
+                         int64_t rows, int n, float w_add, const RopeArgs& ra, hipStream_t st) {
   const int64_t part_stride = static_cast<int64_t>(pl.P) * n;
-  auto kern = pl.PF == 2 ? norm_bwd_rows<T, K, D, 2, A, LN> : norm_bwd_rows<T, K, D, 1, A, LN>;
-  hipLaunchKernelGGL(kern, dim3(pl.P), dim3(64 * pl.W), 0, st,
-                     static_cast<const T*>(dy), static_cast<const T*>(x),
-                     static_cast<const T*>(w), mean, rstat, static_cast<T*>(dx), part,
-                     part_stride, rows, n, w_add);
+  auto kern = pl.PF == 2 ? norm_bwd_rows<T, K, D, 2, A, LN, RP> : norm_bwd_rows<T, K, D, 1, A, LN, RP>;
+  hipLaunchKernelGGL(kern, dim3(pl.P), dim3(64 * pl.W), 0, st, static_cast<const T*>(dy),
+                     static_cast<const T*>(x), static_cast<const T*>(w), mean, rstat,
+                     static_cast<T*>(dx), part, part_stride, rows, n, w_add, ra);
   return hipGetLastError();
 }
 
 // (K, D) pairs with K * D <= 8: the row batch stays within the register
 // budget of a 1024-thread workgroup.
-template <typename T, bool A, bool LN>
+template <typename T, bool A, bool LN, bool RP>
 hipError_t launch_bwd_a(const BwdPlan& pl, const void* dy, const void* x, const void* w,
                         const float* mean, const float* rstat, void* dx, float* part,
-                        int64_t rows, int n, float w_add, hipStream_t st) {
+                        int64_t rows, int n, float w_add, const RopeArgs& ra, hipStream_t st) {
   const int key = pl.K * 16 + pl.D;
   switch (key) {
-#define NR_CASE(KK, DD)                                                                       \
-  case KK * 16 + DD:                                                                          \
-    return launch_bwd_kd<T, KK, DD, A, LN>(pl, dy, x, w, mean, rstat, dx, part, rows, n, w_add, st);
+#define NR_CASE(KK, DD)                                                                          \
+  case KK * 16 + DD:                                                                             \
+    return launch_bwd_kd<T, KK, DD, A, LN, RP>(pl, dy, x, w, mean, rstat, dx, part, rows, n, w_add, \
+                                               ra, st);
     NR_CASE(1, 1) NR_CASE(1, 2) NR_CASE(1, 4) NR_CASE(1, 8)
     NR_CASE(2, 1) NR_CASE(2, 2) NR_CASE(2, 4)
     NR_CASE(4, 1) NR_CASE(4, 2)
@@ -316,12 +361,12 @@ hipError_t launch_bwd_a(const BwdPlan& pl, const void* dy, const void* x, const 
   }
 }
 
-template <typename T, bool LN>
+template <typename T, bool LN, bool RP>
 hipError_t launch_bwd_t(const BwdPlan& pl, const void* dy, const void* x, const void* w,
                         const float* mean, const float* rstat, void* dx, float* part,
-                        int64_t rows, int n, float w_add, hipStream_t st) {
-  return pl.aligned ? launch_bwd_a<T, true, LN>(pl, dy, x, w, mean, rstat, dx, part, rows, n, w_add, st)
-                    : launch_bwd_a<T, false, LN>(pl, dy, x, w, mean, rstat, dx, part, rows, n, w_add, st);
+                        int64_t rows, int n, float w_add, const RopeArgs& ra, hipStream_t st) {
+  return pl.aligned ? launch_bwd_a<T, true, LN, RP>(pl, dy, x, w, mean, rstat, dx, part, rows, n, w_add, ra, st)
+                    : launch_bwd_a<T, false, LN, RP>(pl, dy, x, w, mean, rstat, dx, part, rows, n, w_add, ra, st);
 }
 
 }  // namespace
@@ -329,11 +374,22 @@ hipError_t launch_bwd_t(const BwdPlan& pl, const void* dy, const void* x, const 
 hipError_t launch_norm_bwd(bool ln, int dt, const BwdPlan& pl, const void* dy, const void* x,
                            const void* w, const float* mean, const float* rstat, void* dx,
                            float* part, int64_t rows, int n, float w_add, hipStream_t st) {
+  const RopeArgs none{nullptr, nullptr, 2, 1};
   if (dt == kF32)
-    return ln ? launch_bwd_t<float, true>(pl, dy, x, w, mean, rstat, dx, part, rows, n, w_add, st)
-              : launch_bwd_t<float, false>(pl, dy, x, w, mean, rstat, dx, part, rows, n, w_add, st);
-  return ln ? launch_bwd_t<bf16, true>(pl, dy, x, w, mean, rstat, dx, part, rows, n, w_add, st)
-            : launch_bwd_t<bf16, false>(pl, dy, x, w, mean, rstat, dx, part, rows, n, w_add, st);
+    return ln ? launch_bwd_t<float, true, false>(pl, dy, x, w, mean, rstat, dx, part, rows, n, w_add, none, st)
+              : launch_bwd_t<float, false, false>(pl, dy, x, w, mean, rstat, dx, part, rows, n, w_add, none, st);
+  return ln ? launch_bwd_t<bf16, true, false>(pl, dy, x, w, mean, rstat, dx, part, rows, n, w_add, none, st)
+            : launch_bwd_t<bf16, false, false>(pl, dy, x, w, mean, rstat, dx, part, rows, n, w_add, none, st);
+}
+
+hipError_t launch_rms_rope_bwd(int dt, const BwdPlan& pl, const void* dout, const void* x,
+                               const void* w, const float* inv_rms, const RopeArgs& ra, void* dx,
+                               float* part, int64_t rows, int n, float w_add, hipStream_t st) {
+  if (dt == kF32)
+    return launch_bwd_t<float, false, true>(pl, dout, x, w, nullptr, inv_rms, dx, part, rows, n,
+                                            w_add, ra, st);
+  return launch_bwd_t<bf16, false, true>(pl, dout, x, w, nullptr, inv_rms, dx, part, rows, n,
+                                         w_add, ra, st);
 }
 
 hipError_t launch_colreduce(const float* part, int64_t part_stride, int P, int n, float* out0,

@@ -41,11 +41,13 @@ __device__ __forceinline__ void group_sum_n(float (&v)[J], int W, int wave, int 
 }
 
 // A row group (W waves) normalises J consecutive rows; the weight chunks it
-// loads serve all J of them.
-template <typename T, int K, int J, bool VEC, bool LN>
+// loads serve all J of them.  ROPE (RMSNorm only): before the single rounding,
+// the normalised row is rotated as interleaved RoPE pairs by its token's
+// angles, so the norm -> RoPE chain costs one read and one write of the row.
+template <typename T, int K, int J, bool VEC, bool LN, bool ROPE>
 __device__ __forceinline__ void norm_fwd_body(const T* x, const T* w, const T* b, T* y,
                                               float* stat0, float* stat1, int64_t rows, int n,
-                                              float eps, float w_add, int W) {
+                                              float eps, float w_add, int W, const RopeArgs& ra) {
   constexpr int E = Vec<T>::N;
   __shared__ float red0[J][16], red1[J][16];
   const int lane = threadIdx.x & 63;
@@ -143,6 +145,15 @@ __device__ __forceinline__ void norm_fwd_body(const T* x, const T* w, const T* b
     const int64_t row = row0 + j;
     const bool active = row < rows;
     const rsrc_t yr = make_rsrc(y + (active ? row : 0) * static_cast<int64_t>(n), active ? rbytes : 0u);
+    // RoPE: the token's table rows, and the offset within its head of this
+    // lane's first chunk (advancing by a fixed step per chunk)
+    const int half = ra.head_dim >> 1;
+    const int64_t tok = ROPE ? (active ? row : 0) / ra.rows_per_token : 0;
+    const uint32_t tb = (ROPE && active) ? static_cast<uint32_t>(half) * 4u : 0u;
+    const rsrc_t cr = make_rsrc(ra.cos_tab + tok * half, tb);
+    const rsrc_t sr = make_rsrc(ra.sin_tab + tok * half, tb);
+    int hoff = ROPE ? (t * E) % ra.head_dim : 0;
+    const int hstep = ROPE ? (nthr * E) % ra.head_dim : 0;
 #pragma unroll
     for (int k = 0; k < K; ++k) {
       float v[E], wv[E], bv[E], o[E];
@@ -157,6 +168,25 @@ __device__ __forceinline__ void norm_fwd_body(const T* x, const T* w, const T* b
         } else {
           o[e] = (v[e] * r[j]) * ww;
         }
+      }
+      if constexpr (ROPE) {
+        constexpr int PP = E / 2;
+        float cf[PP], sf[PP];
+        if constexpr (VEC) {
+          // whole chunks lie inside one head: PP consecutive pairs
+          load_tab<PP>(cr, hoff >> 1, cf);
+          load_tab<PP>(sr, hoff >> 1, sf);
+        } else {
+#pragma unroll
+          for (int p = 0; p < PP; ++p) {
+            const int ho = (hoff + 2 * p) % ra.head_dim;
+            cf[p] = ld_f32(cr, (ho >> 1) * 4);
+            sf[p] = ld_f32(sr, (ho >> 1) * 4);
+          }
+        }
+        rotate_pairs<PP>(o, cf, sf, 1.0f);
+        hoff += hstep;
+        if (hoff >= ra.head_dim) hoff -= ra.head_dim;
       }
       st_chunk<T, VEC, kStream>(yr, t + k * nthr, pack<T>(o));
     }
@@ -173,75 +203,77 @@ __device__ __forceinline__ void norm_fwd_body(const T* x, const T* w, const T* b
 
 // One wavefront per row group (W == 1), at most 4 row groups (256 threads)
 // per workgroup.
-template <typename T, int K, int J, bool VEC, bool LN>
+template <typename T, int K, int J, bool VEC, bool LN, bool ROPE>
 __global__ void __launch_bounds__(256)
 norm_fwd_wave(const T* x, const T* w, const T* b, T* y, float* stat0, float* stat1,
-              int64_t rows, int n, float eps, float w_add) {
-  norm_fwd_body<T, K, J, VEC, LN>(x, w, b, y, stat0, stat1, rows, n, eps, w_add, 1);
+              int64_t rows, int n, float eps, float w_add, RopeArgs ra) {
+  norm_fwd_body<T, K, J, VEC, LN, ROPE>(x, w, b, y, stat0, stat1, rows, n, eps, w_add, 1, ra);
 }
 
 // Several waves per row group (W > 1), up to 16 waves per workgroup.
-template <typename T, int K, int J, bool VEC, bool LN>
+template <typename T, int K, int J, bool VEC, bool LN, bool ROPE>
 __global__ void __launch_bounds__(1024)
 norm_fwd_group(const T* x, const T* w, const T* b, T* y, float* stat0, float* stat1,
-               int64_t rows, int n, float eps, float w_add, int W) {
-  norm_fwd_body<T, K, J, VEC, LN>(x, w, b, y, stat0, stat1, rows, n, eps, w_add, W);
+               int64_t rows, int n, float eps, float w_add, int W, RopeArgs ra) {
+  norm_fwd_body<T, K, J, VEC, LN, ROPE>(x, w, b, y, stat0, stat1, rows, n, eps, w_add, W, ra);
 }
 
 namespace {
 
-template <typename T, int K, int J, bool A, bool LN>
+template <typename T, int K, int J, bool A, bool LN, bool RP>
 hipError_t launch_fwd_kj(const FwdPlan& pl, const void* x, const void* w, const void* b, void* y,
                          float* s0, float* s1, int64_t rows, int n, float eps, float w_add,
-                         hipStream_t st) {
+                         const RopeArgs& ra, hipStream_t st) {
   const int64_t per_block = static_cast<int64_t>(pl.R) * J;
   const dim3 grid(static_cast<unsigned>((rows + per_block - 1) / per_block));
   const dim3 block(64 * pl.W * pl.R);
   if (pl.W == 1) {
-    hipLaunchKernelGGL((norm_fwd_wave<T, K, J, A, LN>), grid, block, 0, st,
-                       static_cast<const T*>(x), static_cast<const T*>(w),
-                       static_cast<const T*>(b), static_cast<T*>(y), s0, s1, rows, n, eps, w_add);
-  } else if constexpr (K * J <= 10 && K <= 8) {
-    hipLaunchKernelGGL((norm_fwd_group<T, K, J, A, LN>), grid, block, 0, st,
+    hipLaunchKernelGGL((norm_fwd_wave<T, K, J, A, LN, RP>), grid, block, 0, st,
                        static_cast<const T*>(x), static_cast<const T*>(w),
                        static_cast<const T*>(b), static_cast<T*>(y), s0, s1, rows, n, eps, w_add,
-                       pl.W);
+                       ra);
+  } else if constexpr (K * J <= 10 && K <= 8) {
+    hipLaunchKernelGGL((norm_fwd_group<T, K, J, A, LN, RP>), grid, block, 0, st,
+                       static_cast<const T*>(x), static_cast<const T*>(w),
+                       static_cast<const T*>(b), static_cast<T*>(y), s0, s1, rows, n, eps, w_add,
+                       pl.W, ra);
   } else {
     return hipErrorInvalidValue;  // the planner keeps K <= 8 and K * J <= 10 when W > 1
   }
   return hipGetLastError();
 }
 
-template <typename T, int K, bool A, bool LN>
+template <typename T, int K, bool A, bool LN, bool RP>
 hipError_t launch_fwd_k(const FwdPlan& pl, const void* x, const void* w, const void* b, void* y,
                         float* s0, float* s1, int64_t rows, int n, float eps, float w_add,
-                        hipStream_t st) {
+                        const RopeArgs& ra, hipStream_t st) {
   if constexpr (K <= 5) {
-    if (pl.J == 2) return launch_fwd_kj<T, K, 2, A, LN>(pl, x, w, b, y, s0, s1, rows, n, eps, w_add, st);
+    if (pl.J == 2)
+      return launch_fwd_kj<T, K, 2, A, LN, RP>(pl, x, w, b, y, s0, s1, rows, n, eps, w_add, ra, st);
   }
   if (pl.J != 1) return hipErrorInvalidValue;
-  return launch_fwd_kj<T, K, 1, A, LN>(pl, x, w, b, y, s0, s1, rows, n, eps, w_add, st);
+  return launch_fwd_kj<T, K, 1, A, LN, RP>(pl, x, w, b, y, s0, s1, rows, n, eps, w_add, ra, st);
 }
 
-template <typename T, bool A, bool LN>
+template <typename T, bool A, bool LN, bool RP>
 hipError_t launch_fwd_a(const FwdPlan& pl, const void* x, const void* w, const void* b, void* y,
                         float* s0, float* s1, int64_t rows, int n, float eps, float w_add,
-                        hipStream_t st) {
+                        const RopeArgs& ra, hipStream_t st) {
   switch (pl.K) {
 #define NR_CASE(KK) \
-  case KK: return launch_fwd_k<T, KK, A, LN>(pl, x, w, b, y, s0, s1, rows, n, eps, w_add, st);
+  case KK: return launch_fwd_k<T, KK, A, LN, RP>(pl, x, w, b, y, s0, s1, rows, n, eps, w_add, ra, st);
     NR_CASE(1) NR_CASE(2) NR_CASE(4) NR_CASE(5) NR_CASE(6) NR_CASE(8) NR_CASE(10)
 #undef NR_CASE
     default: return hipErrorInvalidValue;
   }
 }
 
-template <typename T, bool LN>
+template <typename T, bool LN, bool RP>
 hipError_t launch_fwd_t(const FwdPlan& pl, const void* x, const void* w, const void* b, void* y,
                         float* s0, float* s1, int64_t rows, int n, float eps, float w_add,
-                        hipStream_t st) {
-  return pl.aligned ? launch_fwd_a<T, true, LN>(pl, x, w, b, y, s0, s1, rows, n, eps, w_add, st)
-                    : launch_fwd_a<T, false, LN>(pl, x, w, b, y, s0, s1, rows, n, eps, w_add, st);
+                        const RopeArgs& ra, hipStream_t st) {
+  return pl.aligned ? launch_fwd_a<T, true, LN, RP>(pl, x, w, b, y, s0, s1, rows, n, eps, w_add, ra, st)
+                    : launch_fwd_a<T, false, LN, RP>(pl, x, w, b, y, s0, s1, rows, n, eps, w_add, ra, st);
 }
 
 }  // namespace
@@ -249,11 +281,22 @@ hipError_t launch_fwd_t(const FwdPlan& pl, const void* x, const void* w, const v
 hipError_t launch_norm_fwd(bool ln, int dt, const FwdPlan& pl, const void* x, const void* w,
                            const void* b, void* y, float* s0, float* s1, int64_t rows, int n,
                            float eps, float w_add, hipStream_t st) {
+  const RopeArgs none{nullptr, nullptr, 2, 1};
   if (dt == kF32)
-    return ln ? launch_fwd_t<float, true>(pl, x, w, b, y, s0, s1, rows, n, eps, w_add, st)
-              : launch_fwd_t<float, false>(pl, x, w, b, y, s0, s1, rows, n, eps, w_add, st);
-  return ln ? launch_fwd_t<bf16, true>(pl, x, w, b, y, s0, s1, rows, n, eps, w_add, st)
-            : launch_fwd_t<bf16, false>(pl, x, w, b, y, s0, s1, rows, n, eps, w_add, st);
+    return ln ? launch_fwd_t<float, true, false>(pl, x, w, b, y, s0, s1, rows, n, eps, w_add, none, st)
+              : launch_fwd_t<float, false, false>(pl, x, w, b, y, s0, s1, rows, n, eps, w_add, none, st);
+  return ln ? launch_fwd_t<bf16, true, false>(pl, x, w, b, y, s0, s1, rows, n, eps, w_add, none, st)
+            : launch_fwd_t<bf16, false, false>(pl, x, w, b, y, s0, s1, rows, n, eps, w_add, none, st);
+}
+
+hipError_t launch_rms_rope_fwd(int dt, const FwdPlan& pl, const void* x, const void* w, void* y,
+                               float* inv_rms, const RopeArgs& ra, int64_t rows, int n, float eps,
+                               float w_add, hipStream_t st) {
+  if (dt == kF32)
+    return launch_fwd_t<float, false, true>(pl, x, w, nullptr, y, inv_rms, nullptr, rows, n, eps,
+                                            w_add, ra, st);
+  return launch_fwd_t<bf16, false, true>(pl, x, w, nullptr, y, inv_rms, nullptr, rows, n, eps,
+                                         w_add, ra, st);
 }
 
 }  // namespace nr

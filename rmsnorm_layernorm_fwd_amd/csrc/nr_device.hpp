@@ -166,6 +166,41 @@ template <> __device__ __forceinline__ void st_elem<bf16>(rsrc_t r, int byte_off
                                         byte_off, 0, 0);
 }
 
+// ---- interleaved RoPE helpers ------------------------------------------
+
+// PP consecutive fp32 entries starting at entry e0 of a table row buffer
+template <int PP>
+__device__ __forceinline__ void load_tab(rsrc_t r, int e0, float (&v)[PP]) {
+  if constexpr (PP == 4) {
+    const u32x4 t = __builtin_amdgcn_raw_buffer_load_b128(r, e0 * 4, 0, 0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = __uint_as_float(t[i]);
+  } else if constexpr (PP == 2) {
+    typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+    const u32x2 t = __builtin_amdgcn_raw_buffer_load_b64(r, e0 * 4, 0, 0);
+    v[0] = __uint_as_float(t[0]);
+    v[1] = __uint_as_float(t[1]);
+  } else {
+#pragma unroll
+    for (int i = 0; i < PP; ++i) v[i] = ld_f32(r, (e0 + i) * 4);
+  }
+}
+
+// Rotate the pairs (v[2p], v[2p+1]) = (real, imaginary) of a chunk by their
+// angles: a' = a c - b (sign s), b' = a (sign s) + b c; sign = -1 is the
+// inverse rotation.
+template <int PP>
+__device__ __forceinline__ void rotate_pairs(float* v, const float (&c)[PP], const float (&s)[PP],
+                                             float sign) {
+#pragma unroll
+  for (int p = 0; p < PP; ++p) {
+    const float sn = sign * s[p];
+    const float a = v[2 * p], b = v[2 * p + 1];
+    v[2 * p] = fmaf(a, c[p], -(b * sn));
+    v[2 * p + 1] = fmaf(a, sn, b * c[p]);
+  }
+}
+
 // index of the calling wave within its workgroup, as a scalar (SGPR) value
 __device__ __forceinline__ int wave_id() {
   return __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));

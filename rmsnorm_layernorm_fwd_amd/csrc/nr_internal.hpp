@@ -34,6 +34,22 @@ struct RopePlan {
   bool aligned, fast;
 };
 
+// Interleaved-RoPE epilogue of the fused RMSNorm + RoPE kernels: row i
+// belongs to token i / rows_per_token, whose table row has head_dim / 2
+// entries; the row is n / head_dim consecutive head vectors.
+struct RopeArgs {
+  const float* cos_tab;
+  const float* sin_tab;
+  int head_dim;
+  int64_t rows_per_token;
+};
+
+hipError_t launch_rms_rope_fwd(int dt, const FwdPlan& pl, const void* x, const void* w, void* y,
+                               float* inv_rms, const RopeArgs& ra, int64_t rows, int n, float eps,
+                               float w_add, hipStream_t st);
+hipError_t launch_rms_rope_bwd(int dt, const BwdPlan& pl, const void* dout, const void* x,
+                               const void* w, const float* inv_rms, const RopeArgs& ra, void* dx,
+                               float* part, int64_t rows, int n, float w_add, hipStream_t st);
 hipError_t launch_norm_fwd(bool ln, int dt, const FwdPlan& pl, const void* x, const void* w,
                            const void* b, void* y, float* s0, float* s1, int64_t rows, int n,
                            float eps, float w_add, hipStream_t st);

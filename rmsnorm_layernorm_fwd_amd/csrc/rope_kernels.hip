@@ -21,23 +21,6 @@
 
 namespace nr {
 
-// PP consecutive fp32 table entries starting at entry e0 of a table row
-template <int PP>
-__device__ __forceinline__ void load_tab(rsrc_t r, int e0, float (&v)[PP]) {
-  if constexpr (PP == 4) {
-    const u32x4 t = __builtin_amdgcn_raw_buffer_load_b128(r, e0 * 4, 0, 0);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) v[i] = __uint_as_float(t[i]);
-  } else if constexpr (PP == 2) {
-    typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-    const u32x2 t = __builtin_amdgcn_raw_buffer_load_b64(r, e0 * 4, 0, 0);
-    v[0] = __uint_as_float(t[0]);
-    v[1] = __uint_as_float(t[1]);
-  } else {
-    v[0] = ld_f32(r, e0 * 4);
-  }
-}
-
 // byte offset handed to lanes that own no chunk: beyond every token span the
 // host accepts, so their loads read 0 and their stores are dropped
 constexpr int kNoChunk = 0x7ffffff0;
@@ -92,20 +75,16 @@ rope_apply_kernel(T* x, const float* cos_tab, const float* sin_tab, int64_t ntok
     }
 #pragma unroll
     for (int k = 0; k < K; ++k) {
-      float o[E];
-#pragma unroll
-      for (int p = 0; p < PP; ++p) {
-        const float c = FAST ? cf[p] : ck[k][p];
-        const float sn = sign * (FAST ? sf[p] : sk[k][p]);
-        const float a = v[k][2 * p], b = v[k][2 * p + 1];
-        o[2 * p] = fmaf(a, c, -(b * sn));
-        o[2 * p + 1] = fmaf(a, sn, b * c);
+      if constexpr (FAST) {
+        rotate_pairs<PP>(v[k], cf, sf, sign);
+      } else {
+        rotate_pairs<PP>(v[k], ck[k], sk[k], sign);
       }
       if constexpr (VEC) {
-        __builtin_amdgcn_raw_buffer_store_b128(pack<T>(o), xr, off[k], 0, kStream);
+        __builtin_amdgcn_raw_buffer_store_b128(pack<T>(v[k]), xr, off[k], 0, kStream);
       } else {
-        st_elem<T>(xr, off[k], o[0]);
-        st_elem<T>(xr, off[k] + static_cast<int>(sizeof(T)), o[1]);
+        st_elem<T>(xr, off[k], v[k][0]);
+        st_elem<T>(xr, off[k] + static_cast<int>(sizeof(T)), v[k][1]);
       }
     }
   }

@@ -1,0 +1,126 @@
+"""GPU parity of the fused RMSNorm + RoPE pair against the oracle's fp64
+composition (no intermediate rounding on either side of the comparison: the
+fused kernels round once, so the plain 1-ulp bound applies)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import rmsnorm_layernorm_fwd_amd as nr
+import workloads
+from tolerance import check, grad_scale, out_kind, to64
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def say(msg):
+    print(f"[case] {msg}", flush=True)
+
+
+def g(t):
+    return None if t is None else t.to(DEV)
+
+
+def check_fused(tag, x, w, dout, ang, head_dim, rows_per_token, gemma=False, eps=1e-6,
+                layout="packed"):
+    rows, n = x.shape
+    tokens = ang.shape[0]
+    say(f"{tag}: fused rmsnorm+rope {rows}x{n} head_dim={head_dim} rows/token={rows_per_token} "
+        f"{x.dtype} gemma={gemma} {layout}")
+    ct = torch.from_numpy(np.cos(ang)).float().to(DEV)
+    st = torch.from_numpy(np.sin(ang)).float().to(DEV)
+    if layout == "unaligned":
+        buf = torch.empty(rows * n + 1, dtype=x.dtype, device=DEV)
+        xg = buf[1:].view(rows, n)
+        xg.copy_(g(x))
+    else:
+        xg = g(x)
+    y, r = nr.rmsnorm_rope_fwd(xg, g(w), ct, st, head_dim, rows_per_token, eps, gemma)
+    dx, dw = nr.rmsnorm_rope_bwd(g(dout), xg, g(w), r, ct, st, head_dim, rows_per_token, gemma)
+    torch.cuda.synchronize()
+    ry, rr = oracle.rmsnorm_rope_fwd(x, w, ang, head_dim, rows_per_token, eps, gemma)
+    rdx, rdw = oracle.rmsnorm_rope_bwd(dout, x, w, ang, head_dim, rows_per_token, eps, gemma)
+    k = out_kind(x.dtype)
+    check(f"{tag} y", y, ry, k)
+    check(f"{tag} inv_rms", r, rr, "stat", s=0.0)
+    dy64 = oracle.rope_apply(dout.reshape(1, rows, n // head_dim, head_dim),
+                             ang[np.arange(rows) // rows_per_token], inverse=True).reshape(rows, n)
+    check(f"{tag} dx", dx, rdx, k, s=grad_scale(rr, dy64, w, gemma))
+    if w is not None:
+        check(f"{tag} dw", dw, rdw, "col")
+    # the table built by the library gives the same result within the bound
+    return ct, st
+
+
+# (rows, heads per row, head_dim, rows_per_token, dtype, gemma, layout)
+CASES = [
+    (64, 4, 64, 1, torch.float32, False, "packed"),
+    (99, 40, 128, 1, torch.bfloat16, False, "packed"),
+    (132, 1, 64, 4, torch.bfloat16, True, "packed"),      # each head normalised on its own
+    (50, 3, 6, 1, torch.bfloat16, False, "packed"),       # head_dim 6: element-wise path
+    (40, 2, 32, 2, torch.float32, True, "packed"),
+    (33, 8, 128, 1, torch.bfloat16, False, "unaligned"),
+]
+
+
+@pytest.mark.parametrize("rows,heads,d,rpt,dtype,gemma,layout", CASES)
+def test_fused_cases(rows, heads, d, rpt, dtype, gemma, layout):
+    n = heads * d
+    seed = 7000 + rows + n
+    x = workloads.normal((rows, n), seed, dtype)
+    w = workloads.normal((n,), seed + 1, dtype, mean=0.0 if gemma else 1.0, std=0.1)
+    dout = workloads.normal((rows, n), seed + 2, dtype)
+    ang = oracle.rope_angles_1d(-(-rows // rpt), d, 5, 10000.0)
+    check_fused(f"fused {rows}x{heads}x{d}", x, w, dout, ang, d, rpt, gemma, layout=layout)
+
+
+def test_fused_in_place_and_library_table():
+    rows, heads, d = 70, 4, 64
+    n = heads * d
+    x = workloads.normal((rows, n), 7101, torch.bfloat16)
+    w = workloads.normal((n,), 7102, torch.bfloat16, mean=1.0, std=0.1)
+    dout = workloads.normal((rows, n), 7103, torch.bfloat16)
+    ang = oracle.rope_angles_1d(rows, d, 0, 10000.0)
+    ry, rr = oracle.rmsnorm_rope_fwd(x, w, ang, d)
+    rdx, rdw = oracle.rmsnorm_rope_bwd(dout, x, w, ang, d)
+    say("fused in place (y == x, dx == dout) with library-built tables")
+    ct, st = nr.rope_table_1d(rows, d, 0, 10000.0)
+    xg, gg = g(x), g(dout)
+    _, r = nr.rmsnorm_rope_fwd(xg.clone(), g(w), ct, st, d)
+    nr.rmsnorm_rope_bwd(gg, xg, g(w), r, ct, st, d, dx=gg)
+    nr.rmsnorm_rope_fwd(xg, g(w), ct, st, d, y=xg)
+    torch.cuda.synchronize()
+    check("in-place y", xg, ry, "bf16")
+    dy64 = oracle.rope_apply(dout.reshape(1, rows, heads, d), ang, inverse=True).reshape(rows, n)
+    check("in-place dx", gg, rdx, "bf16", s=grad_scale(rr, dy64, w))
+
+
+def test_fused_longseq():
+    inp = workloads.norm_inputs("longseq_65536x5120")
+    x, w, dout, eps = inp["x"], inp["w"], inp["dy"], inp["eps"]
+    m, n = x.shape
+    d = 128
+    rng = np.random.default_rng(11)
+    rows = np.array(sorted(set(rng.choice(m, 48, replace=False).tolist())
+                           | {0, m - 1, *inp["outlier_rows"][:16].tolist()}), dtype=np.int64)
+    say("fused longseq_65536x5120: rmsnorm+rope fwd and bwd, sampled rows + full dw")
+    ct, st = nr.rope_table_1d(m, d, 0, 10000.0)
+    y, r = nr.rmsnorm_rope_fwd(g(x), g(w), ct, st, d, 1, eps)
+    dx, dw = nr.rmsnorm_rope_bwd(g(dout), g(x), g(w), r, ct, st, d)
+    torch.cuda.synchronize()
+    ang = oracle.rope_angles_1d(m, d, 0, 10000.0)
+    xs, ds = x[rows], dout[rows]
+    ry, rr = oracle.rmsnorm_rope_fwd(xs, w, ang[rows], d, 1, eps)
+    rdx, _ = oracle.rmsnorm_rope_bwd(ds, xs, w, ang[rows], d, 1, eps, want_dw=False)
+    idx = torch.from_numpy(rows).to(DEV)
+    check("fused longseq y", y[idx], ry, "bf16")
+    check("fused longseq inv_rms", r[idx], rr, "stat", s=0.0)
+    dy64 = oracle.rope_apply(ds.reshape(1, len(rows), n // d, d), ang[rows], inverse=True)
+    check("fused longseq dx", dx[idx], rdx, "bf16", s=grad_scale(rr, dy64.reshape(len(rows), n), w))
+    # dw over every row, the oracle taken in row chunks and added in fp64
+    rdw = np.zeros(n)
+    for c0 in range(0, m, 8192):
+        sl = slice(c0, c0 + 8192)
+        rdw += oracle.rmsnorm_rope_bwd(dout[sl], x[sl], w, ang[sl], d, 1, eps, want_dx=False)[1]
+    check("fused longseq dw", dw, rdw, "col")

@@ -16,7 +16,7 @@ import torch
 import oracle
 import rmsnorm_layernorm_fwd_amd as nr
 import workloads
-from tolerance import check, out_kind, to64, ulp_bf16
+from tolerance import check, grad_scale, out_kind, to64, ulp_bf16
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -56,16 +56,6 @@ def check_table(name, cos_t, sin_t, angle):
         i = np.unravel_index(np.argmax(err - tol), err.shape)
         assert np.all(err <= tol), (f"{name} {nm}: worst at {i}: angle={angle[i]!r} gpu={o[i]!r} "
                                     f"oracle={r[i]!r} err={err[i]:.3e} bound={tol[i]:.3e}")
-
-
-def grad_scale(r, dy, w, gemma=False):
-    """Row scale for dx: RMS over the row of r * dy * w' (the terms dx is a
-    difference of).  dx can cancel to far below this (a one-column row, where
-    RMSNorm's dx is ~eps-sized and LayerNorm's is exactly 0), and fp32 is only
-    accurate relative to the terms, so the bound is scaled by them."""
-    wp = np.ones(dy.shape[-1]) if w is None else to64(w) + (1.0 if gemma else 0.0)
-    t = to64(r)[:, None] * to64(dy).reshape(len(r), -1) * wp[None, :]
-    return np.sqrt(np.mean(t * t, axis=1, keepdims=True))
 
 
 # ---------------------------------------------------------------- RMSNorm

@@ -76,3 +76,13 @@ def check(name, o, r, kind, s=None, extra=None):
 
 def out_kind(dtype) -> str:
     return "bf16" if dtype == torch.bfloat16 else "f32"
+
+
+def grad_scale(r, dy, w, gemma=False):
+    """Row scale for dx: RMS over the row of r * dy * w' (the terms dx is a
+    difference of).  dx can cancel to far below this (a one-column row, where
+    RMSNorm's dx is ~eps-sized and LayerNorm's is exactly 0), and fp32 is only
+    accurate relative to the terms, so the bound is scaled by them."""
+    wp = np.ones(dy.shape[-1]) if w is None else to64(w) + (1.0 if gemma else 0.0)
+    t = to64(r)[:, None] * to64(dy).reshape(len(r), -1) * wp[None, :]
+    return np.sqrt(np.mean(t * t, axis=1, keepdims=True))
