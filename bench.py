@@ -34,8 +34,7 @@ sys.path.insert(0, ROOT)
 METRIC = "achieved HBM GB/s (and % of peak) for fused norm fwd+bwd and RoPE"
 PEAK_GBS = 8000.0  # MI355X HBM3E
 PROFILES = os.path.join(ROOT, "profiles")
-KERNEL_SOURCES = ["rmsnorm_layernorm_fwd_amd/csrc/" + f for f in
-                  ("nr_device.hpp", "norm_fwd.hip", "norm_bwd.hip", "rope_kernels.hip", "api.hip")]
+CSRC = os.path.join(ROOT, "rmsnorm_layernorm_fwd_amd", "csrc")
 
 
 # ---------------------------------------------------------------- bytes
@@ -61,10 +60,13 @@ def rope_bytes(t, h, d, e=2):
 
 
 def source_hash():
+    """Hash of the library sources: counter summaries taken on other sources
+    are not reused."""
     hsh = hashlib.sha256()
-    for f in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, f), "rb") as fh:
-            hsh.update(fh.read())
+    for f in sorted(os.listdir(CSRC)):
+        if f.endswith((".hip", ".hpp")):
+            with open(os.path.join(CSRC, f), "rb") as fh:
+                hsh.update(f.encode() + fh.read())
     return hsh.hexdigest()[:16]
 
 
@@ -121,7 +123,7 @@ def build_ops(name, dev):
         y, dx = torch.empty_like(x), torch.empty_like(x)
         r = torch.empty(m, dtype=torch.float32, device=dev)
         dw = torch.empty(n, dtype=torch.float32, device=dev)
-        ws = torch.empty(max(nr.nr_bwd_workspace_bytes(m, n, 0), 16), dtype=torch.uint8, device=dev)
+        ws = torch.empty(max(nr.nr_bwd_workspace_bytes(m, n, 2), 16), dtype=torch.uint8, device=dev)
         ct, st = nr.rope_table_1d(m, d, 0, 10000.0, device=dev)
         tab = 2 * 4 * m * (d // 2)
         ops = [
@@ -165,6 +167,23 @@ def build_ops(name, dev):
              ln_bwd_bytes(m, n)),
         ]
         desc = dict(workload=name, rows=m, hidden=n, io_dtype="bf16")
+    elif name == "ln_gelu_15360x5120":
+        inp = workloads.norm_inputs("ln_affine_15360x5120")
+        m, n = inp["x"].shape
+        x, gm, bt, dy = g(inp["x"]), g(inp["w"]), g(inp["b"]), g(inp["dy"])
+        y, dx = torch.empty_like(x), torch.empty_like(x)
+        mu = torch.empty(m, dtype=torch.float32, device=dev)
+        rs = torch.empty_like(mu)
+        dg, db = (torch.empty(n, dtype=torch.float32, device=dev) for _ in range(2))
+        ws = torch.empty(max(nr.nr_bwd_workspace_bytes(m, n, 1), 16), dtype=torch.uint8, device=dev)
+        ops = [
+            ("layernorm_gelu_fwd", "norm_fwd[ln+gelu]",
+             lambda: nr.layernorm_gelu_fwd(x, gm, bt, 1e-5, y=y, mean=mu, rstd=rs), ln_fwd_bytes(m, n)),
+            ("layernorm_gelu_bwd", "norm_bwd_rows[ln+gelu]+colreduce",
+             lambda: nr.layernorm_gelu_bwd(dy, x, gm, bt, mu, rs, dx=dx, dgamma=dg, dbeta=db, workspace=ws),
+             ln_bwd_bytes(m, n) + 2 * n),
+        ]
+        desc = dict(workload=name, rows=m, hidden=n, io_dtype="bf16", activation="tanh-GeLU")
     elif name == "rope3d_15360x40x128":
         inp = workloads.rope_inputs(name)
         b, t, h, d = inp["shape"]
@@ -264,7 +283,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="longseq_65536x5120",
                     choices=["longseq_65536x5120", "longseq_fused_65536x5120", "rms_gemma_3840x5120",
-                             "ln_affine_15360x5120", "rope3d_15360x40x128"])
+                             "ln_affine_15360x5120", "ln_gelu_15360x5120", "rope3d_15360x40x128"])
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", action="store_true")

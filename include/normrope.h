@@ -184,8 +184,8 @@ nr_status_t rmsnorm_rope_fwd(nr_dtype_t dt, const void* x, const void* w,
  * rmsnorm_rope_bwd -- backward of rmsnorm_rope_fwd: dout (the gradient of
  * the rotated output) is rotated back by the same angles (sin negated) in
  * registers and fed to the rmsnorm_bwd arithmetic; dx [rows][n] (may be
- * dout), dw [n] fp32 or NULL.  Workspace as for rmsnorm_bwd
- * (nr_bwd_workspace_bytes(rows, n, 0)).
+ * dout), dw [n] fp32 or NULL.  Workspace rules as for rmsnorm_bwd, size
+ * nr_bwd_workspace_bytes(rows, n, 2).
  */
 nr_status_t rmsnorm_rope_bwd(nr_dtype_t dt, const void* dout, const void* x,
                              const void* w, const float* inv_rms,
@@ -195,10 +195,37 @@ nr_status_t rmsnorm_rope_bwd(nr_dtype_t dt, const void* dout, const void* x,
                              int gemma_offset, void* workspace,
                              size_t workspace_bytes, void* stream);
 
-/* Workspace bytes rmsnorm_bwd (is_layernorm = 0) or layernorm_bwd (1) needs
- * for dw / dgamma / dbeta at this shape.  Host only; pure function of its
- * arguments and the current tuning table. */
-size_t nr_bwd_workspace_bytes(int64_t rows, int64_t n, int is_layernorm);
+/*
+ * layernorm_gelu_fwd -- layernorm_fwd with the tanh-approximated GeLU applied
+ * to its output in the same pass, the fused LayerNorm + GeLU of "LLM层的优化
+ * 算子", section 编写定制融合算子:
+ *   y = gelu(a), a = (x - mu) r gamma + beta,
+ *   gelu(v) = v/2 (1 + tanh(sqrt(2/pi) (v + 0.044715 v^3))).
+ * mean and rstd are stored as in layernorm_fwd (the backward recomputes a).
+ */
+nr_status_t layernorm_gelu_fwd(nr_dtype_t dt, const void* x, const void* gamma,
+                               const void* beta, void* y, float* mean,
+                               float* rstd, int64_t rows, int64_t n, float eps,
+                               void* stream);
+
+/*
+ * layernorm_gelu_bwd -- backward of layernorm_gelu_fwd: the pre-activation a
+ * is recomputed from x, the cached mean / rstd, gamma and beta; dy = dout *
+ * gelu'(a) feeds the layernorm_bwd arithmetic.  Outputs and workspace as
+ * for layernorm_bwd (nr_bwd_workspace_bytes(rows, n, 1)).
+ */
+nr_status_t layernorm_gelu_bwd(nr_dtype_t dt, const void* dout, const void* x,
+                               const void* gamma, const void* beta,
+                               const float* mean, const float* rstd, void* dx,
+                               float* dgamma, float* dbeta, int64_t rows,
+                               int64_t n, void* workspace,
+                               size_t workspace_bytes, void* stream);
+
+/* Workspace bytes a backward call needs for dw / dgamma / dbeta at this
+ * shape: op = 0 rmsnorm_bwd, 1 layernorm_bwd or layernorm_gelu_bwd,
+ * 2 rmsnorm_rope_bwd (0 for any other op).  Host only; pure function of its arguments and the current
+ * tuning table. */
+size_t nr_bwd_workspace_bytes(int64_t rows, int64_t n, int op);
 
 /* Static description of a status code.  Host only. */
 const char* nr_status_str(nr_status_t s);

@@ -51,9 +51,15 @@ def lib():
         L.oracle_rope_angles_1d.argtypes = [i64, i64, i64, f64, vp]
         L.oracle_rope_angles_3d.argtypes = [i64, i64, i64, i64, i64, i64, f64, vp]
         L.oracle_rope_apply.argtypes = [vp, i32, i64, i64, i64, i64, vp, i32, vp]
+        L.oracle_layernorm_gelu_fwd.argtypes = [vp, i32, vp, vp, i32, i64, i64, f64, vp, vp, vp]
+        L.oracle_layernorm_gelu_bwd.argtypes = [vp, vp, i32, vp, vp, i32, i64, i64, f64, vp, vp, vp]
+        L.oracle_gelu_tanh.argtypes = [f64]
+        L.oracle_gelu_tanh_grad.argtypes = [f64]
+        L.oracle_gelu_tanh.restype = f64
+        L.oracle_gelu_tanh_grad.restype = f64
         for f in ("oracle_rmsnorm_fwd", "oracle_rmsnorm_bwd", "oracle_layernorm_fwd",
                   "oracle_layernorm_bwd", "oracle_rope_angles_1d", "oracle_rope_angles_3d",
-                  "oracle_rope_apply"):
+                  "oracle_rope_apply", "oracle_layernorm_gelu_fwd", "oracle_layernorm_gelu_bwd"):
             getattr(L, f).restype = None
         _lib = L
     return _lib
@@ -201,3 +207,37 @@ def rmsnorm_rope_bwd(dout, x, w, angle, head_dim, rows_per_token=1, eps=1e-6, ge
     xd = x.detach().cpu().double() if isinstance(x, torch.Tensor) else torch.from_numpy(x)
     return rmsnorm_bwd(torch.from_numpy(dy.reshape(rows, n)), xd, w, eps, gemma,
                        want_dx=want_dx, want_dw=want_dw)
+
+
+def gelu_tanh(v):
+    """D7 activation on a scalar (float64)."""
+    return lib().oracle_gelu_tanh(float(v))
+
+
+def gelu_tanh_grad(v):
+    """Derivative of D7's activation on a scalar (float64)."""
+    return lib().oracle_gelu_tanh_grad(float(v))
+
+
+def layernorm_gelu_fwd(x, gamma=None, beta=None, eps=1e-5):
+    """D7 forward: gelu_tanh(D3(x)) -> (y, mean, rstd) in float64."""
+    X, G, B = _In(x), _In(gamma), _In(beta)
+    m, n = _rows_n(X.t)
+    y, mu, r = _out(m, n), _out(m), _out(m)
+    lib().oracle_layernorm_gelu_fwd(X.p, X.dt, G.p, B.p, G.dt if G.t is not None else B.dt,
+                                    m, n, float(eps), _ptr(y), _ptr(mu), _ptr(r))
+    return y, mu, r
+
+
+def layernorm_gelu_bwd(dout, x, gamma=None, beta=None, eps=1e-5, want_dx=True, want_dw=True):
+    """D7 backward -> (dx, dgamma, dbeta) in float64."""
+    DY, X, G, B = _In(dout), _In(x), _In(gamma), _In(beta)
+    if DY.dt != X.dt:
+        raise TypeError("oracle: dout and x must share a dtype")
+    m, n = _rows_n(X.t)
+    dx = _out(m, n) if want_dx else None
+    dg = _out(n) if want_dw else None
+    db = _out(n) if want_dw else None
+    lib().oracle_layernorm_gelu_bwd(DY.p, X.p, X.dt, G.p, B.p, G.dt if G.t is not None else B.dt,
+                                    m, n, float(eps), _ptr(dx), _ptr(dg), _ptr(db))
+    return dx, dg, db

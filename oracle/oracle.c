@@ -303,3 +303,104 @@ void oracle_rope_apply(const void *x, int xdt, int64_t batch, int64_t tokens,
                 }
             }
 }
+
+/* ------------------------------------------------------------------ */
+/* D7  LayerNorm followed by the tanh-approximated GeLU.               */
+/* LLM层的优化算子, 编写定制融合算子: the fused example normalises the  */
+/* row, applies weight and bias, then                                  */
+/*   gelu(v) = 0.5 v (1 + tanh(c (v + 0.044715 v^3))),                  */
+/* with c = sqrt(2/pi) (printed there as 0.79788456).                  */
+/* Backward (calculus): with the pre-activation a = xhat gamma + beta  */
+/* recomputed from x, dy = dout gelu'(a), then D4 with dy:             */
+/*   gelu'(v) = 0.5 (1 + t) + 0.5 v (1 - t^2) c (1 + 3 0.044715 v^2),    */
+/*   t = tanh(c (v + 0.044715 v^3)).                                    */
+/* ------------------------------------------------------------------ */
+static const double GELU_A = 0.044715;
+
+static double gelu_c(void)
+{
+    const double pi = 3.14159265358979323846;
+    return sqrt(2.0 / pi);
+}
+
+double oracle_gelu_tanh(double v)
+{
+    return 0.5 * v * (1.0 + tanh(gelu_c() * (v + GELU_A * v * v * v)));
+}
+
+double oracle_gelu_tanh_grad(double v)
+{
+    double c = gelu_c();
+    double t = tanh(c * (v + GELU_A * v * v * v));
+    return 0.5 * (1.0 + t) + 0.5 * v * (1.0 - t * t) * c * (1.0 + 3.0 * GELU_A * v * v);
+}
+
+void oracle_layernorm_gelu_fwd(const void *x, int xdt, const void *gamma,
+                               const void *beta, int wdt, int64_t rows,
+                               int64_t n, double eps, double *y,
+                               double *mean, double *rstd)
+{
+    oracle_layernorm_fwd(x, xdt, gamma, beta, wdt, rows, n, eps, y, mean, rstd);
+    if (y) {
+#pragma omp parallel for schedule(static)
+        for (int64_t i = 0; i < rows; ++i)
+            for (int64_t j = 0; j < n; ++j)
+                y[i * n + j] = oracle_gelu_tanh(y[i * n + j]);
+    }
+}
+
+void oracle_layernorm_gelu_bwd(const void *dout, const void *x, int dt,
+                               const void *gamma, const void *beta, int wdt,
+                               int64_t rows, int64_t n, double eps,
+                               double *dx, double *dgamma, double *dbeta)
+{
+    size_t m = (size_t)(rows > 0 ? rows : 1);
+    double *mu = (double *)malloc(sizeof(double) * m);
+    double *r = (double *)malloc(sizeof(double) * m);
+    double *dy = (double *)malloc(sizeof(double) * (size_t)(n > 0 ? n : 1) * m);
+    oracle_layernorm_fwd(x, dt, NULL, NULL, 0, rows, n, eps, NULL, mu, r);
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < rows; ++i)
+        for (int64_t j = 0; j < n; ++j) {
+            double xhat = (ld(x, dt, i * n + j) - mu[i]) * r[i];
+            double a = xhat * (gamma ? ld(gamma, wdt, j) : 1.0) + (beta ? ld(beta, wdt, j) : 0.0);
+            dy[i * n + j] = ld(dout, dt, i * n + j) * oracle_gelu_tanh_grad(a);
+        }
+    if (dx) {
+#pragma omp parallel for schedule(static)
+        for (int64_t i = 0; i < rows; ++i) {
+            double sa = 0.0, sb = 0.0;
+            for (int64_t j = 0; j < n; ++j) {
+                double g = dy[i * n + j] * (gamma ? ld(gamma, wdt, j) : 1.0);
+                double xhat = (ld(x, dt, i * n + j) - mu[i]) * r[i];
+                sa += g;
+                sb += g * xhat;
+            }
+            double a = sa / (double)n, b = sb / (double)n;
+            for (int64_t j = 0; j < n; ++j) {
+                double g = dy[i * n + j] * (gamma ? ld(gamma, wdt, j) : 1.0);
+                double xhat = (ld(x, dt, i * n + j) - mu[i]) * r[i];
+                dx[i * n + j] = r[i] * (g - a - xhat * b);
+            }
+        }
+    }
+    if (dgamma || dbeta) {
+        for (int64_t j = 0; j < n; ++j) {
+            if (dgamma)
+                dgamma[j] = 0.0;
+            if (dbeta)
+                dbeta[j] = 0.0;
+        }
+        for (int64_t i = 0; i < rows; ++i)
+            for (int64_t j = 0; j < n; ++j) {
+                double d = dy[i * n + j];
+                if (dgamma)
+                    dgamma[j] += d * ((ld(x, dt, i * n + j) - mu[i]) * r[i]);
+                if (dbeta)
+                    dbeta[j] += d;
+            }
+    }
+    free(mu);
+    free(r);
+    free(dy);
+}

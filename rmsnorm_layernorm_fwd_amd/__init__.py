@@ -18,7 +18,7 @@ import torch
 
 __all__ = [
     "NormRopeError", "rmsnorm_fwd", "rmsnorm_bwd", "layernorm_fwd", "layernorm_bwd",
-    "rmsnorm_rope_fwd", "rmsnorm_rope_bwd",
+    "rmsnorm_rope_fwd", "rmsnorm_rope_bwd", "layernorm_gelu_fwd", "layernorm_gelu_bwd",
     "rope_interleaved_apply", "rope_table_1d", "rope_table_3d", "nr_bwd_workspace_bytes",
     "nr_status_str", "nr_tune", "nr_norm_n_max", "library_path",
 ]
@@ -65,6 +65,8 @@ def _lib():
             "layernorm_bwd": [i32, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, vp, sz, vp],
             "rope_interleaved_apply": [i32, vp, vp, vp, i64, i64, i64, i64, i64, i64, i64, i32, vp],
             "rmsnorm_rope_fwd": [i32, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, f32, i32, vp],
+            "layernorm_gelu_fwd": [i32, vp, vp, vp, vp, vp, vp, i64, i64, f32, vp],
+            "layernorm_gelu_bwd": [i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, vp, sz, vp],
             "rmsnorm_rope_bwd": [i32, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i32, vp, sz, vp],
             "rope_table_1d": [vp, vp, i64, i64, i64, f64, vp],
             "rope_table_3d": [vp, vp, i64, i64, i64, i64, i64, i64, f64, vp],
@@ -224,6 +226,61 @@ def layernorm_bwd(dy, x, gamma, mean, rstd, dx=None, want_dgamma=True, want_dbet
     return dx, dgamma, dbeta
 
 
+# ---------------------------------------------------------------- fused LayerNorm + GeLU
+
+def layernorm_gelu_fwd(x, gamma=None, beta=None, eps=1e-5, y=None, mean=None, rstd=None,
+                       want_stats=True):
+    """y = gelu_tanh((x - mu) r gamma + beta) in one pass; returns (y, mean, rstd)."""
+    _dev("x", x)
+    dt = _dtype_code(x)
+    rows, n = _rows_n(x)
+    _dev("gamma", gamma, x.dtype, (n,))
+    _dev("beta", beta, x.dtype, (n,))
+    if y is None:
+        y = torch.empty_like(x)
+    _dev("y", y, x.dtype, x.shape)
+    if want_stats:
+        if mean is None:
+            mean = torch.empty(x.shape[:-1], dtype=torch.float32, device=x.device)
+        if rstd is None:
+            rstd = torch.empty(x.shape[:-1], dtype=torch.float32, device=x.device)
+    _dev("mean", mean, torch.float32)
+    _dev("rstd", rstd, torch.float32)
+    _check("layernorm_gelu_fwd", _lib().layernorm_gelu_fwd(
+        dt, _ptr(x), _ptr(gamma), _ptr(beta), _ptr(y), _ptr(mean), _ptr(rstd), rows, n, float(eps),
+        _stream(x)))
+    return y, mean, rstd
+
+
+def layernorm_gelu_bwd(dout, x, gamma, beta, mean, rstd, dx=None, want_dgamma=True,
+                       want_dbeta=True, dgamma=None, dbeta=None, workspace=None):
+    """Backward of layernorm_gelu_fwd; returns (dx, dgamma, dbeta)."""
+    _dev("x", x)
+    dt = _dtype_code(x)
+    rows, n = _rows_n(x)
+    _dev("dout", dout, x.dtype, x.shape)
+    _dev("gamma", gamma, x.dtype, (n,))
+    _dev("beta", beta, x.dtype, (n,))
+    _dev("mean", mean, torch.float32, x.shape[:-1])
+    _dev("rstd", rstd, torch.float32, x.shape[:-1])
+    if dx is None:
+        dx = torch.empty_like(x)
+    _dev("dx", dx, x.dtype, x.shape)
+    if dgamma is None and want_dgamma:
+        dgamma = torch.empty(n, dtype=torch.float32, device=x.device)
+    if dbeta is None and want_dbeta:
+        dbeta = torch.empty(n, dtype=torch.float32, device=x.device)
+    _dev("dgamma", dgamma, torch.float32, (n,))
+    _dev("dbeta", dbeta, torch.float32, (n,))
+    ws, wsb = (None, 0)
+    if dgamma is not None or dbeta is not None:
+        ws, wsb = _workspace(rows, n, 1, workspace, x.device)
+    _check("layernorm_gelu_bwd", _lib().layernorm_gelu_bwd(
+        dt, _ptr(dout), _ptr(x), _ptr(gamma), _ptr(beta), _ptr(mean), _ptr(rstd), _ptr(dx),
+        _ptr(dgamma), _ptr(dbeta), rows, n, _ptr(ws), wsb, _stream(x)))
+    return dx, dgamma, dbeta
+
+
 # ---------------------------------------------------------------- fused RMSNorm + RoPE
 
 def _rope_rows(x, cos_tab, sin_tab, head_dim, rows_per_token):
@@ -272,7 +329,7 @@ def rmsnorm_rope_bwd(dout, x, w, inv_rms, cos_tab, sin_tab, head_dim, rows_per_t
     _dev("dw", dw, torch.float32, (n,))
     ws, wsb = (None, 0)
     if dw is not None:
-        ws, wsb = _workspace(rows, n, 0, workspace, x.device)
+        ws, wsb = _workspace(rows, n, 2, workspace, x.device)
     _check("rmsnorm_rope_bwd", _lib().rmsnorm_rope_bwd(
         dt, _ptr(dout), _ptr(x), _ptr(w), _ptr(inv_rms), _ptr(cos_tab), _ptr(sin_tab), _ptr(dx),
         _ptr(dw), rows, n, head_dim, rows_per_token, int(bool(gemma_offset)), _ptr(ws), wsb,
@@ -320,8 +377,9 @@ def rope_table_3d(grid, pairs, theta=10000.0, device="cuda"):
 
 # ---------------------------------------------------------------- helpers
 
-def nr_bwd_workspace_bytes(rows, n, is_layernorm) -> int:
-    return int(_lib().nr_bwd_workspace_bytes(rows, n, int(bool(is_layernorm))))
+def nr_bwd_workspace_bytes(rows, n, op) -> int:
+    """op: 0 rmsnorm_bwd, 1 layernorm_bwd, 2 rmsnorm_rope_bwd."""
+    return int(_lib().nr_bwd_workspace_bytes(rows, n, int(op)))
 
 
 def nr_status_str(status: int) -> str:

@@ -126,14 +126,15 @@ nr_status_t plan_fwd(nr_dtype_t dt, int64_t n, bool aligned, FwdPlan* pl) {
 //     also carries the dbeta accumulators, D = 1, PF = 1.
 //   P (workgroups): each handles about rows/P rows, dealt out round robin.
 //     At least 16 rows per workgroup keep the fp32 partial rows small next
-//     to the row traffic.  At most 256 (RMSNorm, D = 2) or 512 (LayerNorm):
-//     on MI355X's 256 CUs that is one or two resident workgroups per CU;
-//     more gave a second, partial round of workgroups and measured slower.
+//     to the row traffic.  At most 256 (plain RMSNorm, D = 2) or 512
+//     (LayerNorm and the fused RMSNorm + RoPE, D = 1): on MI355X's 256 CUs
+//     that is one or two resident workgroups per CU; more gave a second,
+//     partial round of workgroups and measured slower.
 //   P depends on the row count and the operator only, so the summation order
 //   and the workspace size are the same on every device.
-void bwd_grid(int64_t rows, bool ln, int64_t* P_out, int64_t* rpb_out) {
+void bwd_grid(int64_t rows, bool two_per_cu, int64_t* P_out, int64_t* rpb_out) {
   const int64_t rows_min = tune(BWD_ROWS_MIN) > 0 ? tune(BWD_ROWS_MIN) : 16;
-  const int64_t pcap = tune(BWD_P) > 0 ? tune(BWD_P) : (ln ? 512 : 256);
+  const int64_t pcap = tune(BWD_P) > 0 ? tune(BWD_P) : (two_per_cu ? 512 : 256);
   int64_t P = tune(BWD_P) > 0 ? pcap : (rows + rows_min - 1) / rows_min;
   if (P > pcap) P = pcap;
   if (P > rows) P = rows;
@@ -169,7 +170,7 @@ nr_status_t plan_bwd(nr_dtype_t dt, bool ln, int64_t rows, int64_t n, bool align
   if (PF < 1 || PF > 2) return NR_ERR_SHAPE;
   if (static_cast<int64_t>(64) * W * K < nchunk) return NR_ERR_SHAPE;
   int64_t P, rpb;
-  bwd_grid(rows, ln, &P, &rpb);
+  bwd_grid(rows, ln || rope, &P, &rpb);
   *pl = BwdPlan{W, K, D, static_cast<int>(P), PF, rpb, aligned};
   return NR_OK;
 }
@@ -224,12 +225,11 @@ nr_status_t nr_tune(const char* key, int value) {
   return NR_ERR_TUNE;
 }
 
-size_t nr_bwd_workspace_bytes(int64_t rows, int64_t n, int is_layernorm) {
-  if (rows <= 0 || n < 1) return 0;
+size_t nr_bwd_workspace_bytes(int64_t rows, int64_t n, int op) {
+  if (rows <= 0 || n < 1 || op < 0 || op > 2) return 0;
   int64_t P, rpb;
-  bwd_grid(rows, is_layernorm != 0, &P, &rpb);
-  return static_cast<size_t>(P) * static_cast<size_t>(n) * sizeof(float) *
-         (is_layernorm ? 2u : 1u);
+  bwd_grid(rows, op != 0, &P, &rpb);
+  return static_cast<size_t>(P) * static_cast<size_t>(n) * sizeof(float) * (op == 1 ? 2u : 1u);
 }
 
 nr_status_t rmsnorm_fwd(nr_dtype_t dt, const void* x, const void* w, void* y, float* inv_rms,
@@ -275,7 +275,8 @@ namespace {
 nr_status_t norm_bwd_common(bool ln, nr_dtype_t dt, const void* dy, const void* x, const void* w,
                             const float* mean, const float* rstat, void* dx, float* o0, float* o1,
                             int64_t rows, int64_t n, float w_add, void* workspace,
-                            size_t workspace_bytes, void* stream) {
+                            size_t workspace_bytes, void* stream, bool gelu = false,
+                            const void* beta = nullptr) {
   nr_status_t s;
   if ((s = check_dtype(dt)) != NR_OK) return s;
   if ((s = check_norm_shape(dt, rows, n)) != NR_OK) return s;
@@ -294,7 +295,8 @@ nr_status_t norm_bwd_common(bool ln, nr_dtype_t dt, const void* dy, const void* 
   const size_t bytes = static_cast<size_t>(rows * n) * elem_bytes(dt);
   if (bad_overlap(dx, bytes, dy, bytes) || bad_overlap(dx, bytes, x, bytes)) return NR_ERR_ALIAS;
   const bool aligned = (n % vec_elems(dt)) == 0 && aligned16(dy) && aligned16(x) &&
-                       aligned16(dx) && (w == nullptr || aligned16(w));
+                       aligned16(dx) && (w == nullptr || aligned16(w)) &&
+                       (beta == nullptr || aligned16(beta));
   BwdPlan pl;
   if ((s = plan_bwd(dt, ln, rows, n, aligned, &pl)) != NR_OK) return s;
   float* part = nullptr;
@@ -304,9 +306,11 @@ nr_status_t norm_bwd_common(bool ln, nr_dtype_t dt, const void* dy, const void* 
       return NR_ERR_WORKSPACE;
     part = static_cast<float*>(workspace);
   }
-  if ((s = hip_status(nr::launch_norm_bwd(ln, dt, pl, dy, x, w, mean, rstat, dx, part, rows,
-                                          static_cast<int>(n), w_add, st))) != NR_OK)
-    return s;
+  const hipError_t e = gelu ? nr::launch_ln_gelu_bwd(dt, pl, dy, x, w, beta, mean, rstat, dx, part,
+                                                      rows, static_cast<int>(n), st)
+                            : nr::launch_norm_bwd(ln, dt, pl, dy, x, w, mean, rstat, dx, part, rows,
+                                                  static_cast<int>(n), w_add, st);
+  if ((s = hip_status(e)) != NR_OK) return s;
   if (want_cols)
     return hip_status(nr::launch_colreduce(part, static_cast<int64_t>(pl.P) * n, pl.P,
                                            static_cast<int>(n), o0, o1, st));
@@ -328,6 +332,34 @@ nr_status_t layernorm_bwd(nr_dtype_t dt, const void* dy, const void* x, const vo
                           size_t workspace_bytes, void* stream) {
   return norm_bwd_common(true, dt, dy, x, gamma, mean, rstd, dx, dgamma, dbeta, rows, n, 0.0f,
                          workspace, workspace_bytes, stream);
+}
+
+nr_status_t layernorm_gelu_fwd(nr_dtype_t dt, const void* x, const void* gamma, const void* beta,
+                               void* y, float* mean, float* rstd, int64_t rows, int64_t n,
+                               float eps, void* stream) {
+  nr_status_t s;
+  if ((s = check_dtype(dt)) != NR_OK) return s;
+  if ((s = check_norm_shape(dt, rows, n)) != NR_OK) return s;
+  if (rows == 0) return NR_OK;
+  if (x == nullptr || y == nullptr) return NR_ERR_NULLPTR;
+  const size_t bytes = static_cast<size_t>(rows * n) * elem_bytes(dt);
+  if (bad_overlap(y, bytes, x, bytes)) return NR_ERR_ALIAS;
+  const bool aligned = (n % vec_elems(dt)) == 0 && aligned16(x) && aligned16(y) &&
+                       (gamma == nullptr || aligned16(gamma)) &&
+                       (beta == nullptr || aligned16(beta));
+  FwdPlan pl;
+  if ((s = plan_fwd(dt, n, aligned, &pl)) != NR_OK) return s;
+  return hip_status(nr::launch_ln_gelu_fwd(dt, pl, x, gamma, beta, y, mean, rstd, rows,
+                                           static_cast<int>(n), eps,
+                                           static_cast<hipStream_t>(stream)));
+}
+
+nr_status_t layernorm_gelu_bwd(nr_dtype_t dt, const void* dout, const void* x, const void* gamma,
+                               const void* beta, const float* mean, const float* rstd, void* dx,
+                               float* dgamma, float* dbeta, int64_t rows, int64_t n,
+                               void* workspace, size_t workspace_bytes, void* stream) {
+  return norm_bwd_common(true, dt, dout, x, gamma, mean, rstd, dx, dgamma, dbeta, rows, n, 0.0f,
+                         workspace, workspace_bytes, stream, true, beta);
 }
 
 namespace {

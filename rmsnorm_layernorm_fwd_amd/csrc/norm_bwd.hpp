@@ -1,5 +1,5 @@
-// norm_bwd.hip -- RMSNorm / LayerNorm backward for gfx950 and the
-// deterministic column reduction that finishes dW, dgamma and dbeta.
+// norm_bwd.hpp -- RMSNorm / LayerNorm backward for gfx950 (stage 1 of the
+// deterministic column reduction that finishes dW, dgamma and dbeta).
 //
 // The backward reads each row's cached statistic (inverse root; LayerNorm
 // also the mean) instead of recomputing it (Helios 性能优化全解析, 内核一
@@ -22,6 +22,8 @@
 // its fp32 partial row; stage 2 adds the partial rows column by column in
 // workgroup order.  Every summation order is fixed by the shape, so the
 // results are bitwise reproducible run to run.
+#pragma once
+
 #include "nr_device.hpp"
 #include "nr_internal.hpp"
 
@@ -104,11 +106,15 @@ __device__ __forceinline__ void dy_chunk(const RowBatch<T, K, D, ROPE ? 1 : 0>& 
   if constexpr (ROPE) rotate_pairs<Vec<T>::N / 2>(dv, b.tc[i], b.ts[i], -1.0f);
 }
 
-template <typename T, int K, int D, bool VEC, bool LN, bool ROPE>
+// EPI == kEpiGelu (LayerNorm): the upstream gradient is that of
+// gelu(xhat gamma + beta); the pre-activation is recomputed from the cached
+// statistics and dy = dout * gelu'(pre-activation).
+template <typename T, int K, int D, bool VEC, bool LN, bool ROPE, int EPI>
 __device__ __forceinline__ void process_batch(RowBatch<T, K, D, ROPE ? 1 : 0>& b, int64_t base,
                                               int64_t rows, T* dx, int n, int t, int nthr, int W,
                                               int wave, int lane, float inv_n,
                                               const float (&wv)[K][Vec<T>::N],
+                                              const float (&bv)[K][Vec<T>::N],
                                               float (&acc1)[K][Vec<T>::N],
                                               float (&acc2)[K][Vec<T>::N],
                                               float (*red)[16], int& parity) {
@@ -131,15 +137,17 @@ __device__ __forceinline__ void process_batch(RowBatch<T, K, D, ROPE ? 1 : 0>& b
       for (int e = 0; e < E; ++e) {
         float xh = (xv[e] - b.mu[d]) * b.rs[d];
         if constexpr (LN) xh = (c * E + e < n) ? xh : 0.0f;
-        const float gg = dv[e] * wv[k][e];
+        float dd = dv[e];
+        if constexpr (EPI == kEpiGelu) dd *= gelu_tanh_grad(fmaf(xh, wv[k][e], bv[k][e]));
+        const float gg = dd * wv[k][e];
         if constexpr (LN) {
           s1 += gg;
           s2 = fmaf(gg, xh, s2);
-          acc2[k][e] += dv[e];
+          acc2[k][e] += dd;
         } else {
           s1 = fmaf(gg, xh, s1);
         }
-        acc1[k][e] = fmaf(dv[e], xh, acc1[k][e]);
+        acc1[k][e] = fmaf(dd, xh, acc1[k][e]);
       }
     }
     s[NS * d] = s1;
@@ -183,7 +191,9 @@ __device__ __forceinline__ void process_batch(RowBatch<T, K, D, ROPE ? 1 : 0>& b
 #pragma unroll
       for (int e = 0; e < E; ++e) {
         const float xh = (xv[e] - b.mu[d]) * b.rs[d];
-        const float gg = dv[e] * wv[k][e];
+        float dd = dv[e];
+        if constexpr (EPI == kEpiGelu) dd *= gelu_tanh_grad(fmaf(xh, wv[k][e], bv[k][e]));
+        const float gg = dd * wv[k][e];
         if constexpr (LN) {
           o[e] = b.rs[d] * (gg - c1 - xh * c2);
         } else {
@@ -195,11 +205,12 @@ __device__ __forceinline__ void process_batch(RowBatch<T, K, D, ROPE ? 1 : 0>& b
   }
 }
 
-template <typename T, int K, int D, int PF, bool VEC, bool LN, bool ROPE>
+template <typename T, int K, int D, int PF, bool VEC, bool LN, int EPI>
 __global__ void __launch_bounds__(1024)
-norm_bwd_rows(const T* dy, const T* x, const T* w, const float* mean, const float* rstat,
-              T* dx, float* part, int64_t part_stride, int64_t rows, int n, float w_add,
-              RopeArgs ra) {
+norm_bwd_rows(const T* dy, const T* x, const T* w, const T* beta, const float* mean,
+              const float* rstat, T* dx, float* part, int64_t part_stride, int64_t rows, int n,
+              float w_add, RopeArgs ra) {
+  constexpr bool ROPE = EPI == kEpiRope;
   constexpr int E = Vec<T>::N;
   constexpr int NS = LN ? 2 : 1;
   __shared__ float red[2 * NS * D][16];
@@ -220,6 +231,13 @@ norm_bwd_rows(const T* dy, const T* x, const T* w, const float* mean, const floa
 #pragma unroll
       for (int e = 0; e < E; ++e) wv[k][e] = (w != nullptr) ? wv[k][e] + w_add : 1.0f;
     }
+  }
+
+  float bv[K][E];  // beta, only read by the GeLU epilogue
+  {
+    const rsrc_t br = make_rsrc(beta, (EPI == kEpiGelu && beta != nullptr) ? rbytes : 0u);
+#pragma unroll
+    for (int k = 0; k < K; ++k) unpack<T>(ld_chunk<T, VEC>(br, t + k * nthr), bv[k]);
   }
 
   float acc1[K][E], acc2[K][E];
@@ -248,8 +266,8 @@ norm_bwd_rows(const T* dy, const T* x, const T* w, const float* mean, const floa
       if (base >= rows) goto done;
       load_batch<T, K, D, VEC, LN, ROPE>(buf[(i + PF) % (PF + 1)], base + PF * step, rows, x, dy,
                                          mean, rstat, n, t, nthr, ra);
-      process_batch<T, K, D, VEC, LN, ROPE>(buf[i], base, rows, dx, n, t, nthr, W, wave, lane,
-                                            inv_n, wv, acc1, acc2, red, parity);
+      process_batch<T, K, D, VEC, LN, ROPE, EPI>(buf[i], base, rows, dx, n, t, nthr, W, wave, lane,
+                                                 inv_n, wv, bv, acc1, acc2, red, parity);
       base += step;
     }
   }
@@ -288,70 +306,34 @@ done:
   }
 }
 
-// Stage 2: out[j] = sum over p of part[p][j].  One column per lane, 64
-// columns per workgroup; wave q of the 16 adds the fixed slice
-// [qP/16, (q+1)P/16) in order, 16 loads in flight, and the 16 slice sums
-// meet in LDS and are added in wave order.  blockIdx.y selects the matrix
-// (dW / dgamma, or dbeta).
-__global__ void __launch_bounds__(1024)
-colreduce(const float* part, int64_t part_stride, int P, int n, float* out0, float* out1) {
-  float* out = blockIdx.y == 0 ? out0 : out1;
-  if (out == nullptr) return;  // uniform over the workgroup
-  const float* src = part + blockIdx.y * part_stride;
-  __shared__ float acc_lds[16][64];
-  const int wave = wave_id(), lane = threadIdx.x & 63;
-  const int nw = blockDim.x >> 6;
-  const int col = blockIdx.x * 64 + lane;
-  const int p0 = static_cast<int>((static_cast<int64_t>(P) * wave) / nw);
-  const int p1 = static_cast<int>((static_cast<int64_t>(P) * (wave + 1)) / nw);
-  float s = 0.0f;
-  if (col < n) {
-    const float* c = src + col;
-    int p = p0;
-    for (; p + 16 <= p1; p += 16) {
-      float v[16];
-#pragma unroll
-      for (int i = 0; i < 16; ++i) v[i] = c[static_cast<int64_t>(p + i) * n];
-#pragma unroll
-      for (int i = 0; i < 16; ++i) s += v[i];
-    }
-    for (; p < p1; ++p) s += c[static_cast<int64_t>(p) * n];
-  }
-  acc_lds[wave][lane] = s;
-  __syncthreads();
-  if (wave == 0 && col < n) {
-    float tot = acc_lds[0][lane];
-    for (int i = 1; i < nw; ++i) tot += acc_lds[i][lane];
-    out[col] = tot;
-  }
-}
 
-namespace {
-
-template <typename T, int K, int D, bool A, bool LN, bool RP>
+template <typename T, int K, int D, bool A, bool LN, int EP>
 hipError_t launch_bwd_kd(const BwdPlan& pl, const void* dy, const void* x, const void* w,
-                         const float* mean, const float* rstat, void* dx, float* part,
-                         int64_t rows, int n, float w_add, const RopeArgs& ra, hipStream_t st) {
+                         const void* beta, const float* mean, const float* rstat, void* dx,
+                         float* part, int64_t rows, int n, float w_add, const RopeArgs& ra,
+                         hipStream_t st) {
   const int64_t part_stride = static_cast<int64_t>(pl.P) * n;
-  auto kern = pl.PF == 2 ? norm_bwd_rows<T, K, D, 2, A, LN, RP> : norm_bwd_rows<T, K, D, 1, A, LN, RP>;
+  auto kern = pl.PF == 2 ? norm_bwd_rows<T, K, D, 2, A, LN, EP> : norm_bwd_rows<T, K, D, 1, A, LN, EP>;
   hipLaunchKernelGGL(kern, dim3(pl.P), dim3(64 * pl.W), 0, st, static_cast<const T*>(dy),
-                     static_cast<const T*>(x), static_cast<const T*>(w), mean, rstat,
-                     static_cast<T*>(dx), part, part_stride, rows, n, w_add, ra);
+                     static_cast<const T*>(x), static_cast<const T*>(w),
+                     static_cast<const T*>(beta), mean, rstat, static_cast<T*>(dx), part,
+                     part_stride, rows, n, w_add, ra);
   return hipGetLastError();
 }
 
 // (K, D) pairs with K * D <= 8: the row batch stays within the register
 // budget of a 1024-thread workgroup.
-template <typename T, bool A, bool LN, bool RP>
+template <typename T, bool A, bool LN, int EP>
 hipError_t launch_bwd_a(const BwdPlan& pl, const void* dy, const void* x, const void* w,
-                        const float* mean, const float* rstat, void* dx, float* part,
-                        int64_t rows, int n, float w_add, const RopeArgs& ra, hipStream_t st) {
+                        const void* beta, const float* mean, const float* rstat, void* dx,
+                        float* part, int64_t rows, int n, float w_add, const RopeArgs& ra,
+                        hipStream_t st) {
   const int key = pl.K * 16 + pl.D;
   switch (key) {
 #define NR_CASE(KK, DD)                                                                          \
   case KK * 16 + DD:                                                                             \
-    return launch_bwd_kd<T, KK, DD, A, LN, RP>(pl, dy, x, w, mean, rstat, dx, part, rows, n, w_add, \
-                                               ra, st);
+    return launch_bwd_kd<T, KK, DD, A, LN, EP>(pl, dy, x, w, beta, mean, rstat, dx, part, rows, n, \
+                                               w_add, ra, st);
     NR_CASE(1, 1) NR_CASE(1, 2) NR_CASE(1, 4) NR_CASE(1, 8)
     NR_CASE(2, 1) NR_CASE(2, 2) NR_CASE(2, 4)
     NR_CASE(4, 1) NR_CASE(4, 2)
@@ -361,42 +343,22 @@ hipError_t launch_bwd_a(const BwdPlan& pl, const void* dy, const void* x, const 
   }
 }
 
-template <typename T, bool LN, bool RP>
+template <typename T, bool LN, int EP>
 hipError_t launch_bwd_t(const BwdPlan& pl, const void* dy, const void* x, const void* w,
-                        const float* mean, const float* rstat, void* dx, float* part,
-                        int64_t rows, int n, float w_add, const RopeArgs& ra, hipStream_t st) {
-  return pl.aligned ? launch_bwd_a<T, true, LN, RP>(pl, dy, x, w, mean, rstat, dx, part, rows, n, w_add, ra, st)
-                    : launch_bwd_a<T, false, LN, RP>(pl, dy, x, w, mean, rstat, dx, part, rows, n, w_add, ra, st);
+                        const void* beta, const float* mean, const float* rstat, void* dx,
+                        float* part, int64_t rows, int n, float w_add, const RopeArgs& ra,
+                        hipStream_t st) {
+  return pl.aligned ? launch_bwd_a<T, true, LN, EP>(pl, dy, x, w, beta, mean, rstat, dx, part, rows, n, w_add, ra, st)
+                    : launch_bwd_a<T, false, LN, EP>(pl, dy, x, w, beta, mean, rstat, dx, part, rows, n, w_add, ra, st);
 }
 
-}  // namespace
 
-hipError_t launch_norm_bwd(bool ln, int dt, const BwdPlan& pl, const void* dy, const void* x,
-                           const void* w, const float* mean, const float* rstat, void* dx,
-                           float* part, int64_t rows, int n, float w_add, hipStream_t st) {
-  const RopeArgs none{nullptr, nullptr, 2, 1};
-  if (dt == kF32)
-    return ln ? launch_bwd_t<float, true, false>(pl, dy, x, w, mean, rstat, dx, part, rows, n, w_add, none, st)
-              : launch_bwd_t<float, false, false>(pl, dy, x, w, mean, rstat, dx, part, rows, n, w_add, none, st);
-  return ln ? launch_bwd_t<bf16, true, false>(pl, dy, x, w, mean, rstat, dx, part, rows, n, w_add, none, st)
-            : launch_bwd_t<bf16, false, false>(pl, dy, x, w, mean, rstat, dx, part, rows, n, w_add, none, st);
-}
-
-hipError_t launch_rms_rope_bwd(int dt, const BwdPlan& pl, const void* dout, const void* x,
-                               const void* w, const float* inv_rms, const RopeArgs& ra, void* dx,
-                               float* part, int64_t rows, int n, float w_add, hipStream_t st) {
-  if (dt == kF32)
-    return launch_bwd_t<float, false, true>(pl, dout, x, w, nullptr, inv_rms, dx, part, rows, n,
-                                            w_add, ra, st);
-  return launch_bwd_t<bf16, false, true>(pl, dout, x, w, nullptr, inv_rms, dx, part, rows, n,
-                                         w_add, ra, st);
-}
-
-hipError_t launch_colreduce(const float* part, int64_t part_stride, int P, int n, float* out0,
-                            float* out1, hipStream_t st) {
-  const dim3 grid(static_cast<unsigned>((n + 63) / 64), out1 != nullptr ? 2u : 1u);
-  hipLaunchKernelGGL(colreduce, grid, dim3(1024), 0, st, part, part_stride, P, n, out0, out1);
-  return hipGetLastError();
-}
+// One translation unit instantiates each (type, operator, epilogue)
+// combination, so the build compiles them in parallel.
+#define NR_BWD_INSTANTIATE(T, LN, EPI)                                                         \
+  template hipError_t launch_bwd_t<T, LN, EPI>(const BwdPlan&, const void*, const void*,       \
+                                               const void*, const void*, const float*,          \
+                                               const float*, void*, float*, int64_t, int, float, \
+                                               const RopeArgs&, hipStream_t);
 
 }  // namespace nr

@@ -1,0 +1,100 @@
+// norm_bwd_dispatch.hip -- host entry points of the backward (stage 1 by
+// dtype, operator and epilogue) and stage 2, the fixed-order column sum.
+#include "norm_bwd.hpp"
+
+namespace nr {
+
+// Stage 2: out[j] = sum over p of part[p][j].  One column per lane, 64
+// columns per workgroup; wave q of the 16 adds the fixed slice
+// [qP/16, (q+1)P/16) in order, 16 loads in flight, and the 16 slice sums
+// meet in LDS and are added in wave order.  blockIdx.y selects the matrix
+// (dW / dgamma, or dbeta).
+__global__ void __launch_bounds__(1024)
+colreduce(const float* part, int64_t part_stride, int P, int n, float* out0, float* out1) {
+  float* out = blockIdx.y == 0 ? out0 : out1;
+  if (out == nullptr) return;  // uniform over the workgroup
+  const float* src = part + blockIdx.y * part_stride;
+  __shared__ float acc_lds[16][64];
+  const int wave = wave_id(), lane = threadIdx.x & 63;
+  const int nw = blockDim.x >> 6;
+  const int col = blockIdx.x * 64 + lane;
+  const int p0 = static_cast<int>((static_cast<int64_t>(P) * wave) / nw);
+  const int p1 = static_cast<int>((static_cast<int64_t>(P) * (wave + 1)) / nw);
+  float s = 0.0f;
+  if (col < n) {
+    const float* c = src + col;
+    int p = p0;
+    for (; p + 16 <= p1; p += 16) {
+      float v[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) v[i] = c[static_cast<int64_t>(p + i) * n];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) s += v[i];
+    }
+    for (; p < p1; ++p) s += c[static_cast<int64_t>(p) * n];
+  }
+  acc_lds[wave][lane] = s;
+  __syncthreads();
+  if (wave == 0 && col < n) {
+    float tot = acc_lds[0][lane];
+    for (int i = 1; i < nw; ++i) tot += acc_lds[i][lane];
+    out[col] = tot;
+  }
+}
+
+#define NR_BWD_EXTERN(T, LN, EPI)                                                             \
+  extern template hipError_t launch_bwd_t<T, LN, EPI>(const BwdPlan&, const void*, const void*, \
+                                                      const void*, const void*, const float*,    \
+                                                      const float*, void*, float*, int64_t, int, \
+                                                      float, const RopeArgs&, hipStream_t);
+NR_BWD_EXTERN(float, false, kEpiNone)
+NR_BWD_EXTERN(bf16, false, kEpiNone)
+NR_BWD_EXTERN(float, true, kEpiNone)
+NR_BWD_EXTERN(bf16, true, kEpiNone)
+NR_BWD_EXTERN(float, false, kEpiRope)
+NR_BWD_EXTERN(bf16, false, kEpiRope)
+NR_BWD_EXTERN(float, true, kEpiGelu)
+NR_BWD_EXTERN(bf16, true, kEpiGelu)
+#undef NR_BWD_EXTERN
+
+hipError_t launch_norm_bwd(bool ln, int dt, const BwdPlan& pl, const void* dy, const void* x,
+                           const void* w, const float* mean, const float* rstat, void* dx,
+                           float* part, int64_t rows, int n, float w_add, hipStream_t st) {
+  const RopeArgs none{nullptr, nullptr, 2, 1};
+  if (dt == kF32)
+    return ln ? launch_bwd_t<float, true, kEpiNone>(pl, dy, x, w, nullptr, mean, rstat, dx, part, rows, n, w_add, none, st)
+              : launch_bwd_t<float, false, kEpiNone>(pl, dy, x, w, nullptr, mean, rstat, dx, part, rows, n, w_add, none, st);
+  return ln ? launch_bwd_t<bf16, true, kEpiNone>(pl, dy, x, w, nullptr, mean, rstat, dx, part, rows, n, w_add, none, st)
+            : launch_bwd_t<bf16, false, kEpiNone>(pl, dy, x, w, nullptr, mean, rstat, dx, part, rows, n, w_add, none, st);
+}
+
+hipError_t launch_rms_rope_bwd(int dt, const BwdPlan& pl, const void* dout, const void* x,
+                               const void* w, const float* inv_rms, const RopeArgs& ra, void* dx,
+                               float* part, int64_t rows, int n, float w_add, hipStream_t st) {
+  if (dt == kF32)
+    return launch_bwd_t<float, false, kEpiRope>(pl, dout, x, w, nullptr, nullptr, inv_rms, dx, part,
+                                                rows, n, w_add, ra, st);
+  return launch_bwd_t<bf16, false, kEpiRope>(pl, dout, x, w, nullptr, nullptr, inv_rms, dx, part,
+                                             rows, n, w_add, ra, st);
+}
+
+hipError_t launch_ln_gelu_bwd(int dt, const BwdPlan& pl, const void* dout, const void* x,
+                              const void* gamma, const void* beta, const float* mean,
+                              const float* rstd, void* dx, float* part, int64_t rows, int n,
+                              hipStream_t st) {
+  const RopeArgs none{nullptr, nullptr, 2, 1};
+  if (dt == kF32)
+    return launch_bwd_t<float, true, kEpiGelu>(pl, dout, x, gamma, beta, mean, rstd, dx, part, rows,
+                                               n, 0.0f, none, st);
+  return launch_bwd_t<bf16, true, kEpiGelu>(pl, dout, x, gamma, beta, mean, rstd, dx, part, rows, n,
+                                            0.0f, none, st);
+}
+
+hipError_t launch_colreduce(const float* part, int64_t part_stride, int P, int n, float* out0,
+                            float* out1, hipStream_t st) {
+  const dim3 grid(static_cast<unsigned>((n + 63) / 64), out1 != nullptr ? 2u : 1u);
+  hipLaunchKernelGGL(colreduce, grid, dim3(1024), 0, st, part, part_stride, P, n, out0, out1);
+  return hipGetLastError();
+}
+
+}  // namespace nr

@@ -1,4 +1,4 @@
-// norm_fwd.hip -- single-pass RMSNorm / LayerNorm forward for gfx950.
+// norm_fwd.hpp -- single-pass RMSNorm / LayerNorm forward for gfx950.
 //
 // Operation (Helios 性能优化全解析, 内核一 FlashNorm): each row is read from
 // HBM once; its sums are formed on chip; the normalised row, scaled by the
@@ -15,6 +15,8 @@
 // rows use W > 1 waves whose wave sums meet in LDS.  All of a lane's loads
 // (row chunks and weight chunks) are issued before the first use, so each
 // wave keeps up to K x 1 KiB of row data in flight.
+#pragma once
+
 #include "nr_device.hpp"
 #include "nr_internal.hpp"
 
@@ -41,10 +43,12 @@ __device__ __forceinline__ void group_sum_n(float (&v)[J], int W, int wave, int 
 }
 
 // A row group (W waves) normalises J consecutive rows; the weight chunks it
-// loads serve all J of them.  ROPE (RMSNorm only): before the single rounding,
-// the normalised row is rotated as interleaved RoPE pairs by its token's
-// angles, so the norm -> RoPE chain costs one read and one write of the row.
-template <typename T, int K, int J, bool VEC, bool LN, bool ROPE>
+// loads serve all J of them.  Epilogues, applied before the single rounding:
+// kEpiRope (RMSNorm) rotates the normalised row as interleaved RoPE pairs by
+// its token's angles, so the norm -> RoPE chain costs one read and one write
+// of the row; kEpiGelu (LayerNorm) passes the affine output through the
+// tanh-approximated GeLU (LLM层的优化算子, 编写定制融合算子).
+template <typename T, int K, int J, bool VEC, bool LN, int EPI>
 __device__ __forceinline__ void norm_fwd_body(const T* x, const T* w, const T* b, T* y,
                                               float* stat0, float* stat1, int64_t rows, int n,
                                               float eps, float w_add, int W, const RopeArgs& ra) {
@@ -148,6 +152,7 @@ __device__ __forceinline__ void norm_fwd_body(const T* x, const T* w, const T* b
     // RoPE: the token's table rows, and the offset within its head of this
     // lane's first chunk (advancing by a fixed step per chunk)
     const int half = ra.head_dim >> 1;
+    constexpr bool ROPE = EPI == kEpiRope;
     const int64_t tok = ROPE ? (active ? row : 0) / ra.rows_per_token : 0;
     const uint32_t tb = (ROPE && active) ? static_cast<uint32_t>(half) * 4u : 0u;
     const rsrc_t cr = make_rsrc(ra.cos_tab + tok * half, tb);
@@ -165,6 +170,7 @@ __device__ __forceinline__ void norm_fwd_body(const T* x, const T* w, const T* b
         const float ww = (w != nullptr) ? wv[e] + w_add : 1.0f;
         if constexpr (LN) {
           o[e] = fmaf((v[e] - mean[j]) * r[j], ww, bv[e]);
+          if constexpr (EPI == kEpiGelu) o[e] = gelu_tanh(o[e]);
         } else {
           o[e] = (v[e] * r[j]) * ww;
         }
@@ -203,24 +209,23 @@ __device__ __forceinline__ void norm_fwd_body(const T* x, const T* w, const T* b
 
 // One wavefront per row group (W == 1), at most 4 row groups (256 threads)
 // per workgroup.
-template <typename T, int K, int J, bool VEC, bool LN, bool ROPE>
+template <typename T, int K, int J, bool VEC, bool LN, int EPI>
 __global__ void __launch_bounds__(256)
 norm_fwd_wave(const T* x, const T* w, const T* b, T* y, float* stat0, float* stat1,
               int64_t rows, int n, float eps, float w_add, RopeArgs ra) {
-  norm_fwd_body<T, K, J, VEC, LN, ROPE>(x, w, b, y, stat0, stat1, rows, n, eps, w_add, 1, ra);
+  norm_fwd_body<T, K, J, VEC, LN, EPI>(x, w, b, y, stat0, stat1, rows, n, eps, w_add, 1, ra);
 }
 
 // Several waves per row group (W > 1), up to 16 waves per workgroup.
-template <typename T, int K, int J, bool VEC, bool LN, bool ROPE>
+template <typename T, int K, int J, bool VEC, bool LN, int EPI>
 __global__ void __launch_bounds__(1024)
 norm_fwd_group(const T* x, const T* w, const T* b, T* y, float* stat0, float* stat1,
                int64_t rows, int n, float eps, float w_add, int W, RopeArgs ra) {
-  norm_fwd_body<T, K, J, VEC, LN, ROPE>(x, w, b, y, stat0, stat1, rows, n, eps, w_add, W, ra);
+  norm_fwd_body<T, K, J, VEC, LN, EPI>(x, w, b, y, stat0, stat1, rows, n, eps, w_add, W, ra);
 }
 
-namespace {
 
-template <typename T, int K, int J, bool A, bool LN, bool RP>
+template <typename T, int K, int J, bool A, bool LN, int RP>
 hipError_t launch_fwd_kj(const FwdPlan& pl, const void* x, const void* w, const void* b, void* y,
                          float* s0, float* s1, int64_t rows, int n, float eps, float w_add,
                          const RopeArgs& ra, hipStream_t st) {
@@ -243,7 +248,7 @@ hipError_t launch_fwd_kj(const FwdPlan& pl, const void* x, const void* w, const 
   return hipGetLastError();
 }
 
-template <typename T, int K, bool A, bool LN, bool RP>
+template <typename T, int K, bool A, bool LN, int RP>
 hipError_t launch_fwd_k(const FwdPlan& pl, const void* x, const void* w, const void* b, void* y,
                         float* s0, float* s1, int64_t rows, int n, float eps, float w_add,
                         const RopeArgs& ra, hipStream_t st) {
@@ -255,7 +260,7 @@ hipError_t launch_fwd_k(const FwdPlan& pl, const void* x, const void* w, const v
   return launch_fwd_kj<T, K, 1, A, LN, RP>(pl, x, w, b, y, s0, s1, rows, n, eps, w_add, ra, st);
 }
 
-template <typename T, bool A, bool LN, bool RP>
+template <typename T, bool A, bool LN, int RP>
 hipError_t launch_fwd_a(const FwdPlan& pl, const void* x, const void* w, const void* b, void* y,
                         float* s0, float* s1, int64_t rows, int n, float eps, float w_add,
                         const RopeArgs& ra, hipStream_t st) {
@@ -268,7 +273,7 @@ hipError_t launch_fwd_a(const FwdPlan& pl, const void* x, const void* w, const v
   }
 }
 
-template <typename T, bool LN, bool RP>
+template <typename T, bool LN, int RP>
 hipError_t launch_fwd_t(const FwdPlan& pl, const void* x, const void* w, const void* b, void* y,
                         float* s0, float* s1, int64_t rows, int n, float eps, float w_add,
                         const RopeArgs& ra, hipStream_t st) {
@@ -276,27 +281,12 @@ hipError_t launch_fwd_t(const FwdPlan& pl, const void* x, const void* w, const v
                     : launch_fwd_a<T, false, LN, RP>(pl, x, w, b, y, s0, s1, rows, n, eps, w_add, ra, st);
 }
 
-}  // namespace
 
-hipError_t launch_norm_fwd(bool ln, int dt, const FwdPlan& pl, const void* x, const void* w,
-                           const void* b, void* y, float* s0, float* s1, int64_t rows, int n,
-                           float eps, float w_add, hipStream_t st) {
-  const RopeArgs none{nullptr, nullptr, 2, 1};
-  if (dt == kF32)
-    return ln ? launch_fwd_t<float, true, false>(pl, x, w, b, y, s0, s1, rows, n, eps, w_add, none, st)
-              : launch_fwd_t<float, false, false>(pl, x, w, b, y, s0, s1, rows, n, eps, w_add, none, st);
-  return ln ? launch_fwd_t<bf16, true, false>(pl, x, w, b, y, s0, s1, rows, n, eps, w_add, none, st)
-            : launch_fwd_t<bf16, false, false>(pl, x, w, b, y, s0, s1, rows, n, eps, w_add, none, st);
-}
-
-hipError_t launch_rms_rope_fwd(int dt, const FwdPlan& pl, const void* x, const void* w, void* y,
-                               float* inv_rms, const RopeArgs& ra, int64_t rows, int n, float eps,
-                               float w_add, hipStream_t st) {
-  if (dt == kF32)
-    return launch_fwd_t<float, false, true>(pl, x, w, nullptr, y, inv_rms, nullptr, rows, n, eps,
-                                            w_add, ra, st);
-  return launch_fwd_t<bf16, false, true>(pl, x, w, nullptr, y, inv_rms, nullptr, rows, n, eps,
-                                         w_add, ra, st);
-}
+// One translation unit instantiates each (type, operator, epilogue)
+// combination, so the build compiles them in parallel.
+#define NR_FWD_INSTANTIATE(T, LN, EPI)                                                         \
+  template hipError_t launch_fwd_t<T, LN, EPI>(const FwdPlan&, const void*, const void*,       \
+                                               const void*, void*, float*, float*, int64_t, int, \
+                                               float, float, const RopeArgs&, hipStream_t);
 
 }  // namespace nr

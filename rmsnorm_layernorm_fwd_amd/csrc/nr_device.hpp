@@ -201,6 +201,35 @@ __device__ __forceinline__ void rotate_pairs(float* v, const float (&c)[PP], con
   }
 }
 
+// ---- tanh-approximated GeLU --------------------------------------------
+//
+// gelu(v) = v/2 (1 + tanh(u)), u = c (v + 0.044715 v^3), c = sqrt(2/pi).
+// Since 1 + tanh(u) = 2 / (1 + exp(-2u)), it is evaluated as
+// v / (1 + exp(-2u)), which does not cancel for v << 0 and saturates to 0
+// or v without overflow trouble.  The derivative, with s = 1/(1 + exp(-2u))
+// and 1 - s = exp(-2u) s:
+//   gelu'(v) = s + 2 v s (1 - s) c (1 + 3 * 0.044715 v^2).
+constexpr float kGeluC = 0.7978845608028654f;  // sqrt(2/pi)
+constexpr float kGeluA = 0.044715f;
+
+__device__ __forceinline__ float gelu_tanh(float v) {
+  const float u = kGeluC * fmaf(kGeluA * v * v, v, v);
+  return v / (1.0f + expf(-2.0f * u));
+}
+
+__device__ __forceinline__ float gelu_tanh_grad(float v) {
+  const float u = kGeluC * fmaf(kGeluA * v * v, v, v);
+  const float e = expf(-2.0f * u);
+  const float sg = 1.0f / (1.0f + e);
+  const float one_minus = e * sg;
+  return fmaf(2.0f * v * sg * one_minus * kGeluC, fmaf(3.0f * kGeluA, v * v, 1.0f), sg);
+}
+
+// Epilogues of the fused row kernels
+constexpr int kEpiNone = 0;
+constexpr int kEpiRope = 1;  // RMSNorm output rotated as interleaved RoPE pairs
+constexpr int kEpiGelu = 2;  // LayerNorm output through the tanh-approximated GeLU
+
 // index of the calling wave within its workgroup, as a scalar (SGPR) value
 __device__ __forceinline__ int wave_id() {
   return __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));

@@ -50,6 +50,13 @@ hipError_t launch_rms_rope_fwd(int dt, const FwdPlan& pl, const void* x, const v
 hipError_t launch_rms_rope_bwd(int dt, const BwdPlan& pl, const void* dout, const void* x,
                                const void* w, const float* inv_rms, const RopeArgs& ra, void* dx,
                                float* part, int64_t rows, int n, float w_add, hipStream_t st);
+hipError_t launch_ln_gelu_fwd(int dt, const FwdPlan& pl, const void* x, const void* gamma,
+                              const void* beta, void* y, float* mean, float* rstd, int64_t rows,
+                              int n, float eps, hipStream_t st);
+hipError_t launch_ln_gelu_bwd(int dt, const BwdPlan& pl, const void* dout, const void* x,
+                              const void* gamma, const void* beta, const float* mean,
+                              const float* rstd, void* dx, float* part, int64_t rows, int n,
+                              hipStream_t st);
 hipError_t launch_norm_fwd(bool ln, int dt, const FwdPlan& pl, const void* x, const void* w,
                            const void* b, void* y, float* s0, float* s1, int64_t rows, int n,
                            float eps, float w_add, hipStream_t st);

@@ -35,6 +35,7 @@ def lib():
 def test_header_functions_exported(lib):
     names = declared_functions()
     expected = {"rmsnorm_fwd", "rmsnorm_bwd", "layernorm_fwd", "layernorm_bwd",
+                "rmsnorm_rope_fwd", "rmsnorm_rope_bwd", "layernorm_gelu_fwd", "layernorm_gelu_bwd",
                 "rope_interleaved_apply", "rope_table_1d", "rope_table_3d",
                 "nr_bwd_workspace_bytes", "nr_status_str", "nr_last_hip_error", "nr_tune",
                 "nr_norm_n_max"}
@@ -72,6 +73,8 @@ def test_workspace_bytes():
     assert nr.nr_bwd_workspace_bytes(1, 7, 0) == 7 * 4
     assert nr.nr_bwd_workspace_bytes(0, 7, 0) == 0
     assert nr.nr_bwd_workspace_bytes(17, 8, 0) == 2 * 8 * 4
+    assert nr.nr_bwd_workspace_bytes(65536, 5120, 2) == 512 * 5120 * 4  # fused RMSNorm + RoPE
+    assert nr.nr_bwd_workspace_bytes(64, 8, 3) == 0
 
 
 def test_tune_keys(lib):

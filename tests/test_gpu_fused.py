@@ -124,3 +124,51 @@ def test_fused_longseq():
         sl = slice(c0, c0 + 8192)
         rdw += oracle.rmsnorm_rope_bwd(dout[sl], x[sl], w, ang[sl], d, 1, eps, want_dx=False)[1]
     check("fused longseq dw", dw, rdw, "col")
+
+
+# ---------------------------------------------------------------- LayerNorm + GeLU
+
+def check_ln_gelu(tag, x, gm, bt, dout, eps=1e-5, layout="packed"):
+    rows, n = x.shape
+    say(f"{tag}: fused layernorm+gelu {rows}x{n} {x.dtype} gamma={gm is not None} "
+        f"beta={bt is not None} {layout}")
+    if layout == "unaligned":
+        buf = torch.empty(rows * n + 1, dtype=x.dtype, device=DEV)
+        xg = buf[1:].view(rows, n)
+        xg.copy_(g(x))
+    else:
+        xg = g(x)
+    y, mu, rs = nr.layernorm_gelu_fwd(xg, g(gm), g(bt), eps)
+    dx, dg, db = nr.layernorm_gelu_bwd(g(dout), xg, g(gm), g(bt), mu, rs)
+    torch.cuda.synchronize()
+    ry, rmu, rrs = oracle.layernorm_gelu_fwd(x, gm, bt, eps)
+    rdx, rdg, rdb = oracle.layernorm_gelu_bwd(dout, x, gm, bt, eps)
+    k = out_kind(x.dtype)
+    x64 = to64(x)
+    check(f"{tag} y", y, ry, k)
+    check(f"{tag} mean", mu, rmu, "stat", s=np.sqrt(np.mean(x64 * x64, axis=1)))
+    check(f"{tag} rstd", rs, rrs, "stat", s=0.0)
+    # row scale of dx: the terms r * dout * gamma (|gelu'| stays below 1.13)
+    check(f"{tag} dx", dx, rdx, k, s=1.13 * grad_scale(rrs, dout, gm))
+    check(f"{tag} dgamma", dg, rdg, "col")
+    check(f"{tag} dbeta", db, rdb, "col")
+
+
+def test_ln_gelu_full_size():
+    inp = workloads.norm_inputs("ln_affine_15360x5120")
+    check_ln_gelu("ln_gelu_15360x5120", inp["x"], inp["w"], inp["b"], inp["dy"], inp["eps"])
+
+
+@pytest.mark.parametrize("rows,n,dtype,affine,layout", [
+    (1, 1, torch.float32, True, "packed"), (3, 7, torch.bfloat16, True, "packed"),
+    (257, 64, torch.float32, True, "packed"), (33, 1000, torch.bfloat16, False, "packed"),
+    (17, 5128, torch.bfloat16, True, "packed"), (9, 8191, torch.bfloat16, True, "packed"),
+    (40, 520, torch.bfloat16, True, "unaligned"), (3, 32768, torch.float32, True, "packed"),
+])
+def test_ln_gelu_edges(rows, n, dtype, affine, layout):
+    seed = 8000 + rows * 3 + n
+    x = workloads.normal((rows, n), seed, dtype, mean=0.5, std=2.0)
+    gm = workloads.normal((n,), seed + 1, dtype, mean=1.0, std=0.1) if affine else None
+    bt = workloads.normal((n,), seed + 2, dtype, std=0.5) if affine else None
+    dout = workloads.normal((rows, n), seed + 3, dtype)
+    check_ln_gelu(f"ln+gelu edge {rows}x{n}", x, gm, bt, dout, layout=layout)
