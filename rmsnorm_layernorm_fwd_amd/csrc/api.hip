@@ -123,12 +123,15 @@ nr_status_t plan_fwd(nr_dtype_t dt, int64_t n, bool aligned, FwdPlan* pl) {
 //   D (rows per batch) and PF (batches loaded ahead): the largest that fit
 //     the 128-VGPR budget of a 1024-thread workgroup without spilling.
 //     RMSNorm with one chunk per lane takes D = 2, PF = 2; LayerNorm, which
-//     also carries the dbeta accumulators, D = 1, PF = 1.
+//     also carries the dbeta accumulators, D = 1, PF = 1.  LayerNorm + GeLU
+//     spends far more ALU time per row (the activation's derivative), so it
+//     loads two batches ahead (PF = 2) to keep HBM busy meanwhile.
 //   P (workgroups): each handles about rows/P rows, dealt out round robin.
 //     At least 16 rows per workgroup keep the fp32 partial rows small next
-//     to the row traffic.  At most 256 (plain RMSNorm, D = 2) or 512
-//     (LayerNorm and the fused RMSNorm + RoPE, D = 1): on MI355X's 256 CUs
-//     that is one or two resident workgroups per CU; more gave a second,
+//     to the row traffic.  At most 256 (plain RMSNorm, D = 2; LayerNorm +
+//     GeLU, whose 104 VGPRs leave room for one 10-wave workgroup per CU) or
+//     512 (LayerNorm and the fused RMSNorm + RoPE, D = 1): on MI355X's 256
+//     CUs that is one or two resident workgroups per CU; more gave a second,
 //     partial round of workgroups and measured slower.
 //   P depends on the row count and the operator only, so the summation order
 //   and the workspace size are the same on every device.
@@ -145,7 +148,7 @@ void bwd_grid(int64_t rows, bool two_per_cu, int64_t* P_out, int64_t* rpb_out) {
 }
 
 nr_status_t plan_bwd(nr_dtype_t dt, bool ln, int64_t rows, int64_t n, bool aligned, BwdPlan* pl,
-                     bool rope = false) {
+                     bool rope = false, bool gelu = false) {
   const int E = vec_elems(dt);
   const int64_t nchunk = (n + E - 1) / E;
   const int64_t need = (nchunk + 63) / 64;
@@ -162,7 +165,7 @@ nr_status_t plan_bwd(nr_dtype_t dt, bool ln, int64_t rows, int64_t n, bool align
   // (the fused RMSNorm + RoPE backward also holds each chunk's cos/sin: one
   // row per batch, two batches ahead)
   int D = (!ln && !rope && K == 1) ? 2 : 1;
-  int PF = (!ln && K == 1) ? 2 : 1;
+  int PF = ((!ln || gelu) && K == 1) ? 2 : 1;
   if (tune(BWD_D) > 0) D = tune(BWD_D);
   if (tune(BWD_PF) > 0) PF = tune(BWD_PF);
   if (!in_set(K, kBwdK, 4) || !in_set(D, kBwdD, 4) || K * D > 8 || W < 1 || W > 16)
@@ -170,7 +173,7 @@ nr_status_t plan_bwd(nr_dtype_t dt, bool ln, int64_t rows, int64_t n, bool align
   if (PF < 1 || PF > 2) return NR_ERR_SHAPE;
   if (static_cast<int64_t>(64) * W * K < nchunk) return NR_ERR_SHAPE;
   int64_t P, rpb;
-  bwd_grid(rows, ln || rope, &P, &rpb);
+  bwd_grid(rows, (ln && !gelu) || rope, &P, &rpb);
   *pl = BwdPlan{W, K, D, static_cast<int>(P), PF, rpb, aligned};
   return NR_OK;
 }
@@ -298,7 +301,7 @@ nr_status_t norm_bwd_common(bool ln, nr_dtype_t dt, const void* dy, const void* 
                        aligned16(dx) && (w == nullptr || aligned16(w)) &&
                        (beta == nullptr || aligned16(beta));
   BwdPlan pl;
-  if ((s = plan_bwd(dt, ln, rows, n, aligned, &pl)) != NR_OK) return s;
+  if ((s = plan_bwd(dt, ln, rows, n, aligned, &pl, false, gelu)) != NR_OK) return s;
   float* part = nullptr;
   if (want_cols) {
     const size_t need = static_cast<size_t>(pl.P) * n * sizeof(float) * (ln ? 2 : 1);

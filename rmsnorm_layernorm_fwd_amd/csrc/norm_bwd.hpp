@@ -121,25 +121,30 @@ __device__ __forceinline__ void process_batch(RowBatch<T, K, D, ROPE ? 1 : 0>& b
   constexpr int E = Vec<T>::N;
   constexpr int NS = LN ? 2 : 1;  // row sums per row
   // per-lane partial row sums, and the column partials.  Elements past n
-  // were read as 0 (x and dy), so they add nothing; only LayerNorm's
-  // centred xhat needs the explicit mask.
+  // (and rows past the end) were read as 0, so their dy is 0 and every
+  // term they contribute is 0 times a finite value: no mask is needed,
+  // LayerNorm's centred xhat = -mean * rstd there included.
   float s[NS * D];
+  // GeLU: dy * gamma with dy = dout * gelu'(pre-activation), kept for the
+  // second pass (the activation's derivative is the costliest arithmetic
+  // here)
+  constexpr int GD = EPI == kEpiGelu ? D * K : 0;
+  float gdd[GD > 0 ? GD : 1][E];
 #pragma unroll
   for (int d = 0; d < D; ++d) {
     float s1 = 0.0f, s2 = 0.0f;
 #pragma unroll
     for (int k = 0; k < K; ++k) {
-      const int c = t + k * nthr;
       float xv[E], dv[E];
       unpack<T>(b.x[d * K + k], xv);
       dy_chunk<T, K, D, ROPE>(b, d * K + k, dv);
 #pragma unroll
       for (int e = 0; e < E; ++e) {
-        float xh = (xv[e] - b.mu[d]) * b.rs[d];
-        if constexpr (LN) xh = (c * E + e < n) ? xh : 0.0f;
+        const float xh = (xv[e] - b.mu[d]) * b.rs[d];
         float dd = dv[e];
         if constexpr (EPI == kEpiGelu) dd *= gelu_tanh_grad(fmaf(xh, wv[k][e], bv[k][e]));
         const float gg = dd * wv[k][e];
+        if constexpr (EPI == kEpiGelu) gdd[d * K + k][e] = gg;
         if constexpr (LN) {
           s1 += gg;
           s2 = fmaf(gg, xh, s2);
@@ -154,7 +159,7 @@ __device__ __forceinline__ void process_batch(RowBatch<T, K, D, ROPE ? 1 : 0>& b
     if constexpr (LN) s[NS * d + 1] = s2;
   }
   reload_barrier<D * K>(b.x);
-  reload_barrier<D * K>(b.g);
+  if constexpr (EPI != kEpiGelu) reload_barrier<D * K>(b.g);
 
   // reduce the batch's NS*D sums across the workgroup
 #pragma unroll
@@ -187,13 +192,16 @@ __device__ __forceinline__ void process_batch(RowBatch<T, K, D, ROPE ? 1 : 0>& b
     for (int k = 0; k < K; ++k) {
       float xv[E], dv[E], o[E];
       unpack<T>(b.x[d * K + k], xv);
-      dy_chunk<T, K, D, ROPE>(b, d * K + k, dv);
+      if constexpr (EPI != kEpiGelu) dy_chunk<T, K, D, ROPE>(b, d * K + k, dv);
 #pragma unroll
       for (int e = 0; e < E; ++e) {
         const float xh = (xv[e] - b.mu[d]) * b.rs[d];
-        float dd = dv[e];
-        if constexpr (EPI == kEpiGelu) dd *= gelu_tanh_grad(fmaf(xh, wv[k][e], bv[k][e]));
-        const float gg = dd * wv[k][e];
+        float gg;
+        if constexpr (EPI == kEpiGelu) {
+          gg = gdd[d * K + k][e];
+        } else {
+          gg = dv[e] * wv[k][e];
+        }
         if constexpr (LN) {
           o[e] = b.rs[d] * (gg - c1 - xh * c2);
         } else {

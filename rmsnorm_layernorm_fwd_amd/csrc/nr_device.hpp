@@ -206,23 +206,42 @@ __device__ __forceinline__ void rotate_pairs(float* v, const float (&c)[PP], con
 // gelu(v) = v/2 (1 + tanh(u)), u = c (v + 0.044715 v^3), c = sqrt(2/pi).
 // Since 1 + tanh(u) = 2 / (1 + exp(-2u)), it is evaluated as
 // v / (1 + exp(-2u)), which does not cancel for v << 0 and saturates to 0
-// or v without overflow trouble.  The derivative, with s = 1/(1 + exp(-2u))
-// and 1 - s = exp(-2u) s:
+// or v.  The derivative, with s = 1/(1 + exp(-2u)) and 1 - s = exp(-2u) s:
 //   gelu'(v) = s + 2 v s (1 - s) c (1 + 3 * 0.044715 v^2).
-constexpr float kGeluC = 0.7978845608028654f;  // sqrt(2/pi)
-constexpr float kGeluA = 0.044715f;
+//
+// The activation runs once per element of an HBM-bound row kernel, so its
+// ALU cost is what decides whether the fused kernel keeps up with memory:
+// exp(-2u) is one hardware base-2 exponential of v (k0 + k1 v^2) (the
+// constants fold -2 c log2(e) in), and the divisions are hardware
+// reciprocals (about 1 ulp each).  Rounding the exponent's argument costs
+// a relative error of |arg| * 2^-24 * ln 2 in exp(-2u), a few 1e-6 at most
+// where the sigmoid is not saturated: well inside an fp32 tolerance of
+// 1e-5 and far inside one bf16 ulp.
+constexpr double kGeluCd = 0.79788456080286535588;  // sqrt(2/pi)
+constexpr double kLog2e = 1.44269504088896340736;
+constexpr float kGeluK0 = static_cast<float>(-2.0 * kGeluCd * kLog2e);
+constexpr float kGeluK1 = static_cast<float>(-2.0 * kGeluCd * kLog2e * 0.044715);
+constexpr float kGeluT0 = static_cast<float>(2.0 * kGeluCd);           // 2c
+constexpr float kGeluT1 = static_cast<float>(2.0 * kGeluCd * 3.0 * 0.044715);  // 6ac
+
+// exp(-2u) for the activation's argument v.  The exponent is capped at 64:
+// beyond it the sigmoid is below 2^-64 either way, and the cap keeps
+// 1 + exp(-2u) finite so the derivative's s (1 - s) = e s^2 never meets
+// inf * 0.
+__device__ __forceinline__ float gelu_exp(float v, float cap) {
+  return __builtin_amdgcn_exp2f(fminf(v * fmaf(kGeluK1, v * v, kGeluK0), cap));
+}
 
 __device__ __forceinline__ float gelu_tanh(float v) {
-  const float u = kGeluC * fmaf(kGeluA * v * v, v, v);
-  return v / (1.0f + expf(-2.0f * u));
+  // no cap needed: exp = inf gives v * 0 = -0, the limit for v -> -inf
+  return v * __builtin_amdgcn_rcpf(1.0f + gelu_exp(v, __builtin_inff()));
 }
 
 __device__ __forceinline__ float gelu_tanh_grad(float v) {
-  const float u = kGeluC * fmaf(kGeluA * v * v, v, v);
-  const float e = expf(-2.0f * u);
-  const float sg = 1.0f / (1.0f + e);
-  const float one_minus = e * sg;
-  return fmaf(2.0f * v * sg * one_minus * kGeluC, fmaf(3.0f * kGeluA, v * v, 1.0f), sg);
+  const float e = gelu_exp(v, 64.0f);
+  const float s = __builtin_amdgcn_rcpf(1.0f + e);
+  const float t = v * fmaf(kGeluT1, v * v, kGeluT0);  // 2 c v (1 + 3a v^2)
+  return fmaf(t * s, e * s, s);
 }
 
 // Epilogues of the fused row kernels
