@@ -16,6 +16,12 @@ once per call; statistics and column gradients in fp32; no workspace) divided
 by the measured time per step.  The other workloads (--workload) time their
 own operations the same way.  One JSON line goes to stdout.
 
+After the timed steps, outside them: the library's streaming copy over one
+65536 x 5120 bf16 activation gives the practical HBM ceiling ("ceiling";
+the roofline also reports its fraction of it), and each operation is timed
+alone --cold-rounds times with the caches flushed before every call
+("ops_cold": mean, std, min).
+
 --copy-probe runs only a plain device copy of known size: the reference the
 HBM byte counters are scaled by.
 """
@@ -256,7 +262,7 @@ def cpu_baseline(seconds):
         el = time.perf_counter() - t0
         if el >= seconds:
             break
-    cores = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    cores = oracle.max_threads()
     return dict(value=round(per_pass * passes / el / 1e9, 4), unit="GB/s", cores=cores, kind="oracle",
                 sample=(f"the long-sequence step (rmsnorm fwd, rope fwd, rope inverse, rmsnorm bwd, "
                         f"layernorm fwd, layernorm bwd) on rows 0..{rows - 1} of 65536, {passes} passes "
@@ -264,6 +270,66 @@ def cpu_baseline(seconds):
 
 
 # ---------------------------------------------------------------- main
+
+def stream_ceiling(dev, reps=10):
+    """The practical HBM ceiling: the library's streaming copy (the row
+    kernels' access pattern, no arithmetic) over one activation of the
+    long-sequence size, 65536 x 5120 bf16."""
+    import torch
+
+    import rmsnorm_layernorm_fwd_amd as nr
+
+    nbytes = 65536 * 5120 * 2
+    a = torch.ones(nbytes // 2, dtype=torch.bfloat16, device=dev)
+    b = torch.empty_like(a)
+    for _ in range(3):
+        nr.nr_stream_copy(a, b)
+    stream = torch.cuda.current_stream(dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(reps):
+        nr.nr_stream_copy(a, b)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    del a, b
+    return dict(kind="nr_stream_copy (16-byte non-temporal loads/stores, one pass)",
+                bytes_per_launch=2 * nbytes, ms_per_launch=round(ms, 5),
+                gbs=round(2 * nbytes / (ms * 1e-3) / 1e9, 1),
+                frac_of_peak=round(2 * nbytes / (ms * 1e-3) / 1e9 / PEAK_GBS, 4))
+
+
+def cold_op_times(ops, rounds, dev):
+    """Each operation timed alone with the caches cold: before every round a
+    1 GiB scratch buffer is written (untimed), which evicts the 256 MB
+    Infinity Cache and the L2s; then HIP events bracket the one call."""
+    import statistics
+
+    import torch
+
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    res = {}
+    for label, kname, fn, b in ops:
+        ev = []
+        for r in range(rounds):
+            flush.fill_(r & 0x7F)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+            ev.append((e0, e1))
+        torch.cuda.synchronize()
+        t = [e0.elapsed_time(e1) for e0, e1 in ev]
+        mean = statistics.fmean(t)
+        res[label] = dict(kernel=kname, ms_mean=round(mean, 5),
+                          ms_std=round(statistics.pstdev(t), 5), ms_min=round(min(t), 5),
+                          gbs=round(b / (mean * 1e-3) / 1e9, 1),
+                          frac_of_peak=round(b / (mean * 1e-3) / 1e9 / PEAK_GBS, 4))
+    del flush
+    return res
+
 
 def copy_probe(dev):
     import torch
@@ -287,6 +353,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", action="store_true")
+    ap.add_argument("--cold-rounds", type=int, default=10,
+                    help="rounds of the per-operation cold-cache timing (0: skip)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -334,7 +402,9 @@ def main():
     for i, (label, kname, _, b) in enumerate(ops):
         times = [ev[s][i][0].elapsed_time(ev[s][i][1]) for s in range(args.steps)]
         mean = sum(times) / len(times)
-        per_op[label] = dict(kernel=kname, bytes=b, ms_mean=round(mean, 5), ms_min=round(min(times), 5),
+        std = (sum((t - mean) ** 2 for t in times) / len(times)) ** 0.5
+        per_op[label] = dict(kernel=kname, bytes=b, ms_mean=round(mean, 5), ms_std=round(std, 5),
+                             ms_min=round(min(times), 5),
                              gbs=round(b / (mean * 1e-3) / 1e9, 1),
                              frac_of_peak=round(b / (mean * 1e-3) / 1e9 / PEAK_GBS, 4))
     # dominant kernel: of the single-kernel operations, the kernel (one
@@ -362,14 +432,21 @@ def main():
                     ms_per_launch=round(mspl, 5), share_of_step=round(dk["ms"] / ms_per_step, 3))
 
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
+    # outside the timed steps: the copy ceiling and the cold-cache op times
+    ceiling = stream_ceiling(dev)
+    roofline["frac_of_ceiling"] = round(achieved / ceiling["gbs"], 4)
+    cold = cold_op_times(ops, args.cold_rounds, dev) if args.cold_rounds > 0 else None
     out = {
         "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
         "data": "synthetic (seeded normal draws shaped like the Helios 14B activations; no model weights)",
-        "config": dict(desc, step_bytes=step_bytes, frac_of_peak=round(value / PEAK_GBS, 4)),
+        "config": dict(desc, step_bytes=step_bytes, frac_of_peak=round(value / PEAK_GBS, 4),
+                       frac_of_ceiling=round(value / ceiling["gbs"], 4)),
         "roofline": roofline,
+        "ceiling": ceiling,
         "ops": per_op,
+        "ops_cold": cold,
     }
     if not args.no_cpu_baseline and args.workload == "longseq_65536x5120":
         out["cpu_baseline"] = cpu_baseline(args.cpu_seconds)

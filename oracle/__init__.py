@@ -55,6 +55,8 @@ def lib():
         L.oracle_layernorm_gelu_bwd.argtypes = [vp, vp, i32, vp, vp, i32, i64, i64, f64, vp, vp, vp]
         L.oracle_gelu_tanh.argtypes = [f64]
         L.oracle_gelu_tanh_grad.argtypes = [f64]
+        L.oracle_max_threads.argtypes = []
+        L.oracle_max_threads.restype = i32
         L.oracle_gelu_tanh.restype = f64
         L.oracle_gelu_tanh_grad.restype = f64
         for f in ("oracle_rmsnorm_fwd", "oracle_rmsnorm_bwd", "oracle_layernorm_fwd",
@@ -207,6 +209,11 @@ def rmsnorm_rope_bwd(dout, x, w, angle, head_dim, rows_per_token=1, eps=1e-6, ge
     xd = x.detach().cpu().double() if isinstance(x, torch.Tensor) else torch.from_numpy(x)
     return rmsnorm_bwd(torch.from_numpy(dy.reshape(rows, n)), xd, w, eps, gemma,
                        want_dx=want_dx, want_dw=want_dw)
+
+
+def max_threads() -> int:
+    """OpenMP threads the oracle's row loops run on."""
+    return int(lib().oracle_max_threads())
 
 
 def gelu_tanh(v):

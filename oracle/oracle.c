@@ -40,6 +40,7 @@
  * row order.
  */
 #include <math.h>
+#include <omp.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
@@ -404,3 +405,6 @@ void oracle_layernorm_gelu_bwd(const void *dout, const void *x, int dt,
     free(r);
     free(dy);
 }
+
+/* Threads the OpenMP loops above use (reported with the CPU timing). */
+int oracle_max_threads(void) { return omp_get_max_threads(); }

@@ -20,7 +20,7 @@ __all__ = [
     "NormRopeError", "rmsnorm_fwd", "rmsnorm_bwd", "layernorm_fwd", "layernorm_bwd",
     "rmsnorm_rope_fwd", "rmsnorm_rope_bwd", "layernorm_gelu_fwd", "layernorm_gelu_bwd",
     "rope_interleaved_apply", "rope_table_1d", "rope_table_3d", "nr_bwd_workspace_bytes",
-    "nr_status_str", "nr_tune", "nr_norm_n_max", "library_path",
+    "nr_status_str", "nr_tune", "nr_norm_n_max", "nr_stream_copy", "library_path",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -75,6 +75,7 @@ def _lib():
             "nr_last_hip_error": [],
             "nr_tune": [ctypes.c_char_p, i32],
             "nr_norm_n_max": [i32],
+            "nr_stream_copy": [vp, vp, sz, vp],
         }
         for name, args in sig.items():
             fn = getattr(L, name)
@@ -378,8 +379,19 @@ def rope_table_3d(grid, pairs, theta=10000.0, device="cuda"):
 # ---------------------------------------------------------------- helpers
 
 def nr_bwd_workspace_bytes(rows, n, op) -> int:
-    """op: 0 rmsnorm_bwd, 1 layernorm_bwd, 2 rmsnorm_rope_bwd."""
+    """op: 0 rmsnorm_bwd, 1 layernorm_bwd or layernorm_gelu_bwd, 2 rmsnorm_rope_bwd."""
     return int(_lib().nr_bwd_workspace_bytes(rows, n, int(op)))
+
+
+def nr_stream_copy(src: torch.Tensor, dst: torch.Tensor):
+    """Measurement aid: copy src's bytes into dst with the row kernels'
+    streaming access pattern (the practical HBM ceiling)."""
+    _dev("src", src)
+    _dev("dst", dst)
+    nbytes = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() != nbytes or src.device != dst.device:
+        raise ValueError("nr_stream_copy: src and dst must have the same size and device")
+    _check("nr_stream_copy", _lib().nr_stream_copy(_ptr(src), _ptr(dst), nbytes, _stream(src)))
 
 
 def nr_status_str(status: int) -> str:

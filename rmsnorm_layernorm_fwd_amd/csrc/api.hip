@@ -510,4 +510,15 @@ nr_status_t rope_table_3d(float* cos_tab, float* sin_tab, int64_t frames, int64_
       static_cast<hipStream_t>(stream)));
 }
 
+nr_status_t nr_stream_copy(const void* src, void* dst, size_t bytes, void* stream) {
+  if (bytes == 0) return NR_OK;
+  if (src == nullptr || dst == nullptr) return NR_ERR_NULLPTR;
+  if ((bytes & 15u) != 0 || !aligned16(src) || !aligned16(dst)) return NR_ERR_SHAPE;
+  const int64_t nvec = static_cast<int64_t>(bytes / 16);
+  // one workgroup per 16 KiB: the grid must fit hardware limits
+  if (nvec / 1024 >= (int64_t{1} << 31)) return NR_ERR_SHAPE;
+  if (bad_overlap(dst, bytes, src, bytes) || dst == src) return NR_ERR_ALIAS;
+  return hip_status(nr::launch_stream_copy(src, dst, nvec, static_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

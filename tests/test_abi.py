@@ -38,7 +38,7 @@ def test_header_functions_exported(lib):
                 "rmsnorm_rope_fwd", "rmsnorm_rope_bwd", "layernorm_gelu_fwd", "layernorm_gelu_bwd",
                 "rope_interleaved_apply", "rope_table_1d", "rope_table_3d",
                 "nr_bwd_workspace_bytes", "nr_status_str", "nr_last_hip_error", "nr_tune",
-                "nr_norm_n_max"}
+                "nr_norm_n_max", "nr_stream_copy"}
     assert expected <= set(names), names
     out = subprocess.run(["nm", "-D", "--defined-only", nr.library_path()],
                          capture_output=True, text=True, check=True).stdout
@@ -127,6 +127,13 @@ def test_rejected_calls_return_status(lib):
     assert L.rmsnorm_bwd(F32, FAKE, 0x90000, None, FAKE, 0xA0000, FAKE, 64, 256, 0, 0xB0004, need, None) == NR_ERR_WORKSPACE
     need_ln = nr.nr_bwd_workspace_bytes(64, 256, 1)
     assert L.layernorm_bwd(F32, FAKE, 0x90000, None, FAKE, FAKE, 0xA0000, None, FAKE, 64, 256, 0xB0000, need_ln - 1, None) == NR_ERR_WORKSPACE
+    # the copy probe: null, size / alignment, overlap; zero bytes is a no-op
+    assert L.nr_stream_copy(None, FAKE, 64, None) == NR_ERR_NULLPTR
+    assert L.nr_stream_copy(FAKE, 0x90000, 60, None) == NR_ERR_SHAPE
+    assert L.nr_stream_copy(FAKE + 8, 0x90000, 64, None) == NR_ERR_SHAPE
+    assert L.nr_stream_copy(FAKE, FAKE + 32, 64, None) == NR_ERR_ALIAS
+    assert L.nr_stream_copy(FAKE, FAKE, 64, None) == NR_ERR_ALIAS
+    assert L.nr_stream_copy(None, None, 0, None) == NR_OK
     # a forced launch shape that cannot cover the row
     assert L.nr_tune(b"fwd_k", 1) == NR_OK
     try:
