@@ -42,13 +42,16 @@
 extern "C" {
 #endif
 
-typedef enum { NR_F32 = 0, NR_BF16 = 1 } nr_dtype_t;
+/* Storage type of the row / token tensors and their weights.  Arithmetic is
+ * fp32 whatever the storage type; each stored result is rounded once, to
+ * nearest even. */
+typedef enum { NR_F32 = 0, NR_BF16 = 1, NR_F16 = 2 /* IEEE binary16 */ } nr_dtype_t;
 
 typedef enum {
   NR_OK = 0,
   NR_ERR_NULLPTR = 1,       /* a required pointer is NULL */
   NR_ERR_SHAPE = 2,         /* negative size, n < 1, odd head_dim, bad grid */
-  NR_ERR_DTYPE = 3,         /* dt is not NR_F32 / NR_BF16 */
+  NR_ERR_DTYPE = 3,         /* dt is not NR_F32 / NR_BF16 / NR_F16 */
   NR_ERR_UNSUPPORTED_N = 4, /* n (or a head's size) beyond the on-chip limit */
   NR_ERR_WORKSPACE = 5,     /* workspace missing, too small or not 16-byte aligned */
   NR_ERR_HIP = 6,           /* the HIP runtime refused a launch */
@@ -56,7 +59,7 @@ typedef enum {
   NR_ERR_TUNE = 8           /* unknown tuning key or value */
 } nr_status_t;
 
-/* Largest row length the norm kernels accept: 65536 (bf16), 32768 (fp32). */
+/* Largest row length the norm kernels accept: 65536 (bf16, fp16), 32768 (fp32). */
 int64_t nr_norm_n_max(nr_dtype_t dt); /* host only */
 
 /*

@@ -4,7 +4,8 @@ TEST INFRASTRUCTURE ONLY: imported by ``tests/``, by the package smoke check
 and by the benchmark's CPU-baseline leg, never by the product library.  It
 shares no code with the HIP path.  Every function takes the exact input
 tensors the GPU consumed (fp32 / bf16 / fp64, CPU) and returns float64 numpy
-arrays that are never rounded to the storage dtype.
+arrays that are never rounded to the storage dtype.  Storage types: fp64,
+fp32, bf16 and IEEE fp16, widened exactly.
 
 The arithmetic lives in oracle.c; each function there cites the page section
 it follows.
@@ -22,7 +23,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "oracle.c")
 _LIB = os.path.join(_HERE, "liboracle.so")
 
-_DT = {torch.float64: 0, torch.float32: 1, torch.bfloat16: 2}
+_DT = {torch.float64: 0, torch.float32: 1, torch.bfloat16: 2, torch.float16: 3}
 
 
 def build(force: bool = False) -> str:
@@ -55,6 +56,8 @@ def lib():
         L.oracle_layernorm_gelu_bwd.argtypes = [vp, vp, i32, vp, vp, i32, i64, i64, f64, vp, vp, vp]
         L.oracle_gelu_tanh.argtypes = [f64]
         L.oracle_gelu_tanh_grad.argtypes = [f64]
+        L.oracle_widen.argtypes = [vp, i32, i64, vp]
+        L.oracle_widen.restype = None
         L.oracle_max_threads.argtypes = []
         L.oracle_max_threads.restype = i32
         L.oracle_gelu_tanh.restype = f64
@@ -209,6 +212,14 @@ def rmsnorm_rope_bwd(dout, x, w, angle, head_dim, rows_per_token=1, eps=1e-6, ge
     xd = x.detach().cpu().double() if isinstance(x, torch.Tensor) else torch.from_numpy(x)
     return rmsnorm_bwd(torch.from_numpy(dy.reshape(rows, n)), xd, w, eps, gemma,
                        want_dx=want_dx, want_dw=want_dw)
+
+
+def widen(t) -> np.ndarray:
+    """The oracle's exact widening of stored values to float64."""
+    T = _In(t)
+    out = _out(T.t.numel())
+    lib().oracle_widen(T.p, T.dt, T.t.numel(), _ptr(out))
+    return out.reshape(tuple(T.t.shape))
 
 
 def max_threads() -> int:

@@ -48,6 +48,23 @@
 #define OR_F64 0
 #define OR_F32 1
 #define OR_BF16 2
+#define OR_F16 3
+
+/* IEEE binary16 -> double, exactly: 1 sign bit, 5 exponent bits (bias 15),
+ * 10 fraction bits; exponent 0 is the subnormal range (fraction * 2^-24),
+ * exponent 31 is infinity or NaN. */
+static double half_to_double(uint16_t h)
+{
+    int sign = h >> 15, e = (h >> 10) & 31, f = h & 1023;
+    double v;
+    if (e == 0)
+        v = ldexp((double)f, -24);
+    else if (e == 31)
+        v = f ? NAN : INFINITY;
+    else
+        v = ldexp((double)(1024 + f), e - 25);
+    return sign ? -v : v;
+}
 
 static double ld(const void *p, int dt, int64_t i)
 {
@@ -55,11 +72,20 @@ static double ld(const void *p, int dt, int64_t i)
         return ((const double *)p)[i];
     if (dt == OR_F32)
         return (double)((const float *)p)[i];
+    if (dt == OR_F16)
+        return half_to_double(((const uint16_t *)p)[i]);
     /* bf16: the 16 stored bits are the top half of an IEEE single */
     uint32_t u = (uint32_t)((const uint16_t *)p)[i] << 16;
     float f;
     memcpy(&f, &u, sizeof f);
     return (double)f;
+}
+
+/* The widening above, exposed so that it can be checked on its own. */
+void oracle_widen(const void *p, int dt, int64_t count, double *out)
+{
+    for (int64_t i = 0; i < count; ++i)
+        out[i] = ld(p, dt, i);
 }
 
 /* weight as used by the scaling step: w, or 1 + w for the Gemma variant,

@@ -26,8 +26,8 @@ __all__ = [
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libnormrope.so")
 
-NR_F32, NR_BF16 = 0, 1
-_DT = {torch.float32: NR_F32, torch.bfloat16: NR_BF16}
+NR_F32, NR_BF16, NR_F16 = 0, 1, 2
+_DT = {torch.float32: NR_F32, torch.bfloat16: NR_BF16, torch.float16: NR_F16}
 
 
 class NormRopeError(RuntimeError):
@@ -121,7 +121,7 @@ def _rows_n(x: torch.Tensor):
 
 def _dtype_code(x: torch.Tensor) -> int:
     if x.dtype not in _DT:
-        raise ValueError(f"unsupported dtype {x.dtype} (fp32 or bf16)")
+        raise ValueError(f"unsupported dtype {x.dtype} (fp32, bf16 or fp16)")
     return _DT[x.dtype]
 
 

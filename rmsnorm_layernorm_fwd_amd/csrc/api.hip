@@ -73,7 +73,7 @@ bool bad_overlap(const void* a, size_t na, const void* b, size_t nb) {
 }
 
 nr_status_t check_dtype(nr_dtype_t dt) {
-  return (dt == NR_F32 || dt == NR_BF16) ? NR_OK : NR_ERR_DTYPE;
+  return (dt == NR_F32 || dt == NR_BF16 || dt == NR_F16) ? NR_OK : NR_ERR_DTYPE;
 }
 
 nr_status_t check_norm_shape(nr_dtype_t dt, int64_t rows, int64_t n) {

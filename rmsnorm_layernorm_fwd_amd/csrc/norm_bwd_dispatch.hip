@@ -55,27 +55,33 @@ NR_BWD_EXTERN(float, false, kEpiRope)
 NR_BWD_EXTERN(bf16, false, kEpiRope)
 NR_BWD_EXTERN(float, true, kEpiGelu)
 NR_BWD_EXTERN(bf16, true, kEpiGelu)
+NR_BWD_EXTERN(f16, false, kEpiNone)
+NR_BWD_EXTERN(f16, true, kEpiNone)
+NR_BWD_EXTERN(f16, false, kEpiRope)
+NR_BWD_EXTERN(f16, true, kEpiGelu)
 #undef NR_BWD_EXTERN
 
 hipError_t launch_norm_bwd(bool ln, int dt, const BwdPlan& pl, const void* dy, const void* x,
                            const void* w, const float* mean, const float* rstat, void* dx,
                            float* part, int64_t rows, int n, float w_add, hipStream_t st) {
   const RopeArgs none{nullptr, nullptr, 2, 1};
-  if (dt == kF32)
-    return ln ? launch_bwd_t<float, true, kEpiNone>(pl, dy, x, w, nullptr, mean, rstat, dx, part, rows, n, w_add, none, st)
-              : launch_bwd_t<float, false, kEpiNone>(pl, dy, x, w, nullptr, mean, rstat, dx, part, rows, n, w_add, none, st);
-  return ln ? launch_bwd_t<bf16, true, kEpiNone>(pl, dy, x, w, nullptr, mean, rstat, dx, part, rows, n, w_add, none, st)
-            : launch_bwd_t<bf16, false, kEpiNone>(pl, dy, x, w, nullptr, mean, rstat, dx, part, rows, n, w_add, none, st);
+  return by_dtype(dt, [&](auto tag) {
+    using T = decltype(tag);
+    return ln ? launch_bwd_t<T, true, kEpiNone>(pl, dy, x, w, nullptr, mean, rstat, dx, part, rows, n,
+                                                w_add, none, st)
+              : launch_bwd_t<T, false, kEpiNone>(pl, dy, x, w, nullptr, mean, rstat, dx, part, rows,
+                                                 n, w_add, none, st);
+  });
 }
 
 hipError_t launch_rms_rope_bwd(int dt, const BwdPlan& pl, const void* dout, const void* x,
                                const void* w, const float* inv_rms, const RopeArgs& ra, void* dx,
                                float* part, int64_t rows, int n, float w_add, hipStream_t st) {
-  if (dt == kF32)
-    return launch_bwd_t<float, false, kEpiRope>(pl, dout, x, w, nullptr, nullptr, inv_rms, dx, part,
-                                                rows, n, w_add, ra, st);
-  return launch_bwd_t<bf16, false, kEpiRope>(pl, dout, x, w, nullptr, nullptr, inv_rms, dx, part,
-                                             rows, n, w_add, ra, st);
+  return by_dtype(dt, [&](auto tag) {
+    using T = decltype(tag);
+    return launch_bwd_t<T, false, kEpiRope>(pl, dout, x, w, nullptr, nullptr, inv_rms, dx, part,
+                                            rows, n, w_add, ra, st);
+  });
 }
 
 hipError_t launch_ln_gelu_bwd(int dt, const BwdPlan& pl, const void* dout, const void* x,
@@ -83,11 +89,11 @@ hipError_t launch_ln_gelu_bwd(int dt, const BwdPlan& pl, const void* dout, const
                               const float* rstd, void* dx, float* part, int64_t rows, int n,
                               hipStream_t st) {
   const RopeArgs none{nullptr, nullptr, 2, 1};
-  if (dt == kF32)
-    return launch_bwd_t<float, true, kEpiGelu>(pl, dout, x, gamma, beta, mean, rstd, dx, part, rows,
-                                               n, 0.0f, none, st);
-  return launch_bwd_t<bf16, true, kEpiGelu>(pl, dout, x, gamma, beta, mean, rstd, dx, part, rows, n,
-                                            0.0f, none, st);
+  return by_dtype(dt, [&](auto tag) {
+    using T = decltype(tag);
+    return launch_bwd_t<T, true, kEpiGelu>(pl, dout, x, gamma, beta, mean, rstd, dx, part, rows, n,
+                                           0.0f, none, st);
+  });
 }
 
 hipError_t launch_colreduce(const float* part, int64_t part_stride, int P, int n, float* out0,

@@ -1,0 +1,7 @@
+// norm_bwd_ln_f16.hip -- backward row kernels instantiated for one
+// (type, operator, epilogue) combination; see norm_bwd.hpp.
+#include "norm_bwd.hpp"
+
+namespace nr {
+NR_BWD_INSTANTIATE(f16, true, kEpiNone)
+}  // namespace nr

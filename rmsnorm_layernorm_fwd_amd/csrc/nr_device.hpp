@@ -3,7 +3,7 @@
 // reductions for gfx950 (CDNA4).
 //
 // Data model: a row (norms) or a token (RoPE) is cut into 16-byte chunks,
-// 8 bf16 or 4 fp32 elements each.  Lane t of a row group owns chunks
+// 8 bf16 or fp16, or 4 fp32 elements each.  Lane t of a row group owns chunks
 // t, t + 64W, t + 128W, ... so that every wave-wide load instruction touches
 // 1 KiB of contiguous memory (fully coalesced global_load_dwordx4).  Chunks
 // are kept in VGPRs as raw 32-bit words and widened to fp32 where used; every
@@ -20,14 +20,33 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
 // bfloat16 storage tag: the top 16 bits of an IEEE single.
 struct bf16 {
+  uint16_t bits;
+};
+// IEEE binary16 storage tag.
+struct f16 {
   uint16_t bits;
 };
 
 template <typename T> struct Vec;
 template <> struct Vec<float> { static constexpr int N = 4; };
 template <> struct Vec<bf16> { static constexpr int N = 8; };
+template <> struct Vec<f16> { static constexpr int N = 8; };
+
+// Calls f(T{}) with T the storage type of a dtype code (0 fp32, 1 bf16,
+// 2 fp16): one place maps the C ABI's dtype onto kernel instantiations.
+template <typename F>
+__host__ hipError_t by_dtype(int dt, F&& f) {
+  switch (dt) {
+    case 0: return f(float{});
+    case 1: return f(bf16{});
+    case 2: return f(f16{});
+  }
+  return hipErrorInvalidValue;
+}
 
 // ---- conversions ---------------------------------------------------------
 
@@ -36,6 +55,12 @@ template <> struct Vec<bf16> { static constexpr int N = 8; };
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   f32x2 f = {lo, hi};
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2));
+}
+
+// fp32 pair -> packed binary16 pair, round to nearest even
+__device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
+  f32x2 f = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, f16x2));
 }
 
 // ---- 16-byte chunk <-> fp32 --------------------------------------------
@@ -56,6 +81,19 @@ __device__ __forceinline__ void unpack<bf16>(const u32x4 c, float (&v)[8]) {
   }
 }
 
+template <>
+__device__ __forceinline__ void unpack<f16>(const u32x4 c, float (&v)[8]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    // through a named word: hipcc (ROCm 7.2) lowers a bit_cast of the
+    // subscript c[i] itself as a cast of c[0]
+    const uint32_t word = c[i];
+    const f32x2 f = __builtin_convertvector(__builtin_bit_cast(f16x2, word), f32x2);
+    v[2 * i] = f[0];
+    v[2 * i + 1] = f[1];
+  }
+}
+
 template <typename T>
 __device__ __forceinline__ u32x4 pack(const float (&v)[Vec<T>::N]);
 template <>
@@ -70,6 +108,13 @@ __device__ __forceinline__ u32x4 pack<bf16>(const float (&v)[8]) {
   u32x4 c;
 #pragma unroll
   for (int i = 0; i < 4; ++i) c[i] = pack_bf16x2(v[2 * i], v[2 * i + 1]);
+  return c;
+}
+template <>
+__device__ __forceinline__ u32x4 pack<f16>(const float (&v)[8]) {
+  u32x4 c;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) c[i] = pack_f16x2(v[2 * i], v[2 * i + 1]);
   return c;
 }
 
@@ -157,12 +202,20 @@ template <> __device__ __forceinline__ float ld_elem<float>(rsrc_t r, int byte_o
 template <> __device__ __forceinline__ float ld_elem<bf16>(rsrc_t r, int byte_off) {
   return __uint_as_float(static_cast<uint32_t>(__builtin_amdgcn_raw_buffer_load_b16(r, byte_off, 0, 0)) << 16);
 }
+template <> __device__ __forceinline__ float ld_elem<f16>(rsrc_t r, int byte_off) {
+  const uint16_t h = static_cast<uint16_t>(__builtin_amdgcn_raw_buffer_load_b16(r, byte_off, 0, 0));
+  return static_cast<float>(__builtin_bit_cast(_Float16, h));
+}
 template <typename T> __device__ __forceinline__ void st_elem(rsrc_t r, int byte_off, float v);
 template <> __device__ __forceinline__ void st_elem<float>(rsrc_t r, int byte_off, float v) {
   st_f32(r, byte_off, v);
 }
 template <> __device__ __forceinline__ void st_elem<bf16>(rsrc_t r, int byte_off, float v) {
   __builtin_amdgcn_raw_buffer_store_b16(static_cast<uint16_t>(pack_bf16x2(v, 0.0f) & 0xffffu), r,
+                                        byte_off, 0, 0);
+}
+template <> __device__ __forceinline__ void st_elem<f16>(rsrc_t r, int byte_off, float v) {
+  __builtin_amdgcn_raw_buffer_store_b16(static_cast<uint16_t>(pack_f16x2(v, 0.0f) & 0xffffu), r,
                                         byte_off, 0, 0);
 }
 

@@ -9,6 +9,7 @@ namespace nr {
 
 constexpr int kF32 = 0;   // matches NR_F32
 constexpr int kBF16 = 1;  // matches NR_BF16
+constexpr int kF16 = 2;   // matches NR_F16
 
 // Forward row kernel: W waves per row group, K 16-byte chunks per lane, J
 // rows per row group, R row groups per workgroup.  aligned: 128-bit

@@ -183,9 +183,10 @@ hipError_t launch_rope(int dt, const RopePlan& pl, void* x, const float* cos_tab
                        const float* sin_tab, int64_t batch, int64_t tokens, int heads,
                        int head_dim, int64_t sb, int64_t stok, int64_t sh, float sign,
                        hipStream_t st) {
-  if (dt == kF32)
-    return launch_rope_t<float>(pl, x, cos_tab, sin_tab, batch, tokens, heads, head_dim, sb, stok, sh, sign, st);
-  return launch_rope_t<bf16>(pl, x, cos_tab, sin_tab, batch, tokens, heads, head_dim, sb, stok, sh, sign, st);
+  return by_dtype(dt, [&](auto tag) {
+    return launch_rope_t<decltype(tag)>(pl, x, cos_tab, sin_tab, batch, tokens, heads, head_dim, sb,
+                                        stok, sh, sign, st);
+  });
 }
 
 hipError_t launch_rope_table_1d(float* cos_tab, float* sin_tab, int64_t tokens, int head_dim,

@@ -17,7 +17,7 @@ HEADER = os.path.join(ROOT, "include", "normrope.h")
 
 NR_OK, NR_ERR_NULLPTR, NR_ERR_SHAPE, NR_ERR_DTYPE, NR_ERR_UNSUPPORTED_N = 0, 1, 2, 3, 4
 NR_ERR_WORKSPACE, NR_ERR_HIP, NR_ERR_ALIAS, NR_ERR_TUNE = 5, 6, 7, 8
-F32, BF16 = 0, 1
+F32, BF16, F16 = 0, 1, 2
 FAKE = 0x10000  # never dereferenced: every call below fails validation first
 
 
@@ -60,6 +60,7 @@ def test_norm_n_max():
     import torch
     assert nr.nr_norm_n_max(torch.bfloat16) == 65536
     assert nr.nr_norm_n_max(torch.float32) == 32768
+    assert nr.nr_norm_n_max(torch.float16) == 65536
 
 
 def test_workspace_bytes():
@@ -95,7 +96,8 @@ def test_rejected_calls_return_status(lib):
     L = lib
     # dtype
     assert L.rmsnorm_fwd(7, FAKE, None, FAKE, None, 4, 8, 1e-6, 0, None) == NR_ERR_DTYPE
-    assert L.rope_interleaved_apply(2, FAKE, FAKE, FAKE, 1, 1, 1, 8, 8, 8, 8, 0, None) == NR_ERR_DTYPE
+    assert L.rope_interleaved_apply(3, FAKE, FAKE, FAKE, 1, 1, 1, 8, 8, 8, 8, 0, None) == NR_ERR_DTYPE
+    assert L.layernorm_gelu_fwd(-1, FAKE, None, None, FAKE, None, None, 4, 8, 1e-5, None) == NR_ERR_DTYPE
     # null required pointers
     assert L.rmsnorm_fwd(BF16, None, None, FAKE, None, 4, 8, 1e-6, 0, None) == NR_ERR_NULLPTR
     assert L.rmsnorm_fwd(BF16, FAKE, None, None, None, 4, 8, 1e-6, 0, None) == NR_ERR_NULLPTR
@@ -112,6 +114,7 @@ def test_rejected_calls_return_status(lib):
     assert L.rope_table_1d(FAKE, FAKE, 4, 7, 0, 1e4, None) == NR_ERR_SHAPE
     assert L.rope_table_1d(FAKE, FAKE, 4, 8, 0, -1.0, None) == NR_ERR_SHAPE
     assert L.rope_table_3d(FAKE, FAKE, 2, 3, 4, 0, 2, 2, 1e4, None) == NR_ERR_SHAPE
+    assert L.rmsnorm_fwd(F16, FAKE, None, None, None, 4, 8, 1e-6, 0, None) == NR_ERR_NULLPTR
     # row length beyond the on-chip limit
     assert L.rmsnorm_fwd(BF16, FAKE, None, FAKE, None, 4, 65537, 1e-6, 0, None) == NR_ERR_UNSUPPORTED_N
     assert L.rmsnorm_fwd(F32, FAKE, None, FAKE, None, 4, 32769, 1e-6, 0, None) == NR_ERR_UNSUPPORTED_N

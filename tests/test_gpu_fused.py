@@ -61,6 +61,8 @@ CASES = [
     (50, 3, 6, 1, torch.bfloat16, False, "packed"),       # head_dim 6: element-wise path
     (40, 2, 32, 2, torch.float32, True, "packed"),
     (33, 8, 128, 1, torch.bfloat16, False, "unaligned"),
+    (77, 40, 128, 1, torch.float16, False, "packed"),
+    (48, 2, 64, 2, torch.float16, True, "packed"),
 ]
 
 
@@ -164,6 +166,7 @@ def test_ln_gelu_full_size():
     (257, 64, torch.float32, True, "packed"), (33, 1000, torch.bfloat16, False, "packed"),
     (17, 5128, torch.bfloat16, True, "packed"), (9, 8191, torch.bfloat16, True, "packed"),
     (40, 520, torch.bfloat16, True, "unaligned"), (3, 32768, torch.float32, True, "packed"),
+    (45, 5120, torch.float16, True, "packed"), (6, 1003, torch.float16, True, "packed"),
 ])
 def test_ln_gelu_edges(rows, n, dtype, affine, layout):
     seed = 8000 + rows * 3 + n

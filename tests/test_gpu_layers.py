@@ -16,7 +16,7 @@ import oracle
 import rmsnorm_layernorm_fwd_amd as nr
 import workloads
 from rmsnorm_layernorm_fwd_amd import layers as L
-from tolerance import check, grad_scale, out_kind, to64, ulp_bf16
+from tolerance import check, grad_scale, out_kind, to64, ulp_bf16, ulp_f16
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -28,12 +28,13 @@ def say(msg):
 
 def param_grad_check(name, o, r, dtype):
     """A weight gradient: fp32 from the kernel, then rounded to the
-    parameter's dtype (one more rounding for bf16)."""
-    extra = ulp_bf16(to64(r)) if dtype == torch.bfloat16 else None
+    parameter's dtype (one more rounding for bf16 and fp16)."""
+    extra = {torch.bfloat16: ulp_bf16, torch.float16: ulp_f16}.get(dtype)
+    extra = None if extra is None else extra(to64(r))
     check(name, o, r, "col", extra=extra)
 
 
-@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16, torch.float16])
 @pytest.mark.parametrize("gemma", [False, True])
 def test_rms_module(dtype, gemma):
     say(f"FlashRMSNorm {dtype} gemma={gemma}")
@@ -57,7 +58,7 @@ def test_rms_module(dtype, gemma):
     param_grad_check("dw", m.weight.grad, rdw, dtype)
 
 
-@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16, torch.float16])
 @pytest.mark.parametrize("gelu", [False, True])
 @pytest.mark.parametrize("affine", [True, False])
 def test_layernorm_modules(dtype, gelu, affine):
@@ -95,7 +96,7 @@ def test_layernorm_modules(dtype, gelu, affine):
         param_grad_check("dbeta", m.bias.grad, rdb, dtype)
 
 
-@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16, torch.float16])
 @pytest.mark.parametrize("inplace", [False, True])
 def test_rope_function(dtype, inplace):
     say(f"apply_rotary_emb_interleaved {dtype} inplace={inplace}")
@@ -278,8 +279,8 @@ def test_ten_training_steps_follow_the_oracle():
                 p -= lr * p.grad
             for p in c_params:
                 p -= lr * p.grad
-        g_losses.append(float(lg))
-        c_losses.append(float(lc))
+        g_losses.append(float(lg.detach()))
+        c_losses.append(float(lc.detach()))
     torch.cuda.synchronize()
     say(f"losses gpu {g_losses[0]:.6f}..{g_losses[-1]:.6f} cpu {c_losses[0]:.6f}..{c_losses[-1]:.6f}")
     assert g_losses[-1] < g_losses[0]  # it trains

@@ -249,6 +249,9 @@ NORM_EDGES = [
     (5, 255, torch.bfloat16), (64, 256, torch.bfloat16), (33, 1000, torch.float32),
     (17, 5128, torch.bfloat16), (9, 8191, torch.bfloat16), (4, 12288, torch.float32),
     (3, 32768, torch.float32), (3, 65536, torch.bfloat16), (1000, 40, torch.bfloat16),
+    # IEEE fp16 storage
+    (7, 40, torch.float16), (33, 1000, torch.float16), (65, 5120, torch.float16),
+    (5, 4097, torch.float16), (2, 65536, torch.float16),
 ]
 
 
@@ -363,6 +366,8 @@ ROPE_EDGES = [
     (2, 10, 4, 64, torch.bfloat16, "bhtd"),          # heads-major storage, strided view
     (1, 11, 3, 32, torch.float32, "unaligned"),      # element-wise path
     (1, 13, 2, 10, torch.bfloat16, "padded"),        # head stride > head_dim
+    (1, 33, 40, 128, torch.float16, "packed"),
+    (2, 9, 3, 34, torch.float16, "unaligned"),
 ]
 
 

@@ -258,3 +258,25 @@ def test_inputs_widened_exactly():
     a, _, _ = oracle.layernorm_fwd(xf, eps=1e-5)
     b, _, _ = oracle.layernorm_fwd(xf.double(), eps=1e-5)
     assert np.array_equal(a, b)
+
+
+def test_half_inputs_widened_exactly():
+    # every one of the 65536 binary16 bit patterns widens to the value
+    # torch's own (exact) float16 -> float64 conversion gives: normals,
+    # subnormals, signed zeros, infinities; NaN patterns stay NaN
+    bits = torch.arange(65536, dtype=torch.int32).to(torch.int16)
+    h = bits.view(torch.float16)
+    got = oracle.widen(h)
+    want = h.double().numpy()
+    nan = np.isnan(want)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], want[~nan])
+    assert np.array_equal(np.signbit(got[~nan]), np.signbit(want[~nan]))
+    # and through an operator: fp16 input == its fp64 widening
+    x = _f64((3, 16), 40).to(torch.float16)
+    a, _, _ = oracle.layernorm_fwd(x, eps=1e-5)
+    b, _, _ = oracle.layernorm_fwd(x.double(), eps=1e-5)
+    assert np.array_equal(a, b)
+    # bf16 through the same entry point
+    xb = _f64((2, 8), 41).to(torch.bfloat16)
+    assert np.array_equal(oracle.widen(xb), xb.double().numpy())

@@ -8,6 +8,7 @@ for a column-gradient vector, the RMS of the whole vector).
   fp32 outputs              |O - R| <= 1e-5 (|R| + s)
   column gradients (fp32)   |O - R| <= 1e-4 (|R| + s)
   bf16 outputs              |O - R| <= ulp_bf16(R) + 1e-5 s      ("1 bf16 ulp")
+  fp16 outputs              |O - R| <= ulp_f16(R) + 1e-5 s       ("1 fp16 ulp")
 
   per-row statistics        |O - R| <= 1e-5 (|R| + s), s = 0 except for the
                             LayerNorm mean, whose s is the RMS of the x row
@@ -39,6 +40,14 @@ def ulp_bf16(r: np.ndarray) -> np.ndarray:
     return np.where(a > 0, u, 0.0)
 
 
+def ulp_f16(r: np.ndarray) -> np.ndarray:
+    """Spacing of IEEE binary16 numbers at R: 11 significant bits, so
+    2^(floor(log2 |R|) - 10) for normal values and 2^-24 below 2^-14."""
+    a = np.abs(r)
+    _, e = np.frexp(a)
+    return np.ldexp(1.0, np.maximum(e - 11, -24))
+
+
 def row_rms(r: np.ndarray) -> np.ndarray:
     """RMS over the last axis, broadcastable against r."""
     return np.sqrt(np.mean(r * r, axis=-1, keepdims=True))
@@ -58,10 +67,12 @@ def check(name, o, r, kind, s=None, extra=None):
     o, r = to64(o), to64(r)
     assert o.shape == r.shape, f"{name}: shape {o.shape} vs {r.shape}"
     if s is None:
-        s = row_rms(r) if kind in ("f32", "bf16") else np.sqrt(np.mean(r * r))
+        s = row_rms(r) if kind in ("f32", "bf16", "f16") else np.sqrt(np.mean(r * r))
     err = np.abs(o - r)
     if kind == "bf16":
         tol = ulp_bf16(r) + 1e-5 * s
+    elif kind == "f16":
+        tol = ulp_f16(r) + 1e-5 * s
     elif kind == "col":
         tol = 1e-4 * (np.abs(r) + s)
     else:  # f32, stat
@@ -75,7 +86,7 @@ def check(name, o, r, kind, s=None, extra=None):
 
 
 def out_kind(dtype) -> str:
-    return "bf16" if dtype == torch.bfloat16 else "f32"
+    return {torch.bfloat16: "bf16", torch.float16: "f16"}.get(dtype, "f32")
 
 
 def grad_scale(r, dy, w, gemma=False):
