@@ -83,30 +83,45 @@ nr_status_t check_norm_shape(nr_dtype_t dt, int64_t rows, int64_t n) {
   return NR_OK;
 }
 
-nr_status_t plan_fwd(nr_dtype_t dt, int64_t n, bool aligned, FwdPlan* pl) {
+enum FwdOp { kFwdRms, kFwdLn, kFwdRmsRope };
+
+nr_status_t plan_fwd(nr_dtype_t dt, int64_t n, bool aligned, FwdPlan* pl, FwdOp op) {
   const int64_t nchunk = (n + vec_elems(dt) - 1) / vec_elems(dt);
   const int64_t need = (nchunk + 63) / 64;
-  // Short rows: a wavefront per row, no barrier.  Rows of 6..16 chunk slots
-  // (up to 8192 bf16 / 4096 fp32): two waves per row and about 5 chunks per
-  // lane, which keeps the row resident in fewer VGPRs (LayerNorm holds x,
-  // gamma and beta), and two rows per row group so that each weight chunk
-  // loaded serves both; that measured fastest at 5120 bf16.  Longer rows: up
-  // to 8 chunks per lane and as many waves as needed.
-  int W, K, J = 1;
+  // Short rows: a wavefront per row, no barrier.  Rows of 5..16 chunk slots
+  // (up to 8192 bf16 / 4096 fp32), two rows per row group so that each
+  // weight chunk loaded serves both:
+  //   LayerNorm: two waves per row and about 5 chunks per lane, which keeps
+  //     the row resident in fewer VGPRs (it holds x, gamma and beta);
+  //   RMSNorm (plain or with the RoPE epilogue): 2 chunks per lane and as
+  //     many waves as that needs, i.e. more waves with fewer loads each;
+  //     plain RMSNorm also puts two row groups in a workgroup.
+  // Each measured fastest at 5120 bf16 on MI355X (LayerNorm 5.9 TB/s;
+  // RMSNorm 6.05 -> 6.19, RMSNorm + RoPE 5.85 -> 6.1-6.2 TB/s against the
+  // two-wave shape).  Longer rows: up to 8 chunks per lane and as many waves
+  // as needed.
+  int W, K, J = 1, R;
   if (need <= 4) {
     W = 1;
     K = pick_at_least(need, kFwdK, 7);
+    R = 4;
+  } else if (need <= 16 && op != kFwdLn) {
+    W = static_cast<int>((need + 1) / 2);
+    K = 2;
+    J = 2;
+    R = (op == kFwdRms && W <= 8) ? 2 : 1;
   } else if (need <= 16) {
     W = 2;
     K = pick_at_least((need + 1) / 2, kFwdK, 6);
     if (K <= 5) J = 2;  // one weight load serves two rows
+    R = J == 1 ? 2 : 1;
   } else {
     W = static_cast<int>((need + 7) / 8);
     K = pick_at_least((need + W - 1) / W, kFwdK, 6);  // K <= 8 when W > 1
+    R = 1;
   }
   if (tune(FWD_W) > 0) W = tune(FWD_W);
   if (tune(FWD_K) > 0) K = tune(FWD_K);
-  int R = W == 1 ? 4 : (W == 2 && J == 1 ? 2 : 1);
   if (tune(FWD_R) > 0) R = tune(FWD_R);
   if (tune(FWD_J) > 0) J = tune(FWD_J);
   if (W < 1 || W > 16 || !in_set(K, kFwdK, 7) || (W > 1 && K > 8)) return NR_ERR_SHAPE;
@@ -247,7 +262,7 @@ nr_status_t rmsnorm_fwd(nr_dtype_t dt, const void* x, const void* w, void* y, fl
   const bool aligned = (n % vec_elems(dt)) == 0 && aligned16(x) && aligned16(y) &&
                        (w == nullptr || aligned16(w));
   FwdPlan pl;
-  if ((s = plan_fwd(dt, n, aligned, &pl)) != NR_OK) return s;
+  if ((s = plan_fwd(dt, n, aligned, &pl, kFwdRms)) != NR_OK) return s;
   return hip_status(nr::launch_norm_fwd(false, dt, pl, x, w, nullptr, y, inv_rms, nullptr, rows,
                                         static_cast<int>(n), eps, gemma_offset ? 1.0f : 0.0f,
                                         static_cast<hipStream_t>(stream)));
@@ -267,7 +282,7 @@ nr_status_t layernorm_fwd(nr_dtype_t dt, const void* x, const void* gamma, const
                        (gamma == nullptr || aligned16(gamma)) &&
                        (beta == nullptr || aligned16(beta));
   FwdPlan pl;
-  if ((s = plan_fwd(dt, n, aligned, &pl)) != NR_OK) return s;
+  if ((s = plan_fwd(dt, n, aligned, &pl, kFwdLn)) != NR_OK) return s;
   return hip_status(nr::launch_norm_fwd(true, dt, pl, x, gamma, beta, y, mean, rstd, rows,
                                         static_cast<int>(n), eps, 0.0f,
                                         static_cast<hipStream_t>(stream)));
@@ -351,7 +366,7 @@ nr_status_t layernorm_gelu_fwd(nr_dtype_t dt, const void* x, const void* gamma, 
                        (gamma == nullptr || aligned16(gamma)) &&
                        (beta == nullptr || aligned16(beta));
   FwdPlan pl;
-  if ((s = plan_fwd(dt, n, aligned, &pl)) != NR_OK) return s;
+  if ((s = plan_fwd(dt, n, aligned, &pl, kFwdLn)) != NR_OK) return s;
   return hip_status(nr::launch_ln_gelu_fwd(dt, pl, x, gamma, beta, y, mean, rstd, rows,
                                            static_cast<int>(n), eps,
                                            static_cast<hipStream_t>(stream)));
@@ -400,7 +415,7 @@ nr_status_t rmsnorm_rope_fwd(nr_dtype_t dt, const void* x, const void* w, void* 
   const bool aligned = vec_tab && (n % vec_elems(dt)) == 0 && aligned16(x) && aligned16(y) &&
                        (w == nullptr || aligned16(w));
   FwdPlan pl;
-  if ((s = plan_fwd(dt, n, aligned, &pl)) != NR_OK) return s;
+  if ((s = plan_fwd(dt, n, aligned, &pl, kFwdRmsRope)) != NR_OK) return s;
   const nr::RopeArgs ra{cos_tab, sin_tab, static_cast<int>(head_dim), rows_per_token};
   return hip_status(nr::launch_rms_rope_fwd(dt, pl, x, w, y, inv_rms, ra, rows, static_cast<int>(n),
                                             eps, gemma_offset ? 1.0f : 0.0f,
