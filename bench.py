@@ -302,8 +302,11 @@ def stream_ceiling(dev, reps=10):
 
 def cold_op_times(ops, rounds, dev):
     """Each operation timed alone with the caches cold: before every round a
-    1 GiB scratch buffer is written (untimed), which evicts the 256 MB
-    Infinity Cache and the L2s; then HIP events bracket the one call."""
+    1 GiB scratch buffer is written and then read back (untimed), which
+    evicts the 256 MB Infinity Cache and the L2s and leaves them holding
+    clean, unrelated lines (after the write alone, the timed call would also
+    pay for writing the scratch buffer's dirty lines back); then HIP events
+    bracket the one call."""
     import statistics
 
     import torch
@@ -315,6 +318,7 @@ def cold_op_times(ops, rounds, dev):
         ev = []
         for r in range(rounds):
             flush.fill_(r & 0x7F)
+            flush.sum(dtype=torch.int64)
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record(stream)
             fn()

@@ -1,12 +1,11 @@
 """PyTorch-facing layer over the C ABI: autograd Functions, drop-in modules
 and model patch functions.
 
-The write-up this library follows ("Helios 性能优化全解析", section 内核全景 and
-the closing section on injecting the kernels) ships its kernels as patch
-functions that swap a model's norm modules and its RoPE helper without
-changing the model's interface, and an autograd Function whose backward is
-the forward kernel with sin negated (内核二 FlashRoPE).  This module offers
-the same shape of interface:
+The write-up this library follows ("Helios 性能优化全解析", sections 内核全景
+and 如何启用) ships its kernels as patch functions that swap a model's norm
+modules and its RoPE helper without changing the model's interface, and an
+autograd Function whose backward is the forward kernel with sin negated
+(内核二 FlashRoPE).  This module offers the same shape of interface:
 
 * functional ops with autograd: ``rms_norm``, ``layer_norm``,
   ``layer_norm_gelu``, ``rms_norm_rope``, ``apply_rotary_emb_interleaved``;
