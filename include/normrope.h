@@ -225,9 +225,10 @@ nr_status_t layernorm_gelu_bwd(nr_dtype_t dt, const void* dout, const void* x,
                                size_t workspace_bytes, void* stream);
 
 /* Workspace bytes a backward call needs for dw / dgamma / dbeta at this
- * shape: op = 0 rmsnorm_bwd, 1 layernorm_bwd or layernorm_gelu_bwd (the
- * latter may use less), 2 rmsnorm_rope_bwd (0 for any other op).  Host only;
- * a pure function of its arguments and the current tuning table. */
+ * shape, for any dtype: op = 0 rmsnorm_bwd, 1 layernorm_bwd or
+ * layernorm_gelu_bwd, 2 rmsnorm_rope_bwd (0 for any other op).  An upper
+ * bound: some (dtype, n) use fewer workgroups and so less.  Host only; a
+ * pure function of its arguments and the current tuning table. */
 size_t nr_bwd_workspace_bytes(int64_t rows, int64_t n, int op);
 
 /* Static description of a status code.  Host only. */

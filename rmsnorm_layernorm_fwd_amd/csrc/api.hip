@@ -187,8 +187,10 @@ nr_status_t plan_bwd(nr_dtype_t dt, bool ln, int64_t rows, int64_t n, bool align
     return NR_ERR_SHAPE;
   if (PF < 1 || PF > 2) return NR_ERR_SHAPE;
   if (static_cast<int64_t>(64) * W * K < nchunk) return NR_ERR_SHAPE;
+  // two resident workgroups per CU only when two of them fit: 2 W waves
+  // over the CU's 4 SIMDs at the kernels' ~76-100 VGPRs allow W <= 10
   int64_t P, rpb;
-  bwd_grid(rows, (ln && !gelu) || rope, &P, &rpb);
+  bwd_grid(rows, ((ln && !gelu) || rope) && W <= 10, &P, &rpb);
   *pl = BwdPlan{W, K, D, static_cast<int>(P), PF, rpb, aligned};
   return NR_OK;
 }

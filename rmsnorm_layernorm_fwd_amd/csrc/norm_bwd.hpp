@@ -129,7 +129,7 @@ __device__ __forceinline__ void process_batch(RowBatch<T, K, D, ROPE ? 1 : 0>& b
   // second pass (the activation's derivative is the costliest arithmetic
   // here)
   constexpr int GD = EPI == kEpiGelu ? D * K : 0;
-  float gdd[GD > 0 ? GD : 1][E];
+  float gdd[GD > 0 ? GD : 1][E], gxh[GD > 0 ? GD : 1][E];
 #pragma unroll
   for (int d = 0; d < D; ++d) {
     float s1 = 0.0f, s2 = 0.0f;
@@ -144,7 +144,10 @@ __device__ __forceinline__ void process_batch(RowBatch<T, K, D, ROPE ? 1 : 0>& b
         float dd = dv[e];
         if constexpr (EPI == kEpiGelu) dd *= gelu_tanh_grad(fmaf(xh, wv[k][e], bv[k][e]));
         const float gg = dd * wv[k][e];
-        if constexpr (EPI == kEpiGelu) gdd[d * K + k][e] = gg;
+        if constexpr (EPI == kEpiGelu) {
+          gdd[d * K + k][e] = gg;
+          gxh[d * K + k][e] = xh;
+        }
         if constexpr (LN) {
           s1 += gg;
           s2 = fmaf(gg, xh, s2);
@@ -158,8 +161,10 @@ __device__ __forceinline__ void process_batch(RowBatch<T, K, D, ROPE ? 1 : 0>& b
     s[NS * d] = s1;
     if constexpr (LN) s[NS * d + 1] = s2;
   }
-  reload_barrier<D * K>(b.x);
-  if constexpr (EPI != kEpiGelu) reload_barrier<D * K>(b.g);
+  if constexpr (EPI != kEpiGelu) {
+    reload_barrier<D * K>(b.x);
+    reload_barrier<D * K>(b.g);
+  }
 
   // reduce the batch's NS*D sums across the workgroup
 #pragma unroll
@@ -188,22 +193,28 @@ __device__ __forceinline__ void process_batch(RowBatch<T, K, D, ROPE ? 1 : 0>& b
     const rsrc_t dr = make_rsrc(dx + (okr ? row : 0) * static_cast<int64_t>(n), okr ? rbytes : 0u);
     const float c1 = s[NS * d] * inv_n;
     const float c2 = LN ? s[NS * d + 1] * inv_n : 0.0f;
+    // LayerNorm: dx = r g - (r c1 + r c2 xhat), the bracket one fma per
+    // element with the row constants folded in
+    const float k1 = -b.rs[d] * c1, k2 = -b.rs[d] * c2;
 #pragma unroll
     for (int k = 0; k < K; ++k) {
       float xv[E], dv[E], o[E];
-      unpack<T>(b.x[d * K + k], xv);
-      if constexpr (EPI != kEpiGelu) dy_chunk<T, K, D, ROPE>(b, d * K + k, dv);
+      if constexpr (EPI != kEpiGelu) {
+        unpack<T>(b.x[d * K + k], xv);
+        dy_chunk<T, K, D, ROPE>(b, d * K + k, dv);
+      }
 #pragma unroll
       for (int e = 0; e < E; ++e) {
-        const float xh = (xv[e] - b.mu[d]) * b.rs[d];
-        float gg;
+        float xh, gg;
         if constexpr (EPI == kEpiGelu) {
           gg = gdd[d * K + k][e];
+          xh = gxh[d * K + k][e];
         } else {
           gg = dv[e] * wv[k][e];
+          xh = (xv[e] - b.mu[d]) * b.rs[d];
         }
         if constexpr (LN) {
-          o[e] = b.rs[d] * (gg - c1 - xh * c2);
+          o[e] = fmaf(b.rs[d], gg, fmaf(xh, k2, k1));
         } else {
           o[e] = b.rs[d] * (gg - xh * c1);
         }
