@@ -14,8 +14,8 @@
  *   - Tensors are dense and row-major: a norm input is [rows][n] with row
  *     stride n.  x, y, dy, dx, w, gamma and beta share the dtype `dt`.
  *     Per-row statistics, dw / dgamma / dbeta and RoPE tables are fp32.
- *   - All arithmetic is fp32; each stored bf16 value is rounded once, to
- *     nearest even.
+ *   - All arithmetic is fp32; each stored bf16 or fp16 value is rounded
+ *     once, to nearest even.
  *   - Work is queued on `stream` (a hipStream_t; NULL = default stream) and
  *     the call returns without waiting for it.
  *   - Arguments are checked on the host before anything is queued.  On any
@@ -242,7 +242,8 @@ int nr_last_hip_error(void);
  * stay within the same tolerances, but the backward's summation order, and
  * so its exact bits, depend on the shape).  value 0 restores the automatic
  * choice.  Keys: "fwd_w", "fwd_k", "fwd_r", "fwd_j", "bwd_w", "bwd_k",
- * "bwd_d", "bwd_p", "bwd_rows_min", "bwd_pf", "rope_k", "rope_wpb".  A key whose forced value
+ * "bwd_d", "bwd_p", "bwd_rows_min", "bwd_pf", "rope_k", "rope_wpb",
+ * "rope_groups".  A key whose forced value
  * does not fit a call's shape makes that call return NR_ERR_SHAPE.
  * Returns NR_ERR_TUNE for an unknown key or a negative value.  Host only.
  */

@@ -8,6 +8,7 @@
 // wave's registers (up to 640 16-byte chunks, i.e. 5120 bf16) gets one
 // wavefront and no barrier; longer rows get W waves.  Every check runs before
 // any HIP call, so a rejected call touches neither the device nor the stream.
+#include <algorithm>
 #include <atomic>
 #include <cstdint>
 #include <cstring>
@@ -24,10 +25,10 @@ using nr::RopePlan;
 // ---- tuning overrides ---------------------------------------------------
 
 enum TuneKey { FWD_W, FWD_K, FWD_R, FWD_J, BWD_W, BWD_K, BWD_D, BWD_P, BWD_ROWS_MIN, BWD_PF,
-               ROPE_K, ROPE_WPB, NKEYS };
+               ROPE_K, ROPE_WPB, ROPE_GROUPS, NKEYS };
 const char* const kTuneNames[NKEYS] = {"fwd_w", "fwd_k", "fwd_r", "fwd_j", "bwd_w", "bwd_k",
                                        "bwd_d", "bwd_p", "bwd_rows_min", "bwd_pf", "rope_k",
-                                       "rope_wpb"};
+                                       "rope_wpb", "rope_groups"};
 std::atomic<int> g_tune[NKEYS];
 
 int tune(TuneKey k) { return g_tune[k].load(std::memory_order_relaxed); }
@@ -62,7 +63,7 @@ int pick_at_least(int64_t need, const int* set, int n) {
 const int kFwdK[] = {1, 2, 4, 5, 6, 8, 10};
 const int kBwdK[] = {1, 2, 4, 8};
 const int kBwdD[] = {1, 2, 4, 8};
-const int kRopeK[] = {1, 2, 4, 6, 8, 10};
+const int kRopeK[] = {1, 2, 4, 5, 6, 8, 10};
 
 // Two byte ranges either coincide exactly or are disjoint.
 bool bad_overlap(const void* a, size_t na, const void* b, size_t nb) {
@@ -132,6 +133,13 @@ nr_status_t plan_fwd(nr_dtype_t dt, int64_t n, bool aligned, FwdPlan* pl, FwdOp 
   return NR_OK;
 }
 
+// The forward launches one workgroup per J*R rows: the grid must fit the
+// hardware's 2^31 - 1 workgroups.
+bool fwd_grid_ok(int64_t rows, const FwdPlan& pl) {
+  const int64_t per = static_cast<int64_t>(pl.J) * pl.R;
+  return (rows + per - 1) / per <= INT32_MAX;
+}
+
 // Backward launch shape.
 //   K, W: as few chunks per lane as lets at most 16 waves cover the row
 //     (5120 bf16: K = 1, W = 10).
@@ -142,8 +150,11 @@ nr_status_t plan_fwd(nr_dtype_t dt, int64_t n, bool aligned, FwdPlan* pl, FwdOp 
 //     spends far more ALU time per row (the activation's derivative), so it
 //     loads two batches ahead (PF = 2) to keep HBM busy meanwhile.
 //   P (workgroups): each handles about rows/P rows, dealt out round robin.
-//     At least 16 rows per workgroup keep the fp32 partial rows small next
-//     to the row traffic.  At most 256 (plain RMSNorm, D = 2; LayerNorm +
+//     At least 8 rows per workgroup keep the fp32 partial rows small next
+//     to the row traffic (under 9% extra at 16-bit storage, under 2% once
+//     the cap below applies: 65536 rows).  Short batches want every CU busy
+//     more than they want fewer partial rows: 3840 rows of 5120 bf16 took
+//     25 us on 256 workgroups against 28 us on 240.  At most 256 (plain RMSNorm, D = 2; LayerNorm +
 //     GeLU, whose 104 VGPRs leave room for one 10-wave workgroup per CU) or
 //     512 (LayerNorm and the fused RMSNorm + RoPE, D = 1): on MI355X's 256
 //     CUs that is one or two resident workgroups per CU; more gave a second,
@@ -151,7 +162,7 @@ nr_status_t plan_fwd(nr_dtype_t dt, int64_t n, bool aligned, FwdPlan* pl, FwdOp 
 //   P depends on the row count and the operator only, so the summation order
 //   and the workspace size are the same on every device.
 void bwd_grid(int64_t rows, bool two_per_cu, int64_t* P_out, int64_t* rpb_out) {
-  const int64_t rows_min = tune(BWD_ROWS_MIN) > 0 ? tune(BWD_ROWS_MIN) : 16;
+  const int64_t rows_min = tune(BWD_ROWS_MIN) > 0 ? tune(BWD_ROWS_MIN) : 8;
   const int64_t pcap = tune(BWD_P) > 0 ? tune(BWD_P) : (two_per_cu ? 512 : 256);
   int64_t P = tune(BWD_P) > 0 ? pcap : (rows + rows_min - 1) / rows_min;
   if (P > pcap) P = pcap;
@@ -200,12 +211,20 @@ nr_status_t plan_rope(nr_dtype_t dt, int64_t heads, int64_t head_dim, bool align
   const int E = aligned ? vec_elems(dt) : 2;
   const int64_t cph = head_dim / E;
   const int64_t nchunk = heads * cph;
-  int K = pick_at_least((nchunk + 63) / 64, kRopeK, 6);
+  // A token's chunks are shared by `groups` waves of about 4 chunks per
+  // lane each (a 40 x 128 bf16 token: 640 chunks, 3 waves of 4): against
+  // one wave of 10 chunks per token that measured 6.3 -> 6.45-6.5 TB/s on
+  // 65536 such tokens and 6.0 -> 6.4 TB/s on 15360, i.e. the streaming-copy
+  // ceiling.  Very long tokens keep at most 64 waves and loop.
+  int groups = static_cast<int>(std::min<int64_t>((nchunk + 255) / 256, 64));
+  if (tune(ROPE_GROUPS) > 0) groups = tune(ROPE_GROUPS);
+  int K = pick_at_least((nchunk + 64 * groups - 1) / (64 * groups), kRopeK, 7);
   if (K == 0) K = 10;  // several passes over the heads
   if (tune(ROPE_K) > 0) K = tune(ROPE_K);
   int wpb = tune(ROPE_WPB) > 0 ? tune(ROPE_WPB) : 4;
-  if (!in_set(K, kRopeK, 6) || wpb < 1 || wpb > 4) return NR_ERR_SHAPE;
-  *pl = RopePlan{K, wpb, aligned, (64 % cph) == 0};
+  if (!in_set(K, kRopeK, 7) || wpb < 1 || wpb > 4) return NR_ERR_SHAPE;
+  if (groups < 1 || groups > 64) return NR_ERR_SHAPE;
+  *pl = RopePlan{K, wpb, groups, aligned, (64 % cph) == 0};
   return NR_OK;
 }
 
@@ -265,6 +284,7 @@ nr_status_t rmsnorm_fwd(nr_dtype_t dt, const void* x, const void* w, void* y, fl
                        (w == nullptr || aligned16(w));
   FwdPlan pl;
   if ((s = plan_fwd(dt, n, aligned, &pl, kFwdRms)) != NR_OK) return s;
+  if (!fwd_grid_ok(rows, pl)) return NR_ERR_SHAPE;
   return hip_status(nr::launch_norm_fwd(false, dt, pl, x, w, nullptr, y, inv_rms, nullptr, rows,
                                         static_cast<int>(n), eps, gemma_offset ? 1.0f : 0.0f,
                                         static_cast<hipStream_t>(stream)));
@@ -285,6 +305,7 @@ nr_status_t layernorm_fwd(nr_dtype_t dt, const void* x, const void* gamma, const
                        (beta == nullptr || aligned16(beta));
   FwdPlan pl;
   if ((s = plan_fwd(dt, n, aligned, &pl, kFwdLn)) != NR_OK) return s;
+  if (!fwd_grid_ok(rows, pl)) return NR_ERR_SHAPE;
   return hip_status(nr::launch_norm_fwd(true, dt, pl, x, gamma, beta, y, mean, rstd, rows,
                                         static_cast<int>(n), eps, 0.0f,
                                         static_cast<hipStream_t>(stream)));
@@ -369,6 +390,7 @@ nr_status_t layernorm_gelu_fwd(nr_dtype_t dt, const void* x, const void* gamma, 
                        (beta == nullptr || aligned16(beta));
   FwdPlan pl;
   if ((s = plan_fwd(dt, n, aligned, &pl, kFwdLn)) != NR_OK) return s;
+  if (!fwd_grid_ok(rows, pl)) return NR_ERR_SHAPE;
   return hip_status(nr::launch_ln_gelu_fwd(dt, pl, x, gamma, beta, y, mean, rstd, rows,
                                            static_cast<int>(n), eps,
                                            static_cast<hipStream_t>(stream)));
@@ -418,6 +440,7 @@ nr_status_t rmsnorm_rope_fwd(nr_dtype_t dt, const void* x, const void* w, void* 
                        (w == nullptr || aligned16(w));
   FwdPlan pl;
   if ((s = plan_fwd(dt, n, aligned, &pl, kFwdRmsRope)) != NR_OK) return s;
+  if (!fwd_grid_ok(rows, pl)) return NR_ERR_SHAPE;
   const nr::RopeArgs ra{cos_tab, sin_tab, static_cast<int>(head_dim), rows_per_token};
   return hip_status(nr::launch_rms_rope_fwd(dt, pl, x, w, y, inv_rms, ra, rows, static_cast<int>(n),
                                             eps, gemma_offset ? 1.0f : 0.0f,
@@ -492,6 +515,11 @@ nr_status_t rope_interleaved_apply(nr_dtype_t dt, void* x, const float* cos_tab,
                        aligned16(sin_tab);
   RopePlan pl;
   if ((s = plan_rope(dt, heads, head_dim, aligned, &pl)) != NR_OK) return s;
+  // `groups` waves per token, waves_per_block waves per workgroup: the grid
+  // must fit the hardware's 2^31 - 1 workgroups
+  if (batch * tokens > INT64_MAX / 64 ||
+      (batch * tokens * pl.groups + pl.waves_per_block - 1) / pl.waves_per_block > INT32_MAX)
+    return NR_ERR_SHAPE;
   return hip_status(nr::launch_rope(dt, pl, x, cos_tab, sin_tab, batch, tokens,
                                     static_cast<int>(heads), static_cast<int>(head_dim),
                                     stride_batch, stride_token, stride_head,

@@ -27,11 +27,12 @@ struct BwdPlan {
   bool aligned;
 };
 
-// RoPE: one wave per token, K chunks per lane per pass over the heads,
-// waves_per_block tokens per workgroup.  aligned: 128-bit path; fast: the
-// table slice a lane needs is the same for every chunk it owns.
+// RoPE: `groups` waves per token, each taking K chunks per lane per pass
+// over the heads; waves_per_block waves per workgroup.  aligned: 128-bit
+// path; fast: the table slice a lane needs is the same for every chunk it
+// owns.
 struct RopePlan {
-  int K, waves_per_block;
+  int K, waves_per_block, groups;
   bool aligned, fast;
 };
 

@@ -8,10 +8,11 @@
 // tensor.  The inverse (which is also the backward, a rotation's transpose
 // being its inverse) is the same kernel with sin negated.
 //
-// Mapping: one wavefront per token.  The token's H head vectors of D elements
-// are cut into 16-byte chunks (4 bf16 pairs or 2 fp32 pairs); lane l owns
-// chunks l, l + 64, ... of the token, so each wave-wide load covers 1 KiB of
-// contiguous memory when heads are packed.  When 64 is a multiple of the
+// Mapping: `groups` wavefronts per token (the host picks about 4 chunks per
+// lane per wave).  The token's H head vectors of D elements are cut into
+// 16-byte chunks (4 bf16 pairs or 2 fp32 pairs); lane l of the token's wave
+// g owns chunks 64 K g + l, + 64, ..., so each wave-wide load covers 1 KiB
+// of contiguous memory when heads are packed.  When 64 is a multiple of the
 // chunks per head (D = 128 bf16: 16 chunks), a lane always lands on the same
 // pair slot of every head it visits, so it fetches its cos/sin slice of the
 // token's table row once and reuses it for all heads.  Every element is read
@@ -29,11 +30,15 @@ template <typename T, int K, bool VEC, bool FAST>
 __global__ void __launch_bounds__(256)
 rope_apply_kernel(T* x, const float* cos_tab, const float* sin_tab, int64_t ntok,
                   int64_t tokens, int heads, int head_dim, int64_t sb, int64_t stok,
-                  int64_t sh, uint32_t span_bytes, float sign) {
+                  int64_t sh, uint32_t span_bytes, float sign, int groups) {
   constexpr int E = VEC ? Vec<T>::N : 2;  // elements per chunk
   constexpr int PP = E / 2;               // pairs per chunk
   const int lane = threadIdx.x & 63;
-  const int64_t tok = static_cast<int64_t>(blockIdx.x) * (blockDim.x >> 6) + wave_id();
+  // `groups` waves share a token: wave g of it starts at chunk 64 K g and
+  // steps by 64 K groups
+  const int64_t gw = static_cast<int64_t>(blockIdx.x) * (blockDim.x >> 6) + wave_id();
+  const int64_t tok = gw / groups;
+  const int grp = static_cast<int>(gw - tok * groups);
   if (tok >= ntok) return;  // whole wave; no barrier below
   const int64_t bi = tok / tokens;
   const int64_t s = tok - bi * tokens;
@@ -51,7 +56,7 @@ rope_apply_kernel(T* x, const float* cos_tab, const float* sin_tab, int64_t ntok
     load_tab<PP>(sr, c * PP, sf);
   }
 
-  for (int c0 = 0; c0 < nchunk; c0 += 64 * K) {
+  for (int c0 = 64 * K * grp; c0 < nchunk; c0 += 64 * K * groups) {
     float v[K][E];
     float ck[K][PP], sk[K][PP];
     int off[K];
@@ -145,10 +150,11 @@ hipError_t launch_rope_kaf(const RopePlan& pl, void* x, const float* ct, const f
                            int64_t stok, int64_t sh, float sign, hipStream_t st) {
   const int64_t ntok = batch * tokens;
   const uint32_t span = static_cast<uint32_t>(((heads - 1) * sh + head_dim) * static_cast<int64_t>(sizeof(T)));
-  const dim3 grid(static_cast<unsigned>((ntok + pl.waves_per_block - 1) / pl.waves_per_block));
+  const int64_t waves = ntok * pl.groups;
+  const dim3 grid(static_cast<unsigned>((waves + pl.waves_per_block - 1) / pl.waves_per_block));
   hipLaunchKernelGGL((rope_apply_kernel<T, K, A, F>), grid, dim3(64 * pl.waves_per_block), 0, st,
                      static_cast<T*>(x), ct, stb, ntok, tokens, heads, head_dim, sb, stok, sh,
-                     span, sign);
+                     span, sign, pl.groups);
   return hipGetLastError();
 }
 
@@ -171,7 +177,7 @@ hipError_t launch_rope_t(const RopePlan& pl, void* x, const float* ct, const flo
   switch (pl.K) {
 #define NR_CASE(KK) \
   case KK: return launch_rope_k<T, KK>(pl, x, ct, stb, batch, tokens, heads, head_dim, sb, stok, sh, sign, st);
-    NR_CASE(1) NR_CASE(2) NR_CASE(4) NR_CASE(6) NR_CASE(8) NR_CASE(10)
+    NR_CASE(1) NR_CASE(2) NR_CASE(4) NR_CASE(5) NR_CASE(6) NR_CASE(8) NR_CASE(10)
 #undef NR_CASE
     default: return hipErrorInvalidValue;
   }

@@ -64,16 +64,17 @@ def test_norm_n_max():
 
 
 def test_workspace_bytes():
-    # one fp32 partial row per backward workgroup; workgroups take >= 16 rows,
+    # one fp32 partial row per backward workgroup; workgroups take >= 8 rows,
     # at most 256 (RMSNorm) or 512 (LayerNorm) of them, none empty
-    assert nr.nr_bwd_workspace_bytes(3840, 5120, 0) == 240 * 5120 * 4
-    assert nr.nr_bwd_workspace_bytes(3840, 5120, 1) == 2 * 240 * 5120 * 4
+    assert nr.nr_bwd_workspace_bytes(3840, 5120, 0) == 256 * 5120 * 4
+    assert nr.nr_bwd_workspace_bytes(3840, 5120, 1) == 2 * 480 * 5120 * 4
     assert nr.nr_bwd_workspace_bytes(65536, 5120, 0) == 256 * 5120 * 4
     assert nr.nr_bwd_workspace_bytes(65536, 5120, 1) == 2 * 512 * 5120 * 4
     assert nr.nr_bwd_workspace_bytes(15360, 5120, 1) == 2 * 512 * 5120 * 4
     assert nr.nr_bwd_workspace_bytes(1, 7, 0) == 7 * 4
     assert nr.nr_bwd_workspace_bytes(0, 7, 0) == 0
-    assert nr.nr_bwd_workspace_bytes(17, 8, 0) == 2 * 8 * 4
+    # 17 rows: 3 workgroups of at most 6 rows
+    assert nr.nr_bwd_workspace_bytes(17, 8, 0) == 3 * 8 * 4
     assert nr.nr_bwd_workspace_bytes(65536, 5120, 2) == 512 * 5120 * 4  # fused RMSNorm + RoPE
     assert nr.nr_bwd_workspace_bytes(64, 8, 3) == 0
 
@@ -89,7 +90,7 @@ def test_tune_keys(lib):
         assert nr.nr_bwd_workspace_bytes(3840, 5120, 0) == 120 * 5120 * 4
     finally:
         assert lib.nr_tune(b"bwd_p", 0) == NR_OK
-    assert nr.nr_bwd_workspace_bytes(3840, 5120, 0) == 240 * 5120 * 4
+    assert nr.nr_bwd_workspace_bytes(3840, 5120, 0) == 256 * 5120 * 4
 
 
 def test_rejected_calls_return_status(lib):
@@ -130,6 +131,11 @@ def test_rejected_calls_return_status(lib):
     assert L.rmsnorm_bwd(F32, FAKE, 0x90000, None, FAKE, 0xA0000, FAKE, 64, 256, 0, 0xB0004, need, None) == NR_ERR_WORKSPACE
     need_ln = nr.nr_bwd_workspace_bytes(64, 256, 1)
     assert L.layernorm_bwd(F32, FAKE, 0x90000, None, FAKE, FAKE, 0xA0000, None, FAKE, 64, 256, 0xB0000, need_ln - 1, None) == NR_ERR_WORKSPACE
+    # grids beyond the hardware's 2^31 - 1 workgroups are refused, not truncated
+    FAR = 1 << 40
+    assert L.rmsnorm_fwd(BF16, FAKE, None, FAR, None, 1 << 33, 1, 1e-6, 0, None) == NR_ERR_SHAPE
+    assert L.rope_interleaved_apply(BF16, FAKE, FAR, FAR + (1 << 36), 1, 1 << 33, 1, 2, 2, 2, 2, 0,
+                                    None) == NR_ERR_SHAPE
     # the copy probe: null, size / alignment, overlap; zero bytes is a no-op
     assert L.nr_stream_copy(None, FAKE, 64, None) == NR_ERR_NULLPTR
     assert L.nr_stream_copy(FAKE, 0x90000, 60, None) == NR_ERR_SHAPE
