@@ -84,9 +84,13 @@ nr_status_t rmsnorm_fwd(nr_dtype_t dt, const void* x, const void* w, void* y,
  *   dx_ij = r_i (g_ij - xhat_ij c_i)            -> dx [rows][n] (may be dy)
  *   dw_j  = sum_i dy_ij xhat_ij (fp32)          -> dw [n] or NULL (not formed)
  *   dw is a two-stage fixed-order reduction through `workspace` (device,
- *   16-byte aligned, at least nr_bwd_workspace_bytes(rows, n, 0) bytes;
- *   may be NULL when dw is NULL).  The workspace is scratch: its content on
- *   entry does not matter and is overwritten.
+ *   16-byte aligned, at least nr_bwd_workspace_bytes(rows, n, 0) bytes).
+ *   Rows of more than 16384 elements take two passes over the rows (a row
+ *   reduction first, then dx and the column partials by column slices) and
+ *   keep two fp32 terms per row in the workspace, so for them it is
+ *   required even when dw is NULL; otherwise it may be NULL when dw is.
+ *   The workspace is scratch: its content on entry does not matter and is
+ *   overwritten.
  */
 nr_status_t rmsnorm_bwd(nr_dtype_t dt, const void* dy, const void* x,
                         const void* w, const float* inv_rms, void* dx,
@@ -110,8 +114,8 @@ nr_status_t layernorm_fwd(nr_dtype_t dt, const void* x, const void* gamma,
  *   xhat = (x - mu) r, g = dy gamma, a_i = mean_j g, b_i = mean_j g xhat
  *   dx = r (g - a - xhat b)                      -> dx [rows][n] (may be dy)
  *   dgamma_j = sum_i dy xhat, dbeta_j = sum_i dy -> fp32 [n] each, or NULL
- *   workspace: at least nr_bwd_workspace_bytes(rows, n, 1) bytes when
- *   dgamma or dbeta is wanted (same rules as rmsnorm_bwd).
+ *   workspace: at least nr_bwd_workspace_bytes(rows, n, 1) bytes, under
+ *   the same rules as rmsnorm_bwd.
  */
 nr_status_t layernorm_bwd(nr_dtype_t dt, const void* dy, const void* x,
                           const void* gamma, const float* mean,

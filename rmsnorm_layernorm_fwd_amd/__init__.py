@@ -27,6 +27,9 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libnormrope.so")
 
 NR_F32, NR_BF16, NR_F16 = 0, 1, 2
+# rows longer than this take the two-pass backward, whose workspace is
+# needed even without column gradients (see rmsnorm_bwd in normrope.h)
+_LONG_ROW = 16384
 _DT = {torch.float32: NR_F32, torch.bfloat16: NR_BF16, torch.float16: NR_F16}
 
 
@@ -167,7 +170,7 @@ def rmsnorm_bwd(dy, x, w, inv_rms, gemma_offset=False, dx=None, want_dw=True, dw
         dw = torch.empty(n, dtype=torch.float32, device=x.device)
     _dev("dw", dw, torch.float32, (n,))
     ws, wsb = (None, 0)
-    if dw is not None:
+    if dw is not None or n > _LONG_ROW:
         ws, wsb = _workspace(rows, n, 0, workspace, x.device)
     _check("rmsnorm_bwd", _lib().rmsnorm_bwd(dt, _ptr(dy), _ptr(x), _ptr(w), _ptr(inv_rms),
                                              _ptr(dx), _ptr(dw), rows, n, int(bool(gemma_offset)),
@@ -219,7 +222,7 @@ def layernorm_bwd(dy, x, gamma, mean, rstd, dx=None, want_dgamma=True, want_dbet
     _dev("dgamma", dgamma, torch.float32, (n,))
     _dev("dbeta", dbeta, torch.float32, (n,))
     ws, wsb = (None, 0)
-    if dgamma is not None or dbeta is not None:
+    if dgamma is not None or dbeta is not None or n > _LONG_ROW:
         ws, wsb = _workspace(rows, n, 1, workspace, x.device)
     _check("layernorm_bwd", _lib().layernorm_bwd(dt, _ptr(dy), _ptr(x), _ptr(gamma), _ptr(mean),
                                                  _ptr(rstd), _ptr(dx), _ptr(dgamma), _ptr(dbeta),
@@ -274,7 +277,7 @@ def layernorm_gelu_bwd(dout, x, gamma, beta, mean, rstd, dx=None, want_dgamma=Tr
     _dev("dgamma", dgamma, torch.float32, (n,))
     _dev("dbeta", dbeta, torch.float32, (n,))
     ws, wsb = (None, 0)
-    if dgamma is not None or dbeta is not None:
+    if dgamma is not None or dbeta is not None or n > _LONG_ROW:
         ws, wsb = _workspace(rows, n, 1, workspace, x.device)
     _check("layernorm_gelu_bwd", _lib().layernorm_gelu_bwd(
         dt, _ptr(dout), _ptr(x), _ptr(gamma), _ptr(beta), _ptr(mean), _ptr(rstd), _ptr(dx),
@@ -329,7 +332,7 @@ def rmsnorm_rope_bwd(dout, x, w, inv_rms, cos_tab, sin_tab, head_dim, rows_per_t
         dw = torch.empty(n, dtype=torch.float32, device=x.device)
     _dev("dw", dw, torch.float32, (n,))
     ws, wsb = (None, 0)
-    if dw is not None:
+    if dw is not None or n > _LONG_ROW:
         ws, wsb = _workspace(rows, n, 2, workspace, x.device)
     _check("rmsnorm_rope_bwd", _lib().rmsnorm_rope_bwd(
         dt, _ptr(dout), _ptr(x), _ptr(w), _ptr(inv_rms), _ptr(cos_tab), _ptr(sin_tab), _ptr(dx),

@@ -266,6 +266,11 @@ nr_status_t nr_tune(const char* key, int value) {
 
 size_t nr_bwd_workspace_bytes(int64_t rows, int64_t n, int op) {
   if (rows <= 0 || n < 1 || op < 0 || op > 2) return 0;
+  if (n >= nr::kLongRowMin) {  // two passes: partial rows, then two fp32 terms per row
+    const int64_t P = nr::long_bwd_groups(rows);
+    return static_cast<size_t>(P) * static_cast<size_t>(n) * sizeof(float) * (op == 1 ? 2u : 1u) +
+           static_cast<size_t>(rows) * 2u * sizeof(float);
+  }
   int64_t P, rpb;
   bwd_grid(rows, op != 0, &P, &rpb);
   return static_cast<size_t>(P) * static_cast<size_t>(n) * sizeof(float) * (op == 1 ? 2u : 1u);
@@ -313,6 +318,32 @@ nr_status_t layernorm_fwd(nr_dtype_t dt, const void* x, const void* gamma, const
 
 namespace {
 
+// Backward of rows of kLongRowMin or more elements: pass A stores two fp32
+// terms per row after the partial rows in the workspace, pass B writes dx
+// and the partial rows, stage 2 adds those.
+nr_status_t bwd_long(nr_dtype_t dt, bool ln, int epi, bool aligned, const void* dy, const void* x,
+                     const void* w, const void* beta, const float* mean, const float* rstat,
+                     void* dx, float* o0, float* o1, int64_t rows, int64_t n, float w_add,
+                     const nr::RopeArgs& ra, void* workspace, size_t workspace_bytes,
+                     hipStream_t st) {
+  if (rows > INT32_MAX) return NR_ERR_SHAPE;  // pass A: one workgroup per row
+  const bool want_cols = o0 != nullptr || o1 != nullptr;
+  const int64_t P = nr::long_bwd_groups(rows);
+  const size_t part_bytes =
+      want_cols ? static_cast<size_t>(P) * n * sizeof(float) * (ln ? 2u : 1u) : 0u;
+  const size_t need = part_bytes + static_cast<size_t>(rows) * 2u * sizeof(float);
+  if (workspace == nullptr || workspace_bytes < need || !aligned16(workspace))
+    return NR_ERR_WORKSPACE;
+  float* part = want_cols ? static_cast<float*>(workspace) : nullptr;
+  float* terms = reinterpret_cast<float*>(static_cast<char*>(workspace) + part_bytes);
+  nr_status_t s = hip_status(nr::launch_norm_bwd_long(dt, ln, epi, aligned, dy, x, w, beta, mean,
+                                                      rstat, terms, dx, part, P, rows,
+                                                      static_cast<int>(n), w_add, ra, st));
+  if (s != NR_OK || !want_cols) return s;
+  return hip_status(nr::launch_colreduce(part, P * n, static_cast<int>(P), static_cast<int>(n), o0,
+                                         o1, st));
+}
+
 nr_status_t norm_bwd_common(bool ln, nr_dtype_t dt, const void* dy, const void* x, const void* w,
                             const float* mean, const float* rstat, void* dx, float* o0, float* o1,
                             int64_t rows, int64_t n, float w_add, void* workspace,
@@ -338,6 +369,11 @@ nr_status_t norm_bwd_common(bool ln, nr_dtype_t dt, const void* dy, const void* 
   const bool aligned = (n % vec_elems(dt)) == 0 && aligned16(dy) && aligned16(x) &&
                        aligned16(dx) && (w == nullptr || aligned16(w)) &&
                        (beta == nullptr || aligned16(beta));
+  if (n >= nr::kLongRowMin) {
+    const nr::RopeArgs none{nullptr, nullptr, 2, 1};
+    return bwd_long(dt, ln, gelu ? 2 : 0, aligned, dy, x, w, beta, mean, rstat, dx, o0, o1, rows,
+                    n, w_add, none, workspace, workspace_bytes, st);
+  }
   BwdPlan pl;
   if ((s = plan_bwd(dt, ln, rows, n, aligned, &pl, false, gelu)) != NR_OK) return s;
   float* part = nullptr;
@@ -470,6 +506,10 @@ nr_status_t rmsnorm_rope_bwd(nr_dtype_t dt, const void* dout, const void* x, con
   if (bad_overlap(dx, bytes, dout, bytes) || bad_overlap(dx, bytes, x, bytes)) return NR_ERR_ALIAS;
   const bool aligned = vec_tab && (n % vec_elems(dt)) == 0 && aligned16(dout) && aligned16(x) &&
                        aligned16(dx) && (w == nullptr || aligned16(w));
+  const nr::RopeArgs ra{cos_tab, sin_tab, static_cast<int>(head_dim), rows_per_token};
+  if (n >= nr::kLongRowMin)
+    return bwd_long(dt, false, 1, aligned, dout, x, w, nullptr, nullptr, inv_rms, dx, dw, nullptr,
+                    rows, n, gemma_offset ? 1.0f : 0.0f, ra, workspace, workspace_bytes, st);
   BwdPlan pl;
   if ((s = plan_bwd(dt, false, rows, n, aligned, &pl, true)) != NR_OK) return s;
   float* part = nullptr;
@@ -479,7 +519,6 @@ nr_status_t rmsnorm_rope_bwd(nr_dtype_t dt, const void* dout, const void* x, con
       return NR_ERR_WORKSPACE;
     part = static_cast<float*>(workspace);
   }
-  const nr::RopeArgs ra{cos_tab, sin_tab, static_cast<int>(head_dim), rows_per_token};
   if ((s = hip_status(nr::launch_rms_rope_bwd(dt, pl, dout, x, w, inv_rms, ra, dx, part, rows,
                                               static_cast<int>(n), gemma_offset ? 1.0f : 0.0f,
                                               st))) != NR_OK)

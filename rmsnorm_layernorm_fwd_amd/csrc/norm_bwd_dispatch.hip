@@ -1,6 +1,7 @@
 // norm_bwd_dispatch.hip -- host entry points of the backward (stage 1 by
 // dtype, operator and epilogue) and stage 2, the fixed-order column sum.
 #include "norm_bwd.hpp"
+#include "norm_bwd_long.hpp"
 
 namespace nr {
 
@@ -93,6 +94,44 @@ hipError_t launch_ln_gelu_bwd(int dt, const BwdPlan& pl, const void* dout, const
     using T = decltype(tag);
     return launch_bwd_t<T, true, kEpiGelu>(pl, dout, x, gamma, beta, mean, rstd, dx, part, rows, n,
                                            0.0f, none, st);
+  });
+}
+
+#define NR_BWD_LONG_EXTERN(T, LN, EPI)                                                         \
+  extern template hipError_t launch_bwd_long_t<T, LN, EPI>(                                      \
+      bool, const void*, const void*, const void*, const void*, const float*, const float*,     \
+      float*, void*, float*, int64_t, int64_t, int, float, const RopeArgs&, hipStream_t);
+NR_BWD_LONG_EXTERN(float, false, kEpiNone)
+NR_BWD_LONG_EXTERN(bf16, false, kEpiNone)
+NR_BWD_LONG_EXTERN(f16, false, kEpiNone)
+NR_BWD_LONG_EXTERN(float, true, kEpiNone)
+NR_BWD_LONG_EXTERN(bf16, true, kEpiNone)
+NR_BWD_LONG_EXTERN(f16, true, kEpiNone)
+NR_BWD_LONG_EXTERN(float, false, kEpiRope)
+NR_BWD_LONG_EXTERN(bf16, false, kEpiRope)
+NR_BWD_LONG_EXTERN(f16, false, kEpiRope)
+NR_BWD_LONG_EXTERN(float, true, kEpiGelu)
+NR_BWD_LONG_EXTERN(bf16, true, kEpiGelu)
+NR_BWD_LONG_EXTERN(f16, true, kEpiGelu)
+#undef NR_BWD_LONG_EXTERN
+
+hipError_t launch_norm_bwd_long(int dt, bool ln, int epi, bool aligned, const void* dy,
+                                const void* x, const void* w, const void* beta, const float* mean,
+                                const float* rstat, float* terms, void* dx, float* part,
+                                int64_t P, int64_t rows, int n, float w_add, const RopeArgs& ra,
+                                hipStream_t st) {
+  return by_dtype(dt, [&](auto tag) {
+    using T = decltype(tag);
+    if (epi == kEpiRope)
+      return launch_bwd_long_t<T, false, kEpiRope>(aligned, dy, x, w, nullptr, nullptr, rstat,
+                                                   terms, dx, part, P, rows, n, w_add, ra, st);
+    if (epi == kEpiGelu)
+      return launch_bwd_long_t<T, true, kEpiGelu>(aligned, dy, x, w, beta, mean, rstat, terms, dx,
+                                                  part, P, rows, n, 0.0f, ra, st);
+    return ln ? launch_bwd_long_t<T, true, kEpiNone>(aligned, dy, x, w, nullptr, mean, rstat, terms,
+                                                     dx, part, P, rows, n, w_add, ra, st)
+              : launch_bwd_long_t<T, false, kEpiNone>(aligned, dy, x, w, nullptr, nullptr, rstat,
+                                                      terms, dx, part, P, rows, n, w_add, ra, st);
   });
 }
 

@@ -1,7 +1,10 @@
 // norm_bwd_rms_bf16.hip -- backward row kernels instantiated for one
-// (type, operator, epilogue) combination; see norm_bwd.hpp.
+// (type, operator, epilogue) combination; see norm_bwd.hpp and
+// norm_bwd_long.hpp.
 #include "norm_bwd.hpp"
+#include "norm_bwd_long.hpp"
 
 namespace nr {
 NR_BWD_INSTANTIATE(bf16, false, kEpiNone)
+NR_BWD_LONG_INSTANTIATE(bf16, false, kEpiNone)
 }  // namespace nr

@@ -46,6 +46,24 @@ struct RopeArgs {
   int64_t rows_per_token;
 };
 
+// Rows of at least kLongRowMin elements take the two-pass backward
+// (norm_bwd_long.hpp).  Its pass B uses long_bwd_groups(rows) row groups:
+// a function of the row count only, so the summation order and the
+// workspace size do not depend on the device.
+constexpr int64_t kLongRowMin = 16385;
+inline int64_t long_bwd_groups(int64_t rows) {
+  int64_t p = (rows + 15) / 16;
+  if (p > 128) p = 128;
+  return p < 1 ? 1 : p;
+}
+
+// epi: 0 none, 1 RoPE (RMSNorm only), 2 GeLU (LayerNorm only).  terms:
+// fp32 [rows][2] scratch; part: fp32 [2][P][n] partial rows or null.
+hipError_t launch_norm_bwd_long(int dt, bool ln, int epi, bool aligned, const void* dy,
+                                const void* x, const void* w, const void* beta, const float* mean,
+                                const float* rstat, float* terms, void* dx, float* part,
+                                int64_t P, int64_t rows, int n, float w_add, const RopeArgs& ra,
+                                hipStream_t st);
 hipError_t launch_rms_rope_fwd(int dt, const FwdPlan& pl, const void* x, const void* w, void* y,
                                float* inv_rms, const RopeArgs& ra, int64_t rows, int n, float eps,
                                float w_add, hipStream_t st);

@@ -77,6 +77,11 @@ def test_workspace_bytes():
     assert nr.nr_bwd_workspace_bytes(17, 8, 0) == 3 * 8 * 4
     assert nr.nr_bwd_workspace_bytes(65536, 5120, 2) == 512 * 5120 * 4  # fused RMSNorm + RoPE
     assert nr.nr_bwd_workspace_bytes(64, 8, 3) == 0
+    # rows of more than 16384 elements: ceil(rows / 16) (at most 128) partial
+    # rows, then two fp32 terms per row
+    assert nr.nr_bwd_workspace_bytes(100, 20000, 1) == 7 * 20000 * 4 * 2 + 100 * 8
+    assert nr.nr_bwd_workspace_bytes(100, 20000, 0) == 7 * 20000 * 4 + 100 * 8
+    assert nr.nr_bwd_workspace_bytes(4096, 32768, 2) == 128 * 32768 * 4 + 4096 * 8
 
 
 def test_tune_keys(lib):
@@ -143,6 +148,10 @@ def test_rejected_calls_return_status(lib):
     assert L.nr_stream_copy(FAKE, FAKE + 32, 64, None) == NR_ERR_ALIAS
     assert L.nr_stream_copy(FAKE, FAKE, 64, None) == NR_ERR_ALIAS
     assert L.nr_stream_copy(None, None, 0, None) == NR_OK
+    # long rows need the workspace even without a column gradient
+    X2, DX2, WS2 = 1 << 24, 1 << 25, 1 << 26
+    assert L.rmsnorm_bwd(BF16, FAKE, X2, None, FAKE, DX2, None, 4, 20000, 0, None, 0, None) == NR_ERR_WORKSPACE
+    assert L.layernorm_bwd(F32, FAKE, X2, None, FAKE, FAKE, DX2, None, None, 4, 20000, WS2, 31, None) == NR_ERR_WORKSPACE
     # a forced launch shape that cannot cover the row
     assert L.nr_tune(b"fwd_k", 1) == NR_OK
     try:

@@ -63,6 +63,8 @@ CASES = [
     (33, 8, 128, 1, torch.bfloat16, False, "unaligned"),
     (77, 40, 128, 1, torch.float16, False, "packed"),
     (48, 2, 64, 2, torch.float16, True, "packed"),
+    (21, 160, 128, 1, torch.bfloat16, False, "packed"),   # 20480 wide: two-pass backward
+    (9, 170, 102, 1, torch.float32, True, "packed"),      # 17340 wide, element-wise tables
 ]
 
 
@@ -167,6 +169,7 @@ def test_ln_gelu_full_size():
     (17, 5128, torch.bfloat16, True, "packed"), (9, 8191, torch.bfloat16, True, "packed"),
     (40, 520, torch.bfloat16, True, "unaligned"), (3, 32768, torch.float32, True, "packed"),
     (45, 5120, torch.float16, True, "packed"), (6, 1003, torch.float16, True, "packed"),
+    (7, 20480, torch.bfloat16, True, "packed"), (5, 17003, torch.bfloat16, True, "unaligned"),
 ])
 def test_ln_gelu_edges(rows, n, dtype, affine, layout):
     seed = 8000 + rows * 3 + n

@@ -252,6 +252,8 @@ NORM_EDGES = [
     # IEEE fp16 storage
     (7, 40, torch.float16), (33, 1000, torch.float16), (65, 5120, torch.float16),
     (5, 4097, torch.float16), (2, 65536, torch.float16),
+    # rows past 16384 elements: the two-pass backward (aligned and element-wise)
+    (37, 20480, torch.bfloat16), (5, 17001, torch.float16), (9, 24576, torch.float32),
 ]
 
 
@@ -353,6 +355,46 @@ def test_backward_bitwise_deterministic(kind):
     torch.cuda.synchronize()
     for a, b in zip(outs[0], outs[1]):
         assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("kind", ["rms", "ln"])
+def test_long_row_backward_deterministic_and_without_column_gradients(kind):
+    rows, n = 300, 20480  # two-pass backward; 19 row groups
+    x = workloads.normal((rows, n), 6100, torch.bfloat16)
+    w = workloads.normal((n,), 6101, torch.bfloat16, mean=1.0, std=0.1)
+    dy = workloads.normal((rows, n), 6102, torch.bfloat16)
+    say(f"{kind} long-row bwd determinism {rows}x{n}")
+    xg, wg, dyg = g(x), g(w), g(dy)
+    outs = []
+    for _ in range(2):
+        if kind == "rms":
+            _, r = nr.rmsnorm_fwd(xg, wg)
+            outs.append(nr.rmsnorm_bwd(dyg, xg, wg, r))
+        else:
+            _, mu, rs = nr.layernorm_fwd(xg, wg, wg)
+            outs.append(nr.layernorm_bwd(dyg, xg, wg, mu, rs))
+    # dx alone (the workspace still carries the row terms)
+    if kind == "rms":
+        dx_only, none = nr.rmsnorm_bwd(dyg, xg, wg, r, want_dw=False)
+        assert none is None
+    else:
+        dx_only, n1, n2 = nr.layernorm_bwd(dyg, xg, wg, mu, rs, want_dgamma=False, want_dbeta=False)
+        assert n1 is None and n2 is None
+    torch.cuda.synchronize()
+    for a, b in zip(outs[0], outs[1]):
+        assert torch.equal(a, b)
+    assert torch.equal(dx_only, outs[0][0])
+    if kind == "rms":
+        rdx, rdw = oracle.rmsnorm_bwd(dy, x, w, 1e-6)
+        _, rr = oracle.rmsnorm_fwd(x, w, 1e-6)
+        check("long rms dx", outs[0][0], rdx, "bf16", s=grad_scale(rr, dy, w))
+        check("long rms dw", outs[0][1], rdw, "col")
+    else:
+        rdx, rdg, rdb = oracle.layernorm_bwd(dy, x, w, 1e-5)
+        _, _, rrs = oracle.layernorm_fwd(x, w, w, 1e-5)
+        check("long ln dx", outs[0][0], rdx, "bf16", s=grad_scale(rrs, dy, w))
+        check("long ln dgamma", outs[0][1], rdg, "col")
+        check("long ln dbeta", outs[0][2], rdb, "col")
 
 
 ROPE_EDGES = [
