@@ -362,8 +362,9 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
-              "(the path shards by tokens; see the sharding note in the design document)",
+        print(f"bench.py: one GPU only; --gpus {args.gpus} is not supported (the operators "
+              "shard by tokens, with one all-reduce of the column gradients per backward, "
+              "which multi-GPU training code does in its own gradient buckets)",
               file=sys.stderr)
         sys.exit(2)
 

@@ -15,7 +15,7 @@
  * consistency test so that the speed-up does not change results).  So the
  * reference is the definition, not the fused algorithm.
  *
- * Readings where the pages are silent (each also listed in the design doc):
+ * Readings taken where the pages are silent:
  *   - eps sits inside the square root, 1/sqrt(ms + eps) and 1/sqrt(var + eps)
  *     (LLM层的优化算子, 编写定制融合算子: the LayerNorm example divides by
  *     sqrt(var + eps));
@@ -29,9 +29,11 @@
  *   - RoPE angles: 1-D, pos * theta^(-2i/D); 3-D, the D/2 pairs are split
  *     into consecutive t / h / w blocks of P_t, P_h, P_w pairs, and pair j of
  *     axis a's block uses pos_a * theta^(-2j/(2 P_a)); tokens are ordered
- *     frame-major, then height, then width.
+ *     frame-major, then height, then width;
+ *   - the tanh-approximated GeLU uses c = sqrt(2/pi), printed as 0.79788456
+ *     in 编写定制融合算子 (the two differ by 1e-9 relative).
  *
- * Inputs are read through a dtype tag (fp64, fp32 or bf16 bit patterns) and
+ * Inputs are read through a dtype tag (fp64, fp32, bf16 or fp16 bit patterns) and
  * widened exactly to double, so the oracle sees the very bytes the GPU saw.
  * Outputs are always double and are never rounded to the storage dtype.
  *
