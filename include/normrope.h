@@ -228,6 +228,27 @@ nr_status_t layernorm_gelu_bwd(nr_dtype_t dt, const void* dout, const void* x,
                                int64_t n, void* workspace,
                                size_t workspace_bytes, void* stream);
 
+/*
+ * rmsnorm_linear_fwd -- RMSNorm folded into the linear layer that consumes
+ * it (the write-up's fusion of element-wise work into its neighbours, Helios
+ * 性能优化全解析, 内核一 FlashNorm: the normalised row never makes a round trip
+ * through memory):
+ *   r_m = 1/sqrt(mean_k x[m][k]^2 + eps)            -> inv_rms [M] (or NULL)
+ *   out[m][n] = r_m sum_k x[m][k] w'_k W[n][k]      -> out [M][N]
+ * i.e. out = rmsnorm_fwd(x, w_norm) W^T with W [N][K] row-major (the layout
+ * of a linear layer's weight), w'_k = w_k, 1 + w_k (gemma_offset) or 1
+ * (w_norm NULL).  bf16 only (NR_BF16): x enters the bf16 matrix cores
+ * exactly, w'_k W[n][k] is rounded once to bf16, accumulation is fp32 and
+ * out is rounded once.  Forward only.
+ * Shapes: K a multiple of 64 (at most 65536), N a multiple of 128, any M;
+ * x, W, out and w_norm 16-byte aligned (else NR_ERR_SHAPE); out may not
+ * overlap x or W.
+ */
+nr_status_t rmsnorm_linear_fwd(nr_dtype_t dt, const void* x, const void* w_norm,
+                               const void* W, void* out, float* inv_rms,
+                               int64_t M, int64_t N, int64_t K, float eps,
+                               int gemma_offset, void* stream);
+
 /* Workspace bytes a backward call needs for dw / dgamma / dbeta at this
  * shape, for any dtype: op = 0 rmsnorm_bwd, 1 layernorm_bwd or
  * layernorm_gelu_bwd, 2 rmsnorm_rope_bwd (0 for any other op).  An upper

@@ -259,3 +259,13 @@ def layernorm_gelu_bwd(dout, x, gamma=None, beta=None, eps=1e-5, want_dx=True, w
     lib().oracle_layernorm_gelu_bwd(DY.p, X.p, X.dt, G.p, B.p, G.dt if G.t is not None else B.dt,
                                     m, n, float(eps), _ptr(dx), _ptr(dg), _ptr(db))
     return dx, dg, db
+
+
+def rmsnorm_linear(x, w, W, eps=1e-6, gemma=False):
+    """D1 followed by the linear layer y @ W^T, in float64 with no rounding in
+    between; W is [N, K].  Returns (out [rows, N], inv_rms [rows], S) where
+    S = |y| @ |W|^T bounds each output's rounding sensitivity (the sum of
+    the magnitudes of its K products)."""
+    y, r = rmsnorm_fwd(x, w, eps, gemma)
+    Wd = W.detach().cpu().double().numpy() if isinstance(W, torch.Tensor) else np.asarray(W, np.float64)
+    return y @ Wd.T, r, np.abs(y) @ np.abs(Wd).T

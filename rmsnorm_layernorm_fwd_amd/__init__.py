@@ -20,7 +20,8 @@ __all__ = [
     "NormRopeError", "rmsnorm_fwd", "rmsnorm_bwd", "layernorm_fwd", "layernorm_bwd",
     "rmsnorm_rope_fwd", "rmsnorm_rope_bwd", "layernorm_gelu_fwd", "layernorm_gelu_bwd",
     "rope_interleaved_apply", "rope_table_1d", "rope_table_3d", "nr_bwd_workspace_bytes",
-    "nr_status_str", "nr_tune", "nr_norm_n_max", "nr_stream_copy", "library_path",
+    "nr_status_str", "nr_tune", "nr_norm_n_max", "nr_stream_copy", "rmsnorm_linear_fwd",
+    "library_path",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -79,6 +80,7 @@ def _lib():
             "nr_tune": [ctypes.c_char_p, i32],
             "nr_norm_n_max": [i32],
             "nr_stream_copy": [vp, vp, sz, vp],
+            "rmsnorm_linear_fwd": [i32, vp, vp, vp, vp, vp, i64, i64, i64, f32, i32, vp],
         }
         for name, args in sig.items():
             fn = getattr(L, name)
@@ -377,6 +379,31 @@ def rope_table_3d(grid, pairs, theta=10000.0, device="cuda"):
     _check("rope_table_3d", _lib().rope_table_3d(_ptr(c), _ptr(s), f, h, w, pt, ph, pw,
                                                  float(theta), _stream(c)))
     return c, s
+
+
+# ---------------------------------------------------------------- RMSNorm -> linear
+
+def rmsnorm_linear_fwd(x, w_norm, W, eps=1e-6, gemma_offset=False, out=None, inv_rms=None,
+                       want_stats=True):
+    """out = rmsnorm(x, w_norm) @ W.T with the norm folded into the GEMM
+    (bf16; W [N, K] as a linear layer stores it); returns (out, inv_rms)."""
+    _dev("x", x, torch.bfloat16)
+    rows, k = _rows_n(x)
+    _dev("W", W, torch.bfloat16)
+    if W.dim() != 2 or W.shape[1] != k:
+        raise ValueError(f"W must be [N, {k}]")
+    n = W.shape[0]
+    _dev("w_norm", w_norm, torch.bfloat16, (k,))
+    if out is None:
+        out = torch.empty(x.shape[:-1] + (n,), dtype=torch.bfloat16, device=x.device)
+    _dev("out", out, torch.bfloat16, x.shape[:-1] + (n,))
+    if inv_rms is None and want_stats:
+        inv_rms = torch.empty(x.shape[:-1], dtype=torch.float32, device=x.device)
+    _dev("inv_rms", inv_rms, torch.float32)
+    _check("rmsnorm_linear_fwd", _lib().rmsnorm_linear_fwd(
+        NR_BF16, _ptr(x), _ptr(w_norm), _ptr(W), _ptr(out), _ptr(inv_rms), rows, n, k, float(eps),
+        int(bool(gemma_offset)), _stream(x)))
+    return out, inv_rms
 
 
 # ---------------------------------------------------------------- helpers

@@ -594,6 +594,30 @@ nr_status_t rope_table_3d(float* cos_tab, float* sin_tab, int64_t frames, int64_
       static_cast<hipStream_t>(stream)));
 }
 
+nr_status_t rmsnorm_linear_fwd(nr_dtype_t dt, const void* x, const void* w_norm, const void* W,
+                               void* out, float* inv_rms, int64_t M, int64_t N, int64_t K,
+                               float eps, int gemma_offset, void* stream) {
+  if (dt != NR_BF16) return NR_ERR_DTYPE;  // the bf16 matrix cores only
+  if (M < 0 || M > INT32_MAX || N < 128 || N % 128 != 0 || K < 64 || K % 64 != 0)
+    return NR_ERR_SHAPE;
+  if (K > 65536 || N > (int64_t{1} << 22)) return NR_ERR_UNSUPPORTED_N;
+  if (M == 0) return NR_OK;
+  if (x == nullptr || W == nullptr || out == nullptr) return NR_ERR_NULLPTR;
+  if (!aligned16(x) || !aligned16(W) || !aligned16(out) || (w_norm != nullptr && !aligned16(w_norm)))
+    return NR_ERR_SHAPE;
+  if (M > INT64_MAX / K / 2 || M > INT64_MAX / N / 2) return NR_ERR_SHAPE;
+  const int64_t tiles = ((M + 127) / 128) * (N / 128);
+  if (tiles > INT32_MAX) return NR_ERR_SHAPE;
+  const size_t xb = static_cast<size_t>(M * K) * 2, wb = static_cast<size_t>(N * K) * 2,
+               ob = static_cast<size_t>(M * N) * 2;
+  if (bad_overlap(out, ob, x, xb) || out == x || bad_overlap(out, ob, W, wb) || out == W)
+    return NR_ERR_ALIAS;
+  return hip_status(nr::launch_rmsnorm_linear(x, w_norm, W, out, inv_rms, static_cast<int>(M),
+                                              static_cast<int>(N), static_cast<int>(K), eps,
+                                              gemma_offset ? 1.0f : 0.0f,
+                                              static_cast<hipStream_t>(stream)));
+}
+
 nr_status_t nr_stream_copy(const void* src, void* dst, size_t bytes, void* stream) {
   if (bytes == 0) return NR_OK;
   if (src == nullptr || dst == nullptr) return NR_ERR_NULLPTR;

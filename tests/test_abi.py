@@ -38,7 +38,7 @@ def test_header_functions_exported(lib):
                 "rmsnorm_rope_fwd", "rmsnorm_rope_bwd", "layernorm_gelu_fwd", "layernorm_gelu_bwd",
                 "rope_interleaved_apply", "rope_table_1d", "rope_table_3d",
                 "nr_bwd_workspace_bytes", "nr_status_str", "nr_last_hip_error", "nr_tune",
-                "nr_norm_n_max", "nr_stream_copy"}
+                "nr_norm_n_max", "nr_stream_copy", "rmsnorm_linear_fwd"}
     assert expected <= set(names), names
     out = subprocess.run(["nm", "-D", "--defined-only", nr.library_path()],
                          capture_output=True, text=True, check=True).stdout
@@ -141,6 +141,17 @@ def test_rejected_calls_return_status(lib):
     assert L.rmsnorm_fwd(BF16, FAKE, None, FAR, None, 1 << 33, 1, 1e-6, 0, None) == NR_ERR_SHAPE
     assert L.rope_interleaved_apply(BF16, FAKE, FAR, FAR + (1 << 36), 1, 1 << 33, 1, 2, 2, 2, 2, 0,
                                     None) == NR_ERR_SHAPE
+    # RMSNorm -> linear: bf16 only, K % 64, N % 128, pointers, alignment, overlap
+    XA, WA, OA = 1 << 24, 1 << 28, 1 << 32
+    lin = L.rmsnorm_linear_fwd
+    assert lin(F32, XA, None, WA, OA, None, 4, 128, 64, 1e-6, 0, None) == NR_ERR_DTYPE
+    assert lin(BF16, XA, None, WA, OA, None, 4, 100, 64, 1e-6, 0, None) == NR_ERR_SHAPE
+    assert lin(BF16, XA, None, WA, OA, None, 4, 128, 72, 1e-6, 0, None) == NR_ERR_SHAPE
+    assert lin(BF16, XA, None, WA, OA, None, 4, 128, 65600, 1e-6, 0, None) == NR_ERR_UNSUPPORTED_N
+    assert lin(BF16, None, None, WA, OA, None, 4, 128, 64, 1e-6, 0, None) == NR_ERR_NULLPTR
+    assert lin(BF16, XA + 2, None, WA, OA, None, 4, 128, 64, 1e-6, 0, None) == NR_ERR_SHAPE
+    assert lin(BF16, XA, None, WA, XA + 64, None, 4, 128, 64, 1e-6, 0, None) == NR_ERR_ALIAS
+    assert lin(BF16, None, None, None, None, None, 0, 128, 64, 1e-6, 0, None) == NR_OK
     # the copy probe: null, size / alignment, overlap; zero bytes is a no-op
     assert L.nr_stream_copy(None, FAKE, 64, None) == NR_ERR_NULLPTR
     assert L.nr_stream_copy(FAKE, 0x90000, 60, None) == NR_ERR_SHAPE
