@@ -39,6 +39,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "achieved HBM GB/s (and % of peak) for fused norm fwd+bwd and RoPE"
 PEAK_GBS = 8000.0  # MI355X HBM3E
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 matrix-core peak
 PROFILES = os.path.join(ROOT, "profiles")
 CSRC = os.path.join(ROOT, "rmsnorm_layernorm_fwd_amd", "csrc")
 
@@ -205,9 +206,48 @@ def build_ops(name, dev):
         ]
         desc = dict(workload=name, tokens=t, heads=h, head_dim=d, io_dtype="bf16",
                     positions="3-D 16x24x40, pairs 22/21/21, theta 1e4")
+    elif name == "rms_linear_65536x5120x5120":
+        # RMSNorm folded into the following linear layer (a 5120 -> 5120
+        # projection of the long-sequence activation): matrix-core bound
+        inp = workloads.norm_inputs("longseq_65536x5120")
+        m, k = inp["x"].shape
+        n = 5120
+        x, w = g(inp["x"]), g(inp["w"])
+        W = workloads.normal((n, k), 4242, torch.bfloat16, std=k ** -0.5).to(dev)
+        out = torch.empty(m, n, dtype=torch.bfloat16, device=dev)
+        r = torch.empty(m, dtype=torch.float32, device=dev)
+        ops = [
+            ("rmsnorm_linear_fwd", "rmsnorm_linear_kernel",
+             lambda: nr.rmsnorm_linear_fwd(x, w, W, 1e-6, out=out, inv_rms=r),
+             2 * m * k + 2 * n * k + 2 * k + 2 * m * n + 4 * m),
+        ]
+        y = torch.empty_like(x)
+        desc = dict(workload=name, rows=m, hidden=k, out_features=n, io_dtype="bf16",
+                    flops_per_step=2 * m * n * k, weight="W ~ N(0, 1/K), seed 4242",
+                    unfused=dict(fns=[lambda: nr.rmsnorm_fwd(x, w, 1e-6, y=y, inv_rms=r),
+                                      lambda: torch.matmul(y, W.t(), out=out)],
+                                 what="rmsnorm_fwd, then torch.matmul (the vendor GEMM) on y"))
     else:
         raise SystemExit(f"unknown workload {name}")
     return ops, desc
+
+
+def time_fns(fns, reps=10):
+    """Mean milliseconds of one pass over fns (events on the launch stream)."""
+    import torch
+
+    for _ in range(3):
+        for f in fns:
+            f()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        for f in fns:
+            f()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps
 
 
 # ---------------------------------------------------------------- traffic
@@ -353,7 +393,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="longseq_65536x5120",
                     choices=["longseq_65536x5120", "longseq_fused_65536x5120", "rms_gemma_3840x5120",
-                             "ln_affine_15360x5120", "ln_gelu_15360x5120", "rope3d_15360x40x128"])
+                             "ln_affine_15360x5120", "ln_gelu_15360x5120", "rope3d_15360x40x128",
+                             "rms_linear_65536x5120x5120"])
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", action="store_true")
@@ -443,11 +484,23 @@ def main():
                     frac=round(achieved / PEAK_GBS, 4), traffic=read_traffic(dname, args.workload),
                     kernel=dname, ops=dk["ops"], bytes_per_launch=int(bpl),
                     ms_per_launch=round(mspl, 5), share_of_step=round(dk["ms"] / ms_per_step, 3))
+    unfused = desc.pop("unfused", None)
+    if "flops_per_step" in desc:
+        # a contraction: the matrix cores' bf16 dense peak bounds it
+        tflops = desc["flops_per_step"] / (mspl * 1e-3) / 1e12
+        roofline.update(bound="mfma", achieved=round(tflops, 1), peak=PEAK_BF16_TFLOPS,
+                        unit="TFLOP/s", frac=round(tflops / PEAK_BF16_TFLOPS, 4), traffic=None,
+                        flops_per_launch=desc["flops_per_step"])
+    if unfused is not None:
+        ums = time_fns(unfused["fns"])
+        desc["unfused_reference"] = dict(what=unfused["what"], ms=round(ums, 5),
+                                         speedup_of_fused=round(ums / mspl, 4))
 
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
     # outside the timed steps: the copy ceiling and the cold-cache op times
     ceiling = stream_ceiling(dev)
-    roofline["frac_of_ceiling"] = round(achieved / ceiling["gbs"], 4)
+    if roofline["bound"] == "hbm":
+        roofline["frac_of_ceiling"] = round(achieved / ceiling["gbs"], 4)
     cold = cold_op_times(ops, args.cold_rounds, dev) if args.cold_rounds > 0 else None
     out = {
         "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,

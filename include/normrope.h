@@ -268,7 +268,7 @@ int nr_last_hip_error(void);
  * so its exact bits, depend on the shape).  value 0 restores the automatic
  * choice.  Keys: "fwd_w", "fwd_k", "fwd_r", "fwd_j", "bwd_w", "bwd_k",
  * "bwd_d", "bwd_p", "bwd_rows_min", "bwd_pf", "rope_k", "rope_wpb",
- * "rope_groups".  A key whose forced value
+ * "rope_groups", "gemm_tile".  A key whose forced value
  * does not fit a call's shape makes that call return NR_ERR_SHAPE.
  * Returns NR_ERR_TUNE for an unknown key or a negative value.  Host only.
  */
