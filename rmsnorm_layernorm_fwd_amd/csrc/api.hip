@@ -86,7 +86,8 @@ nr_status_t check_norm_shape(nr_dtype_t dt, int64_t rows, int64_t n) {
 
 enum FwdOp { kFwdRms, kFwdLn, kFwdRmsRope };
 
-nr_status_t plan_fwd(nr_dtype_t dt, int64_t n, bool aligned, FwdPlan* pl, FwdOp op) {
+nr_status_t plan_fwd(nr_dtype_t dt, int64_t rows, int64_t n, bool aligned, FwdPlan* pl,
+                     FwdOp op) {
   const int64_t nchunk = (n + vec_elems(dt) - 1) / vec_elems(dt);
   const int64_t need = (nchunk + 63) / 64;
   // Short rows: a wavefront per row, no barrier.  Rows of 5..16 chunk slots
@@ -94,19 +95,22 @@ nr_status_t plan_fwd(nr_dtype_t dt, int64_t n, bool aligned, FwdPlan* pl, FwdOp 
   // weight chunk loaded serves both:
   //   LayerNorm: two waves per row and about 5 chunks per lane, which keeps
   //     the row resident in fewer VGPRs (it holds x, gamma and beta);
-  //   RMSNorm (plain or with the RoPE epilogue): 2 chunks per lane and as
-  //     many waves as that needs, i.e. more waves with fewer loads each;
-  //     plain RMSNorm also puts two row groups in a workgroup.
+  //   RMSNorm (plain or with the RoPE epilogue) on batches of 16384 rows or
+  //     more: 2 chunks per lane and as many waves as that needs, i.e. more
+  //     waves with fewer loads each; plain RMSNorm also puts two row groups
+  //     in a workgroup.  Smaller batches take the LayerNorm shape, whose
+  //     fewer, fuller workgroups leave less of a partial last round.
   // Each measured fastest at 5120 bf16 on MI355X (LayerNorm 5.9 TB/s;
-  // RMSNorm 6.05 -> 6.19, RMSNorm + RoPE 5.85 -> 6.1-6.2 TB/s against the
-  // two-wave shape).  Longer rows: up to 8 chunks per lane and as many waves
-  // as needed.
+  // 65536 rows: RMSNorm 6.05 -> 6.19, RMSNorm + RoPE 5.85 -> 6.1-6.2 TB/s
+  // against the two-wave shape; 3840 rows: RMSNorm 15.5 -> 14.8 us the other
+  // way round).  Longer rows: up to 8 chunks per lane and as many waves as
+  // needed.
   int W, K, J = 1, R;
   if (need <= 4) {
     W = 1;
     K = pick_at_least(need, kFwdK, 7);
     R = 4;
-  } else if (need <= 16 && op != kFwdLn) {
+  } else if (need <= 16 && op != kFwdLn && rows >= 16384) {
     W = static_cast<int>((need + 1) / 2);
     K = 2;
     J = 2;
@@ -288,7 +292,7 @@ nr_status_t rmsnorm_fwd(nr_dtype_t dt, const void* x, const void* w, void* y, fl
   const bool aligned = (n % vec_elems(dt)) == 0 && aligned16(x) && aligned16(y) &&
                        (w == nullptr || aligned16(w));
   FwdPlan pl;
-  if ((s = plan_fwd(dt, n, aligned, &pl, kFwdRms)) != NR_OK) return s;
+  if ((s = plan_fwd(dt, rows, n, aligned, &pl, kFwdRms)) != NR_OK) return s;
   if (!fwd_grid_ok(rows, pl)) return NR_ERR_SHAPE;
   return hip_status(nr::launch_norm_fwd(false, dt, pl, x, w, nullptr, y, inv_rms, nullptr, rows,
                                         static_cast<int>(n), eps, gemma_offset ? 1.0f : 0.0f,
@@ -309,7 +313,7 @@ nr_status_t layernorm_fwd(nr_dtype_t dt, const void* x, const void* gamma, const
                        (gamma == nullptr || aligned16(gamma)) &&
                        (beta == nullptr || aligned16(beta));
   FwdPlan pl;
-  if ((s = plan_fwd(dt, n, aligned, &pl, kFwdLn)) != NR_OK) return s;
+  if ((s = plan_fwd(dt, rows, n, aligned, &pl, kFwdLn)) != NR_OK) return s;
   if (!fwd_grid_ok(rows, pl)) return NR_ERR_SHAPE;
   return hip_status(nr::launch_norm_fwd(true, dt, pl, x, gamma, beta, y, mean, rstd, rows,
                                         static_cast<int>(n), eps, 0.0f,
@@ -425,7 +429,7 @@ nr_status_t layernorm_gelu_fwd(nr_dtype_t dt, const void* x, const void* gamma, 
                        (gamma == nullptr || aligned16(gamma)) &&
                        (beta == nullptr || aligned16(beta));
   FwdPlan pl;
-  if ((s = plan_fwd(dt, n, aligned, &pl, kFwdLn)) != NR_OK) return s;
+  if ((s = plan_fwd(dt, rows, n, aligned, &pl, kFwdLn)) != NR_OK) return s;
   if (!fwd_grid_ok(rows, pl)) return NR_ERR_SHAPE;
   return hip_status(nr::launch_ln_gelu_fwd(dt, pl, x, gamma, beta, y, mean, rstd, rows,
                                            static_cast<int>(n), eps,
@@ -475,7 +479,7 @@ nr_status_t rmsnorm_rope_fwd(nr_dtype_t dt, const void* x, const void* w, void* 
   const bool aligned = vec_tab && (n % vec_elems(dt)) == 0 && aligned16(x) && aligned16(y) &&
                        (w == nullptr || aligned16(w));
   FwdPlan pl;
-  if ((s = plan_fwd(dt, n, aligned, &pl, kFwdRmsRope)) != NR_OK) return s;
+  if ((s = plan_fwd(dt, rows, n, aligned, &pl, kFwdRmsRope)) != NR_OK) return s;
   if (!fwd_grid_ok(rows, pl)) return NR_ERR_SHAPE;
   const nr::RopeArgs ra{cos_tab, sin_tab, static_cast<int>(head_dim), rows_per_token};
   return hip_status(nr::launch_rms_rope_fwd(dt, pl, x, w, y, inv_rms, ra, rows, static_cast<int>(n),
