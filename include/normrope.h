@@ -243,11 +243,37 @@ nr_status_t layernorm_gelu_bwd(nr_dtype_t dt, const void* dout, const void* x,
  * Shapes: K a multiple of 64 (at most 65536), N a multiple of 128, any M;
  * x, W, out and w_norm 16-byte aligned (else NR_ERR_SHAPE); out may not
  * overlap x or W.
+ * Workspace: on large grids (N a multiple of 256) the kernel first writes
+ * the folded weight w'_k W[n][k] (N K bf16) into the caller's workspace;
+ * nr_rmsnorm_linear_workspace_bytes gives the size needed (0 when none).
+ * A workspace that is NULL, smaller than that or not 16-byte aligned when
+ * one is needed is NR_ERR_WORKSPACE; one overlapping an operand is
+ * NR_ERR_ALIAS.  Its contents on return are unspecified.
  */
 nr_status_t rmsnorm_linear_fwd(nr_dtype_t dt, const void* x, const void* w_norm,
                                const void* W, void* out, float* inv_rms,
                                int64_t M, int64_t N, int64_t K, float eps,
-                               int gemma_offset, void* stream);
+                               int gemma_offset, void* workspace,
+                               size_t workspace_bytes, void* stream);
+
+/* Workspace bytes rmsnorm_linear_fwd needs at this shape (has_weight: a
+ * norm weight is passed): N K 2 on the large-tile path, else 0.  Host only;
+ * a pure function of its arguments and the current tuning table. */
+size_t nr_rmsnorm_linear_workspace_bytes(int64_t M, int64_t N, int64_t K, int has_weight);
+
+/*
+ * rmsnorm_linear_fold_weight -- the folded weight of rmsnorm_linear_fwd on
+ * its own: W_folded[n][k] = bf16(W[n][k] w'_k), w'_k = w_k or 1 + w_k
+ * (gemma_offset), one rounding.  For callers whose weights do not change
+ * between calls: rmsnorm_linear_fwd(x, NULL, W_folded, ...) then gives the
+ * same output, bit for bit, as rmsnorm_linear_fwd(x, w_norm, W, ...) and
+ * needs no workspace.  bf16 only; K a multiple of 8 (at most 65536), N at
+ * most 2^22; all three pointers 16-byte aligned; W_folded may be W (in
+ * place) but may not partly overlap it or overlap w_norm.
+ */
+nr_status_t rmsnorm_linear_fold_weight(nr_dtype_t dt, const void* w_norm, const void* W,
+                                       void* W_folded, int64_t N, int64_t K,
+                                       int gemma_offset, void* stream);
 
 /* Workspace bytes a backward call needs for dw / dgamma / dbeta at this
  * shape, for any dtype: op = 0 rmsnorm_bwd, 1 layernorm_bwd or
@@ -268,7 +294,8 @@ int nr_last_hip_error(void);
  * so its exact bits, depend on the shape).  value 0 restores the automatic
  * choice.  Keys: "fwd_w", "fwd_k", "fwd_r", "fwd_j", "bwd_w", "bwd_k",
  * "bwd_d", "bwd_p", "bwd_rows_min", "bwd_pf", "rope_k", "rope_wpb",
- * "rope_groups", "gemm_tile".  A key whose forced value
+ * "rope_groups", "gemm_tile" (1: 128 x 128 outputs per workgroup, 2: 256 x
+ * 256).  A key whose forced value
  * does not fit a call's shape makes that call return NR_ERR_SHAPE.
  * Returns NR_ERR_TUNE for an unknown key or a negative value.  Host only.
  */

@@ -21,6 +21,7 @@ __all__ = [
     "rmsnorm_rope_fwd", "rmsnorm_rope_bwd", "layernorm_gelu_fwd", "layernorm_gelu_bwd",
     "rope_interleaved_apply", "rope_table_1d", "rope_table_3d", "nr_bwd_workspace_bytes",
     "nr_status_str", "nr_tune", "nr_norm_n_max", "nr_stream_copy", "rmsnorm_linear_fwd",
+    "rmsnorm_linear_fold_weight", "nr_rmsnorm_linear_workspace_bytes",
     "library_path",
 ]
 
@@ -80,13 +81,16 @@ def _lib():
             "nr_tune": [ctypes.c_char_p, i32],
             "nr_norm_n_max": [i32],
             "nr_stream_copy": [vp, vp, sz, vp],
-            "rmsnorm_linear_fwd": [i32, vp, vp, vp, vp, vp, i64, i64, i64, f32, i32, vp],
+            "rmsnorm_linear_fwd": [i32, vp, vp, vp, vp, vp, i64, i64, i64, f32, i32, vp, sz, vp],
+            "nr_rmsnorm_linear_workspace_bytes": [i64, i64, i64, i32],
+            "rmsnorm_linear_fold_weight": [i32, vp, vp, vp, i64, i64, i32, vp],
         }
         for name, args in sig.items():
             fn = getattr(L, name)
             fn.argtypes = args
             fn.restype = i32
         L.nr_bwd_workspace_bytes.restype = sz
+        L.nr_rmsnorm_linear_workspace_bytes.restype = sz
         L.nr_status_str.restype = ctypes.c_char_p
         L.nr_norm_n_max.restype = i64
         _L = L
@@ -384,9 +388,11 @@ def rope_table_3d(grid, pairs, theta=10000.0, device="cuda"):
 # ---------------------------------------------------------------- RMSNorm -> linear
 
 def rmsnorm_linear_fwd(x, w_norm, W, eps=1e-6, gemma_offset=False, out=None, inv_rms=None,
-                       want_stats=True):
+                       want_stats=True, workspace=None):
     """out = rmsnorm(x, w_norm) @ W.T with the norm folded into the GEMM
-    (bf16; W [N, K] as a linear layer stores it); returns (out, inv_rms)."""
+    (bf16; W [N, K] as a linear layer stores it); returns (out, inv_rms).
+    The folded weight goes to `workspace` (allocated here when None and the
+    call needs one)."""
     _dev("x", x, torch.bfloat16)
     rows, k = _rows_n(x)
     _dev("W", W, torch.bfloat16)
@@ -400,10 +406,34 @@ def rmsnorm_linear_fwd(x, w_norm, W, eps=1e-6, gemma_offset=False, out=None, inv
     if inv_rms is None and want_stats:
         inv_rms = torch.empty(x.shape[:-1], dtype=torch.float32, device=x.device)
     _dev("inv_rms", inv_rms, torch.float32)
+    wsb = nr_rmsnorm_linear_workspace_bytes(rows, n, k, w_norm is not None)
+    if workspace is None and wsb > 0:
+        workspace = torch.empty(wsb, dtype=torch.uint8, device=x.device)
     _check("rmsnorm_linear_fwd", _lib().rmsnorm_linear_fwd(
         NR_BF16, _ptr(x), _ptr(w_norm), _ptr(W), _ptr(out), _ptr(inv_rms), rows, n, k, float(eps),
-        int(bool(gemma_offset)), _stream(x)))
+        int(bool(gemma_offset)), _ptr(workspace),
+        0 if workspace is None else workspace.numel() * workspace.element_size(), _stream(x)))
     return out, inv_rms
+
+
+def rmsnorm_linear_fold_weight(w_norm, W, gemma_offset=False, out=None):
+    """W_folded = bf16(W * w'): the weight rmsnorm_linear_fwd multiplies by,
+    for calls with w_norm=None (bit-identical output, no workspace)."""
+    _dev("W", W, torch.bfloat16)
+    if W.dim() != 2:
+        raise ValueError("W must be [N, K]")
+    n, k = W.shape
+    _dev("w_norm", w_norm, torch.bfloat16, (k,))
+    if out is None:
+        out = torch.empty_like(W)
+    _dev("W_folded", out, torch.bfloat16, (n, k))
+    _check("rmsnorm_linear_fold_weight", _lib().rmsnorm_linear_fold_weight(
+        NR_BF16, _ptr(w_norm), _ptr(W), _ptr(out), n, k, int(bool(gemma_offset)), _stream(W)))
+    return out
+
+
+def nr_rmsnorm_linear_workspace_bytes(m, n, k, has_weight) -> int:
+    return int(_lib().nr_rmsnorm_linear_workspace_bytes(m, n, k, int(bool(has_weight))))
 
 
 # ---------------------------------------------------------------- helpers

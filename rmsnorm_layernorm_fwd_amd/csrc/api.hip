@@ -598,9 +598,28 @@ nr_status_t rope_table_3d(float* cos_tab, float* sin_tab, int64_t frames, int64_
       static_cast<hipStream_t>(stream)));
 }
 
+namespace {
+// Output tile of the RMSNorm -> linear kernels: 256 x 256 (direct-to-LDS,
+// folded weight) when N allows it and there are enough tiles to fill the
+// GPU several times over (65536 x 5120 x 5120: 1050 against 737 TFLOP/s for
+// the 128 x 128 kernel's best shape), else 128 x 128 (3840 rows: the small
+// tile fills the 256 CUs).  The tuning table can force either.
+int linear_tile(int64_t M, int64_t N) {
+  int tile = (N % 256 == 0 && ((M + 255) / 256) * (N / 256) >= 1024) ? 2 : 1;
+  if (tune(GEMM_TILE) > 0) tile = tune(GEMM_TILE);
+  return tile;
+}
+}  // namespace
+
+size_t nr_rmsnorm_linear_workspace_bytes(int64_t M, int64_t N, int64_t K, int has_weight) {
+  if (!has_weight || M <= 0 || N <= 0 || K <= 0 || N > (int64_t{1} << 22) || K > 65536) return 0;
+  return linear_tile(M, N) == 2 ? static_cast<size_t>(N * K) * 2 : 0;
+}
+
 nr_status_t rmsnorm_linear_fwd(nr_dtype_t dt, const void* x, const void* w_norm, const void* W,
                                void* out, float* inv_rms, int64_t M, int64_t N, int64_t K,
-                               float eps, int gemma_offset, void* stream) {
+                               float eps, int gemma_offset, void* workspace,
+                               size_t workspace_bytes, void* stream) {
   if (dt != NR_BF16) return NR_ERR_DTYPE;  // the bf16 matrix cores only
   if (M < 0 || M > INT32_MAX || N < 128 || N % 128 != 0 || K < 64 || K % 64 != 0)
     return NR_ERR_SHAPE;
@@ -610,25 +629,48 @@ nr_status_t rmsnorm_linear_fwd(nr_dtype_t dt, const void* x, const void* w_norm,
   if (!aligned16(x) || !aligned16(W) || !aligned16(out) || (w_norm != nullptr && !aligned16(w_norm)))
     return NR_ERR_SHAPE;
   if (M > INT64_MAX / K / 2 || M > INT64_MAX / N / 2) return NR_ERR_SHAPE;
-  const int64_t tiles = ((M + 127) / 128) * (N / 128);
-  if (tiles > INT32_MAX) return NR_ERR_SHAPE;
+  const int tile = linear_tile(M, N);
+  if (tile < 1 || tile > 2 || (tile == 2 && N % 256 != 0)) return NR_ERR_SHAPE;
+  const int64_t edge = tile == 2 ? 256 : 128;
+  if (((M + edge - 1) / edge) * (N / edge) > INT32_MAX) return NR_ERR_SHAPE;
   const size_t xb = static_cast<size_t>(M * K) * 2, wb = static_cast<size_t>(N * K) * 2,
                ob = static_cast<size_t>(M * N) * 2;
   if (bad_overlap(out, ob, x, xb) || out == x || bad_overlap(out, ob, W, wb) || out == W)
     return NR_ERR_ALIAS;
-  // output tile per workgroup (see launch_rmsnorm_linear): 256 x 256 when
-  // there are enough of them to fill the GPU several times over (measured:
-  // 590 -> 740 TFLOP/s at 65536 x 5120 x 5120), else 128 x 128 (3840 rows:
-  // 620 against 420 TFLOP/s)
-  int tile = (N % 256 == 0 && ((M + 255) / 256) * (N / 256) >= 1024) ? 4 : 1;
-  if (tune(GEMM_TILE) > 0) tile = tune(GEMM_TILE);
-  if (tile < 1 || tile > 4 || ((tile == 2 || tile == 4) && N % 256 != 0)) return NR_ERR_SHAPE;
-  const int64_t bm = (tile >= 3) ? 256 : 128, bn = (tile == 2 || tile == 4) ? 256 : 128;
-  if (((M + bm - 1) / bm) * (N / bn) > INT32_MAX) return NR_ERR_SHAPE;
-  return hip_status(nr::launch_rmsnorm_linear(x, w_norm, W, out, inv_rms, static_cast<int>(M),
-                                              static_cast<int>(N), static_cast<int>(K), eps,
-                                              gemma_offset ? 1.0f : 0.0f, tile,
-                                              static_cast<hipStream_t>(stream)));
+  void* wfold = nullptr;
+  if (tile == 2 && w_norm != nullptr) {
+    // the folded weight: N K bf16, 16-byte aligned, apart from every operand
+    if (workspace == nullptr || workspace_bytes < wb || !aligned16(workspace))
+      return NR_ERR_WORKSPACE;
+    if (bad_overlap(workspace, wb, x, xb) || bad_overlap(workspace, wb, W, wb) ||
+        bad_overlap(workspace, wb, out, ob) || bad_overlap(workspace, wb, w_norm, static_cast<size_t>(K) * 2) ||
+        workspace == x || workspace == W || workspace == out || workspace == w_norm)
+      return NR_ERR_ALIAS;
+    wfold = workspace;
+  }
+  return hip_status(nr::launch_rmsnorm_linear(x, w_norm, W, out, inv_rms, wfold,
+                                              static_cast<int>(M), static_cast<int>(N),
+                                              static_cast<int>(K), eps, gemma_offset ? 1.0f : 0.0f,
+                                              tile, static_cast<hipStream_t>(stream)));
+}
+
+nr_status_t rmsnorm_linear_fold_weight(nr_dtype_t dt, const void* w_norm, const void* W,
+                                       void* W_folded, int64_t N, int64_t K, int gemma_offset,
+                                       void* stream) {
+  if (dt != NR_BF16) return NR_ERR_DTYPE;
+  if (N < 0 || K < 0 || K % 8 != 0) return NR_ERR_SHAPE;
+  if (K > 65536 || N > (int64_t{1} << 22)) return NR_ERR_UNSUPPORTED_N;
+  if (N == 0 || K == 0) return NR_OK;
+  if (w_norm == nullptr || W == nullptr || W_folded == nullptr) return NR_ERR_NULLPTR;
+  if (!aligned16(w_norm) || !aligned16(W) || !aligned16(W_folded)) return NR_ERR_SHAPE;
+  const size_t wb = static_cast<size_t>(N * K) * 2;
+  // in place (W_folded == W) is fine: each element is read, then written, by one lane
+  if ((bad_overlap(W_folded, wb, W, wb) && W_folded != W) ||
+      bad_overlap(W_folded, wb, w_norm, static_cast<size_t>(K) * 2) || W_folded == w_norm)
+    return NR_ERR_ALIAS;
+  return hip_status(nr::launch_fold_norm_weight(w_norm, W, W_folded, N, static_cast<int>(K),
+                                                gemma_offset ? 1.0f : 0.0f,
+                                                static_cast<hipStream_t>(stream)));
 }
 
 nr_status_t nr_stream_copy(const void* src, void* dst, size_t bytes, void* stream) {

@@ -91,11 +91,15 @@ hipError_t launch_rope(int dt, const RopePlan& pl, void* x, const float* cos_tab
                        hipStream_t st);
 hipError_t launch_rope_table_1d(float* cos_tab, float* sin_tab, int64_t tokens, int head_dim,
                                 int64_t pos0, double theta, hipStream_t st);
-// tile: 1 = 128 x 128, 2 = 128 x 256, 3 = 256 x 128, 4 = 256 x 256 outputs
-// per workgroup
+// tile: 1 = 128 x 128 outputs per workgroup (W scaled by the norm weight in
+// the kernel), 2 = 256 x 256 (N % 256 == 0; with a norm weight, W folded
+// into wfold, N K bf16, first)
 hipError_t launch_rmsnorm_linear(const void* x, const void* wn, const void* W, void* out,
-                                 float* inv_rms, int M, int N, int K, float eps, float w_add,
-                                 int tile, hipStream_t st);
+                                 float* inv_rms, void* wfold, int M, int N, int K, float eps,
+                                 float w_add, int tile, hipStream_t st);
+// Wf[n][k] = bf16(W[n][k] (wn[k] + w_add)); N K % 8 == 0, 16-byte aligned
+hipError_t launch_fold_norm_weight(const void* wn, const void* W, void* Wf, int64_t N, int K,
+                                   float w_add, hipStream_t st);
 hipError_t launch_stream_copy(const void* src, void* dst, int64_t nvec, hipStream_t st);
 hipError_t launch_rope_table_3d(float* cos_tab, float* sin_tab, int64_t frames, int64_t height,
                                 int64_t width, int pt, int ph, int pw, double theta,

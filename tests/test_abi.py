@@ -38,7 +38,8 @@ def test_header_functions_exported(lib):
                 "rmsnorm_rope_fwd", "rmsnorm_rope_bwd", "layernorm_gelu_fwd", "layernorm_gelu_bwd",
                 "rope_interleaved_apply", "rope_table_1d", "rope_table_3d",
                 "nr_bwd_workspace_bytes", "nr_status_str", "nr_last_hip_error", "nr_tune",
-                "nr_norm_n_max", "nr_stream_copy", "rmsnorm_linear_fwd"}
+                "nr_norm_n_max", "nr_stream_copy", "rmsnorm_linear_fwd",
+                "rmsnorm_linear_fold_weight", "nr_rmsnorm_linear_workspace_bytes"}
     assert expected <= set(names), names
     out = subprocess.run(["nm", "-D", "--defined-only", nr.library_path()],
                          capture_output=True, text=True, check=True).stdout
@@ -82,6 +83,16 @@ def test_workspace_bytes():
     assert nr.nr_bwd_workspace_bytes(100, 20000, 1) == 7 * 20000 * 4 * 2 + 100 * 8
     assert nr.nr_bwd_workspace_bytes(100, 20000, 0) == 7 * 20000 * 4 + 100 * 8
     assert nr.nr_bwd_workspace_bytes(4096, 32768, 2) == 128 * 32768 * 4 + 4096 * 8
+
+
+def test_linear_workspace_bytes():
+    # the folded weight (N K bf16) on the 256 x 256 path: N % 256 == 0 and at
+    # least 1024 such tiles; none without a norm weight or on the 128 x 128 path
+    assert nr.nr_rmsnorm_linear_workspace_bytes(65536, 5120, 5120, True) == 5120 * 5120 * 2
+    assert nr.nr_rmsnorm_linear_workspace_bytes(65536, 5120, 5120, False) == 0
+    assert nr.nr_rmsnorm_linear_workspace_bytes(3840, 5120, 5120, True) == 0
+    assert nr.nr_rmsnorm_linear_workspace_bytes(65536, 5120 + 128, 5120, True) == 0
+    assert nr.nr_rmsnorm_linear_workspace_bytes(0, 5120, 5120, True) == 0
 
 
 def test_tune_keys(lib):
@@ -144,14 +155,38 @@ def test_rejected_calls_return_status(lib):
     # RMSNorm -> linear: bf16 only, K % 64, N % 128, pointers, alignment, overlap
     XA, WA, OA = 1 << 24, 1 << 28, 1 << 32
     lin = L.rmsnorm_linear_fwd
-    assert lin(F32, XA, None, WA, OA, None, 4, 128, 64, 1e-6, 0, None) == NR_ERR_DTYPE
-    assert lin(BF16, XA, None, WA, OA, None, 4, 100, 64, 1e-6, 0, None) == NR_ERR_SHAPE
-    assert lin(BF16, XA, None, WA, OA, None, 4, 128, 72, 1e-6, 0, None) == NR_ERR_SHAPE
-    assert lin(BF16, XA, None, WA, OA, None, 4, 128, 65600, 1e-6, 0, None) == NR_ERR_UNSUPPORTED_N
-    assert lin(BF16, None, None, WA, OA, None, 4, 128, 64, 1e-6, 0, None) == NR_ERR_NULLPTR
-    assert lin(BF16, XA + 2, None, WA, OA, None, 4, 128, 64, 1e-6, 0, None) == NR_ERR_SHAPE
-    assert lin(BF16, XA, None, WA, XA + 64, None, 4, 128, 64, 1e-6, 0, None) == NR_ERR_ALIAS
-    assert lin(BF16, None, None, None, None, None, 0, 128, 64, 1e-6, 0, None) == NR_OK
+    assert lin(F32, XA, None, WA, OA, None, 4, 128, 64, 1e-6, 0, None, 0, None) == NR_ERR_DTYPE
+    assert lin(BF16, XA, None, WA, OA, None, 4, 100, 64, 1e-6, 0, None, 0, None) == NR_ERR_SHAPE
+    assert lin(BF16, XA, None, WA, OA, None, 4, 128, 72, 1e-6, 0, None, 0, None) == NR_ERR_SHAPE
+    assert lin(BF16, XA, None, WA, OA, None, 4, 128, 65600, 1e-6, 0, None, 0, None) == NR_ERR_UNSUPPORTED_N
+    assert lin(BF16, None, None, WA, OA, None, 4, 128, 64, 1e-6, 0, None, 0, None) == NR_ERR_NULLPTR
+    assert lin(BF16, XA + 2, None, WA, OA, None, 4, 128, 64, 1e-6, 0, None, 0, None) == NR_ERR_SHAPE
+    assert lin(BF16, XA, None, WA, XA + 64, None, 4, 128, 64, 1e-6, 0, None, 0, None) == NR_ERR_ALIAS
+    assert lin(BF16, None, None, None, None, None, 0, 128, 64, 1e-6, 0, None, 0, None) == NR_OK
+    # the 256 x 256 path with a norm weight needs the folded-weight workspace
+    # (N K bf16), aligned and apart from the operands
+    BX, BW, BO, BN_, BS = 1 << 34, 1 << 36, 1 << 38, 1 << 40, 1 << 41
+    big = (65536, 5120, 64, 1e-6, 0)
+    need = 5120 * 64 * 2
+    assert lin(BF16, BX, BN_, BW, BO, None, *big, None, 0, None) == NR_ERR_WORKSPACE
+    assert lin(BF16, BX, BN_, BW, BO, None, *big, BS, need - 16, None) == NR_ERR_WORKSPACE
+    assert lin(BF16, BX, BN_, BW, BO, None, *big, BS + 8, need, None) == NR_ERR_WORKSPACE
+    assert lin(BF16, BX, BN_, BW, BO, None, *big, BW + 1024, need, None) == NR_ERR_ALIAS
+    # forcing the 256 x 256 tile where N is not a multiple of 256
+    assert L.nr_tune(b"gemm_tile", 2) == NR_OK
+    try:
+        assert lin(BF16, XA, None, WA, OA, None, 4, 384, 64, 1e-6, 0, None, 0, None) == NR_ERR_SHAPE
+    finally:
+        L.nr_tune(b"gemm_tile", 0)
+    # the standalone fold: bf16, K % 8, pointers, alignment, partial overlap
+    fold = L.rmsnorm_linear_fold_weight
+    assert fold(F32, XA, WA, OA, 16, 64, 0, None) == NR_ERR_DTYPE
+    assert fold(BF16, XA, WA, OA, 16, 60, 0, None) == NR_ERR_SHAPE
+    assert fold(BF16, None, WA, OA, 16, 64, 0, None) == NR_ERR_NULLPTR
+    assert fold(BF16, XA, WA + 2, OA, 16, 64, 0, None) == NR_ERR_SHAPE
+    assert fold(BF16, XA, WA, WA + 128, 16, 64, 0, None) == NR_ERR_ALIAS
+    assert fold(BF16, XA, WA, XA, 16, 64, 0, None) == NR_ERR_ALIAS
+    assert fold(BF16, None, None, None, 0, 64, 0, None) == NR_OK
     # the copy probe: null, size / alignment, overlap; zero bytes is a no-op
     assert L.nr_stream_copy(None, FAKE, 64, None) == NR_ERR_NULLPTR
     assert L.nr_stream_copy(FAKE, 0x90000, 60, None) == NR_ERR_SHAPE

@@ -5,7 +5,12 @@ Bound, derived from the arithmetic: x enters the bf16 matrix cores exactly;
 each product's weight w'_k W[n][k] is rounded once to bf16 (2^-9 relative)
 and the K products are added in fp32 (at most K 2^-24 relative of their
 magnitude sum), so |O - R| <= ulp_bf16(R) + 2^-8 S, S = sum_k |y_k W[n][k]|
-(exact for w_norm NULL up to the fp32 sum), for K <= 65536."""
+(exact for w_norm NULL up to the fp32 sum), for K <= 65536.
+
+Two kernels serve the call: 128 x 128 output tiles (small grids) and 256 x
+256 tiles with the norm weight folded into W first (large grids); the tests
+force each on the same shapes."""
+import contextlib
 import numpy as np
 import pytest
 import torch
@@ -17,6 +22,15 @@ from tolerance import check, to64, ulp_bf16
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
+
+
+@contextlib.contextmanager
+def gemm_tile(tile):
+    nr.nr_tune("gemm_tile", tile)
+    try:
+        yield
+    finally:
+        nr.nr_tune("gemm_tile", 0)
 
 
 def run_case(tag, m, n, k, seed, weight="w", gemma=False, rows=None):
@@ -46,6 +60,64 @@ def run_case(tag, m, n, k, seed, weight="w", gemma=False, rows=None):
 ])
 def test_rmsnorm_linear_cases(m, n, k, weight, gemma):
     run_case(f"{m}x{n}x{k}", m, n, k, 9800 + m + n + k, weight, gemma)
+
+
+@pytest.mark.parametrize("m,n,k,weight,gemma", [
+    (1, 256, 64, "w", False), (777, 256, 5120, "w", False), (1000, 512, 320, "w", True),
+    (300, 768, 192, None, False), (513, 1280, 1024, "w", False),
+])
+def test_rmsnorm_linear_tile256(m, n, k, weight, gemma):
+    # the 256 x 256 kernel on small shapes: ragged M (rows past M read out of
+    # range), an odd number of K steps (320 = 5 x 64), a single row
+    with gemm_tile(2):
+        run_case(f"tile256 {m}x{n}x{k}", m, n, k, 9700 + m + n + k, weight, gemma)
+
+
+@pytest.mark.parametrize("tile", [1, 2])
+def test_rmsnorm_linear_folded_weight_is_bit_identical(tile):
+    # rmsnorm_linear_fold_weight, then a call without norm weight, gives the
+    # same bits as the call with it (one rounding of w' W either way)
+    print(f"[case] folded weight, tile {tile}", flush=True)
+    m, n, k = 600, 512, 448
+    x = workloads.normal((m, k), 9960, torch.bfloat16).to(DEV)
+    w = workloads.normal((k,), 9961, torch.bfloat16, mean=0.0, std=0.1).to(DEV)
+    W = workloads.normal((n, k), 9962, torch.bfloat16, std=k ** -0.5).to(DEV)
+    with gemm_tile(tile):
+        a, ra = nr.rmsnorm_linear_fwd(x, w, W, 1e-6, True)
+        Wf = nr.rmsnorm_linear_fold_weight(w, W, True)
+        b, rb = nr.rmsnorm_linear_fwd(x, None, Wf, 1e-6)
+        # the fold in place gives the same folded weight
+        W2 = W.clone()
+        nr.rmsnorm_linear_fold_weight(w, W2, True, out=W2)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b) and torch.equal(ra, rb)
+    assert torch.equal(W2, Wf)
+    ref = (W.float() * (1.0 + w.float())).to(torch.bfloat16)  # one rounding of an exact product
+    assert torch.equal(Wf, ref)
+
+
+def test_rmsnorm_linear_tiles_agree_and_workspace_is_reused():
+    # both kernels on one shape: each within the oracle bound (run_case), and
+    # close to each other (their x^2 sums run in different orders); a caller
+    # workspace serves repeated calls
+    print("[case] tile 128 vs 256, 1024x1024x2048", flush=True)
+    m, n, k = 1024, 1024, 2048
+    x = workloads.normal((m, k), 9970, torch.bfloat16).to(DEV)
+    w = workloads.normal((k,), 9971, torch.bfloat16, mean=1.0, std=0.1).to(DEV)
+    W = workloads.normal((n, k), 9972, torch.bfloat16, std=k ** -0.5).to(DEV)
+    with gemm_tile(1):
+        a, ra = nr.rmsnorm_linear_fwd(x, w, W)
+    with gemm_tile(2):
+        ws = torch.empty(nr.nr_rmsnorm_linear_workspace_bytes(m, n, k, True), dtype=torch.uint8,
+                         device=DEV)
+        assert ws.numel() == n * k * 2
+        b, rb = nr.rmsnorm_linear_fwd(x, w, W, workspace=ws)
+        c, rc = nr.rmsnorm_linear_fwd(x, w, W, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(b, c) and torch.equal(rb, rc)
+    assert torch.allclose(ra, rb, rtol=2e-6, atol=0)
+    d = (a.float() - b.float()).abs().cpu().double().numpy()
+    assert np.all(d <= 2 * ulp_bf16(a.float().cpu().double().numpy()) + 1e-6)
 
 
 def test_rmsnorm_linear_long_sequence_sampled():
