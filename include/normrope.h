@@ -243,12 +243,14 @@ nr_status_t layernorm_gelu_bwd(nr_dtype_t dt, const void* dout, const void* x,
  * Shapes: K a multiple of 64 (at most 65536), N a multiple of 128, any M;
  * x, W, out and w_norm 16-byte aligned (else NR_ERR_SHAPE); out may not
  * overlap x or W.
- * Workspace: on large grids (N a multiple of 256) the kernel first writes
- * the folded weight w'_k W[n][k] (N K bf16) into the caller's workspace;
- * nr_rmsnorm_linear_workspace_bytes gives the size needed (0 when none).
- * A workspace that is NULL, smaller than that or not 16-byte aligned when
- * one is needed is NR_ERR_WORKSPACE; one overlapping an operand is
- * NR_ERR_ALIAS.  Its contents on return are unspecified.
+ * Workspace: on large grids (N a multiple of 256) the call first computes
+ * the row statistics (into inv_rms, or the workspace's first ceil(4 M /
+ * 256) 256 bytes when inv_rms is NULL) and, with a norm weight, writes the
+ * folded weight w'_k W[n][k] (N K bf16) into the workspace after them;
+ * nr_rmsnorm_linear_workspace_bytes gives the size to pass (0 when none is
+ * needed).  A workspace that is NULL, smaller than needed or not 16-byte
+ * aligned when one is needed is NR_ERR_WORKSPACE; one overlapping an operand
+ * is NR_ERR_ALIAS.  Its contents on return are unspecified.
  */
 nr_status_t rmsnorm_linear_fwd(nr_dtype_t dt, const void* x, const void* w_norm,
                                const void* W, void* out, float* inv_rms,
@@ -256,8 +258,9 @@ nr_status_t rmsnorm_linear_fwd(nr_dtype_t dt, const void* x, const void* w_norm,
                                int gemma_offset, void* workspace,
                                size_t workspace_bytes, void* stream);
 
-/* Workspace bytes rmsnorm_linear_fwd needs at this shape (has_weight: a
- * norm weight is passed): N K 2 on the large-tile path, else 0.  Host only;
+/* Workspace bytes rmsnorm_linear_fwd may need at this shape (has_weight: a
+ * norm weight is passed): on the large-tile path ceil(4 M / 256) 256 for
+ * the row statistics plus N K 2 for the folded weight, else 0.  Host only;
  * a pure function of its arguments and the current tuning table. */
 size_t nr_rmsnorm_linear_workspace_bytes(int64_t M, int64_t N, int64_t K, int has_weight);
 

@@ -612,8 +612,9 @@ int linear_tile(int64_t M, int64_t N) {
 }  // namespace
 
 size_t nr_rmsnorm_linear_workspace_bytes(int64_t M, int64_t N, int64_t K, int has_weight) {
-  if (!has_weight || M <= 0 || N <= 0 || K <= 0 || N > (int64_t{1} << 22) || K > 65536) return 0;
-  return linear_tile(M, N) == 2 ? static_cast<size_t>(N * K) * 2 : 0;
+  if (M <= 0 || M > INT32_MAX || N <= 0 || K <= 0 || N > (int64_t{1} << 22) || K > 65536) return 0;
+  if (linear_tile(M, N) != 2) return 0;
+  return nr::linear_rows_bytes(M) + (has_weight ? static_cast<size_t>(N * K) * 2 : 0);
 }
 
 nr_status_t rmsnorm_linear_fwd(nr_dtype_t dt, const void* x, const void* w_norm, const void* W,
@@ -637,18 +638,21 @@ nr_status_t rmsnorm_linear_fwd(nr_dtype_t dt, const void* x, const void* w_norm,
                ob = static_cast<size_t>(M * N) * 2;
   if (bad_overlap(out, ob, x, xb) || out == x || bad_overlap(out, ob, W, wb) || out == W)
     return NR_ERR_ALIAS;
-  void* wfold = nullptr;
-  if (tile == 2 && w_norm != nullptr) {
-    // the folded weight: N K bf16, 16-byte aligned, apart from every operand
-    if (workspace == nullptr || workspace_bytes < wb || !aligned16(workspace))
+  if (tile == 2 && (w_norm != nullptr || inv_rms == nullptr)) {
+    // the row statistics (unless inv_rms takes them), then the folded weight
+    // (N K bf16): 16-byte aligned, apart from every operand
+    const size_t need = nr::linear_rows_bytes(M) + (w_norm != nullptr ? wb : 0);
+    if (workspace == nullptr || workspace_bytes < need || !aligned16(workspace))
       return NR_ERR_WORKSPACE;
-    if (bad_overlap(workspace, wb, x, xb) || bad_overlap(workspace, wb, W, wb) ||
-        bad_overlap(workspace, wb, out, ob) || bad_overlap(workspace, wb, w_norm, static_cast<size_t>(K) * 2) ||
-        workspace == x || workspace == W || workspace == out || workspace == w_norm)
+    const size_t rb = static_cast<size_t>(M) * 4;
+    if (bad_overlap(workspace, need, x, xb) || bad_overlap(workspace, need, W, wb) ||
+        bad_overlap(workspace, need, out, ob) ||
+        bad_overlap(workspace, need, w_norm, static_cast<size_t>(K) * 2) ||
+        bad_overlap(workspace, need, inv_rms, rb) || workspace == x || workspace == W ||
+        workspace == out || workspace == w_norm || workspace == inv_rms)
       return NR_ERR_ALIAS;
-    wfold = workspace;
   }
-  return hip_status(nr::launch_rmsnorm_linear(x, w_norm, W, out, inv_rms, wfold,
+  return hip_status(nr::launch_rmsnorm_linear(x, w_norm, W, out, inv_rms, workspace,
                                               static_cast<int>(M), static_cast<int>(N),
                                               static_cast<int>(K), eps, gemma_offset ? 1.0f : 0.0f,
                                               tile, static_cast<hipStream_t>(stream)));

@@ -11,21 +11,22 @@
 // each row's sum of squares from the same x tiles it feeds to the matrix
 // cores, and applies r_m to the fp32 accumulators in the epilogue.
 //
-// gfx950 mapping, two kernels with v_mfma_f32_32x32x16_bf16 and a 256-lane
-// (4-wave) workgroup:
-//  - tile256: a 256 x 256 output tile (each wave 128 x 128, 4 x 4 MFMA
-//    tiles, accumulators in the AGPRs) for large grids.  The norm weight is
-//    folded into W beforehand (fold_norm_weight_kernel, w'_k W[n][k]
-//    rounded once to bf16, into a caller workspace), so both operands go
-//    from HBM straight into LDS with buffer_load ... lds (no VGPR staging,
-//    no VALU on the way): two LDS stages of K 64, the next stage's loads in
-//    flight while the matrix cores work on the current one, one barrier per
-//    stage.  LDS rows are 128 bytes, 16-byte chunk index XOR-swizzled by the
-//    row so the operand reads of 16 consecutive rows hit distinct banks.
-//    Each wave adds up its rows' x^2 from the A operands it reads anyway.
-//  - tile128: a 128 x 128 tile for grids too small to fill the GPU with
-//    256 x 256 tiles; operands staged through VGPRs, W scaled by the norm
-//    weight on the way into LDS (no workspace).
+// gfx950 mapping, two kernels with v_mfma_f32_32x32x16_bf16:
+//  - tile256: a 256 x 256 output tile per 8-wave workgroup (2 waves per
+//    SIMD, each wave 128 x 64, 4 x 2 MFMA tiles) for large grids.  The row
+//    statistics come from a light pass over x (row_inv_rms_kernel) and the
+//    norm weight is folded into W beforehand (fold_norm_weight_kernel,
+//    w'_k W[n][k] rounded once to bf16, into a caller workspace), so both
+//    operands go from HBM straight into LDS with buffer_load ... lds (no
+//    VGPR staging, no VALU on the way): two LDS stages of K 64, the next
+//    stage's loads in flight while the matrix cores work on the current
+//    one, one barrier per stage.  LDS rows are 128 bytes, 16-byte chunk
+//    index XOR-swizzled by the row so the operand reads of 16 consecutive
+//    rows hit distinct banks.  r_m scales the accumulators in the epilogue.
+//  - tile128: a 128 x 128 tile per 4-wave workgroup for grids too small to
+//    fill the GPU with 256 x 256 tiles; operands staged through VGPRs, W
+//    scaled by the norm weight on the way into LDS, the row sums of squares
+//    taken from the staged x (no workspace).
 // Both number the workgroups so that each of the 8 XCDs (own L2 each) works
 // through a contiguous run of tiles, and write the output tile through LDS
 // for 16-byte stores.
@@ -211,8 +212,10 @@ typedef __attribute__((address_space(3))) char lds_char;
 typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
 
 constexpr int kBig = 256;                       // output tile edge
+constexpr int kBigThreads = 512;                // 8 waves, 2 per SIMD
 constexpr int kBigABytes = kBig * BK * 2;       // one operand of one stage (32 KiB)
 constexpr int kBigStage = 2 * kBigABytes;       // x and W of one K step (64 KiB)
+constexpr int kGroupM = 8;                      // row tiles per group of the tile order
 
 struct BigLoads {
   rsrc_t xr, wr;  // x rows of the tile, W rows of the tile
@@ -221,44 +224,45 @@ struct BigLoads {
   int K;
 };
 
-// The loads of one K step into stage `dst`: load q (0..15) of a wave moves
-// 1 KiB: q < 8 x, else W; rows 64 wave + 8 (q % 8) + lane / 8, 16-byte chunk
-// lane % 8 of the row's LDS slot.  A lane's LDS slot is fixed by the
-// instruction (lane * 16 from the wave's base), so the swizzle is applied on
-// the global side: the slot holds logical chunk (lane % 8) ^ swz(row), with
-// swz(row) = (row & 7) ^ ((row >> 3) & 1) = (lane / 8) ^ (q & 1) here.
-// Rows past M read out of range (zero, or stale LDS): they only feed output
-// rows that are never stored.  The restrict qualifier gives these LDS writes
-// an alias scope of their own, so the compiler's wait-count pass does not
-// make the other stage's operand reads wait for them.
+// The loads of one K step into stage `dst`: 64 instructions of 1 KiB, 8 per
+// wave, 4 of x and 4 of W; instruction j = 4 wave + q % 4 covers rows 8 j ..
+// 8 j + 7, lane -> row 8 j + lane / 8, 16-byte chunk lane % 8 of the row's
+// LDS slot.  A lane's LDS slot is fixed by the instruction (lane * 16 from
+// the wave-uniform base), so the swizzle is applied on the global side: the
+// slot holds logical chunk (lane % 8) ^ swz(row), swz(row) = (row & 7) ^
+// ((row >> 3) & 1) = (lane / 8) ^ (j & 1).  Rows past M read out of range
+// (zero, or stale LDS): they only feed output rows that are never stored.
+// The restrict qualifier gives these LDS writes an alias scope of their own,
+// so the compiler's wait-count pass does not make the other stage's operand
+// reads wait for them.
 __device__ __forceinline__ void big_load_stage(lds_char* __restrict__ dst, const BigLoads& c,
                                                int k0) {
 #pragma unroll
-  for (int q = 0; q < 16; ++q) {
-    const int j = q & 7;
-    lds_char* d = dst + (q >> 3) * kBigABytes + c.wave * 8192 + j * 1024;
+  for (int q = 0; q < 8; ++q) {
+    const int j = 4 * c.wave + (q & 3);
+    lds_char* d = dst + (q >> 2) * kBigABytes + j * 1024;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(
-        (q >> 3) ? c.wr : c.xr, reinterpret_cast<__attribute__((address_space(3))) void*>(d), 16,
-        (j & 1) ? c.v1 : c.v0, k0 * 2 + (64 * c.wave + 8 * j) * c.K * 2, 0, 0);
+        (q >> 2) ? c.wr : c.xr, reinterpret_cast<__attribute__((address_space(3))) void*>(d), 16,
+        (q & 1) ? c.v1 : c.v0, k0 * 2 + 8 * j * c.K * 2, 0, 0);
   }
 }
 
 // One K step of 64 on stage `cur` (4 sub-steps of 16), with the next step's
-// loads into `nxt` issued first.  Operands of sub-step ks + 1 are read while
-// the 16 MFMAs of sub-step ks run; the sum of squares of the x operands is
-// spread between the MFMAs.
+// loads into `nxt` issued first.  Each wave owns a 128 x 64 block of the
+// output (4 x 2 MFMA tiles); the operands of sub-step ks + 1 are read while
+// the 8 MFMAs of sub-step ks run, at raised wave priority so that the
+// SIMD's other wave fills the gaps rather than delaying the matrix work.
 __device__ __forceinline__ void big_step(const lds_char* __restrict__ cur, lds_char* __restrict__ nxt,
                                          const BigLoads& c, int k_next, bool load, int arow,
-                                         int brow, const int (&ko)[4], f32x16 (&acc)[4][4],
-                                         float (&ss)[4]) {
+                                         int brow, const int (&ko)[4], f32x16 (&acc)[4][2]) {
   if (load) big_load_stage(nxt, c, k_next);
-  u32x4 af[2][4], bfr[2][4];
+  u32x4 af[2][4], bfr[2][2];
   auto read = [&](int ks, int b) {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
       af[b][i] = *reinterpret_cast<const lds_u32x4*>(cur + (arow + i * 32) * 128 + ko[ks]);
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < 2; ++j)
       bfr[b][j] = *reinterpret_cast<const lds_u32x4*>(cur + kBigABytes + (brow + j * 32) * 128 + ko[ks]);
   };
   read(0, 0);
@@ -266,45 +270,28 @@ __device__ __forceinline__ void big_step(const lds_char* __restrict__ cur, lds_c
   for (int ks = 0; ks < 4; ++ks) {
     const int b = ks & 1;
     if (ks < 3) read(ks + 1, b ^ 1);
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int d = 0; d < 4; ++d) {
-        const float lo = __uint_as_float(af[b][i][d] << 16);
-        const float hi = __uint_as_float(af[b][i][d] & 0xffff0000u);
-        ss[i] = fmaf(lo, lo, fmaf(hi, hi, ss[i]));
-      }
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
+      for (int j = 0; j < 2; ++j)
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_frag(af[b][i]), as_frag(bfr[b][j]),
                                                            acc[i][j], 0, 0, 0);
-    // scheduling: the next sub-step's 8 operand reads, then each MFMA
-    // followed by 4 of the sum-of-squares VALU instructions
-    if (ks < 3) __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
-#pragma unroll
-    for (int q = 0; q < 16; ++q) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
-    }
+    __builtin_amdgcn_s_setprio(0);
+    // scheduling: the next sub-step's 6 operand reads, then the 8 MFMAs
+    if (ks < 3) __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
   }
 }
 
-// Row sums of squares and the output tile.  Each wave's ss[i] covers its row
-// fr + 32 i of its row half over half of each K sub-step (lanes l and l ^ 32
-// hold the two halves); both waves of a row half hold the same sums.
-constexpr int kGroupM = 8;  // row tiles per tile group of the workgroup order
-
-__global__ void __launch_bounds__(kThreads)
+__global__ void __launch_bounds__(kBigThreads)
 rmsnorm_linear_tile256_kernel(const bf16* __restrict__ x, const bf16* __restrict__ W,
-                              bf16* __restrict__ out, float* inv_rms, int M, int N, int K,
-                              float eps, int tiles_m, int tiles_n) {
+                              bf16* __restrict__ out, const float* __restrict__ rin, int M, int N,
+                              int K, int tiles_m, int tiles_n) {
   // two LDS stages as separate arrays: the loads into one and the operand
   // reads of the other are then provably disjoint
   __shared__ __align__(1024) char st0[kBigStage];
   __shared__ __align__(1024) char st1[kBigStage];
-  __shared__ float ssrow[kBig];
   __shared__ float rrow[kBig];
 
   // tile order: XCD (workgroup id mod 8) takes a contiguous run of tile
@@ -320,7 +307,7 @@ rmsnorm_linear_tile256_kernel(const bf16* __restrict__ x, const bf16* __restrict
   const int m0 = mt * kBig, n0 = nt * kBig;
 
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
-  const int wm = wave >> 1, wn_ = wave & 1;
+  const int wm = wave >> 2, wn_ = wave & 3;  // 2 x 4 waves of 128 x 64 outputs
   const int xrows = min(M - m0, kBig);
   BigLoads c;
   c.xr = make_rsrc(x + static_cast<int64_t>(m0) * K, static_cast<uint32_t>(xrows * K * 2));
@@ -330,6 +317,7 @@ rmsnorm_linear_tile256_kernel(const bf16* __restrict__ x, const bf16* __restrict
   c.v0 = lr * K * 2 + 16 * (pc ^ lr);
   c.v1 = lr * K * 2 + 16 * (pc ^ lr ^ 1);
   c.K = K;
+  if (t < kBig) rrow[t] = t < xrows ? rin[m0 + t] : 0.0f;
 
   // operand reads: lane l takes A row (and B column) l % 32 of each 32-tile,
   // k chunk 2 ks + l / 32 of the step, at physical chunk ^ swz(row)
@@ -338,16 +326,15 @@ rmsnorm_linear_tile256_kernel(const bf16* __restrict__ x, const bf16* __restrict
   int ko[4];
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) ko[ks] = ((2 * ks + h) ^ sw) * 16;
-  const int arow = wm * 128 + fr, brow = wn_ * 128 + fr;
+  const int arow = wm * 128 + fr, brow = wn_ * 64 + fr;
 
-  f32x16 acc[4][4];
+  f32x16 acc[4][2];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
-  float ss[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 
   lds_char* const l0 = (lds_char*)st0;  // generic -> LDS address space
   lds_char* const l1 = (lds_char*)st1;
@@ -360,31 +347,17 @@ rmsnorm_linear_tile256_kernel(const bf16* __restrict__ x, const bf16* __restrict
   for (; kt + 2 <= nk; kt += 2) {
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    big_step(l0, l1, c, (kt + 1) * BK, true, arow, brow, ko, acc, ss);
+    big_step(l0, l1, c, (kt + 1) * BK, true, arow, brow, ko, acc);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    big_step(l1, l0, c, (kt + 2) * BK, kt + 2 < nk, arow, brow, ko, acc, ss);
+    big_step(l1, l0, c, (kt + 2) * BK, kt + 2 < nk, arow, brow, ko, acc);
   }
   if (kt < nk) {
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    big_step(l0, l1, c, 0, false, arow, brow, ko, acc, ss);
+    big_step(l0, l1, c, 0, false, arow, brow, ko, acc);
   }
   __syncthreads();  // every operand read done: the stages take the output tile
-
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    float v = ss[i];
-    v += __shfl_xor(v, 32);
-    if (h == 0 && wn_ == 0) ssrow[wm * 128 + i * 32 + fr] = v;
-  }
-  __syncthreads();
-  if (t < kBig) {
-    const float r = rsqrtf(ssrow[t] / static_cast<float>(K) + eps);
-    rrow[t] = r;
-    if (nt == 0 && inv_rms != nullptr && m0 + t < M) inv_rms[m0 + t] = r;
-  }
-  __syncthreads();
 
   // scaled accumulators -> bf16 output tile: rows of row half wm in stage
   // array wm (128 rows x 32 chunks of 16 bytes), chunk index XOR 4 (bit 2 of
@@ -396,11 +369,11 @@ rmsnorm_linear_tile256_kernel(const bf16* __restrict__ x, const bf16* __restrict
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+      for (int j = 0; j < 2; ++j)
 #pragma unroll
         for (int e = 0; e < 16; e += 2) {
           const int rl = i * 32 + 8 * (e / 4) + 4 * h + (e % 4);
-          const int cc = wn_ * 128 + j * 32 + fr;
+          const int cc = wn_ * 64 + j * 32 + fr;
           const uint32_t p = pack_bf16x2(acc[i][j][e] * rrow[wm * 128 + rl],
                                          acc[i][j][e + 1] * rrow[wm * 128 + rl + 1]);
           const int s0 = ((rl >> 2) & 1) << 2, s1 = (((rl + 1) >> 2) & 1) << 2;
@@ -413,12 +386,31 @@ rmsnorm_linear_tile256_kernel(const bf16* __restrict__ x, const bf16* __restrict
   const rsrc_t orr = make_rsrc(out + static_cast<int64_t>(m0) * N,
                                static_cast<uint32_t>(xrows * N * 2));
 #pragma unroll 4
-  for (int q = t; q < kBig * 32; q += kThreads) {
+  for (int q = t; q < kBig * 32; q += kBigThreads) {
     const int row = q >> 5, ch = q & 31, rl = row & 127;
     const uint16_t* Cs = reinterpret_cast<const uint16_t*>(row < 128 ? st0 : st1);
     const u32x4 v = *reinterpret_cast<const u32x4*>(Cs + rl * kBig + ((ch ^ (((rl >> 2) & 1) << 2)) << 3));
     __builtin_amdgcn_raw_buffer_store_b128(v, orr, (row * N + n0 + 8 * ch) * 2, 0, kStream);
   }
+}
+
+// Row statistics of the tile256 path: r_m = 1/sqrt(mean_k x[m][k]^2 + eps),
+// one wave per row, fp32 sums of 16-byte chunks.
+__global__ void __launch_bounds__(256)
+row_inv_rms_kernel(const bf16* __restrict__ x, float* __restrict__ r, int M, int K, float eps) {
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+  if (row >= M) return;
+  const rsrc_t xr = make_rsrc(x + static_cast<int64_t>(row) * K, static_cast<uint32_t>(K) * 2u);
+  float s = 0.0f;
+  for (int c = lane; c < K / 8; c += 64) {
+    float f[8];
+    unpack<bf16>(__builtin_amdgcn_raw_buffer_load_b128(xr, c * 16, 0, kStream), f);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) s = fmaf(f[e], f[e], s);
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) s += __shfl_xor(s, o);
+  if (lane == 0) r[row] = rsqrtf(s / static_cast<float>(K) + eps);
 }
 
 // W_folded[n][k] = bf16(W[n][k] (w_k + w_add)), 8 elements per lane.
@@ -464,9 +456,14 @@ hipError_t launch_fold_norm_weight(const void* wn, const void* W, void* Wf, int6
 }
 
 hipError_t launch_rmsnorm_linear(const void* x, const void* wn, const void* W, void* out,
-                                 float* inv_rms, void* wfold, int M, int N, int K, float eps,
+                                 float* inv_rms, void* ws, int M, int N, int K, float eps,
                                  float w_add, int tile, hipStream_t st) {
   if (tile != 2) return launch_tile<2, 2>(x, wn, W, out, inv_rms, M, N, K, eps, w_add, st);
+  // workspace: r (M fp32, when inv_rms is NULL), then the folded weight
+  float* r = inv_rms != nullptr ? inv_rms : static_cast<float*>(ws);
+  void* wfold = static_cast<char*>(ws) + linear_rows_bytes(M);
+  hipLaunchKernelGGL(row_inv_rms_kernel, dim3(static_cast<unsigned>((M + 3) / 4)), dim3(256), 0, st,
+                     static_cast<const bf16*>(x), r, M, K, eps);
   const void* Wop = W;
   if (wn != nullptr) {
     const hipError_t e = launch_fold_norm_weight(wn, W, wfold, N, K, w_add, st);
@@ -476,9 +473,9 @@ hipError_t launch_rmsnorm_linear(const void* x, const void* wn, const void* W, v
   const int tiles_m = (M + kBig - 1) / kBig, tiles_n = N / kBig;
   hipLaunchKernelGGL(rmsnorm_linear_tile256_kernel,
                      dim3(static_cast<unsigned>(static_cast<int64_t>(tiles_m) * tiles_n)),
-                     dim3(kThreads), 0, st, static_cast<const bf16*>(x),
-                     static_cast<const bf16*>(Wop), static_cast<bf16*>(out), inv_rms, M, N, K, eps,
-                     tiles_m, tiles_n);
+                     dim3(kBigThreads), 0, st, static_cast<const bf16*>(x),
+                     static_cast<const bf16*>(Wop), static_cast<bf16*>(out), r, M, N, K, tiles_m,
+                     tiles_n);
   return hipGetLastError();
 }
 

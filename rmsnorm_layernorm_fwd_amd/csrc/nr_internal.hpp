@@ -92,10 +92,13 @@ hipError_t launch_rope(int dt, const RopePlan& pl, void* x, const float* cos_tab
 hipError_t launch_rope_table_1d(float* cos_tab, float* sin_tab, int64_t tokens, int head_dim,
                                 int64_t pos0, double theta, hipStream_t st);
 // tile: 1 = 128 x 128 outputs per workgroup (W scaled by the norm weight in
-// the kernel), 2 = 256 x 256 (N % 256 == 0; with a norm weight, W folded
-// into wfold, N K bf16, first)
+// the kernel, no workspace), 2 = 256 x 256 (N % 256 == 0): the row
+// statistics first (into inv_rms, else the workspace's first
+// linear_rows_bytes(M) bytes), then with a norm weight W folded into the
+// workspace after them (N K bf16)
+inline size_t linear_rows_bytes(int64_t M) { return static_cast<size_t>((M * 4 + 255) / 256 * 256); }
 hipError_t launch_rmsnorm_linear(const void* x, const void* wn, const void* W, void* out,
-                                 float* inv_rms, void* wfold, int M, int N, int K, float eps,
+                                 float* inv_rms, void* ws, int M, int N, int K, float eps,
                                  float w_add, int tile, hipStream_t st);
 // Wf[n][k] = bf16(W[n][k] (wn[k] + w_add)); N K % 8 == 0, 16-byte aligned
 hipError_t launch_fold_norm_weight(const void* wn, const void* W, void* Wf, int64_t N, int K,

@@ -86,10 +86,13 @@ def test_workspace_bytes():
 
 
 def test_linear_workspace_bytes():
-    # the folded weight (N K bf16) on the 256 x 256 path: N % 256 == 0 and at
-    # least 1024 such tiles; none without a norm weight or on the 128 x 128 path
-    assert nr.nr_rmsnorm_linear_workspace_bytes(65536, 5120, 5120, True) == 5120 * 5120 * 2
-    assert nr.nr_rmsnorm_linear_workspace_bytes(65536, 5120, 5120, False) == 0
+    # the 256 x 256 path (N % 256 == 0, at least 1024 such tiles): the row
+    # statistics (M fp32, rounded up to 256 bytes), then the folded weight
+    # (N K bf16) when there is a norm weight; nothing on the 128 x 128 path
+    rows = lambda m: (m * 4 + 255) // 256 * 256
+    assert nr.nr_rmsnorm_linear_workspace_bytes(65536, 5120, 5120, True) == rows(65536) + 5120 * 5120 * 2
+    assert nr.nr_rmsnorm_linear_workspace_bytes(65536, 5120, 5120, False) == rows(65536)
+    assert nr.nr_rmsnorm_linear_workspace_bytes(65537, 5120, 64, False) == rows(65537)
     assert nr.nr_rmsnorm_linear_workspace_bytes(3840, 5120, 5120, True) == 0
     assert nr.nr_rmsnorm_linear_workspace_bytes(65536, 5120 + 128, 5120, True) == 0
     assert nr.nr_rmsnorm_linear_workspace_bytes(0, 5120, 5120, True) == 0
@@ -165,13 +168,18 @@ def test_rejected_calls_return_status(lib):
     assert lin(BF16, None, None, None, None, None, 0, 128, 64, 1e-6, 0, None, 0, None) == NR_OK
     # the 256 x 256 path with a norm weight needs the folded-weight workspace
     # (N K bf16), aligned and apart from the operands
-    BX, BW, BO, BN_, BS = 1 << 34, 1 << 36, 1 << 38, 1 << 40, 1 << 41
+    BX, BW, BO, BN_, BS, BR = 1 << 34, 1 << 36, 1 << 38, 1 << 40, 1 << 41, 1 << 42
     big = (65536, 5120, 64, 1e-6, 0)
-    need = 5120 * 64 * 2
-    assert lin(BF16, BX, BN_, BW, BO, None, *big, None, 0, None) == NR_ERR_WORKSPACE
-    assert lin(BF16, BX, BN_, BW, BO, None, *big, BS, need - 16, None) == NR_ERR_WORKSPACE
-    assert lin(BF16, BX, BN_, BW, BO, None, *big, BS + 8, need, None) == NR_ERR_WORKSPACE
-    assert lin(BF16, BX, BN_, BW, BO, None, *big, BW + 1024, need, None) == NR_ERR_ALIAS
+    need = 65536 * 4 + 5120 * 64 * 2
+    assert lin(BF16, BX, BN_, BW, BO, BR, *big, None, 0, None) == NR_ERR_WORKSPACE
+    assert lin(BF16, BX, BN_, BW, BO, BR, *big, BS, need - 16, None) == NR_ERR_WORKSPACE
+    assert lin(BF16, BX, BN_, BW, BO, BR, *big, BS + 8, need, None) == NR_ERR_WORKSPACE
+    assert lin(BF16, BX, BN_, BW, BO, BR, *big, BW + 1024, need, None) == NR_ERR_ALIAS
+    assert lin(BF16, BX, BN_, BW, BO, BR, *big, BR - 1024, need, None) == NR_ERR_ALIAS
+    # without a norm weight the workspace holds the row statistics only, and
+    # is not needed when inv_rms takes them
+    assert lin(BF16, BX, None, BW, BO, None, *big, None, 0, None) == NR_ERR_WORKSPACE
+    assert lin(BF16, BX, None, BW, BO, None, *big, BS, 65536 * 4 - 4, None) == NR_ERR_WORKSPACE
     # forcing the 256 x 256 tile where N is not a multiple of 256
     assert L.nr_tune(b"gemm_tile", 2) == NR_OK
     try:

@@ -110,7 +110,7 @@ def test_rmsnorm_linear_tiles_agree_and_workspace_is_reused():
     with gemm_tile(2):
         ws = torch.empty(nr.nr_rmsnorm_linear_workspace_bytes(m, n, k, True), dtype=torch.uint8,
                          device=DEV)
-        assert ws.numel() == n * k * 2
+        assert ws.numel() == m * 4 + n * k * 2
         b, rb = nr.rmsnorm_linear_fwd(x, w, W, workspace=ws)
         c, rc = nr.rmsnorm_linear_fwd(x, w, W, workspace=ws)
     torch.cuda.synchronize()
