@@ -15,8 +15,8 @@ DEV = "cuda"
 
 
 def test_graph_replays_match_eager():
-    print("[case] graph capture: rms / ln / ln+gelu / rope / fused rms+rope, 515x1280 bf16",
-          flush=True)
+    print("[case] graph capture: rms / ln / ln+gelu / rope / fused rms+rope / rms->linear, "
+          "515x1280 bf16", flush=True)
     rows, n, h, d = 515, 1280, 10, 128
     x = workloads.normal((rows, n), 9700, torch.bfloat16).to(DEV)
     w = workloads.normal((n,), 9701, torch.bfloat16, mean=1.0, std=0.1).to(DEV)
@@ -36,7 +36,16 @@ def test_graph_replays_match_eager():
         y4=torch.empty_like(x), r4=torch.empty(rows, **f32), dx4=torch.empty_like(x),
         dw4=torch.empty(n, **f32),
         e1=torch.empty(n, **f32),
+        o5=torch.empty(rows, 512, dtype=torch.bfloat16, device=DEV), r5=torch.empty(rows, **f32),
+        o6=torch.empty(rows, 512, dtype=torch.bfloat16, device=DEV), r6=torch.empty(rows, **f32),
     )
+    Wl = workloads.normal((512, n), 9704, torch.bfloat16, std=n ** -0.5).to(DEV)
+    nr.nr_tune("gemm_tile", 2)
+    try:
+        wsl = torch.empty(nr.nr_rmsnorm_linear_workspace_bytes(rows, 512, n, True),
+                          dtype=torch.uint8, device=DEV)
+    finally:
+        nr.nr_tune("gemm_tile", 0)
     empty = torch.empty((0, n), dtype=torch.bfloat16, device=DEV)
     e_r = torch.empty(0, **f32)
 
@@ -55,6 +64,14 @@ def test_graph_replays_match_eager():
         nr.rmsnorm_rope_fwd(x, w, ct, st, d, 1, 1e-6, y=o["y4"], inv_rms=o["r4"])
         nr.rmsnorm_rope_bwd(dy, x, w, o["r4"], ct, st, d, 1, dx=o["dx4"], dw=o["dw4"],
                             workspace=ws)
+        # RMSNorm -> linear on both kernels (the 256 x 256 one: statistics,
+        # weight fold and GEMM, three launches)
+        nr.rmsnorm_linear_fwd(x, w, Wl, out=o["o5"], inv_rms=o["r5"])
+        nr.nr_tune("gemm_tile", 2)
+        try:
+            nr.rmsnorm_linear_fwd(x, w, Wl, out=o["o6"], inv_rms=o["r6"], workspace=wsl)
+        finally:
+            nr.nr_tune("gemm_tile", 0)
         # an empty batch: its column gradient (zeros) comes from a kernel
         o["e1"].fill_(7.0)
         nr.rmsnorm_bwd(empty, empty, w, e_r, dx=torch.empty_like(empty), dw=o["e1"],
