@@ -196,16 +196,22 @@ nr_status_t plan_bwd(nr_dtype_t dt, bool ln, int64_t rows, int64_t n, bool align
   // row per batch, two batches ahead)
   int D = (!ln && !rope && K == 1) ? 2 : 1;
   int PF = ((!ln || gelu) && K == 1) ? 2 : 1;
+  // LayerNorm rows of one chunk per lane and at most 10 waves: one workgroup
+  // per CU with three batches in flight (65536 x 5120 bf16: 347 -> 333 us
+  // against two workgroups per CU with one batch each)
+  if (ln && !gelu && !rope && K == 1 && (need + K - 1) / K <= 10) PF = 3;
   if (tune(BWD_D) > 0) D = tune(BWD_D);
   if (tune(BWD_PF) > 0) PF = tune(BWD_PF);
   if (!in_set(K, kBwdK, 4) || !in_set(D, kBwdD, 4) || K * D > 8 || W < 1 || W > 16)
     return NR_ERR_SHAPE;
-  if (PF < 1 || PF > 2) return NR_ERR_SHAPE;
+  // deeper prefetch (3 or 4 batches) only for one chunk per lane, at most 2
+  // rows per batch and 10 waves (one workgroup per CU)
+  if (PF < 1 || PF > 4 || (PF > 2 && (K != 1 || D > 2 || W > 10))) return NR_ERR_SHAPE;
   if (static_cast<int64_t>(64) * W * K < nchunk) return NR_ERR_SHAPE;
   // two resident workgroups per CU only when two of them fit: 2 W waves
   // over the CU's 4 SIMDs at the kernels' ~76-100 VGPRs allow W <= 10
   int64_t P, rpb;
-  bwd_grid(rows, ((ln && !gelu) || rope) && W <= 10, &P, &rpb);
+  bwd_grid(rows, ((ln && !gelu) || rope) && W <= 10 && PF <= 2, &P, &rpb);
   *pl = BwdPlan{W, K, D, static_cast<int>(P), PF, rpb, aligned};
   return NR_OK;
 }

@@ -224,8 +224,11 @@ __device__ __forceinline__ void process_batch(RowBatch<T, K, D, ROPE ? 1 : 0>& b
   }
 }
 
-template <typename T, int K, int D, int PF, bool VEC, bool LN, int EPI>
-__global__ void __launch_bounds__(1024)
+// LB: the largest workgroup the instantiation serves.  1024 (16 waves) caps
+// a lane at 128 VGPRs; the deep-prefetch instantiations (PF 3, 4) take at
+// most 10 waves, i.e. one workgroup per CU, which leaves up to 168.
+template <typename T, int K, int D, int PF, bool VEC, bool LN, int EPI, int LB = 1024>
+__global__ void __launch_bounds__(LB)
 norm_bwd_rows(const T* dy, const T* x, const T* w, const T* beta, const float* mean,
               const float* rstat, T* dx, float* part, int64_t part_stride, int64_t rows, int n,
               float w_add, RopeArgs ra) {
@@ -333,6 +336,13 @@ hipError_t launch_bwd_kd(const BwdPlan& pl, const void* dy, const void* x, const
                          hipStream_t st) {
   const int64_t part_stride = static_cast<int64_t>(pl.P) * n;
   auto kern = pl.PF == 2 ? norm_bwd_rows<T, K, D, 2, A, LN, EP> : norm_bwd_rows<T, K, D, 1, A, LN, EP>;
+  if constexpr (K == 1 && D <= 2) {
+    if (pl.PF >= 3) {
+      if (pl.W > 10) return hipErrorInvalidValue;
+      kern = pl.PF == 3 ? norm_bwd_rows<T, K, D, 3, A, LN, EP, 640>
+                        : norm_bwd_rows<T, K, D, 4, A, LN, EP, 640>;
+    }
+  }
   hipLaunchKernelGGL(kern, dim3(pl.P), dim3(64 * pl.W), 0, st, static_cast<const T*>(dy),
                      static_cast<const T*>(x), static_cast<const T*>(w),
                      static_cast<const T*>(beta), mean, rstat, static_cast<T*>(dx), part,
