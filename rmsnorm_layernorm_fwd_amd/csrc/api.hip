@@ -196,10 +196,12 @@ nr_status_t plan_bwd(nr_dtype_t dt, bool ln, int64_t rows, int64_t n, bool align
   // row per batch, two batches ahead)
   int D = (!ln && !rope && K == 1) ? 2 : 1;
   int PF = ((!ln || gelu) && K == 1) ? 2 : 1;
-  // LayerNorm rows of one chunk per lane and at most 10 waves: one workgroup
-  // per CU with three batches in flight (65536 x 5120 bf16: 347 -> 333 us
-  // against two workgroups per CU with one batch each)
-  if (ln && !gelu && !rope && K == 1 && (need + K - 1) / K <= 10) PF = 3;
+  // LayerNorm, and the fused RMSNorm + RoPE backward, on rows of one chunk
+  // per lane and at most 10 waves: one workgroup per CU with three batches
+  // in flight (65536 x 5120 bf16: LayerNorm 347 -> 333 us against two
+  // workgroups per CU with one batch each, RMSNorm + RoPE 343 -> 336 us
+  // against two per CU with two batches each)
+  if (((ln && !gelu) || rope) && K == 1 && (need + K - 1) / K <= 10) PF = 3;
   if (tune(BWD_D) > 0) D = tune(BWD_D);
   if (tune(BWD_PF) > 0) PF = tune(BWD_PF);
   if (!in_set(K, kBwdK, 4) || !in_set(D, kBwdD, 4) || K * D > 8 || W < 1 || W > 16)
