@@ -45,7 +45,15 @@ extern "C" {
 /* Storage type of the row / token tensors and their weights.  Arithmetic is
  * fp32 whatever the storage type; each stored result is rounded once, to
  * nearest even. */
-typedef enum { NR_F32 = 0, NR_BF16 = 1, NR_F16 = 2 /* IEEE binary16 */ } nr_dtype_t;
+typedef enum {
+  NR_F32 = 0,
+  NR_BF16 = 1,
+  NR_F16 = 2, /* IEEE binary16 */
+  /* not dtypes: they make every int a value of the type, so an unknown code
+     passed in is rejected (NR_ERR_DTYPE) rather than out of the type's range */
+  NR_DTYPE_RANGE_MIN_ = -0x7fffffff - 1,
+  NR_DTYPE_RANGE_MAX_ = 0x7fffffff
+} nr_dtype_t;
 
 typedef enum {
   NR_OK = 0,
@@ -56,7 +64,11 @@ typedef enum {
   NR_ERR_WORKSPACE = 5,     /* workspace missing, too small or not 16-byte aligned */
   NR_ERR_HIP = 6,           /* the HIP runtime refused a launch */
   NR_ERR_ALIAS = 7,         /* an output partially overlaps an input */
-  NR_ERR_TUNE = 8           /* unknown tuning key or value */
+  NR_ERR_TUNE = 8,          /* unknown tuning key or value */
+  /* not statuses: every int is a value of the type (nr_status_str of an
+     unknown code returns a description saying so) */
+  NR_STATUS_RANGE_MIN_ = -0x7fffffff - 1,
+  NR_STATUS_RANGE_MAX_ = 0x7fffffff
 } nr_status_t;
 
 /* Largest row length the norm kernels accept: 65536 (bf16, fp16), 32768 (fp32). */

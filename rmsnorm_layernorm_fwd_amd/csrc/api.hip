@@ -259,6 +259,7 @@ const char* nr_status_str(nr_status_t s) {
     case NR_ERR_HIP: return "HIP launch failed";
     case NR_ERR_ALIAS: return "output partially overlaps an input";
     case NR_ERR_TUNE: return "unknown tuning key or value";
+    default: break;
   }
   return "unknown status";
 }
