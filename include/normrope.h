@@ -255,7 +255,7 @@ nr_status_t layernorm_gelu_bwd(nr_dtype_t dt, const void* dout, const void* x,
  * Shapes: K a multiple of 64 (at most 65536), N a multiple of 128, any M;
  * x, W, out and w_norm 16-byte aligned (else NR_ERR_SHAPE); out may not
  * overlap x or W.
- * Workspace: on large grids (N a multiple of 256) the call first computes
+ * Workspace: when N is a multiple of 256 the call first computes
  * the row statistics (into inv_rms, or the workspace's first ceil(4 M /
  * 256) 256 bytes when inv_rms is NULL) and, with a norm weight, writes the
  * folded weight w'_k W[n][k] (N K bf16) into the workspace after them;

@@ -13,7 +13,8 @@
 //
 // gfx950 mapping, two kernels with v_mfma_f32_32x32x16_bf16:
 //  - tile256: a 256 x 256 output tile per 8-wave workgroup (2 waves per
-//    SIMD, each wave 128 x 64, 4 x 2 MFMA tiles) for large grids.  The row
+//    SIMD, each wave 128 x 64, 4 x 2 MFMA tiles) when N is a multiple of
+//    256.  The row
 //    statistics come from a light pass over x (row_inv_rms_kernel) and the
 //    norm weight is folded into W beforehand (fold_norm_weight_kernel,
 //    w'_k W[n][k] rounded once to bf16, into a caller workspace), so both
@@ -23,8 +24,8 @@
 //    one, one barrier per stage.  LDS rows are 128 bytes, 16-byte chunk
 //    index XOR-swizzled by the row so the operand reads of 16 consecutive
 //    rows hit distinct banks.  r_m scales the accumulators in the epilogue.
-//  - tile128: a 128 x 128 tile per 4-wave workgroup for grids too small to
-//    fill the GPU with 256 x 256 tiles; operands staged through VGPRs, W
+//  - tile128: a 128 x 128 tile per 4-wave workgroup for the other N (a
+//    multiple of 128); operands staged through VGPRs, W
 //    scaled by the norm weight on the way into LDS, the row sums of squares
 //    taken from the staged x (no workspace).
 // Both number the workgroups so that each of the 8 XCDs (own L2 each) works

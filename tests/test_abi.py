@@ -86,14 +86,15 @@ def test_workspace_bytes():
 
 
 def test_linear_workspace_bytes():
-    # the 256 x 256 path (N % 256 == 0, at least 1024 such tiles): the row
-    # statistics (M fp32, rounded up to 256 bytes), then the folded weight
-    # (N K bf16) when there is a norm weight; nothing on the 128 x 128 path
+    # the 256 x 256 path (N % 256 == 0): the row statistics (M fp32, rounded
+    # up to 256 bytes), then the folded weight (N K bf16) when there is a
+    # norm weight; nothing on the 128 x 128 path
     rows = lambda m: (m * 4 + 255) // 256 * 256
     assert nr.nr_rmsnorm_linear_workspace_bytes(65536, 5120, 5120, True) == rows(65536) + 5120 * 5120 * 2
     assert nr.nr_rmsnorm_linear_workspace_bytes(65536, 5120, 5120, False) == rows(65536)
     assert nr.nr_rmsnorm_linear_workspace_bytes(65537, 5120, 64, False) == rows(65537)
-    assert nr.nr_rmsnorm_linear_workspace_bytes(3840, 5120, 5120, True) == 0
+    assert nr.nr_rmsnorm_linear_workspace_bytes(3840, 5120, 5120, True) == rows(3840) + 5120 * 5120 * 2
+    assert nr.nr_rmsnorm_linear_workspace_bytes(1, 256, 64, True) == 256 + 256 * 64 * 2
     assert nr.nr_rmsnorm_linear_workspace_bytes(65536, 5120 + 128, 5120, True) == 0
     assert nr.nr_rmsnorm_linear_workspace_bytes(0, 5120, 5120, True) == 0
 
