@@ -281,8 +281,8 @@ size_t nr_rmsnorm_linear_workspace_bytes(int64_t M, int64_t N, int64_t K, int ha
  * its own: W_folded[n][k] = bf16(W[n][k] w'_k), w'_k = w_k or 1 + w_k
  * (gemma_offset), one rounding.  For callers whose weights do not change
  * between calls: rmsnorm_linear_fwd(x, NULL, W_folded, ...) then gives the
- * same output, bit for bit, as rmsnorm_linear_fwd(x, w_norm, W, ...) and
- * needs no workspace.  bf16 only; K a multiple of 8 (at most 65536), N at
+ * same output, bit for bit, as rmsnorm_linear_fwd(x, w_norm, W, ...) without
+ * folding the weight again (and needs no workspace room for it).  bf16 only; K a multiple of 8 (at most 65536), N at
  * most 2^22; all three pointers 16-byte aligned; W_folded may be W (in
  * place) but may not partly overlap it or overlap w_norm.
  */
