@@ -45,9 +45,10 @@ def run_case(tag, m, n, k, seed, weight="w", gemma=False, rows=None):
     torch.cuda.synchronize()
     sel = np.arange(m) if rows is None else rows
     R, rr, S = oracle.rmsnorm_linear(x[sel], w, W, 1e-6, gemma)
-    O = out.cpu()[sel]
+    idx = torch.as_tensor(sel, device=DEV)
+    O = out[idx].cpu()
     check(f"{tag} out", O, R, "bf16", s=0.0, extra=2.0 ** -8 * S)
-    check(f"{tag} inv_rms", r.cpu()[sel], rr, "stat", s=0.0)
+    check(f"{tag} inv_rms", r[idx].cpu(), rr, "stat", s=0.0)
     # the bound is not vacuous: the error is far below the magnitude sum
     err = np.abs(to64(O) - R)
     assert np.max(err / (ulp_bf16(R) + 2.0 ** -8 * S)) <= 1.0
@@ -118,6 +119,26 @@ def test_rmsnorm_linear_tiles_agree_and_workspace_is_reused():
     assert torch.allclose(ra, rb, rtol=2e-6, atol=0)
     d = (a.float() - b.float()).abs().cpu().double().numpy()
     assert np.all(d <= 2 * ulp_bf16(a.float().cpu().double().numpy()) + 1e-6)
+
+
+@pytest.mark.parametrize("tile", [1, 2])
+def test_rmsnorm_linear_widest_n(tile):
+    # N = 2^22, the largest accepted: within a row tile the output's byte
+    # offsets reach 2^31 - 16, the end of the 32-bit buffer range
+    m, n, k = 300, 1 << 22, 64
+    with gemm_tile(tile):
+        run_case(f"widest N, tile {tile}", m, n, k, 9980 + tile, "w", False,
+                 rows=np.array([0, 1, 127, 128, 255, 256, 299]))
+
+
+@pytest.mark.parametrize("tile", [1, 2])
+def test_rmsnorm_linear_longest_k(tile):
+    # K = 65536, the largest accepted: 1024 K steps, operand offsets of a
+    # 256-row tile up to 32 MiB
+    m, n, k = 300, 256, 65536
+    with gemm_tile(tile):
+        run_case(f"longest K, tile {tile}", m, n, k, 9990 + tile, "w", True,
+                 rows=np.array([0, 1, 100, 255, 256, 299]))
 
 
 def test_rmsnorm_linear_long_sequence_sampled():
