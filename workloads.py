@@ -85,6 +85,27 @@ def normal(shape, seed: int, dtype=torch.float32, mean=0.0, std=1.0,
     return _to(z, dtype)
 
 
+def normal_device(shape, seed: int, dtype=torch.bfloat16, device="cuda", mean=0.0, std=1.0,
+                  block_rows: int = 1 << 18) -> torch.Tensor:
+    """Seeded N(mean, std^2) draw made on the device, for tensors too large to
+    draw on the host (several GiB): torch's device generator seeded with
+    ``seed``, drawn in float32 blocks of rows, each rounded once to ``dtype``.
+    The same seed and shape give the same values on the same device type."""
+    gen = torch.Generator(device=device)
+    gen.manual_seed(seed)
+    out = torch.empty(shape, dtype=dtype, device=device)
+    flat = out.view(shape[0], -1)
+    for r0 in range(0, shape[0], block_rows):
+        r1 = min(shape[0], r0 + block_rows)
+        z = torch.randn((r1 - r0, flat.shape[1]), generator=gen, device=device, dtype=torch.float32)
+        if std != 1.0:
+            z.mul_(std)
+        if mean != 0.0:
+            z.add_(mean)
+        flat[r0:r1] = z.to(dtype)
+    return out
+
+
 def norm_inputs(name: str) -> dict:
     """x, weight, bias, dy for a workload's norm step (CPU tensors)."""
     wl = WORKLOADS[name]
