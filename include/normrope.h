@@ -1,7 +1,8 @@
 /*
  * normrope.h -- C ABI of libnormrope.so: single-pass fused RMSNorm and
- * LayerNorm (forward and backward) and in-place interleaved RoPE (forward
- * and inverse) for AMD Instinct MI355X (gfx950).
+ * LayerNorm (forward and backward), in-place interleaved RoPE (forward and
+ * inverse), their fusions (RMSNorm -> RoPE, LayerNorm -> GeLU) and RMSNorm
+ * folded into the following linear layer, for AMD Instinct MI355X (gfx950).
  *
  * The operations follow "Helios 性能优化全解析" (hncyxsy.com), sections
  * 内核一 FlashNorm and 内核二 FlashRoPE, and the fused LayerNorm example of
@@ -22,9 +23,10 @@
  *     error the call returns a non-zero nr_status_t and queues nothing,
  *     except NR_ERR_HIP, which reports a failed launch (see
  *     nr_last_hip_error).  rows == 0 (or tokens == 0) is a valid no-op.
- *   - Any alignment is accepted.  Rows whose start is 16-byte aligned and
- *     whose byte length is a multiple of 16 take the 128-bit load path;
- *     other shapes take an element-wise path in the same kernels.
+ *   - Any alignment is accepted by the norm and RoPE calls.  Rows whose
+ *     start is 16-byte aligned and whose byte length is a multiple of 16
+ *     take the 128-bit load path; other shapes take an element-wise path in
+ *     the same kernels.  (The linear-layer calls need 16-byte alignment.)
  *   - An output may be the very same buffer as an input of the same shape
  *     (in place, e.g. y == x, dx == dy); partial overlap is not allowed.
  *   - Backward results are bitwise reproducible: for a given shape every
