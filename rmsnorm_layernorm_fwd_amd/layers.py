@@ -46,8 +46,22 @@ def _grad_rows(g: torch.Tensor, like: torch.Tensor) -> torch.Tensor:
     return _rows(g)
 
 
-def _param_grad(g, p):
-    return None if g is None or p is None else g.to(p.dtype)
+def _param_grad(g, dtype):
+    """A weight gradient: fp32 from the kernel, returned in the parameter's
+    own dtype (no rounding for an fp32 parameter)."""
+    return None if g is None or dtype is None else g.to(dtype)
+
+
+def _as_input_dtype(p, x):
+    """The kernels take weights in the input's storage type: a parameter of
+    another dtype (fp32 master weights under bf16 activations) is cast for
+    the kernel, rounding it once; its gradient is still returned in the
+    parameter's dtype, straight from the kernel's fp32 sums."""
+    return p if p is None or p.dtype == x.dtype else p.to(x.dtype)
+
+
+def _dtype(p):
+    return None if p is None else p.dtype
 
 
 # ---------------------------------------------------------------- RMSNorm
@@ -56,9 +70,10 @@ class _RMSNormFn(torch.autograd.Function):
     @staticmethod
     def forward(ctx, x, weight, eps, gemma):
         x2 = _rows(x)
-        y, r = rmsnorm_fwd(x2, weight, eps, gemma)
-        ctx.save_for_backward(x2, weight, r)
-        ctx.gemma = gemma
+        wk = _as_input_dtype(weight, x)
+        y, r = rmsnorm_fwd(x2, wk, eps, gemma)
+        ctx.save_for_backward(x2, wk, r)
+        ctx.gemma, ctx.wdt = gemma, _dtype(weight)
         return y.view(x.shape)
 
     @staticmethod
@@ -66,7 +81,7 @@ class _RMSNormFn(torch.autograd.Function):
         x2, weight, r = ctx.saved_tensors
         want_dw = weight is not None and ctx.needs_input_grad[1]
         dx, dw = rmsnorm_bwd(_grad_rows(dy, x2), x2, weight, r, ctx.gemma, want_dw=want_dw)
-        return dx.view(dy.shape), _param_grad(dw, weight), None, None
+        return dx.view(dy.shape), _param_grad(dw, ctx.wdt), None, None
 
 
 def rms_norm(x, weight=None, eps=1e-6, gemma=False):
@@ -81,10 +96,11 @@ class _LayerNormFn(torch.autograd.Function):
     @staticmethod
     def forward(ctx, x, gamma, beta, eps, gelu):
         x2 = _rows(x)
+        gk, bk = _as_input_dtype(gamma, x), _as_input_dtype(beta, x)
         fwd = layernorm_gelu_fwd if gelu else layernorm_fwd
-        y, mu, rs = fwd(x2, gamma, beta, eps)
-        ctx.save_for_backward(x2, gamma, beta, mu, rs)
-        ctx.gelu = gelu
+        y, mu, rs = fwd(x2, gk, bk, eps)
+        ctx.save_for_backward(x2, gk, bk, mu, rs)
+        ctx.gelu, ctx.gdt, ctx.bdt = gelu, _dtype(gamma), _dtype(beta)
         return y.view(x.shape)
 
     @staticmethod
@@ -99,7 +115,7 @@ class _LayerNormFn(torch.autograd.Function):
         else:
             dx, dg, db = layernorm_bwd(g2, x2, gamma, mu, rs, want_dgamma=want_g,
                                        want_dbeta=want_b)
-        return dx.view(dy.shape), _param_grad(dg, gamma), _param_grad(db, beta), None, None
+        return dx.view(dy.shape), _param_grad(dg, ctx.gdt), _param_grad(db, ctx.bdt), None, None
 
 
 def layer_norm(x, weight=None, bias=None, eps=1e-5):
@@ -192,8 +208,10 @@ def apply_rotary_emb_interleaved(x, cos, sin=None, inplace=False):
 class _RMSNormRopeFn(torch.autograd.Function):
     @staticmethod
     def forward(ctx, x2, weight, cos, sin, head_dim, rows_per_token, eps, gemma):
-        y, r = rmsnorm_rope_fwd(x2, weight, cos, sin, head_dim, rows_per_token, eps, gemma)
-        ctx.save_for_backward(x2, weight, r, cos, sin)
+        wk = _as_input_dtype(weight, x2)
+        y, r = rmsnorm_rope_fwd(x2, wk, cos, sin, head_dim, rows_per_token, eps, gemma)
+        ctx.save_for_backward(x2, wk, r, cos, sin)
+        ctx.wdt = _dtype(weight)
         ctx.cfg = (head_dim, rows_per_token, gemma)
         return y
 
@@ -204,7 +222,7 @@ class _RMSNormRopeFn(torch.autograd.Function):
         want_dw = weight is not None and ctx.needs_input_grad[1]
         dx, dw = rmsnorm_rope_bwd(_grad_rows(dy, x2), x2, weight, r, cos, sin, head_dim, rpt,
                                   gemma, want_dw=want_dw)
-        return dx, _param_grad(dw, weight), None, None, None, None, None, None
+        return dx, _param_grad(dw, ctx.wdt), None, None, None, None, None, None
 
 
 def rms_norm_rope(x, weight, cos, sin=None, eps=1e-6, gemma=False, per_head=False):

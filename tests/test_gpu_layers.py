@@ -96,6 +96,40 @@ def test_layernorm_modules(dtype, gelu, affine):
         param_grad_check("dbeta", m.bias.grad, rdb, dtype)
 
 
+@pytest.mark.parametrize("gelu", [False, True])
+def test_fp32_parameters_with_bf16_activations(gelu):
+    # mixed precision: the module's fp32 parameters are cast to the input's
+    # bf16 for the kernel; the output equals that of a module holding the
+    # rounded parameters, and the parameters' gradients come back in fp32,
+    # straight from the kernel's fp32 sums (the bf16 module rounds them)
+    say(f"fp32 parameters, bf16 input, {'LayerNorm+GeLU' if gelu else 'RMSNorm / LayerNorm'}")
+    n = 256
+    x = workloads.normal((7, n), 9300, torch.bfloat16).to(DEV)
+    dout = workloads.normal((7, n), 9301, torch.bfloat16).to(DEV)
+    w32 = workloads.normal((n,), 9302, torch.float32, mean=1.0, std=0.1).to(DEV)
+    b32 = workloads.normal((n,), 9303, torch.float32, std=0.1).to(DEV)
+    pairs = [(L.FlashRMSNorm(n, device=DEV), L.FlashRMSNorm(n, device=DEV, dtype=torch.bfloat16))]
+    cls = L.FlashLayerNormGelu if gelu else L.FlashLayerNorm
+    pairs.append((cls(n, device=DEV), cls(n, device=DEV, dtype=torch.bfloat16)))
+    for m32, m16 in pairs:
+        with torch.no_grad():
+            m32.weight.copy_(w32)
+            m16.weight.copy_(w32.to(torch.bfloat16))
+            if getattr(m32, "bias", None) is not None:
+                m32.bias.copy_(b32)
+                m16.bias.copy_(b32.to(torch.bfloat16))
+        xa, xb = x.clone().requires_grad_(True), x.clone().requires_grad_(True)
+        ya, yb = m32(xa), m16(xb)
+        ya.backward(dout)
+        yb.backward(dout)
+        torch.cuda.synchronize()
+        assert ya.dtype == torch.bfloat16 and torch.equal(ya, yb)
+        assert torch.equal(xa.grad, xb.grad)
+        assert m32.weight.grad.dtype == torch.float32
+        assert torch.equal(m32.weight.grad.to(torch.bfloat16), m16.weight.grad)
+        assert not torch.equal(m32.weight.grad, m16.weight.grad.float())  # not rounded
+
+
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16, torch.float16])
 @pytest.mark.parametrize("inplace", [False, True])
 def test_rope_function(dtype, inplace):
