@@ -277,24 +277,26 @@ constexpr float kGeluK1 = static_cast<float>(-2.0 * kGeluCd * kLog2e * 0.044715)
 constexpr float kGeluT0 = static_cast<float>(2.0 * kGeluCd);           // 2c
 constexpr float kGeluT1 = static_cast<float>(2.0 * kGeluCd * 3.0 * 0.044715);  // 6ac
 
-// exp(-2u) for the activation's argument v.  The exponent is capped at 64:
-// beyond it the sigmoid is below 2^-64 either way, and the cap keeps
-// 1 + exp(-2u) finite so the derivative's s (1 - s) = e s^2 never meets
-// inf * 0.
-__device__ __forceinline__ float gelu_exp(float v, float cap) {
-  return __builtin_amdgcn_exp2f(fminf(v * fmaf(kGeluK1, v * v, kGeluK0), cap));
+// exp(-2u) for the activation's argument v, u = c (v + a v^3) (one v_exp_f32
+// of the base-2 exponent).  It may overflow to +inf for v << 0; both users
+// take that limit correctly, so no cap (and no v_min) is needed.
+__device__ __forceinline__ float gelu_exp(float v) {
+  return __builtin_amdgcn_exp2f(v * fmaf(kGeluK1, v * v, kGeluK0));
 }
 
 __device__ __forceinline__ float gelu_tanh(float v) {
-  // no cap needed: exp = inf gives v * 0 = -0, the limit for v -> -inf
-  return v * __builtin_amdgcn_rcpf(1.0f + gelu_exp(v, __builtin_inff()));
+  // exp = inf gives v * 0 = -0, the limit for v -> -inf
+  return v * __builtin_amdgcn_rcpf(1.0f + gelu_exp(v));
 }
 
 __device__ __forceinline__ float gelu_tanh_grad(float v) {
-  const float e = gelu_exp(v, 64.0f);
+  // s + t s (1 - s) with 1 - s formed by subtraction: exact for s >= 1/2,
+  // and for v -> -inf (exp = inf, s = 0) the product is t * 0 * 1 = 0
+  // rather than inf * 0
+  const float e = gelu_exp(v);
   const float s = __builtin_amdgcn_rcpf(1.0f + e);
   const float t = v * fmaf(kGeluT1, v * v, kGeluT0);  // 2 c v (1 + 3a v^2)
-  return fmaf(t * s, e * s, s);
+  return fmaf(t * s, 1.0f - s, s);
 }
 
 // Epilogues of the fused row kernels
