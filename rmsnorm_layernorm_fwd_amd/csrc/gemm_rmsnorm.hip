@@ -21,7 +21,9 @@
 //    operands go from HBM straight into LDS with buffer_load ... lds (no
 //    VGPR staging, no VALU on the way): two LDS stages of K 64, the next
 //    stage's loads in flight while the matrix cores work on the current
-//    one, one barrier per stage.  LDS rows are 128 bytes, 16-byte chunk
+//    one, one barrier per stage, placed before the stage's last 8 MFMAs so
+//    that they cover the next stage's first operand reads.  LDS rows are
+//    128 bytes, 16-byte chunk
 //    index XOR-swizzled by the row so the operand reads of 16 consecutive
 //    rows hit distinct banks.  r_m scales the accumulators in the epilogue.
 //  - tile128: a 128 x 128 tile per 4-wave workgroup for the other N (a
@@ -248,16 +250,37 @@ __device__ __forceinline__ void big_load_stage(lds_char* __restrict__ dst, const
   }
 }
 
-// One K step of 64 on stage `cur` (4 sub-steps of 16), with the next step's
-// loads into `nxt` issued first.  Each wave owns a 128 x 64 block of the
-// output (4 x 2 MFMA tiles); the operands of sub-step ks + 1 are read while
-// the 8 MFMAs of sub-step ks run, at raised wave priority so that the
-// SIMD's other wave fills the gaps rather than delaying the matrix work.
+// The 8 MFMAs of one sub-step of 16 (4 x 2 tiles of 32 x 32), at raised
+// wave priority so that the SIMD's other wave fills the gaps rather than
+// delaying the matrix work.
+__device__ __forceinline__ void big_mfma(const u32x4 (&a)[4], const u32x4 (&b)[2],
+                                         f32x16 (&acc)[4][2]) {
+  __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_frag(a[i]), as_frag(b[j]), acc[i][j],
+                                                         0, 0, 0);
+  __builtin_amdgcn_s_setprio(0);
+}
+
+// One K step of 64 on stage `cur` (4 sub-steps of 16), entered right after
+// the barrier that completed `cur`.  Each wave owns a 128 x 64 block of the
+// output (4 x 2 MFMA tiles).  Order: the next step's loads into `nxt`; the
+// operand reads of sub-step 0, covered by the previous step's sub-step 3
+// MFMAs (`prev`: operands still in buffer 1); then sub-steps 0..2, each
+// with the next one's reads in flight.  The step ends at the barrier, once
+// sub-step 3's operands are in registers: its MFMAs open the next step, so
+// the matrix cores have work while every wave waits for its first reads of
+// the new stage.  The barrier also frees `cur` for the loads issued next.
 __device__ __forceinline__ void big_step(const lds_char* __restrict__ cur, lds_char* __restrict__ nxt,
-                                         const BigLoads& c, int k_next, bool load, int arow,
-                                         int brow, const int (&ko)[4], f32x16 (&acc)[4][2]) {
+                                         const BigLoads& c, int k_next, bool load, bool prev,
+                                         int arow, int brow, const int (&ko)[4],
+                                         f32x16 (&acc)[4][2], u32x4 (&af)[2][4],
+                                         u32x4 (&bfr)[2][2]) {
   if (load) big_load_stage(nxt, c, k_next);
-  u32x4 af[2][4], bfr[2][2];
+  __builtin_amdgcn_sched_barrier(0);
   auto read = [&](int ks, int b) {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -267,22 +290,23 @@ __device__ __forceinline__ void big_step(const lds_char* __restrict__ cur, lds_c
       bfr[b][j] = *reinterpret_cast<const lds_u32x4*>(cur + kBigABytes + (brow + j * 32) * 128 + ko[ks]);
   };
   read(0, 0);
-#pragma unroll
-  for (int ks = 0; ks < 4; ++ks) {
-    const int b = ks & 1;
-    if (ks < 3) read(ks + 1, b ^ 1);
-    __builtin_amdgcn_s_setprio(1);
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_frag(af[b][i]), as_frag(bfr[b][j]),
-                                                           acc[i][j], 0, 0, 0);
-    __builtin_amdgcn_s_setprio(0);
-    // scheduling: the next sub-step's 6 operand reads, then the 8 MFMAs
-    if (ks < 3) __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
+  if (prev) {
+    big_mfma(af[1], bfr[1], acc);
+    // scheduling: the 6 operand reads, then the 8 MFMAs
+    __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
     __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
   }
+#pragma unroll
+  for (int ks = 0; ks < 3; ++ks) {
+    const int b = ks & 1;
+    read(ks + 1, b ^ 1);
+    big_mfma(af[b], bfr[b], acc);
+    __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+  }
+  // this wave's loads into `nxt` have landed, its reads of `cur` are done
+  asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+  __syncthreads();
 }
 
 __global__ void __launch_bounds__(kBigThreads)
@@ -341,24 +365,18 @@ rmsnorm_linear_tile256_kernel(const bf16* __restrict__ x, const bf16* __restrict
   lds_char* const l1 = (lds_char*)st1;
   const int nk = K / BK;
   big_load_stage(l0, c, 0);
-  __builtin_amdgcn_sched_barrier(0);
-  // two steps per trip so that each stage is a fixed array; the wait before
-  // each barrier covers this wave's loads, the barrier everyone's
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  // two steps per trip so that each stage is a fixed array
+  u32x4 af[2][4], bfr[2][2];
   int kt = 0;
   for (; kt + 2 <= nk; kt += 2) {
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    big_step(l0, l1, c, (kt + 1) * BK, true, arow, brow, ko, acc);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    big_step(l1, l0, c, (kt + 2) * BK, kt + 2 < nk, arow, brow, ko, acc);
+    big_step(l0, l1, c, (kt + 1) * BK, true, kt > 0, arow, brow, ko, acc, af, bfr);
+    big_step(l1, l0, c, (kt + 2) * BK, kt + 2 < nk, true, arow, brow, ko, acc, af, bfr);
   }
-  if (kt < nk) {
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    big_step(l0, l1, c, 0, false, arow, brow, ko, acc);
-  }
-  __syncthreads();  // every operand read done: the stages take the output tile
+  if (kt < nk) big_step(l0, l1, c, 0, false, kt > 0, arow, brow, ko, acc, af, bfr);
+  big_mfma(af[1], bfr[1], acc);  // the last step's sub-step 3
+  __syncthreads();  // the stages take the output tile
 
   // scaled accumulators -> bf16 output tile: rows of row half wm in stage
   // array wm (128 rows x 32 chunks of 16 bytes), chunk index XOR 4 (bit 2 of
