@@ -110,11 +110,21 @@ def _stream(t: torch.Tensor):
     return torch.cuda.current_stream(t.device).cuda_stream
 
 
-def _dev(name: str, t: torch.Tensor, dtype=None, shape=None):
+def _run(fn: str, ref: torch.Tensor, *args):
+    """Calls library function fn with args plus PyTorch's current stream on
+    ref's device, that device being current (the library launches on the
+    current device)."""
+    with torch.cuda.device(ref.device):
+        _check(fn, getattr(_lib(), fn)(*args, _stream(ref)))
+
+
+def _dev(name: str, t: torch.Tensor, dtype=None, shape=None, device=None):
     if t is None:
         return
     if not isinstance(t, torch.Tensor) or t.device.type != "cuda":
         raise ValueError(f"{name} must be a GPU tensor")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} must be on {device}, got {t.device}")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
     if dtype is not None and t.dtype != dtype:
@@ -138,6 +148,7 @@ def _workspace(rows, n, ln, ws, device):
     need = nr_bwd_workspace_bytes(rows, n, ln)
     if ws is None:
         ws = torch.empty(max(need, 16), dtype=torch.uint8, device=device)
+    _dev("workspace", ws, device=device)
     return ws, ws.numel() * ws.element_size()
 
 
@@ -148,15 +159,16 @@ def rmsnorm_fwd(x, w=None, eps=1e-6, gemma_offset=False, y=None, inv_rms=None, w
     _dev("x", x)
     dt = _dtype_code(x)
     rows, n = _rows_n(x)
-    _dev("w", w, x.dtype, (n,))
+    _dev("w", w, x.dtype, (n,), device=x.device)
     if y is None:
         y = torch.empty_like(x)
-    _dev("y", y, x.dtype, x.shape)
+    _dev("y", y, x.dtype, x.shape, device=x.device)
     if inv_rms is None and want_stats:
         inv_rms = torch.empty(x.shape[:-1], dtype=torch.float32, device=x.device)
-    _dev("inv_rms", inv_rms, torch.float32)
-    _check("rmsnorm_fwd", _lib().rmsnorm_fwd(dt, _ptr(x), _ptr(w), _ptr(y), _ptr(inv_rms), rows, n,
-                                             float(eps), int(bool(gemma_offset)), _stream(x)))
+    _dev("inv_rms", inv_rms, torch.float32, device=x.device)
+    _run("rmsnorm_fwd", x,
+         dt, _ptr(x), _ptr(w), _ptr(y), _ptr(inv_rms), rows, n, float(eps),
+         int(bool(gemma_offset)))
     return y, inv_rms
 
 
@@ -166,21 +178,21 @@ def rmsnorm_bwd(dy, x, w, inv_rms, gemma_offset=False, dx=None, want_dw=True, dw
     _dev("x", x)
     dt = _dtype_code(x)
     rows, n = _rows_n(x)
-    _dev("dy", dy, x.dtype, x.shape)
-    _dev("w", w, x.dtype, (n,))
-    _dev("inv_rms", inv_rms, torch.float32, x.shape[:-1])
+    _dev("dy", dy, x.dtype, x.shape, device=x.device)
+    _dev("w", w, x.dtype, (n,), device=x.device)
+    _dev("inv_rms", inv_rms, torch.float32, x.shape[:-1], device=x.device)
     if dx is None:
         dx = torch.empty_like(x)
-    _dev("dx", dx, x.dtype, x.shape)
+    _dev("dx", dx, x.dtype, x.shape, device=x.device)
     if dw is None and want_dw:
         dw = torch.empty(n, dtype=torch.float32, device=x.device)
-    _dev("dw", dw, torch.float32, (n,))
+    _dev("dw", dw, torch.float32, (n,), device=x.device)
     ws, wsb = (None, 0)
     if dw is not None or n > _LONG_ROW:
         ws, wsb = _workspace(rows, n, 0, workspace, x.device)
-    _check("rmsnorm_bwd", _lib().rmsnorm_bwd(dt, _ptr(dy), _ptr(x), _ptr(w), _ptr(inv_rms),
-                                             _ptr(dx), _ptr(dw), rows, n, int(bool(gemma_offset)),
-                                             _ptr(ws), wsb, _stream(x)))
+    _run("rmsnorm_bwd", x,
+         dt, _ptr(dy), _ptr(x), _ptr(w), _ptr(inv_rms), _ptr(dx), _ptr(dw), rows, n,
+         int(bool(gemma_offset)), _ptr(ws), wsb)
     return dx, dw
 
 
@@ -190,21 +202,21 @@ def layernorm_fwd(x, gamma=None, beta=None, eps=1e-5, y=None, mean=None, rstd=No
     _dev("x", x)
     dt = _dtype_code(x)
     rows, n = _rows_n(x)
-    _dev("gamma", gamma, x.dtype, (n,))
-    _dev("beta", beta, x.dtype, (n,))
+    _dev("gamma", gamma, x.dtype, (n,), device=x.device)
+    _dev("beta", beta, x.dtype, (n,), device=x.device)
     if y is None:
         y = torch.empty_like(x)
-    _dev("y", y, x.dtype, x.shape)
+    _dev("y", y, x.dtype, x.shape, device=x.device)
     if want_stats:
         if mean is None:
             mean = torch.empty(x.shape[:-1], dtype=torch.float32, device=x.device)
         if rstd is None:
             rstd = torch.empty(x.shape[:-1], dtype=torch.float32, device=x.device)
-    _dev("mean", mean, torch.float32)
-    _dev("rstd", rstd, torch.float32)
-    _check("layernorm_fwd", _lib().layernorm_fwd(dt, _ptr(x), _ptr(gamma), _ptr(beta), _ptr(y),
-                                                 _ptr(mean), _ptr(rstd), rows, n, float(eps),
-                                                 _stream(x)))
+    _dev("mean", mean, torch.float32, device=x.device)
+    _dev("rstd", rstd, torch.float32, device=x.device)
+    _run("layernorm_fwd", x,
+         dt, _ptr(x), _ptr(gamma), _ptr(beta), _ptr(y), _ptr(mean), _ptr(rstd), rows, n,
+         float(eps))
     return y, mean, rstd
 
 
@@ -214,25 +226,25 @@ def layernorm_bwd(dy, x, gamma, mean, rstd, dx=None, want_dgamma=True, want_dbet
     _dev("x", x)
     dt = _dtype_code(x)
     rows, n = _rows_n(x)
-    _dev("dy", dy, x.dtype, x.shape)
-    _dev("gamma", gamma, x.dtype, (n,))
-    _dev("mean", mean, torch.float32, x.shape[:-1])
-    _dev("rstd", rstd, torch.float32, x.shape[:-1])
+    _dev("dy", dy, x.dtype, x.shape, device=x.device)
+    _dev("gamma", gamma, x.dtype, (n,), device=x.device)
+    _dev("mean", mean, torch.float32, x.shape[:-1], device=x.device)
+    _dev("rstd", rstd, torch.float32, x.shape[:-1], device=x.device)
     if dx is None:
         dx = torch.empty_like(x)
-    _dev("dx", dx, x.dtype, x.shape)
+    _dev("dx", dx, x.dtype, x.shape, device=x.device)
     if dgamma is None and want_dgamma:
         dgamma = torch.empty(n, dtype=torch.float32, device=x.device)
     if dbeta is None and want_dbeta:
         dbeta = torch.empty(n, dtype=torch.float32, device=x.device)
-    _dev("dgamma", dgamma, torch.float32, (n,))
-    _dev("dbeta", dbeta, torch.float32, (n,))
+    _dev("dgamma", dgamma, torch.float32, (n,), device=x.device)
+    _dev("dbeta", dbeta, torch.float32, (n,), device=x.device)
     ws, wsb = (None, 0)
     if dgamma is not None or dbeta is not None or n > _LONG_ROW:
         ws, wsb = _workspace(rows, n, 1, workspace, x.device)
-    _check("layernorm_bwd", _lib().layernorm_bwd(dt, _ptr(dy), _ptr(x), _ptr(gamma), _ptr(mean),
-                                                 _ptr(rstd), _ptr(dx), _ptr(dgamma), _ptr(dbeta),
-                                                 rows, n, _ptr(ws), wsb, _stream(x)))
+    _run("layernorm_bwd", x,
+         dt, _ptr(dy), _ptr(x), _ptr(gamma), _ptr(mean), _ptr(rstd), _ptr(dx), _ptr(dgamma),
+         _ptr(dbeta), rows, n, _ptr(ws), wsb)
     return dx, dgamma, dbeta
 
 
@@ -244,21 +256,21 @@ def layernorm_gelu_fwd(x, gamma=None, beta=None, eps=1e-5, y=None, mean=None, rs
     _dev("x", x)
     dt = _dtype_code(x)
     rows, n = _rows_n(x)
-    _dev("gamma", gamma, x.dtype, (n,))
-    _dev("beta", beta, x.dtype, (n,))
+    _dev("gamma", gamma, x.dtype, (n,), device=x.device)
+    _dev("beta", beta, x.dtype, (n,), device=x.device)
     if y is None:
         y = torch.empty_like(x)
-    _dev("y", y, x.dtype, x.shape)
+    _dev("y", y, x.dtype, x.shape, device=x.device)
     if want_stats:
         if mean is None:
             mean = torch.empty(x.shape[:-1], dtype=torch.float32, device=x.device)
         if rstd is None:
             rstd = torch.empty(x.shape[:-1], dtype=torch.float32, device=x.device)
-    _dev("mean", mean, torch.float32)
-    _dev("rstd", rstd, torch.float32)
-    _check("layernorm_gelu_fwd", _lib().layernorm_gelu_fwd(
-        dt, _ptr(x), _ptr(gamma), _ptr(beta), _ptr(y), _ptr(mean), _ptr(rstd), rows, n, float(eps),
-        _stream(x)))
+    _dev("mean", mean, torch.float32, device=x.device)
+    _dev("rstd", rstd, torch.float32, device=x.device)
+    _run("layernorm_gelu_fwd", x,
+         dt, _ptr(x), _ptr(gamma), _ptr(beta), _ptr(y), _ptr(mean), _ptr(rstd), rows, n,
+         float(eps))
     return y, mean, rstd
 
 
@@ -268,26 +280,26 @@ def layernorm_gelu_bwd(dout, x, gamma, beta, mean, rstd, dx=None, want_dgamma=Tr
     _dev("x", x)
     dt = _dtype_code(x)
     rows, n = _rows_n(x)
-    _dev("dout", dout, x.dtype, x.shape)
-    _dev("gamma", gamma, x.dtype, (n,))
-    _dev("beta", beta, x.dtype, (n,))
-    _dev("mean", mean, torch.float32, x.shape[:-1])
-    _dev("rstd", rstd, torch.float32, x.shape[:-1])
+    _dev("dout", dout, x.dtype, x.shape, device=x.device)
+    _dev("gamma", gamma, x.dtype, (n,), device=x.device)
+    _dev("beta", beta, x.dtype, (n,), device=x.device)
+    _dev("mean", mean, torch.float32, x.shape[:-1], device=x.device)
+    _dev("rstd", rstd, torch.float32, x.shape[:-1], device=x.device)
     if dx is None:
         dx = torch.empty_like(x)
-    _dev("dx", dx, x.dtype, x.shape)
+    _dev("dx", dx, x.dtype, x.shape, device=x.device)
     if dgamma is None and want_dgamma:
         dgamma = torch.empty(n, dtype=torch.float32, device=x.device)
     if dbeta is None and want_dbeta:
         dbeta = torch.empty(n, dtype=torch.float32, device=x.device)
-    _dev("dgamma", dgamma, torch.float32, (n,))
-    _dev("dbeta", dbeta, torch.float32, (n,))
+    _dev("dgamma", dgamma, torch.float32, (n,), device=x.device)
+    _dev("dbeta", dbeta, torch.float32, (n,), device=x.device)
     ws, wsb = (None, 0)
     if dgamma is not None or dbeta is not None or n > _LONG_ROW:
         ws, wsb = _workspace(rows, n, 1, workspace, x.device)
-    _check("layernorm_gelu_bwd", _lib().layernorm_gelu_bwd(
-        dt, _ptr(dout), _ptr(x), _ptr(gamma), _ptr(beta), _ptr(mean), _ptr(rstd), _ptr(dx),
-        _ptr(dgamma), _ptr(dbeta), rows, n, _ptr(ws), wsb, _stream(x)))
+    _run("layernorm_gelu_bwd", x,
+         dt, _ptr(dout), _ptr(x), _ptr(gamma), _ptr(beta), _ptr(mean), _ptr(rstd), _ptr(dx),
+         _ptr(dgamma), _ptr(dbeta), rows, n, _ptr(ws), wsb)
     return dx, dgamma, dbeta
 
 
@@ -298,8 +310,8 @@ def _rope_rows(x, cos_tab, sin_tab, head_dim, rows_per_token):
     if head_dim <= 0 or n % head_dim:
         raise ValueError("the row length must be a whole number of head vectors")
     tokens = -(-rows // rows_per_token) if rows else 0
-    _dev("cos_tab", cos_tab, torch.float32, (tokens, head_dim // 2))
-    _dev("sin_tab", sin_tab, torch.float32, (tokens, head_dim // 2))
+    _dev("cos_tab", cos_tab, torch.float32, (tokens, head_dim // 2), device=x.device)
+    _dev("sin_tab", sin_tab, torch.float32, (tokens, head_dim // 2), device=x.device)
     return rows, n
 
 
@@ -309,16 +321,16 @@ def rmsnorm_rope_fwd(x, w, cos_tab, sin_tab, head_dim, rows_per_token=1, eps=1e-
     _dev("x", x)
     dt = _dtype_code(x)
     rows, n = _rope_rows(x, cos_tab, sin_tab, head_dim, rows_per_token)
-    _dev("w", w, x.dtype, (n,))
+    _dev("w", w, x.dtype, (n,), device=x.device)
     if y is None:
         y = torch.empty_like(x)
-    _dev("y", y, x.dtype, x.shape)
+    _dev("y", y, x.dtype, x.shape, device=x.device)
     if inv_rms is None and want_stats:
         inv_rms = torch.empty(x.shape[:-1], dtype=torch.float32, device=x.device)
-    _dev("inv_rms", inv_rms, torch.float32)
-    _check("rmsnorm_rope_fwd", _lib().rmsnorm_rope_fwd(
-        dt, _ptr(x), _ptr(w), _ptr(y), _ptr(inv_rms), _ptr(cos_tab), _ptr(sin_tab), rows, n,
-        head_dim, rows_per_token, float(eps), int(bool(gemma_offset)), _stream(x)))
+    _dev("inv_rms", inv_rms, torch.float32, device=x.device)
+    _run("rmsnorm_rope_fwd", x,
+         dt, _ptr(x), _ptr(w), _ptr(y), _ptr(inv_rms), _ptr(cos_tab), _ptr(sin_tab), rows, n,
+         head_dim, rows_per_token, float(eps), int(bool(gemma_offset)))
     return y, inv_rms
 
 
@@ -328,22 +340,21 @@ def rmsnorm_rope_bwd(dout, x, w, inv_rms, cos_tab, sin_tab, head_dim, rows_per_t
     _dev("x", x)
     dt = _dtype_code(x)
     rows, n = _rope_rows(x, cos_tab, sin_tab, head_dim, rows_per_token)
-    _dev("dout", dout, x.dtype, x.shape)
-    _dev("w", w, x.dtype, (n,))
-    _dev("inv_rms", inv_rms, torch.float32, x.shape[:-1])
+    _dev("dout", dout, x.dtype, x.shape, device=x.device)
+    _dev("w", w, x.dtype, (n,), device=x.device)
+    _dev("inv_rms", inv_rms, torch.float32, x.shape[:-1], device=x.device)
     if dx is None:
         dx = torch.empty_like(x)
-    _dev("dx", dx, x.dtype, x.shape)
+    _dev("dx", dx, x.dtype, x.shape, device=x.device)
     if dw is None and want_dw:
         dw = torch.empty(n, dtype=torch.float32, device=x.device)
-    _dev("dw", dw, torch.float32, (n,))
+    _dev("dw", dw, torch.float32, (n,), device=x.device)
     ws, wsb = (None, 0)
     if dw is not None or n > _LONG_ROW:
         ws, wsb = _workspace(rows, n, 2, workspace, x.device)
-    _check("rmsnorm_rope_bwd", _lib().rmsnorm_rope_bwd(
-        dt, _ptr(dout), _ptr(x), _ptr(w), _ptr(inv_rms), _ptr(cos_tab), _ptr(sin_tab), _ptr(dx),
-        _ptr(dw), rows, n, head_dim, rows_per_token, int(bool(gemma_offset)), _ptr(ws), wsb,
-        _stream(x)))
+    _run("rmsnorm_rope_bwd", x,
+         dt, _ptr(dout), _ptr(x), _ptr(w), _ptr(inv_rms), _ptr(cos_tab), _ptr(sin_tab), _ptr(dx),
+         _ptr(dw), rows, n, head_dim, rows_per_token, int(bool(gemma_offset)), _ptr(ws), wsb)
     return dx, dw
 
 
@@ -357,11 +368,11 @@ def rope_interleaved_apply(x, cos_tab, sin_tab, inverse=False):
         raise ValueError("x must be a GPU tensor with a contiguous last axis")
     dt = _dtype_code(x)
     b, t, h, d = x.shape
-    _dev("cos_tab", cos_tab, torch.float32, (t, d // 2))
-    _dev("sin_tab", sin_tab, torch.float32, (t, d // 2))
-    _check("rope_interleaved_apply", _lib().rope_interleaved_apply(
-        dt, _ptr(x), _ptr(cos_tab), _ptr(sin_tab), b, t, h, d, x.stride(0), x.stride(1),
-        x.stride(2), int(bool(inverse)), _stream(x)))
+    _dev("cos_tab", cos_tab, torch.float32, (t, d // 2), device=x.device)
+    _dev("sin_tab", sin_tab, torch.float32, (t, d // 2), device=x.device)
+    _run("rope_interleaved_apply", x,
+         dt, _ptr(x), _ptr(cos_tab), _ptr(sin_tab), b, t, h, d, x.stride(0), x.stride(1),
+         x.stride(2), int(bool(inverse)))
     return x
 
 
@@ -369,8 +380,7 @@ def rope_table_1d(tokens, head_dim, pos0=0, theta=10000.0, device="cuda"):
     """fp32 cos/sin tables [tokens, head_dim/2] for positions pos0.."""
     c = torch.empty((tokens, head_dim // 2), dtype=torch.float32, device=device)
     s = torch.empty_like(c)
-    _check("rope_table_1d", _lib().rope_table_1d(_ptr(c), _ptr(s), tokens, head_dim, pos0,
-                                                 float(theta), _stream(c)))
+    _run("rope_table_1d", c, _ptr(c), _ptr(s), tokens, head_dim, pos0, float(theta))
     return c, s
 
 
@@ -380,8 +390,7 @@ def rope_table_3d(grid, pairs, theta=10000.0, device="cuda"):
     pt, ph, pw = pairs
     c = torch.empty((f * h * w, pt + ph + pw), dtype=torch.float32, device=device)
     s = torch.empty_like(c)
-    _check("rope_table_3d", _lib().rope_table_3d(_ptr(c), _ptr(s), f, h, w, pt, ph, pw,
-                                                 float(theta), _stream(c)))
+    _run("rope_table_3d", c, _ptr(c), _ptr(s), f, h, w, pt, ph, pw, float(theta))
     return c, s
 
 
@@ -395,24 +404,25 @@ def rmsnorm_linear_fwd(x, w_norm, W, eps=1e-6, gemma_offset=False, out=None, inv
     call needs one)."""
     _dev("x", x, torch.bfloat16)
     rows, k = _rows_n(x)
-    _dev("W", W, torch.bfloat16)
+    _dev("W", W, torch.bfloat16, device=x.device)
     if W.dim() != 2 or W.shape[1] != k:
         raise ValueError(f"W must be [N, {k}]")
     n = W.shape[0]
-    _dev("w_norm", w_norm, torch.bfloat16, (k,))
+    _dev("w_norm", w_norm, torch.bfloat16, (k,), device=x.device)
     if out is None:
         out = torch.empty(x.shape[:-1] + (n,), dtype=torch.bfloat16, device=x.device)
-    _dev("out", out, torch.bfloat16, x.shape[:-1] + (n,))
+    _dev("out", out, torch.bfloat16, x.shape[:-1] + (n,), device=x.device)
     if inv_rms is None and want_stats:
         inv_rms = torch.empty(x.shape[:-1], dtype=torch.float32, device=x.device)
-    _dev("inv_rms", inv_rms, torch.float32)
+    _dev("inv_rms", inv_rms, torch.float32, device=x.device)
     wsb = nr_rmsnorm_linear_workspace_bytes(rows, n, k, w_norm is not None)
     if workspace is None and wsb > 0:
         workspace = torch.empty(wsb, dtype=torch.uint8, device=x.device)
-    _check("rmsnorm_linear_fwd", _lib().rmsnorm_linear_fwd(
-        NR_BF16, _ptr(x), _ptr(w_norm), _ptr(W), _ptr(out), _ptr(inv_rms), rows, n, k, float(eps),
-        int(bool(gemma_offset)), _ptr(workspace),
-        0 if workspace is None else workspace.numel() * workspace.element_size(), _stream(x)))
+    _dev("workspace", workspace, device=x.device)
+    _run("rmsnorm_linear_fwd", x,
+         NR_BF16, _ptr(x), _ptr(w_norm), _ptr(W), _ptr(out), _ptr(inv_rms), rows, n, k, float(eps),
+         int(bool(gemma_offset)), _ptr(workspace),
+         0 if workspace is None else workspace.numel() * workspace.element_size())
     return out, inv_rms
 
 
@@ -423,12 +433,12 @@ def rmsnorm_linear_fold_weight(w_norm, W, gemma_offset=False, out=None):
     if W.dim() != 2:
         raise ValueError("W must be [N, K]")
     n, k = W.shape
-    _dev("w_norm", w_norm, torch.bfloat16, (k,))
+    _dev("w_norm", w_norm, torch.bfloat16, (k,), device=W.device)
     if out is None:
         out = torch.empty_like(W)
-    _dev("W_folded", out, torch.bfloat16, (n, k))
-    _check("rmsnorm_linear_fold_weight", _lib().rmsnorm_linear_fold_weight(
-        NR_BF16, _ptr(w_norm), _ptr(W), _ptr(out), n, k, int(bool(gemma_offset)), _stream(W)))
+    _dev("W_folded", out, torch.bfloat16, (n, k), device=W.device)
+    _run("rmsnorm_linear_fold_weight", W,
+         NR_BF16, _ptr(w_norm), _ptr(W), _ptr(out), n, k, int(bool(gemma_offset)))
     return out
 
 
@@ -447,11 +457,11 @@ def nr_stream_copy(src: torch.Tensor, dst: torch.Tensor):
     """Measurement aid: copy src's bytes into dst with the row kernels'
     streaming access pattern (the practical HBM ceiling)."""
     _dev("src", src)
-    _dev("dst", dst)
+    _dev("dst", dst, device=src.device)
     nbytes = src.numel() * src.element_size()
     if dst.numel() * dst.element_size() != nbytes or src.device != dst.device:
         raise ValueError("nr_stream_copy: src and dst must have the same size and device")
-    _check("nr_stream_copy", _lib().nr_stream_copy(_ptr(src), _ptr(dst), nbytes, _stream(src)))
+    _run("nr_stream_copy", src, _ptr(src), _ptr(dst), nbytes)
 
 
 def nr_status_str(status: int) -> str:
