@@ -278,8 +278,19 @@ def read_traffic(kernel_label, workload):
                 kv[k.strip()] = v.strip()
     if kv.get("source_hash") != source_hash(workload):
         return None
-    v = kv.get(f"bytes_per_launch.{kernel_label}")
-    return float(v) if v else None
+    # a label "a[..]+b" names kernels launched together (the backward's rows
+    # and its column reduction): their bytes add; "+" inside [] is a name
+    parts, depth, cur = [], 0, ""
+    for ch in kernel_label:
+        depth += (ch == "[") - (ch == "]")
+        if ch == "+" and depth == 0:
+            parts.append(cur)
+            cur = ""
+        else:
+            cur += ch
+    parts.append(cur)
+    vals = [kv.get(f"bytes_per_launch.{p}") for p in parts]
+    return float(sum(float(v) for v in vals)) if all(vals) else None
 
 
 # ---------------------------------------------------------------- CPU baseline
