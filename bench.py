@@ -484,21 +484,18 @@ def main():
                              ms_min=round(min(times), 5),
                              gbs=round(b / (mean * 1e-3) / 1e9, 1),
                              frac_of_peak=round(b / (mean * 1e-3) / 1e9 / PEAK_GBS, 4))
-    # dominant kernel: of the single-kernel operations, the kernel (one
-    # instantiation, one shape) with the largest share of the step's time;
-    # its per-launch figures average over all its launches in the step
+    # dominant kernel: the kernel (one instantiation, one shape) with the
+    # largest share of the step's time, its per-launch figures averaged over
+    # all its launches in the step.  A backward is one call that launches
+    # two kernels (the rows, then the column reduction): events around the
+    # call time the pair, so the pair counts as one "kernel" ("a+b")
     kern = {}
-    for i, (label, kname, _, b) in enumerate(ops):
-        if "+" in kname:
-            continue
+    for label, kname, _, b in ops:
         k = kern.setdefault(kname, dict(launches=0, bytes=0, ms=0.0, ops=[]))
         k["launches"] += 1
         k["bytes"] += b
         k["ms"] += per_op[label]["ms_mean"]
         k["ops"].append(label)
-    if not kern:  # every operation launches two kernels: take the largest operation
-        for label, kname, _, b in ops:
-            kern[kname] = dict(launches=1, bytes=b, ms=per_op[label]["ms_mean"], ops=[label])
     dname = max(kern, key=lambda k: kern[k]["ms"])
     dk = kern[dname]
     bpl, mspl = dk["bytes"] / dk["launches"], dk["ms"] / dk["launches"]
