@@ -1,0 +1,74 @@
+"""The Python binding's argument checks: tensors the C ABI cannot take are
+refused with ValueError before any call into the library (nothing is
+launched, the outputs keep their contents)."""
+import pytest
+import torch
+
+import rmsnorm_layernorm_fwd_amd as nr
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def _inputs(rows=8, n=256, dtype=torch.bfloat16):
+    x = torch.randn(rows, n, device=DEV).to(dtype)
+    w = torch.ones(n, device=DEV, dtype=dtype)
+    return x, w
+
+
+def test_host_tensor_refused():
+    print("[case] binding: host tensors", flush=True)
+    x, w = _inputs()
+    with pytest.raises(ValueError, match="GPU tensor"):
+        nr.rmsnorm_fwd(x, w.cpu())
+    with pytest.raises(ValueError, match="GPU tensor"):
+        nr.rmsnorm_fwd(x.cpu(), w)
+
+
+def test_dtype_shape_and_layout_refused():
+    print("[case] binding: dtype, shape, layout", flush=True)
+    x, w = _inputs()
+    y = torch.full_like(x, 7.0)
+    with pytest.raises(ValueError, match="must be torch.bfloat16"):
+        nr.rmsnorm_fwd(x, w.float(), y=y)
+    with pytest.raises(ValueError, match="shape"):
+        nr.rmsnorm_fwd(x, w[:128].contiguous(), y=y)
+    with pytest.raises(ValueError, match="contiguous"):
+        nr.rmsnorm_fwd(x, torch.ones(512, device=DEV, dtype=x.dtype)[::2], y=y)
+    with pytest.raises(ValueError, match="shape"):
+        nr.layernorm_fwd(x, w, w, y=torch.empty(8, 128, device=DEV, dtype=x.dtype))
+    torch.cuda.synchronize()
+    assert torch.all(y == 7.0)  # nothing ran
+
+
+def test_workspace_on_host_refused():
+    print("[case] binding: host workspace", flush=True)
+    x, w = _inputs()
+    _, r = nr.rmsnorm_fwd(x, w)
+    ws = torch.empty(nr.nr_bwd_workspace_bytes(8, 256, 0), dtype=torch.uint8)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        nr.rmsnorm_bwd(torch.ones_like(x), x, w, r, workspace=ws)
+
+
+def test_device_check_compares_devices():
+    # the binding checks every tensor against the first one's device; on a
+    # one-GPU machine the rule is exercised directly
+    print("[case] binding: device rule", flush=True)
+    x, _ = _inputs()
+    nr._dev("x", x, device=x.device)  # same device: accepted
+    with pytest.raises(ValueError, match="must be on"):
+        nr._dev("x", x, device=torch.device("cuda", x.device.index + 1))
+
+
+def test_calls_run_on_the_tensors_device_with_its_stream():
+    # a side stream made current: the call is ordered on it (the result is
+    # complete once that stream is synchronised)
+    print("[case] binding: current stream", flush=True)
+    x, w = _inputs(rows=4096, n=1024)
+    s = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    with torch.cuda.stream(s):
+        y, r = nr.rmsnorm_fwd(x, w)
+    s.synchronize()
+    ref = (x.float() * torch.rsqrt(x.float().pow(2).mean(-1, keepdim=True) + 1e-6))
+    assert torch.allclose(y.float(), ref, rtol=1e-2, atol=1e-2)
