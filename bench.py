@@ -357,7 +357,7 @@ def stream_ceiling(dev, reps=10):
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / reps
     del a, b
-    return dict(kind="nr_stream_copy (16-byte non-temporal loads/stores, one pass)",
+    return dict(kind="nr_stream_copy (16-byte streaming loads/stores, one pass)",
                 bytes_per_launch=2 * nbytes, ms_per_launch=round(ms, 5),
                 gbs=round(2 * nbytes / (ms * 1e-3) / 1e9, 1),
                 frac_of_peak=round(2 * nbytes / (ms * 1e-3) / 1e9 / PEAK_GBS, 4))

@@ -321,8 +321,8 @@ nr_status_t nr_tune(const char* key, int value);
 /*
  * nr_stream_copy -- measurement aid, not part of the method: copies `bytes`
  * bytes from src to dst (device memory, not overlapping) with the access
- * pattern of the row kernels (16-byte non-temporal loads and stores, one
- * pass, a one-shot grid).  Its bandwidth is the practical HBM ceiling that
+ * pattern of the row kernels (16-byte streaming loads and stores, one pass,
+ * a one-shot grid).  Its bandwidth is the practical HBM ceiling that
  * the norm and RoPE kernels are reported against (the method's benchmark
  * compares fused kernels by the bytes they move).  Both pointers 16-byte
  * aligned and bytes a multiple of 16, else NR_ERR_SHAPE; NR_ERR_ALIAS when

@@ -691,8 +691,8 @@ nr_status_t nr_stream_copy(const void* src, void* dst, size_t bytes, void* strea
   if (src == nullptr || dst == nullptr) return NR_ERR_NULLPTR;
   if ((bytes & 15u) != 0 || !aligned16(src) || !aligned16(dst)) return NR_ERR_SHAPE;
   const int64_t nvec = static_cast<int64_t>(bytes / 16);
-  // one workgroup per 16 KiB: the grid must fit hardware limits
-  if (nvec / 1024 >= (int64_t{1} << 31)) return NR_ERR_SHAPE;
+  // one workgroup per 4 KiB: the grid must fit the hardware's 2^31 - 1
+  if ((nvec + 255) / 256 > INT32_MAX) return NR_ERR_SHAPE;
   if (bad_overlap(dst, bytes, src, bytes) || dst == src) return NR_ERR_ALIAS;
   return hip_status(nr::launch_stream_copy(src, dst, nvec, static_cast<hipStream_t>(stream)));
 }

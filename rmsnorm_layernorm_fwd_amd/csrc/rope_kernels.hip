@@ -86,7 +86,7 @@ rope_apply_kernel(T* x, const float* cos_tab, const float* sin_tab, int64_t ntok
         rotate_pairs<PP>(v[k], ck[k], sk[k], sign);
       }
       if constexpr (VEC) {
-        __builtin_amdgcn_raw_buffer_store_b128(pack<T>(v[k]), xr, off[k], 0, kStream);
+        __builtin_amdgcn_raw_buffer_store_b128(pack<T>(v[k]), xr, off[k], 0, kStreamStore);
       } else {
         st_elem<T>(xr, off[k], v[k][0]);
         st_elem<T>(xr, off[k] + static_cast<int>(sizeof(T)), v[k][1]);

@@ -1,36 +1,31 @@
 // stream_copy.hip -- a plain streaming copy with the row kernels' memory
-// access pattern (16-byte non-temporal loads and stores, a one-shot grid of
-// 256-lane workgroups).  It computes nothing: its bandwidth is the practical
-// HBM ceiling that the norm and RoPE kernels, which read and write each byte
-// once, are measured against.  Of 1, 2, 4 and 8 vectors per lane, one (the
-// most workgroups, each lane's load and store back to back) copied fastest
-// on MI355X: about 6.5 TB/s over 2 x 671 MB.
+// access pattern (16-byte buffer loads and stores with the same cache
+// policy, a one-shot grid of 256-lane workgroups).  It computes nothing: its
+// bandwidth is the practical HBM ceiling that the norm and RoPE kernels,
+// which read and write each byte once, are measured against.  Of 1, 2, 4
+// and 8 vectors per lane, one (the most workgroups, each lane's load and
+// store back to back) copied fastest on MI355X: about 6.65 TB/s over
+// 2 x 671 MB with the streaming store policy.
 #include "nr_device.hpp"
 #include "nr_internal.hpp"
 
 namespace nr {
 
-constexpr int kCopyU = 1;  // 16-byte vectors per lane (1, 2, 4, 8 measured: 1 is fastest)
-
+// One 16-byte vector per lane; each workgroup's buffer range covers its own
+// 4 KiB, so the last one's tail (and copies past 4 GiB) need no index math.
 __global__ void __launch_bounds__(256) stream_copy_kernel(const u32x4* __restrict__ src,
                                                           u32x4* __restrict__ dst, int64_t nvec) {
-  const int64_t base = static_cast<int64_t>(blockIdx.x) * (256 * kCopyU) + threadIdx.x;
-  u32x4 v[kCopyU];
-#pragma unroll
-  for (int u = 0; u < kCopyU; ++u) {
-    const int64_t i = base + u * 256;
-    if (i < nvec) v[u] = __builtin_nontemporal_load(src + i);
-  }
-#pragma unroll
-  for (int u = 0; u < kCopyU; ++u) {
-    const int64_t i = base + u * 256;
-    if (i < nvec) __builtin_nontemporal_store(v[u], dst + i);
-  }
+  const int64_t first = static_cast<int64_t>(blockIdx.x) * 256;
+  const uint32_t bytes = static_cast<uint32_t>(min(nvec - first, int64_t{256}) * 16);
+  const rsrc_t sr = make_rsrc(src + first, bytes);
+  const rsrc_t dr = make_rsrc(dst + first, bytes);
+  const uint32_t off = threadIdx.x * 16u;
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_amdgcn_raw_buffer_load_b128(sr, off, 0, kStream),
+                                         dr, off, 0, kStreamStore);
 }
 
 hipError_t launch_stream_copy(const void* src, void* dst, int64_t nvec, hipStream_t st) {
-  const int64_t per_block = 256 * kCopyU;
-  const int64_t blocks = (nvec + per_block - 1) / per_block;
+  const int64_t blocks = (nvec + 255) / 256;
   hipLaunchKernelGGL(stream_copy_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, st,
                      static_cast<const u32x4*>(src), static_cast<u32x4*>(dst), nvec);
   return hipGetLastError();
