@@ -115,7 +115,8 @@ __device__ __forceinline__ void process_batch(RowBatch<T, K, D, ROPE ? 1 : 0>& b
                                               int wave, int lane, float inv_n,
                                               const float (&wv)[K][Vec<T>::N],
                                               const float (&bv)[K][Vec<T>::N],
-                                              float (&acc1)[K][Vec<T>::N],
+                                              const u32x4 (&wpk)[K], const u32x4 (&bpk)[K],
+                                              float w_add, float (&acc1)[K][Vec<T>::N],
                                               float (&acc2)[K][Vec<T>::N],
                                               float (*red)[16], int& parity) {
   constexpr int E = Vec<T>::N;
@@ -127,26 +128,40 @@ __device__ __forceinline__ void process_batch(RowBatch<T, K, D, ROPE ? 1 : 0>& b
   float s[NS * D];
   // GeLU: dy * gamma with dy = dout * gelu'(pre-activation), kept for the
   // second pass (the activation's derivative is the costliest arithmetic
-  // here)
+  // here).  With one chunk per lane xhat is kept too.  With more (LEAN) it
+  // is recomputed from x in the second pass, and gamma and beta stay packed
+  // and are widened per batch (behind a register barrier, so the compiler
+  // cannot hoist the widened copies out of the row loop): this keeps the
+  // 1024-thread kernel within its 128 VGPRs, where it spilled before.
   constexpr int GD = EPI == kEpiGelu ? D * K : 0;
-  float gdd[GD > 0 ? GD : 1][E], gxh[GD > 0 ? GD : 1][E];
+  constexpr bool LEAN = EPI == kEpiGelu && K > 1;
+  float gdd[GD > 0 ? GD : 1][E], gxh[(GD > 0 && !LEAN) ? GD : 1][E];
 #pragma unroll
   for (int d = 0; d < D; ++d) {
     float s1 = 0.0f, s2 = 0.0f;
 #pragma unroll
     for (int k = 0; k < K; ++k) {
-      float xv[E], dv[E];
+      float xv[E], dv[E], wl[E], bl[E];
       unpack<T>(b.x[d * K + k], xv);
       dy_chunk<T, K, D, ROPE>(b, d * K + k, dv);
+      if constexpr (LEAN) {
+        u32x4 wq[1] = {wpk[k]}, bq[1] = {bpk[k]};
+        reload_barrier<1>(wq);
+        reload_barrier<1>(bq);
+        unpack<T>(wq[0], wl);
+        unpack<T>(bq[0], bl);
+      }
 #pragma unroll
       for (int e = 0; e < E; ++e) {
         const float xh = (xv[e] - b.mu[d]) * b.rs[d];
+        const float wk = LEAN ? wl[e] + w_add : wv[k][e];
         float dd = dv[e];
-        if constexpr (EPI == kEpiGelu) dd *= gelu_tanh_grad(fmaf(xh, wv[k][e], bv[k][e]));
-        const float gg = dd * wv[k][e];
+        if constexpr (EPI == kEpiGelu)
+          dd *= gelu_tanh_grad(fmaf(xh, wk, LEAN ? bl[e] : bv[k][e]));
+        const float gg = dd * wk;
         if constexpr (EPI == kEpiGelu) {
           gdd[d * K + k][e] = gg;
-          gxh[d * K + k][e] = xh;
+          if constexpr (!LEAN) gxh[d * K + k][e] = xh;
         }
         if constexpr (LN) {
           s1 += gg;
@@ -199,16 +214,14 @@ __device__ __forceinline__ void process_batch(RowBatch<T, K, D, ROPE ? 1 : 0>& b
 #pragma unroll
     for (int k = 0; k < K; ++k) {
       float xv[E], dv[E], o[E];
-      if constexpr (EPI != kEpiGelu) {
-        unpack<T>(b.x[d * K + k], xv);
-        dy_chunk<T, K, D, ROPE>(b, d * K + k, dv);
-      }
+      if constexpr (EPI != kEpiGelu || LEAN) unpack<T>(b.x[d * K + k], xv);
+      if constexpr (EPI != kEpiGelu) dy_chunk<T, K, D, ROPE>(b, d * K + k, dv);
 #pragma unroll
       for (int e = 0; e < E; ++e) {
         float xh, gg;
         if constexpr (EPI == kEpiGelu) {
           gg = gdd[d * K + k][e];
-          xh = gxh[d * K + k][e];
+          xh = LEAN ? (xv[e] - b.mu[d]) * b.rs[d] : gxh[d * K + k][e];
         } else {
           gg = dv[e] * wv[k][e];
           xh = (xv[e] - b.mu[d]) * b.rs[d];
@@ -244,22 +257,44 @@ norm_bwd_rows(const T* dy, const T* x, const T* w, const T* beta, const float* m
   const float inv_n = 1.0f / static_cast<float>(n);
   const uint32_t rbytes = static_cast<uint32_t>(n) * sizeof(T);
 
+  // the weight (1 where there is none), widened once; or, for the GeLU
+  // backward with more than one chunk per lane, kept packed (ones packed
+  // where there is no weight, the offset applied where it is widened)
+  constexpr bool LEAN = EPI == kEpiGelu && K > 1;
   float wv[K][E];
+  u32x4 wpk[K];
+  const float w_add_packed = (w != nullptr) ? w_add : 0.0f;
   {
     const rsrc_t wr = make_rsrc(w, w != nullptr ? rbytes : 0u);
 #pragma unroll
     for (int k = 0; k < K; ++k) {
-      unpack<T>(ld_chunk<T, VEC>(wr, t + k * nthr), wv[k]);
+      wpk[k] = ld_chunk<T, VEC>(wr, t + k * nthr);
+      if constexpr (LEAN) {
+        if (w == nullptr) {
+          float one[E];
 #pragma unroll
-      for (int e = 0; e < E; ++e) wv[k][e] = (w != nullptr) ? wv[k][e] + w_add : 1.0f;
+          for (int e = 0; e < E; ++e) one[e] = 1.0f;
+          wpk[k] = pack<T>(one);
+        }
+      } else {
+        unpack<T>(wpk[k], wv[k]);
+#pragma unroll
+        for (int e = 0; e < E; ++e) wv[k][e] = (w != nullptr) ? wv[k][e] + w_add : 1.0f;
+      }
     }
   }
 
-  float bv[K][E];  // beta, only read by the GeLU epilogue
+  // beta, only read by the GeLU epilogue: widened once, or (more than one
+  // chunk per lane) kept packed and widened where used
+  float bv[K][E];
+  u32x4 bpk[K];
   {
     const rsrc_t br = make_rsrc(beta, (EPI == kEpiGelu && beta != nullptr) ? rbytes : 0u);
 #pragma unroll
-    for (int k = 0; k < K; ++k) unpack<T>(ld_chunk<T, VEC>(br, t + k * nthr), bv[k]);
+    for (int k = 0; k < K; ++k) {
+      bpk[k] = ld_chunk<T, VEC>(br, t + k * nthr);
+      if constexpr (!LEAN) unpack<T>(bpk[k], bv[k]);
+    }
   }
 
   float acc1[K][E], acc2[K][E];
@@ -289,7 +324,7 @@ norm_bwd_rows(const T* dy, const T* x, const T* w, const T* beta, const float* m
       load_batch<T, K, D, VEC, LN, ROPE>(buf[(i + PF) % (PF + 1)], base + PF * step, rows, x, dy,
                                          mean, rstat, n, t, nthr, ra);
       process_batch<T, K, D, VEC, LN, ROPE, EPI>(buf[i], base, rows, dx, n, t, nthr, W, wave, lane,
-                                                 inv_n, wv, bv, acc1, acc2, red, parity);
+                                                 inv_n, wv, bv, wpk, bpk, w_add_packed, acc1, acc2, red, parity);
       base += step;
     }
   }
