@@ -158,9 +158,10 @@ bool fwd_grid_ok(int64_t rows, const FwdPlan& pl) {
 //   D (rows per batch) and PF (batches loaded ahead): the largest that fit
 //     the 128-VGPR budget of a 1024-thread workgroup without spilling.
 //     RMSNorm with one chunk per lane takes D = 2 (aligned rows), PF = 2;
-//     LayerNorm, which also carries the dbeta accumulators, D = 1, PF = 1.  LayerNorm + GeLU
-//     spends far more ALU time per row (the activation's derivative), so it
-//     loads two batches ahead (PF = 2) to keep HBM busy meanwhile.
+//     LayerNorm, which also carries the dbeta accumulators, D = 1, PF = 1.
+//     LayerNorm + GeLU spends far more ALU time per row (the activation's
+//     derivative), so it loads two batches ahead (PF = 2) to keep HBM busy
+//     meanwhile.
 //   P (workgroups): each handles about rows/P rows, dealt out round robin.
 //     At least 8 rows per workgroup keep the fp32 partial rows small next
 //     to the row traffic (under 9% extra at 16-bit storage, under 2% once
