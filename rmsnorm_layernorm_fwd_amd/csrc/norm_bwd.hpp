@@ -36,16 +36,19 @@ namespace nr {
 // part: [2][P][n] fp32 (second matrix, at part + part_stride, for dbeta);
 // null when no column gradient is wanted.
 // D rows of x and dy as loaded (packed), their statistics and, for the fused
-// RMSNorm + RoPE backward, each chunk's cos/sin (R = 1 when unused).
-template <typename T, int K, int D, int R = 1>
+// RMSNorm + RoPE backward, the cos/sin of TS table slots per row: TS = K, one
+// per chunk, or TS = 1 when all of a lane's chunks sit at the same offset in
+// their heads (the row's lane stride a multiple of the head size), which
+// halves the table registers of two chunks per lane; TS = 0 without RoPE.
+template <typename T, int K, int D, int TS>
 struct RowBatch {
   u32x4 x[D * K], g[D * K];
   float rs[D], mu[D];
-  float tc[R * D * K][Vec<T>::N / 2], ts[R * D * K][Vec<T>::N / 2];
+  float tc[D * TS][Vec<T>::N / 2], ts[D * TS][Vec<T>::N / 2];
 };
 
-template <typename T, int K, int D, bool VEC, bool LN, bool ROPE>
-__device__ __forceinline__ void load_batch(RowBatch<T, K, D, ROPE ? 1 : 0>& b, int64_t base,
+template <typename T, int K, int D, bool VEC, bool LN, bool ROPE, int TS>
+__device__ __forceinline__ void load_batch(RowBatch<T, K, D, TS>& b, int64_t base,
                                            int64_t rows, const T* x, const T* dy,
                                            const float* mean, const float* rstat, int n, int t,
                                            int nthr, const RopeArgs& ra) {
@@ -78,16 +81,16 @@ __device__ __forceinline__ void load_batch(RowBatch<T, K, D, ROPE ? 1 : 0>& b, i
       int hoff = (t * E) % ra.head_dim;
       const int hstep = (nthr * E) % ra.head_dim;
 #pragma unroll
-      for (int k = 0; k < K; ++k) {
+      for (int k = 0; k < TS; ++k) {
         if constexpr (VEC) {
-          load_tab<PP>(cr, hoff >> 1, b.tc[d * K + k]);
-          load_tab<PP>(sr, hoff >> 1, b.ts[d * K + k]);
+          load_tab<PP>(cr, hoff >> 1, b.tc[d * TS + k]);
+          load_tab<PP>(sr, hoff >> 1, b.ts[d * TS + k]);
         } else {
 #pragma unroll
           for (int p = 0; p < PP; ++p) {
             const int ho = (hoff + 2 * p) % ra.head_dim;
-            b.tc[d * K + k][p] = ld_f32(cr, (ho >> 1) * 4);
-            b.ts[d * K + k][p] = ld_f32(sr, (ho >> 1) * 4);
+            b.tc[d * TS + k][p] = ld_f32(cr, (ho >> 1) * 4);
+            b.ts[d * TS + k][p] = ld_f32(sr, (ho >> 1) * 4);
           }
         }
         hoff += hstep;
@@ -99,18 +102,21 @@ __device__ __forceinline__ void load_batch(RowBatch<T, K, D, ROPE ? 1 : 0>& b, i
 
 // dy of chunk i as fp32: the loaded values, rotated back by the token's
 // angles when the upstream gradient is that of a RoPE output
-template <typename T, int K, int D, bool ROPE>
-__device__ __forceinline__ void dy_chunk(const RowBatch<T, K, D, ROPE ? 1 : 0>& b, int i,
+template <typename T, int K, int D, bool ROPE, int TS>
+__device__ __forceinline__ void dy_chunk(const RowBatch<T, K, D, TS>& b, int i,
                                          float (&dv)[Vec<T>::N]) {
   unpack<T>(b.g[i], dv);
-  if constexpr (ROPE) rotate_pairs<Vec<T>::N / 2>(dv, b.tc[i], b.ts[i], -1.0f);
+  if constexpr (ROPE) {
+    const int slot = TS == K ? i : i / K;  // chunk i = d K + k of row d
+    rotate_pairs<Vec<T>::N / 2>(dv, b.tc[slot], b.ts[slot], -1.0f);
+  }
 }
 
 // EPI == kEpiGelu (LayerNorm): the upstream gradient is that of
 // gelu(xhat gamma + beta); the pre-activation is recomputed from the cached
 // statistics and dy = dout * gelu'(pre-activation).
-template <typename T, int K, int D, bool VEC, bool LN, bool ROPE, int EPI>
-__device__ __forceinline__ void process_batch(RowBatch<T, K, D, ROPE ? 1 : 0>& b, int64_t base,
+template <typename T, int K, int D, bool VEC, bool LN, bool ROPE, int EPI, int TS>
+__device__ __forceinline__ void process_batch(RowBatch<T, K, D, TS>& b, int64_t base,
                                               int64_t rows, T* dx, int n, int t, int nthr, int W,
                                               int wave, int lane, float inv_n,
                                               const float (&wv)[K][Vec<T>::N],
@@ -143,7 +149,7 @@ __device__ __forceinline__ void process_batch(RowBatch<T, K, D, ROPE ? 1 : 0>& b
     for (int k = 0; k < K; ++k) {
       float xv[E], dv[E], wl[E], bl[E];
       unpack<T>(b.x[d * K + k], xv);
-      dy_chunk<T, K, D, ROPE>(b, d * K + k, dv);
+      dy_chunk<T, K, D, ROPE, TS>(b, d * K + k, dv);
       if constexpr (LEAN) {
         u32x4 wq[1] = {wpk[k]}, bq[1] = {bpk[k]};
         reload_barrier<1>(wq);
@@ -215,7 +221,7 @@ __device__ __forceinline__ void process_batch(RowBatch<T, K, D, ROPE ? 1 : 0>& b
     for (int k = 0; k < K; ++k) {
       float xv[E], dv[E], o[E];
       if constexpr (EPI != kEpiGelu || LEAN) unpack<T>(b.x[d * K + k], xv);
-      if constexpr (EPI != kEpiGelu) dy_chunk<T, K, D, ROPE>(b, d * K + k, dv);
+      if constexpr (EPI != kEpiGelu) dy_chunk<T, K, D, ROPE, TS>(b, d * K + k, dv);
 #pragma unroll
       for (int e = 0; e < E; ++e) {
         float xh, gg;
@@ -240,12 +246,16 @@ __device__ __forceinline__ void process_batch(RowBatch<T, K, D, ROPE ? 1 : 0>& b
 // LB: the largest workgroup the instantiation serves.  1024 (16 waves) caps
 // a lane at 128 VGPRs; the deep-prefetch instantiations (PF 3, 4) take at
 // most 10 waves, i.e. one workgroup per CU, which leaves up to 168.
-template <typename T, int K, int D, int PF, bool VEC, bool LN, int EPI, int LB = 1024>
+// SHARED (RoPE, more than one chunk per lane): one set of table angles per
+// row, valid when the lane stride of the row is a multiple of the head size.
+template <typename T, int K, int D, int PF, bool VEC, bool LN, int EPI, int LB = 1024,
+          bool SHARED = false>
 __global__ void __launch_bounds__(LB)
 norm_bwd_rows(const T* dy, const T* x, const T* w, const T* beta, const float* mean,
               const float* rstat, T* dx, float* part, int64_t part_stride, int64_t rows, int n,
               float w_add, RopeArgs ra) {
   constexpr bool ROPE = EPI == kEpiRope;
+  constexpr int TS = ROPE ? (SHARED ? 1 : K) : 0;
   constexpr int E = Vec<T>::N;
   constexpr int NS = LN ? 2 : 1;
   __shared__ float red[2 * NS * D][16];
@@ -312,18 +322,18 @@ norm_bwd_rows(const T* dy, const T* x, const T* w, const T* beta, const float* m
   // PF batches are loaded ahead of the one being reduced; PF + 1 register
   // buffers are used in turn (the loop is unrolled over them, so no register
   // copy ever waits on a load in flight).
-  RowBatch<T, K, D, ROPE ? 1 : 0> buf[PF + 1];
+  RowBatch<T, K, D, TS> buf[PF + 1];
 #pragma unroll
   for (int i = 0; i < PF; ++i)
-    load_batch<T, K, D, VEC, LN, ROPE>(buf[i], base + i * step, rows, x, dy, mean, rstat, n, t,
+    load_batch<T, K, D, VEC, LN, ROPE, TS>(buf[i], base + i * step, rows, x, dy, mean, rstat, n, t,
                                        nthr, ra);
   while (true) {
 #pragma unroll
     for (int i = 0; i <= PF; ++i) {
       if (base >= rows) goto done;
-      load_batch<T, K, D, VEC, LN, ROPE>(buf[(i + PF) % (PF + 1)], base + PF * step, rows, x, dy,
+      load_batch<T, K, D, VEC, LN, ROPE, TS>(buf[(i + PF) % (PF + 1)], base + PF * step, rows, x, dy,
                                          mean, rstat, n, t, nthr, ra);
-      process_batch<T, K, D, VEC, LN, ROPE, EPI>(buf[i], base, rows, dx, n, t, nthr, W, wave, lane,
+      process_batch<T, K, D, VEC, LN, ROPE, EPI, TS>(buf[i], base, rows, dx, n, t, nthr, W, wave, lane,
                                                  inv_n, wv, bv, wpk, bpk, w_add_packed, acc1, acc2, red, parity);
       base += step;
     }
@@ -377,6 +387,14 @@ hipError_t launch_bwd_kd(const BwdPlan& pl, const void* dy, const void* x, const
       kern = pl.PF == 3 ? norm_bwd_rows<T, K, D, 3, A, LN, EP, 640>
                         : norm_bwd_rows<T, K, D, 4, A, LN, EP, 640>;
     }
+  }
+  // RoPE with several chunks per lane: when a lane's chunks sit at the same
+  // offset in their heads, one set of angles per row (the two-chunk kernel
+  // spilled with one per chunk)
+  if constexpr (EP == kEpiRope && K > 1 && D == 1) {
+    if ((64 * pl.W * Vec<T>::N) % ra.head_dim == 0)
+      kern = pl.PF == 2 ? norm_bwd_rows<T, K, D, 2, A, LN, EP, 1024, true>
+                        : norm_bwd_rows<T, K, D, 1, A, LN, EP, 1024, true>;
   }
   hipLaunchKernelGGL(kern, dim3(pl.P), dim3(64 * pl.W), 0, st, static_cast<const T*>(dy),
                      static_cast<const T*>(x), static_cast<const T*>(w),

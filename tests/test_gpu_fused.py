@@ -63,6 +63,12 @@ CASES = [
     (33, 8, 128, 1, torch.bfloat16, False, "unaligned"),
     (77, 40, 128, 1, torch.float16, False, "packed"),
     (48, 2, 64, 2, torch.float16, True, "packed"),
+    # two chunks per lane in the backward: one set of angles per row where the
+    # lane stride is a multiple of the head size, one per chunk where not (96)
+    (37, 96, 128, 1, torch.bfloat16, False, "packed"),    # 12288 wide, 12 waves
+    (29, 120, 128, 1, torch.float16, True, "packed"),     # 15360 wide, 15 waves
+    (31, 48, 128, 1, torch.float32, False, "packed"),     # 6144 fp32, 12 waves
+    (23, 100, 96, 1, torch.bfloat16, False, "packed"),    # 9600 wide: 5120 % 96 != 0
     (21, 160, 128, 1, torch.bfloat16, False, "packed"),   # 20480 wide: two-pass backward
     (9, 170, 102, 1, torch.float32, True, "packed"),      # 17340 wide, element-wise tables
 ]
