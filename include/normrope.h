@@ -150,8 +150,11 @@ nr_status_t layernorm_bwd(nr_dtype_t dt, const void* dy, const void* x,
  *   transpose).  Tables are fp32 [tokens][head_dim/2], shared by all heads
  *   and batches; build them with rope_table_1d / rope_table_3d or supply
  *   your own.  head_dim must be even.  Distinct (batch, token, head) vectors
- *   must not share elements (stride_head >= head_dim when heads > 1, else
- *   NR_ERR_ALIAS).  A token's heads must span less than 1 GiB
+ *   must not share elements, else NR_ERR_ALIAS: with the axes of size > 1
+ *   ordered by stride, each stride must be at least the span of the axes
+ *   inside it, starting from head_dim (so no stride 0 on such an axis;
+ *   transposed layouts such as [batch][heads][tokens] pass).  A token's
+ *   heads must span less than 1 GiB
  *   ((heads-1)*stride_head + head_dim elements), else NR_ERR_UNSUPPORTED_N.
  */
 nr_status_t rope_interleaved_apply(nr_dtype_t dt, void* x, const float* cos_tab,
@@ -329,6 +332,18 @@ nr_status_t nr_tune(const char* key, int value);
  * the ranges overlap; bytes == 0 is a no-op.  Asynchronous on `stream`.
  */
 nr_status_t nr_stream_copy(const void* src, void* dst, size_t bytes, void* stream);
+
+/*
+ * nr_stream_mix -- measurement aid like nr_stream_copy, for the other
+ * read/write mixes of the path: reads `bytes` bytes from each of a and b
+ * and, when write != 0, writes their bitwise xor to dst (two streams read,
+ * one written: the backward's mix); when write == 0 nothing is written
+ * (dst is only written if the two inputs' xor has an all-ones 16-byte
+ * word, so pass inputs whose words are not complements of each other).
+ * Same rules as nr_stream_copy (dst may not overlap a or b).
+ */
+nr_status_t nr_stream_mix(const void* a, const void* b, void* dst, size_t bytes, int write,
+                          void* stream);
 
 #ifdef __cplusplus
 }

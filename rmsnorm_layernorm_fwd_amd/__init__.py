@@ -20,7 +20,7 @@ __all__ = [
     "NormRopeError", "rmsnorm_fwd", "rmsnorm_bwd", "layernorm_fwd", "layernorm_bwd",
     "rmsnorm_rope_fwd", "rmsnorm_rope_bwd", "layernorm_gelu_fwd", "layernorm_gelu_bwd",
     "rope_interleaved_apply", "rope_table_1d", "rope_table_3d", "nr_bwd_workspace_bytes",
-    "nr_status_str", "nr_tune", "nr_norm_n_max", "nr_stream_copy", "rmsnorm_linear_fwd",
+    "nr_status_str", "nr_tune", "nr_norm_n_max", "nr_stream_copy", "nr_stream_mix", "rmsnorm_linear_fwd",
     "rmsnorm_linear_fold_weight", "nr_rmsnorm_linear_workspace_bytes",
     "library_path",
 ]
@@ -81,6 +81,7 @@ def _lib():
             "nr_tune": [ctypes.c_char_p, i32],
             "nr_norm_n_max": [i32],
             "nr_stream_copy": [vp, vp, sz, vp],
+            "nr_stream_mix": [vp, vp, vp, sz, i32, vp],
             "rmsnorm_linear_fwd": [i32, vp, vp, vp, vp, vp, i64, i64, i64, f32, i32, vp, sz, vp],
             "nr_rmsnorm_linear_workspace_bytes": [i64, i64, i64, i32],
             "rmsnorm_linear_fold_weight": [i32, vp, vp, vp, i64, i64, i32, vp],
@@ -165,7 +166,7 @@ def rmsnorm_fwd(x, w=None, eps=1e-6, gemma_offset=False, y=None, inv_rms=None, w
     _dev("y", y, x.dtype, x.shape, device=x.device)
     if inv_rms is None and want_stats:
         inv_rms = torch.empty(x.shape[:-1], dtype=torch.float32, device=x.device)
-    _dev("inv_rms", inv_rms, torch.float32, device=x.device)
+    _dev("inv_rms", inv_rms, torch.float32, x.shape[:-1], device=x.device)
     _run("rmsnorm_fwd", x,
          dt, _ptr(x), _ptr(w), _ptr(y), _ptr(inv_rms), rows, n, float(eps),
          int(bool(gemma_offset)))
@@ -212,8 +213,8 @@ def layernorm_fwd(x, gamma=None, beta=None, eps=1e-5, y=None, mean=None, rstd=No
             mean = torch.empty(x.shape[:-1], dtype=torch.float32, device=x.device)
         if rstd is None:
             rstd = torch.empty(x.shape[:-1], dtype=torch.float32, device=x.device)
-    _dev("mean", mean, torch.float32, device=x.device)
-    _dev("rstd", rstd, torch.float32, device=x.device)
+    _dev("mean", mean, torch.float32, x.shape[:-1], device=x.device)
+    _dev("rstd", rstd, torch.float32, x.shape[:-1], device=x.device)
     _run("layernorm_fwd", x,
          dt, _ptr(x), _ptr(gamma), _ptr(beta), _ptr(y), _ptr(mean), _ptr(rstd), rows, n,
          float(eps))
@@ -266,8 +267,8 @@ def layernorm_gelu_fwd(x, gamma=None, beta=None, eps=1e-5, y=None, mean=None, rs
             mean = torch.empty(x.shape[:-1], dtype=torch.float32, device=x.device)
         if rstd is None:
             rstd = torch.empty(x.shape[:-1], dtype=torch.float32, device=x.device)
-    _dev("mean", mean, torch.float32, device=x.device)
-    _dev("rstd", rstd, torch.float32, device=x.device)
+    _dev("mean", mean, torch.float32, x.shape[:-1], device=x.device)
+    _dev("rstd", rstd, torch.float32, x.shape[:-1], device=x.device)
     _run("layernorm_gelu_fwd", x,
          dt, _ptr(x), _ptr(gamma), _ptr(beta), _ptr(y), _ptr(mean), _ptr(rstd), rows, n,
          float(eps))
@@ -327,7 +328,7 @@ def rmsnorm_rope_fwd(x, w, cos_tab, sin_tab, head_dim, rows_per_token=1, eps=1e-
     _dev("y", y, x.dtype, x.shape, device=x.device)
     if inv_rms is None and want_stats:
         inv_rms = torch.empty(x.shape[:-1], dtype=torch.float32, device=x.device)
-    _dev("inv_rms", inv_rms, torch.float32, device=x.device)
+    _dev("inv_rms", inv_rms, torch.float32, x.shape[:-1], device=x.device)
     _run("rmsnorm_rope_fwd", x,
          dt, _ptr(x), _ptr(w), _ptr(y), _ptr(inv_rms), _ptr(cos_tab), _ptr(sin_tab), rows, n,
          head_dim, rows_per_token, float(eps), int(bool(gemma_offset)))
@@ -414,7 +415,7 @@ def rmsnorm_linear_fwd(x, w_norm, W, eps=1e-6, gemma_offset=False, out=None, inv
     _dev("out", out, torch.bfloat16, x.shape[:-1] + (n,), device=x.device)
     if inv_rms is None and want_stats:
         inv_rms = torch.empty(x.shape[:-1], dtype=torch.float32, device=x.device)
-    _dev("inv_rms", inv_rms, torch.float32, device=x.device)
+    _dev("inv_rms", inv_rms, torch.float32, x.shape[:-1], device=x.device)
     wsb = nr_rmsnorm_linear_workspace_bytes(rows, n, k, w_norm is not None)
     if workspace is None and wsb > 0:
         workspace = torch.empty(wsb, dtype=torch.uint8, device=x.device)
@@ -462,6 +463,18 @@ def nr_stream_copy(src: torch.Tensor, dst: torch.Tensor):
     if dst.numel() * dst.element_size() != nbytes or src.device != dst.device:
         raise ValueError("nr_stream_copy: src and dst must have the same size and device")
     _run("nr_stream_copy", src, _ptr(src), _ptr(dst), nbytes)
+
+
+def nr_stream_mix(a: torch.Tensor, b: torch.Tensor, dst: torch.Tensor, write: bool = True):
+    """Measurement aid: read a and b (and write a ^ b to dst when `write`)
+    with the same access pattern as nr_stream_copy."""
+    _dev("a", a)
+    _dev("b", b, device=a.device)
+    _dev("dst", dst, device=a.device)
+    nbytes = a.numel() * a.element_size()
+    if any(t.numel() * t.element_size() != nbytes for t in (b, dst)):
+        raise ValueError("nr_stream_mix: a, b and dst must have the same size")
+    _run("nr_stream_mix", a, _ptr(a), _ptr(b), _ptr(dst), nbytes, int(bool(write)))
 
 
 def nr_status_str(status: int) -> str:

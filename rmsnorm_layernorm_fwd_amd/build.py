@@ -1,6 +1,6 @@
 """Build libnormrope.so (the C-ABI library) for gfx950 with hipcc, in-tree.
 
-    python -m rmsnorm_layernorm_fwd_amd.build
+    python -m rmsnorm_layernorm_fwd_amd.build [--incremental]
 
 Each .hip file under csrc/ is compiled to an object in parallel, then linked
 into rmsnorm_layernorm_fwd_amd/libnormrope.so.  Packed-fp32 instruction
@@ -29,8 +29,15 @@ CFLAGS = [
 ]
 
 
-def _compile(src: str) -> str:
+def _compile(src: str, newest_header: float = None) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
+    if newest_header is not None and os.path.exists(obj):
+        deps = [os.path.getmtime(src), newest_header]
+        with open(src) as fh:
+            if "normrope.h" in fh.read():
+                deps += [os.path.getmtime(h) for h in glob.glob(os.path.join(HERE, "..", "include", "*.h"))]
+        if os.path.getmtime(obj) > max(deps):
+            return obj
     cmd = [HIPCC, *CFLAGS, "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
@@ -38,11 +45,15 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
+def build(verbose: bool = False, incremental: bool = False) -> str:
+    """Compiles every source (incremental: only those older than their
+    object, headers included) and links the library."""
     os.makedirs(BUILD, exist_ok=True)
     srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
+    headers = glob.glob(os.path.join(CSRC, "*.hpp"))
+    newest = max(os.path.getmtime(h) for h in headers) if incremental else None
     with cf.ThreadPoolExecutor(max_workers=min(len(srcs), os.cpu_count() or 1)) as ex:
-        objs = list(ex.map(_compile, srcs))
+        objs = list(ex.map(lambda s: _compile(s, newest), srcs))
     tmp = LIB + ".tmp"
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -55,5 +66,5 @@ def build(verbose: bool = False) -> str:
 
 
 if __name__ == "__main__":
-    build(verbose=True)
+    build(verbose=True, incremental="--incremental" in sys.argv)
     sys.exit(0)

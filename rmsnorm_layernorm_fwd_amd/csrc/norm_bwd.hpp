@@ -238,7 +238,7 @@ __device__ __forceinline__ void process_batch(RowBatch<T, K, D, TS>& b, int64_t 
           o[e] = b.rs[d] * (gg - xh * c1);
         }
       }
-      st_chunk<T, VEC, kStream>(dr, t + k * nthr, pack<T>(o));
+      st_chunk<T, VEC, kNormStore>(dr, t + k * nthr, pack<T>(o));
     }
   }
 }

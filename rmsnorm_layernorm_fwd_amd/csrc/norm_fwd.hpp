@@ -42,31 +42,13 @@ __device__ __forceinline__ void group_sum_n(float (&v)[J], int W, int wave, int 
   }
 }
 
-// A row group (W waves) normalises J consecutive rows; the weight chunks it
-// loads serve all J of them.  Epilogues, applied before the single rounding:
-// kEpiRope (RMSNorm) rotates the normalised row as interleaved RoPE pairs by
-// its token's angles, so the norm -> RoPE chain costs one read and one write
-// of the row; kEpiGelu (LayerNorm) passes the affine output through the
-// tanh-approximated GeLU (LLM层的优化算子, 编写定制融合算子).
-template <typename T, int K, int J, bool VEC, bool LN, int EPI>
-__device__ __forceinline__ void norm_fwd_body(const T* x, const T* w, const T* b, T* y,
-                                              float* stat0, float* stat1, int64_t rows, int n,
-                                              float eps, float w_add, int W, const RopeArgs& ra) {
-  constexpr int E = Vec<T>::N;
-  __shared__ float red0[J][16], red1[J][16];
-  const int lane = threadIdx.x & 63;
-  const int wave = wave_id();
-  const int g = wave / W;
-  const int t = (wave - g * W) * 64 + lane;
-  const int nthr = 64 * W;
-  const int R = blockDim.x / nthr;
-  const int64_t row0 = (static_cast<int64_t>(blockIdx.x) * R + g) * J;
+// Loads the J consecutive rows of a row group starting at row0 (16-byte
+// chunks, lane t owning chunks t, t + 64 W, ...).  Rows past the last one see
+// an empty buffer: their loads return 0 and move no data.
+template <typename T, int K, int J, bool VEC>
+__device__ __forceinline__ void fwd_load_rows(u32x4 (&xa)[J * K], const T* x, int64_t row0,
+                                              int64_t rows, int n, int t, int nthr) {
   const uint32_t rbytes = static_cast<uint32_t>(n) * sizeof(T);
-  const rsrc_t wr = make_rsrc(w, w != nullptr ? rbytes : 0u);
-  const rsrc_t br = make_rsrc(b, b != nullptr ? rbytes : 0u);
-
-  // rows past the last one see an empty buffer: loads give 0, stores vanish
-  u32x4 xa[J * K], wa[K], ba[K];
 #pragma unroll
   for (int j = 0; j < J; ++j) {
     const int64_t row = row0 + j;
@@ -75,12 +57,26 @@ __device__ __forceinline__ void norm_fwd_body(const T* x, const T* w, const T* b
 #pragma unroll
     for (int k = 0; k < K; ++k) xa[j * K + k] = ld_chunk<T, VEC, kStream>(xr, t + k * nthr);
   }
-#pragma unroll
-  for (int k = 0; k < K; ++k) {
-    wa[k] = ld_chunk<T, VEC>(wr, t + k * nthr);
-    if constexpr (LN) ba[k] = ld_chunk<T, VEC>(br, t + k * nthr);
-  }
+}
 
+// A row group (W waves) normalises the J consecutive rows it has loaded; the
+// weight chunks serve all J of them.  Epilogues, applied before the single
+// rounding: kEpiRope (RMSNorm) rotates the normalised row as interleaved RoPE
+// pairs by its token's angles, so the norm -> RoPE chain costs one read and
+// one write of the row; kEpiGelu (LayerNorm) passes the affine output through
+// the tanh-approximated GeLU (LLM层的优化算子, 编写定制融合算子).
+// red0, red1: LDS scratch [J][16] for this call's two workgroup reductions;
+// a caller that loops hands in a different pair on consecutive calls (the
+// reductions have one barrier each, so a pair is free again after the next).
+template <typename T, int K, int J, bool VEC, bool LN, int EPI>
+__device__ __forceinline__ void fwd_finish_rows(u32x4 (&xa)[J * K], u32x4 (&wa)[K],
+                                                u32x4 (&ba)[K], const T* w, T* y, float* stat0,
+                                                float* stat1, int64_t row0, int64_t rows, int n,
+                                                float eps, float w_add, int W, int wave, int g,
+                                                int t, int nthr, const RopeArgs& ra,
+                                                float (*red0)[16], float (*red1)[16]) {
+  constexpr int E = Vec<T>::N;
+  const uint32_t rbytes = static_cast<uint32_t>(n) * sizeof(T);
   const float fn = static_cast<float>(n);
   float mean[J], r[J];
   if constexpr (LN) {
@@ -194,7 +190,7 @@ __device__ __forceinline__ void norm_fwd_body(const T* x, const T* w, const T* b
         hoff += hstep;
         if (hoff >= ra.head_dim) hoff -= ra.head_dim;
       }
-      st_chunk<T, VEC, kStream>(yr, t + k * nthr, pack<T>(o));
+      st_chunk<T, VEC, kNormStore>(yr, t + k * nthr, pack<T>(o));
     }
     if (active && t == 0) {
       if constexpr (LN) {
@@ -205,6 +201,39 @@ __device__ __forceinline__ void norm_fwd_body(const T* x, const T* w, const T* b
       }
     }
   }
+}
+
+template <typename T, int K, bool VEC, bool LN>
+__device__ __forceinline__ void fwd_load_weights(u32x4 (&wa)[K], u32x4 (&ba)[K], const T* w,
+                                                 const T* b, int n, int t, int nthr) {
+  const uint32_t rbytes = static_cast<uint32_t>(n) * sizeof(T);
+  const rsrc_t wr = make_rsrc(w, w != nullptr ? rbytes : 0u);
+  const rsrc_t br = make_rsrc(b, b != nullptr ? rbytes : 0u);
+#pragma unroll
+  for (int k = 0; k < K; ++k) {
+    wa[k] = ld_chunk<T, VEC>(wr, t + k * nthr);
+    if constexpr (LN) ba[k] = ld_chunk<T, VEC>(br, t + k * nthr);
+  }
+}
+
+// One-shot form: each row group of the grid normalises its J rows once.
+template <typename T, int K, int J, bool VEC, bool LN, int EPI>
+__device__ __forceinline__ void norm_fwd_body(const T* x, const T* w, const T* b, T* y,
+                                              float* stat0, float* stat1, int64_t rows, int n,
+                                              float eps, float w_add, int W, const RopeArgs& ra) {
+  __shared__ float red0[J][16], red1[J][16];
+  const int lane = threadIdx.x & 63;
+  const int wave = wave_id();
+  const int g = wave / W;
+  const int t = (wave - g * W) * 64 + lane;
+  const int nthr = 64 * W;
+  const int R = blockDim.x / nthr;
+  const int64_t row0 = (static_cast<int64_t>(blockIdx.x) * R + g) * J;
+  u32x4 xa[J * K], wa[K], ba[K];
+  fwd_load_rows<T, K, J, VEC>(xa, x, row0, rows, n, t, nthr);
+  fwd_load_weights<T, K, VEC, LN>(wa, ba, w, b, n, t, nthr);
+  fwd_finish_rows<T, K, J, VEC, LN, EPI>(xa, wa, ba, w, y, stat0, stat1, row0, rows, n, eps, w_add,
+                                         W, wave, g, t, nthr, ra, red0, red1);
 }
 
 // One wavefront per row group (W == 1), at most 4 row groups (256 threads)
@@ -230,8 +259,9 @@ hipError_t launch_fwd_kj(const FwdPlan& pl, const void* x, const void* w, const 
                          float* s0, float* s1, int64_t rows, int n, float eps, float w_add,
                          const RopeArgs& ra, hipStream_t st) {
   const int64_t per_block = static_cast<int64_t>(pl.R) * J;
-  const dim3 grid(static_cast<unsigned>((rows + per_block - 1) / per_block));
+  const int64_t blocks = (rows + per_block - 1) / per_block;
   const dim3 block(64 * pl.W * pl.R);
+  const dim3 grid(static_cast<unsigned>(blocks));
   if (pl.W == 1) {
     hipLaunchKernelGGL((norm_fwd_wave<T, K, J, A, LN, RP>), grid, block, 0, st,
                        static_cast<const T*>(x), static_cast<const T*>(w),

@@ -148,6 +148,11 @@ constexpr int kStream = NR_STREAM_AUX;
 #define NR_STREAM_STORE_AUX 18
 #endif
 constexpr int kStreamStore = NR_STREAM_STORE_AUX;
+// Stores of the norm kernels' outputs (y, dx).
+#ifndef NR_NORM_STORE_AUX
+#define NR_NORM_STORE_AUX NR_STREAM_AUX
+#endif
+constexpr int kNormStore = NR_NORM_STORE_AUX;
 
 __device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0),

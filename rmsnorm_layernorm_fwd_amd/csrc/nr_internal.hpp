@@ -104,6 +104,8 @@ hipError_t launch_rmsnorm_linear(const void* x, const void* wn, const void* W, v
 hipError_t launch_fold_norm_weight(const void* wn, const void* W, void* Wf, int64_t N, int K,
                                    float w_add, hipStream_t st);
 hipError_t launch_stream_copy(const void* src, void* dst, int64_t nvec, hipStream_t st);
+hipError_t launch_stream_mix(const void* a, const void* b, void* dst, int64_t nvec, bool write,
+                             hipStream_t st);
 hipError_t launch_rope_table_3d(float* cos_tab, float* sin_tab, int64_t frames, int64_t height,
                                 int64_t width, int pt, int ph, int pw, double theta,
                                 hipStream_t st);

@@ -38,7 +38,7 @@ def test_header_functions_exported(lib):
                 "rmsnorm_rope_fwd", "rmsnorm_rope_bwd", "layernorm_gelu_fwd", "layernorm_gelu_bwd",
                 "rope_interleaved_apply", "rope_table_1d", "rope_table_3d",
                 "nr_bwd_workspace_bytes", "nr_status_str", "nr_last_hip_error", "nr_tune",
-                "nr_norm_n_max", "nr_stream_copy", "rmsnorm_linear_fwd",
+                "nr_norm_n_max", "nr_stream_copy", "nr_stream_mix", "rmsnorm_linear_fwd",
                 "rmsnorm_linear_fold_weight", "nr_rmsnorm_linear_workspace_bytes"}
     assert expected <= set(names), names
     out = subprocess.run(["nm", "-D", "--defined-only", nr.library_path()],
@@ -203,6 +203,11 @@ def test_rejected_calls_return_status(lib):
     assert L.nr_stream_copy(FAKE, FAKE + 32, 64, None) == NR_ERR_ALIAS
     assert L.nr_stream_copy(FAKE, FAKE, 64, None) == NR_ERR_ALIAS
     assert L.nr_stream_copy(None, None, 0, None) == NR_OK
+    assert L.nr_stream_mix(FAKE, None, 0x90000, 64, 1, None) == NR_ERR_NULLPTR
+    assert L.nr_stream_mix(FAKE, 0x80000, 0x90000, 60, 1, None) == NR_ERR_SHAPE
+    assert L.nr_stream_mix(FAKE, 0x80000, FAKE + 32, 64, 0, None) == NR_ERR_ALIAS
+    assert L.nr_stream_mix(FAKE, 0x80000, 0x80000, 64, 1, None) == NR_ERR_ALIAS
+    assert L.nr_stream_mix(None, None, None, 0, 1, None) == NR_OK
     # long rows need the workspace even without a column gradient
     X2, DX2, WS2 = 1 << 24, 1 << 25, 1 << 26
     assert L.rmsnorm_bwd(BF16, FAKE, X2, None, FAKE, DX2, None, 4, 20000, 0, None, 0, None) == NR_ERR_WORKSPACE
@@ -231,3 +236,84 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(nr, "_LIB_PATH", str(tmp_path / "missing.so"))
     with pytest.raises(ImportError):
         nr._lib()
+
+
+def test_rope_rejects_overlapping_vectors(lib):
+    """Distinct (batch, token, head) vectors of the in-place rotation may not
+    share elements: broadcast (stride 0) axes and strides shorter than the
+    block inside them are refused before anything is queued.  Packed,
+    padded and transposed layouts pass the check; a null table then stops
+    them at the null-pointer check, so nothing is launched."""
+    L = lib
+    A = NR_ERR_ALIAS
+    ra = L.rope_interleaved_apply
+    # (batch, tokens, heads, head_dim, stride_batch, stride_token, stride_head)
+    overlapping = [
+        (1, 4, 2, 8, 64, 0, 8),      # tokens broadcast (expand) over one vector
+        (2, 4, 2, 8, 0, 16, 8),      # batch broadcast
+        (1, 4, 2, 8, 64, 8, 8),      # token stride shorter than a token's two heads
+        (1, 4, 3, 8, 64, 16, 8),     # three heads in a 16-element token stride
+        (2, 4, 2, 8, 32, 16, 8),     # batch stride shorter than its 4 tokens x 16
+        (1, 4, 2, 8, 64, 2, 8),      # token stride inside a head vector
+        (1, 4, 2, 8, 64, 16, 4),     # heads overlap (stride_head < head_dim)
+        (1, 4, 2, 8, 64, 8, 16),     # [H, T]: the second head starts inside token 2's vector
+    ]
+    for shp in overlapping:
+        assert ra(BF16, FAKE, FAKE, FAKE, *shp, 0, None) == A, shp
+    disjoint = [
+        (1, 4, 2, 8, 64, 16, 8),     # packed
+        (2, 4, 2, 8, 64, 16, 8),     # packed batches
+        (1, 4, 2, 8, 128, 24, 8),    # padded tokens
+        (2, 4, 2, 8, 64, 8, 32),     # [B, H, T, D]: heads outermost within a batch
+        (1, 1, 2, 8, 0, 0, 8),       # size-1 axes may have any stride
+        (3, 4, 1, 8, 32, 8, 0),      # one head: its stride is irrelevant
+    ]
+    for shp in disjoint:
+        # passes the overlap check and stops at the (later) null-pointer check
+        assert ra(BF16, FAKE, None, FAKE, *shp, 0, None) == NR_ERR_NULLPTR, shp
+
+
+def test_binding_checks_stat_shapes_before_launch(monkeypatch):
+    """A caller-supplied statistics buffer of the wrong shape is refused by
+    the binding before the library is called (a short buffer would let the
+    kernels' per-row statistics stores run past it).  The tensors are CPU
+    tensors posing as GPU tensors; the library call itself is replaced by a
+    trap, so nothing runs on a device."""
+    import torch
+
+    class Posing(torch.Tensor):
+        @property
+        def device(self):
+            return torch.device("cuda", 0)
+
+    def fake(t):
+        return torch.Tensor._make_subclass(Posing, t)
+
+    def trap(*a, **k):
+        raise AssertionError("library called despite a bad statistics buffer")
+
+    monkeypatch.setattr(nr, "_run", trap)
+    x = fake(torch.zeros(6, 16, dtype=torch.bfloat16))
+    y = fake(torch.zeros(6, 16, dtype=torch.bfloat16))
+    w = fake(torch.zeros(16, dtype=torch.bfloat16))
+    short = fake(torch.zeros(5, dtype=torch.float32))
+    ok = fake(torch.zeros(6, dtype=torch.float32))
+    with pytest.raises(ValueError, match="shape"):
+        nr.rmsnorm_fwd(x, w, y=y, inv_rms=short)
+    with pytest.raises(ValueError, match="shape"):
+        nr.layernorm_fwd(x, w, w, y=y, mean=short, rstd=ok)
+    with pytest.raises(ValueError, match="shape"):
+        nr.layernorm_fwd(x, w, w, y=y, mean=ok, rstd=short)
+    with pytest.raises(ValueError, match="shape"):
+        nr.layernorm_gelu_fwd(x, w, w, y=y, mean=ok, rstd=short)
+    ct = fake(torch.zeros(6, 4, dtype=torch.float32))
+    with pytest.raises(ValueError, match="shape"):
+        nr.rmsnorm_rope_fwd(x, w, ct, ct, 8, 1, y=y, inv_rms=short)
+    xl = fake(torch.zeros(6, 64, dtype=torch.bfloat16))
+    Wl = fake(torch.zeros(128, 64, dtype=torch.bfloat16))
+    ol = fake(torch.zeros(6, 128, dtype=torch.bfloat16))
+    with pytest.raises(ValueError, match="shape"):
+        nr.rmsnorm_linear_fwd(xl, None, Wl, out=ol, inv_rms=short)
+    # the right shapes reach the (trapped) library call
+    with pytest.raises(AssertionError, match="library called"):
+        nr.rmsnorm_fwd(x, w, y=y, inv_rms=ok)

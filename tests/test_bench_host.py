@@ -42,3 +42,11 @@ def test_traffic_taken_on_other_sources_is_not_used(tmp_path, monkeypatch):
     _summary(tmp_path, monkeypatch, ["source_hash = old", "bytes_per_launch.k = 5"], digest="new")
     assert bench.read_traffic("k", "wl") is None
     assert bench.read_traffic("k", "no_such_workload") is None
+
+
+def test_operation_mix():
+    import bench
+    assert bench.op_mix("rmsnorm_bwd") == "2R1W"
+    assert bench.op_mix("layernorm_gelu_bwd") == "2R1W"
+    assert bench.op_mix("rmsnorm_fwd") == "1R1W"
+    assert bench.op_mix("rope_inverse") == "1R1W"

@@ -1,11 +1,15 @@
 """GPU parity of the RMSNorm -> linear fusion (rmsnorm_linear_fwd) against
 the oracle's fp64 RMSNorm followed by an fp64 matrix product.
 
-Bound, derived from the arithmetic: x enters the bf16 matrix cores exactly;
-each product's weight w'_k W[n][k] is rounded once to bf16 (2^-9 relative)
-and the K products are added in fp32 (at most K 2^-24 relative of their
-magnitude sum), so |O - R| <= ulp_bf16(R) + 2^-8 S, S = sum_k |y_k W[n][k]|
-(exact for w_norm NULL up to the fp32 sum), for K <= 65536.
+Bound, derived from the arithmetic (tolerance.linear_extra): x enters the
+bf16 matrix cores exactly; each product's weight w'_k W[n][k] is rounded
+once to bf16 and the K products are added in fp32, so
+  |O - R| <= ulp_bf16(R) + 1e-5 |R| + c1 2^-9 sqrt(sum_k p_k^2) + c2 sqrt(K) 2^-24 S
+with p_k = y_k W[n][k], S = sum_k |p_k|, c1 = 6 (0 without a norm weight,
+W then entering exactly) and c2 = 8.  At K = 5120 with W ~ N(0, 1/K) that
+is about 3 bf16 ulps of an output of size 1; numpy negative controls in
+tests/test_oracle_linear.py show that a dropped 16-wide K step, a twice
+applied norm weight and a coarser folded weight all break it.
 
 Two kernels serve the call: 128 x 128 output tiles (small grids) and 256 x
 256 tiles with the norm weight folded into W first (large grids); the tests
@@ -18,7 +22,7 @@ import torch
 import oracle
 import rmsnorm_layernorm_fwd_amd as nr
 import workloads
-from tolerance import check, to64, ulp_bf16
+from tolerance import check, linear_extra, ulp_bf16
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -47,11 +51,11 @@ def run_case(tag, m, n, k, seed, weight="w", gemma=False, rows=None):
     R, rr, S = oracle.rmsnorm_linear(x[sel], w, W, 1e-6, gemma)
     idx = torch.as_tensor(sel, device=DEV)
     O = out[idx].cpu()
-    check(f"{tag} out", O, R, "bf16", s=0.0, extra=2.0 ** -8 * S)
+    y, _ = oracle.rmsnorm_fwd(x[sel], w, 1e-6, gemma)
+    extra = linear_extra(R, y, W, folded=w is not None)
+    worst = check(f"{tag} out", O, R, "bf16", s=0.0, extra=extra)
     check(f"{tag} inv_rms", r[idx].cpu(), rr, "stat", s=0.0)
-    # the bound is not vacuous: the error is far below the magnitude sum
-    err = np.abs(to64(O) - R)
-    assert np.max(err / (ulp_bf16(R) + 2.0 ** -8 * S)) <= 1.0
+    print(f"[case] {tag}: worst error / bound {worst:.3f}", flush=True)
     return out
 
 
@@ -151,8 +155,7 @@ def test_rmsnorm_linear_long_sequence_sampled():
 
 def test_rmsnorm_linear_matches_unfused_closely():
     # the fused and the unfused path (rmsnorm_fwd, then the vendor GEMM on
-    # the bf16 y) each round once at the operand; both stay within the
-    # oracle bound, and they agree with each other to the same order
+    # the bf16 y) each round once at the operand
     m, n, k = 512, 768, 1024
     x = workloads.normal((m, k), 9950, torch.bfloat16).to(DEV)
     w = workloads.normal((k,), 9951, torch.bfloat16, mean=1.0, std=0.1).to(DEV)
@@ -163,6 +166,10 @@ def test_rmsnorm_linear_matches_unfused_closely():
     torch.cuda.synchronize()
     # the two sum x^2 in different orders: equal to a few fp32 ulps
     assert torch.allclose(r, r2, rtol=2e-6, atol=0)
-    _, _, S = oracle.rmsnorm_linear(x.cpu(), w.cpu(), W.cpu())
-    d = (out.float() - ref).abs().cpu().double().numpy()
-    assert np.all(d <= ulp_bf16(ref.cpu().double().numpy()) + 2.0 ** -7 * S)
+    # both are held to the same derived bound of the fp64 composition (the
+    # unfused path rounds y to bf16 where the fused one rounds w' W)
+    R, _, _ = oracle.rmsnorm_linear(x.cpu(), w.cpu(), W.cpu())
+    y64, _ = oracle.rmsnorm_fwd(x.cpu(), w.cpu(), 1e-6)
+    extra = linear_extra(R, y64, W.cpu(), folded=True)
+    check("fused", out.cpu(), R, "bf16", s=0.0, extra=extra)
+    check("unfused", ref.cpu(), R, "bf16", s=0.0, extra=extra)

@@ -30,13 +30,6 @@ def g(t):
     return None if t is None else t.to(DEV)
 
 
-def sample_rows(m, k, seed, must=()):
-    rng = np.random.default_rng(seed)
-    rows = set(rng.choice(m, size=min(k, m), replace=False).tolist())
-    rows |= {0, m - 1, *[int(r) for r in must]}
-    return np.array(sorted(rows), dtype=np.int64)
-
-
 def ulp32(c):
     a = np.abs(c)
     _, e = np.frexp(a)
@@ -168,27 +161,61 @@ def test_rope3d_15360x40x128(which):
 def longseq():
     inp = workloads.norm_inputs("longseq_65536x5120")
     spec = workloads.WORKLOADS["longseq_65536x5120"]["rope"]
-    rows = sample_rows(65536, 48, 5, must=inp["outlier_rows"][:16].tolist())
-    return inp, spec, rows
+    return inp, spec
+
+
+def row_blocks(m, bs=4096):
+    """Every row, in host-side blocks (bounded fp64 memory)."""
+    for b0 in range(0, m, bs):
+        yield b0, min(m, b0 + bs)
 
 
 def test_longseq_rmsnorm(longseq):
-    inp, _, rows = longseq
+    """Every row of y, inv_rms and dx, and the full dw, at the benchmark's
+    shape and launch configuration (outlier rows included)."""
+    inp, _ = longseq
     x, w, dy, eps = inp["x"], inp["w"], inp["dy"], inp["eps"]
-    say("longseq_65536x5120: rmsnorm fwd+bwd, sampled rows + full dw")
+    say("longseq_65536x5120: rmsnorm fwd+bwd, every row + full dw")
     y, r, dx, dw = run_rms(x, w, dy, eps, False)
-    ry, rr = oracle.rmsnorm_fwd(x[rows], w, eps)
-    rdx, _ = oracle.rmsnorm_bwd(dy[rows], x[rows], w, eps, want_dw=False)
+    y, r, dx = y.cpu(), r.cpu(), dx.cpu()
+    for b0, b1 in row_blocks(65536):
+        ry, rr = oracle.rmsnorm_fwd(x[b0:b1], w, eps)
+        rdx, _ = oracle.rmsnorm_bwd(dy[b0:b1], x[b0:b1], w, eps, want_dw=False)
+        check(f"longseq y rows {b0}..", y[b0:b1], ry, "bf16")
+        check(f"longseq inv_rms rows {b0}..", r[b0:b1], rr, "stat", s=0.0)
+        check(f"longseq dx rows {b0}..", dx[b0:b1], rdx, "bf16", s=grad_scale(rr, dy[b0:b1], w))
     _, rdw = oracle.rmsnorm_bwd(dy, x, w, eps, want_dx=False)
-    idx = torch.from_numpy(rows).to(DEV)
-    check("longseq y", y[idx], ry, "bf16")
-    check("longseq inv_rms", r[idx], rr, "stat", s=0.0)
-    check("longseq dx", dx[idx], rdx, "bf16", s=grad_scale(rr, dy[rows], w))
     check("longseq dw", dw, rdw, "col")
 
 
+def test_longseq_layernorm(longseq):
+    """LayerNorm fwd+bwd at the benchmark's long-sequence shape (x and dout of
+    the long sequence, gamma and beta of the affine workload, eps 1e-5):
+    every row of y, mean, rstd and dx, and the full dgamma and dbeta."""
+    inp, _ = longseq
+    lnp = workloads.norm_inputs("ln_affine_15360x5120")
+    x, dy, gm, bt, eps = inp["x"], inp["dy"], lnp["w"], lnp["b"], 1e-5
+    say("longseq_65536x5120: layernorm fwd+bwd, every row + full dgamma, dbeta")
+    y, mu, rs = nr.layernorm_fwd(g(x), g(gm), g(bt), eps=eps)
+    dx, dg, db = nr.layernorm_bwd(g(dy), g(x), g(gm), mu, rs)
+    torch.cuda.synchronize()
+    y, mu, rs, dx = y.cpu(), mu.cpu(), rs.cpu(), dx.cpu()
+    for b0, b1 in row_blocks(65536):
+        ry, rmu, rrs = oracle.layernorm_fwd(x[b0:b1], gm, bt, eps)
+        rdx, _, _ = oracle.layernorm_bwd(dy[b0:b1], x[b0:b1], gm, eps, want_dw=False)
+        x64 = to64(x[b0:b1])
+        check(f"longseq ln y rows {b0}..", y[b0:b1], ry, "bf16")
+        check(f"longseq ln mean rows {b0}..", mu[b0:b1], rmu, "stat",
+              s=np.sqrt(np.mean(x64 * x64, axis=1)))
+        check(f"longseq ln rstd rows {b0}..", rs[b0:b1], rrs, "stat", s=0.0)
+        check(f"longseq ln dx rows {b0}..", dx[b0:b1], rdx, "bf16", s=grad_scale(rrs, dy[b0:b1], gm))
+    _, rdg, rdb = oracle.layernorm_bwd(dy, x, gm, eps, want_dx=False)
+    check("longseq dgamma", dg, rdg, "col")
+    check("longseq dbeta", db, rdb, "col")
+
+
 def test_longseq_rope(longseq):
-    inp, spec, rows = longseq
+    inp, spec = longseq
     d, h = 128, 40
     ang = oracle.rope_angles(spec["table"], 65536, d)
     say("longseq_65536x5120: rope table 1-D 65536 tokens")
@@ -196,49 +223,50 @@ def test_longseq_rope(longseq):
     torch.cuda.synchronize()
     check_table("longseq", ct, st, ang)
     for name, src, inv in (("x forward", inp["x"], False), ("dout inverse", inp["dy"], True)):
-        say(f"longseq_65536x5120: rope {name}")
+        say(f"longseq_65536x5120: rope {name}, every token")
         xg = g(src).view(1, 65536, h, d).clone()
         nr.rope_interleaved_apply(xg, ct, st, inverse=inv)
         torch.cuda.synchronize()
-        idx = torch.from_numpy(rows).to(DEV)
-        sub = src[rows].view(1, len(rows), h, d)
-        ref = oracle.rope_apply(sub, ang[rows], inv)
-        check(f"longseq rope {name}", xg[0, idx].reshape(-1, d), ref.reshape(-1, d), "bf16")
+        xg = xg.cpu()
+        for b0, b1 in row_blocks(65536, 8192):
+            ref = oracle.rope_apply(src[b0:b1].view(1, b1 - b0, h, d), ang[b0:b1], inv)
+            check(f"longseq rope {name} tokens {b0}..", xg[0, b0:b1].reshape(-1, d), ref.reshape(-1, d),
+                  "bf16")
 
 
 def test_longseq_chain(longseq):
     """norm -> RoPE forward, and RoPE inverse -> norm backward, against the
-    oracle's fp64 chain.  The GPU rounds the intermediate to bf16 once; the
-    bound adds what that rounding can move the final value by."""
-    inp, spec, rows = longseq
+    oracle's fp64 chain, every row.  The GPU rounds the intermediate to bf16
+    once; the bound adds what that rounding can move the final value by."""
+    inp, spec = longseq
     x, w, dout, eps = inp["x"], inp["w"], inp["dy"], inp["eps"]
     d, h = 128, 40
-    idx = torch.from_numpy(rows).to(DEV)
-    ang = oracle.rope_angles(spec["table"], 65536, d)[rows]
+    angs = oracle.rope_angles(spec["table"], 65536, d)
     say("longseq_65536x5120: chain rmsnorm -> rope")
     ct, st = gpu_table(spec["table"], 65536, d)
     y, r = nr.rmsnorm_fwd(g(x), g(w), eps=eps)
     nr.rope_interleaved_apply(y.view(1, 65536, h, d), ct, st)
-    torch.cuda.synchronize()
-    ry, _ = oracle.rmsnorm_fwd(x[rows], w, eps)
-    ref = oracle.rope_apply(torch.from_numpy(ry).view(1, len(rows), h, d), ang)
-    pair = np.abs(ry).reshape(-1, 2).sum(axis=1)
-    extra = (2 ** -8) * 1.01 * np.repeat(pair, 2).reshape(len(rows), -1)
-    check("chain fwd", y[idx], ref.reshape(len(rows), -1), "bf16", extra=extra)
-
     say("longseq_65536x5120: chain rope inverse -> rmsnorm bwd")
     dyg = g(dout).view(1, 65536, h, d).clone()
     nr.rope_interleaved_apply(dyg, ct, st, inverse=True)
     dx, _ = nr.rmsnorm_bwd(dyg.view(65536, -1), g(x), g(w), r, want_dw=False)
     torch.cuda.synchronize()
-    dy64 = oracle.rope_apply(dout[rows].view(1, len(rows), h, d), ang, inverse=True).reshape(len(rows), -1)
-    xs = x[rows].double()
-    rdx, _ = oracle.rmsnorm_bwd(torch.from_numpy(dy64), xs, w, eps, want_dw=False)
-    _, rr = oracle.rmsnorm_fwd(xs, None, eps)
-    gg = np.abs(dy64 * to64(w)[None, :])
-    xh = np.abs(to64(xs) * rr[:, None])
-    extra = (2 ** -8) * 1.01 * rr[:, None] * (gg + xh * np.mean(gg * xh, axis=1, keepdims=True))
-    check("chain bwd dx", dx[idx], rdx, "bf16", extra=extra, s=grad_scale(rr, dy64, w))
+    y, dx = y.cpu(), dx.cpu()
+    for b0, b1 in row_blocks(65536):
+        nb, ang = b1 - b0, angs[b0:b1]
+        ry, _ = oracle.rmsnorm_fwd(x[b0:b1], w, eps)
+        ref = oracle.rope_apply(torch.from_numpy(ry).view(1, nb, h, d), ang)
+        pair = np.abs(ry).reshape(-1, 2).sum(axis=1)
+        extra = (2 ** -8) * 1.01 * np.repeat(pair, 2).reshape(nb, -1)
+        check(f"chain fwd rows {b0}..", y[b0:b1], ref.reshape(nb, -1), "bf16", extra=extra)
+        dy64 = oracle.rope_apply(dout[b0:b1].view(1, nb, h, d), ang, inverse=True).reshape(nb, -1)
+        xs = x[b0:b1].double()
+        rdx, _ = oracle.rmsnorm_bwd(torch.from_numpy(dy64), xs, w, eps, want_dw=False)
+        _, rr = oracle.rmsnorm_fwd(xs, None, eps)
+        gg = np.abs(dy64 * to64(w)[None, :])
+        xh = np.abs(to64(xs) * rr[:, None])
+        extra = (2 ** -8) * 1.01 * rr[:, None] * (gg + xh * np.mean(gg * xh, axis=1, keepdims=True))
+        check(f"chain bwd dx rows {b0}..", dx[b0:b1], rdx, "bf16", extra=extra, s=grad_scale(rr, dy64, w))
 
 
 # ---------------------------------------------------------------- edge cases

@@ -37,3 +37,83 @@ def test_linear_in_W():
     b, _, _ = oracle.rmsnorm_linear(x, w, W2)
     c, _, _ = oracle.rmsnorm_linear(x, w, 2.0 * W1 - W2)
     np.testing.assert_allclose(c, 2.0 * a - b, rtol=1e-12, atol=1e-12)
+
+
+# ---- the GPU test's bound for the fused norm -> linear output bites --------
+#
+# tolerance.linear_extra bounds the fused output against this composition.
+# An emulation of the kernel's arithmetic (fold rounded once to bf16, fp32
+# sums) must pass it, and plausible kernel mistakes must not: a 16-wide K
+# sub-step dropped, the norm weight applied twice, the folded weight rounded
+# to a 4-bit significand instead of bf16's 8.  Each output is rounded to
+# bf16 as the kernel's is.
+
+import pytest  # noqa: E402
+
+from tolerance import check, linear_extra  # noqa: E402
+
+
+def _bf16(a):
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(torch.bfloat16).double().numpy()
+
+
+def _round_sig(a, bits):
+    """Round to nearest with `bits` significant bits (ties away; test aid)."""
+    m, e = np.frexp(a)
+    return np.ldexp(np.round(m * 2.0 ** bits) / 2.0 ** bits, e)
+
+
+@pytest.fixture(scope="module")
+def case():
+    m, n, k = 48, 96, 1024
+    rng = np.random.default_rng(4711)
+    x = torch.from_numpy(rng.standard_normal((m, k)).astype(np.float32)).to(torch.bfloat16)
+    w = torch.from_numpy((1.0 + 0.1 * rng.standard_normal(k)).astype(np.float32)).to(torch.bfloat16)
+    W = torch.from_numpy((rng.standard_normal((n, k)) / np.sqrt(k)).astype(np.float32)).to(torch.bfloat16)
+    R, r, _ = oracle.rmsnorm_linear(x, w, W, 1e-6)
+    y, _ = oracle.rmsnorm_fwd(x, w, 1e-6)
+    extra = linear_extra(R, y, W, folded=True)
+    xd, wd, Wd = (t.double().numpy() for t in (x, w, W))
+    return dict(R=R, r=r, y=y, extra=extra, x=xd, w=wd, W=Wd, k=k)
+
+
+def _kernel_like(c, Wf):
+    # bf16 x times the folded weight, products summed in fp32, times r
+    acc = (c["x"].astype(np.float32) @ Wf.astype(np.float32).T).astype(np.float64)
+    return _bf16(c["r"][:, None] * acc)
+
+
+def test_bound_admits_the_kernels_arithmetic(case):
+    Wf = _bf16(case["W"] * case["w"][None, :])
+    check("emulated fused output", _kernel_like(case, Wf), case["R"], "bf16", s=0.0,
+          extra=case["extra"])
+
+
+def test_bound_rejects_a_dropped_k_substep(case):
+    c = case
+    k0 = 16 * 17
+    drop = c["y"][:, k0:k0 + 16] @ c["W"][:, k0:k0 + 16].T
+    with pytest.raises(AssertionError, match="outside the bound"):
+        check("dropped K step", _bf16(c["R"] - drop), c["R"], "bf16", s=0.0, extra=c["extra"])
+
+
+def test_bound_rejects_a_twice_applied_norm_weight(case):
+    c = case
+    Wf = _bf16(_bf16(c["W"] * c["w"][None, :]) * c["w"][None, :])
+    with pytest.raises(AssertionError, match="outside the bound"):
+        check("norm weight twice", _kernel_like(c, Wf), c["R"], "bf16", s=0.0, extra=c["extra"])
+
+
+def test_bound_rejects_a_coarser_folded_weight(case):
+    c = case
+    Wf = _round_sig(c["W"] * c["w"][None, :], 4)
+    with pytest.raises(AssertionError, match="outside the bound"):
+        check("4-bit folded weight", _kernel_like(c, Wf), c["R"], "bf16", s=0.0, extra=c["extra"])
+
+
+def test_bound_is_far_tighter_than_the_magnitude_sum(case):
+    # the allowance beyond one ulp is about 15% of the worst-case 2^-8 S at
+    # K = 1024 (it shrinks as 1/sqrt(K)), about 3 bf16 ulps of a typical output
+    S = np.abs(case["y"]) @ np.abs(case["W"]).T
+    assert np.median(case["extra"] / (2.0 ** -8 * S)) < 0.2
+    assert np.median(case["extra"] / np.abs(case["R"])) < 0.025

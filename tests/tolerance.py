@@ -34,10 +34,11 @@ def to64(t) -> np.ndarray:
 
 
 def ulp_bf16(r: np.ndarray) -> np.ndarray:
-    a = np.abs(r)
-    _, e = np.frexp(a)              # a = m 2^e, m in [0.5, 1): floor(log2 a) = e - 1
-    u = np.ldexp(1.0, e - 8)
-    return np.where(a > 0, u, 0.0)
+    """2^(floor(log2 |R|) - 7), 0 for R = 0: the float64 exponent field alone
+    (sign and significand masked off) is 2^floor(log2 |R|) for normal R."""
+    a = np.ascontiguousarray(r, dtype=np.float64)
+    p2 = (a.view(np.int64) & np.int64(0x7FF0000000000000)).view(np.float64)
+    return p2 * 2.0 ** -7
 
 
 def ulp_f16(r: np.ndarray) -> np.ndarray:
@@ -97,3 +98,36 @@ def grad_scale(r, dy, w, gemma=False):
     wp = np.ones(dy.shape[-1]) if w is None else to64(w) + (1.0 if gemma else 0.0)
     t = to64(r)[:, None] * to64(dy).reshape(len(r), -1) * wp[None, :]
     return np.sqrt(np.mean(t * t, axis=1, keepdims=True))
+
+
+# Constants of the bound for a norm folded into a linear layer (below).
+LIN_C1 = 6.0  # rounding of the folded weight: 6 x the scale of K independent roundings
+LIN_C2 = 8.0  # fp32 accumulation: probabilistic bound lambda sqrt(K) u S, lambda = 8
+
+
+def linear_extra(R, y, W, folded):
+    """Allowance beyond one bf16 ulp for an output of a norm folded into the
+    following linear layer, out[m][n] = sum_k y[m][k] W[n][k] with y the fp64
+    normalised row, computed on the matrix cores from bf16 operands.
+
+    With p_k = y_k W[n][k]:
+      * the norm weight folded into W is rounded once to bf16, a relative
+        error d_k with |d_k| <= 2^-9 per product; the error sum_k p_k d_k of
+        K independent roundings stays within LIN_C1 2^-9 sqrt(sum_k p_k^2)
+        (Hoeffding: probability <= 2 exp(-LIN_C1^2 / 2) ~ 3e-8 per element;
+        as a normal approximation, over 10 standard deviations).  Without a
+        norm weight the bf16 W enters exactly and this term is 0;
+      * the K products (exact in fp32) are added in fp32 in an order the
+        hardware fixes: within LIN_C2 sqrt(K) 2^-24 S, S = sum_k |p_k|
+        (probabilistic rounding-error bound with lambda = LIN_C2; the
+        worst-case K 2^-24 S would exceed a bf16 ulp at long K);
+      * the row statistic multiplies the sum: its relative error is held to
+        1e-5 by the statistics check, hence 1e-5 |R|.
+    """
+    y, Wd = to64(y), to64(W)
+    K = Wd.shape[1]
+    S = np.abs(y) @ np.abs(Wd).T
+    extra = 1e-5 * np.abs(R) + LIN_C2 * np.sqrt(K) * 2.0 ** -24 * S
+    if folded:
+        extra = extra + LIN_C1 * 2.0 ** -9 * np.sqrt((y * y) @ (Wd * Wd).T)
+    return extra
