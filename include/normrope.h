@@ -32,7 +32,8 @@
  *   - Backward results are bitwise reproducible: for a given shape every
  *     summation order is fixed (no atomics), whatever the device.
  *   - Thread safety: calls may be made from several host threads; the only
- *     shared state is the tuning table set by nr_tune.
+ *     shared state is the tuning table set by nr_tune and the scratch array
+ *     of rmsnorm_bwd_noalloc.
  */
 #ifndef NORMROPE_H
 #define NORMROPE_H
@@ -110,6 +111,29 @@ nr_status_t rmsnorm_bwd(nr_dtype_t dt, const void* dy, const void* x,
                         const void* w, const float* inv_rms, void* dx,
                         float* dw, int64_t rows, int64_t n, int gemma_offset,
                         void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * rmsnorm_bwd_noalloc -- rmsnorm_bwd for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc): the same operation, arguments and kernels without the
+ * workspace arguments.  The partial rows go to a scratch array the library
+ * holds in device memory, one copy per GPU, for as long as it is loaded.
+ * Its limit is NR_NOALLOC_SCRATCH_BYTES: a call whose
+ * nr_bwd_workspace_bytes(rows, n, 0) exceeds it (only rows longer than
+ * 16384 elements can) returns NR_ERR_WORKSPACE and queues nothing.
+ * The call allocates nothing.  Its first call on a device looks the array's
+ * address up on that device (outside any graph capture, so make one call
+ * before capturing); a failed lookup returns NR_ERR_HIP.
+ * Every call on one GPU shares that GPU's array: calls that may run at the
+ * same time on one GPU (different streams without ordering between them)
+ * race on it and must not be made.  Nothing in the array needs to start at
+ * zero; it keeps the last call's contents.
+ */
+#define NR_NOALLOC_SCRATCH_BYTES (16u << 20)
+nr_status_t rmsnorm_bwd_noalloc(nr_dtype_t dt, const void* dy, const void* x,
+                                const void* w, const float* inv_rms, void* dx,
+                                float* dw, int64_t rows, int64_t n,
+                                int gemma_offset, void* stream);
 
 /*
  * layernorm_fwd -- 内核一 FlashNorm (mean, variance and scale in one read of

@@ -17,7 +17,8 @@ import os
 import torch
 
 __all__ = [
-    "NormRopeError", "rmsnorm_fwd", "rmsnorm_bwd", "layernorm_fwd", "layernorm_bwd",
+    "NormRopeError", "rmsnorm_fwd", "rmsnorm_bwd", "rmsnorm_bwd_noalloc", "layernorm_fwd",
+    "layernorm_bwd",
     "rmsnorm_rope_fwd", "rmsnorm_rope_bwd", "layernorm_gelu_fwd", "layernorm_gelu_bwd",
     "rope_interleaved_apply", "rope_table_1d", "rope_table_3d", "nr_bwd_workspace_bytes",
     "nr_status_str", "nr_tune", "nr_norm_n_max", "nr_stream_copy", "nr_stream_mix", "rmsnorm_linear_fwd",
@@ -66,6 +67,7 @@ def _lib():
         sig = {
             "rmsnorm_fwd": [i32, vp, vp, vp, vp, i64, i64, f32, i32, vp],
             "rmsnorm_bwd": [i32, vp, vp, vp, vp, vp, vp, i64, i64, i32, vp, sz, vp],
+            "rmsnorm_bwd_noalloc": [i32, vp, vp, vp, vp, vp, vp, i64, i64, i32, vp],
             "layernorm_fwd": [i32, vp, vp, vp, vp, vp, vp, i64, i64, f32, vp],
             "layernorm_bwd": [i32, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, vp, sz, vp],
             "rope_interleaved_apply": [i32, vp, vp, vp, i64, i64, i64, i64, i64, i64, i64, i32, vp],
@@ -194,6 +196,25 @@ def rmsnorm_bwd(dy, x, w, inv_rms, gemma_offset=False, dx=None, want_dw=True, dw
     _run("rmsnorm_bwd", x,
          dt, _ptr(dy), _ptr(x), _ptr(w), _ptr(inv_rms), _ptr(dx), _ptr(dw), rows, n,
          int(bool(gemma_offset)), _ptr(ws), wsb)
+    return dx, dw
+
+
+def rmsnorm_bwd_noalloc(dy, x, w, inv_rms, dx, dw=None, gemma_offset=False):
+    """rmsnorm_bwd with the library's own scratch array instead of a
+    workspace: nothing is allocated, here or in the library (dx, and dw when
+    wanted, are the caller's).  Calls that may overlap on one GPU race on the
+    shared array."""
+    _dev("x", x)
+    dt = _dtype_code(x)
+    rows, n = _rows_n(x)
+    _dev("dy", dy, x.dtype, x.shape, device=x.device)
+    _dev("w", w, x.dtype, (n,), device=x.device)
+    _dev("inv_rms", inv_rms, torch.float32, x.shape[:-1], device=x.device)
+    _dev("dx", dx, x.dtype, x.shape, device=x.device)
+    _dev("dw", dw, torch.float32, (n,), device=x.device)
+    _run("rmsnorm_bwd_noalloc", x,
+         dt, _ptr(dy), _ptr(x), _ptr(w), _ptr(inv_rms), _ptr(dx), _ptr(dw), rows, n,
+         int(bool(gemma_offset)))
     return dx, dw
 
 

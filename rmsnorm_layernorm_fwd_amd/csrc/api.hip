@@ -293,6 +293,10 @@ nr_status_t plan_rope(nr_dtype_t dt, int64_t heads, int64_t head_dim, bool align
 
 }  // namespace
 
+namespace nr {
+int record_hip_error(hipError_t e) { return static_cast<int>(hip_status(e)); }
+}  // namespace nr
+
 extern "C" {
 
 int64_t nr_norm_n_max(nr_dtype_t dt) {

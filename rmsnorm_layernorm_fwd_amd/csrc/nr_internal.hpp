@@ -103,6 +103,9 @@ hipError_t launch_rmsnorm_linear(const void* x, const void* wn, const void* W, v
 // Wf[n][k] = bf16(W[n][k] (wn[k] + w_add)); N K % 8 == 0, 16-byte aligned
 hipError_t launch_fold_norm_weight(const void* wn, const void* W, void* Wf, int64_t N, int K,
                                    float w_add, hipStream_t st);
+// Keeps e as the calling thread's last HIP error (nr_last_hip_error) and
+// returns the NR_ERR_HIP status code.
+int record_hip_error(hipError_t e);
 hipError_t launch_stream_copy(const void* src, void* dst, int64_t nvec, hipStream_t st);
 hipError_t launch_stream_mix(const void* a, const void* b, void* dst, int64_t nvec, bool write,
                              hipStream_t st);

@@ -34,7 +34,7 @@ def lib():
 
 def test_header_functions_exported(lib):
     names = declared_functions()
-    expected = {"rmsnorm_fwd", "rmsnorm_bwd", "layernorm_fwd", "layernorm_bwd",
+    expected = {"rmsnorm_fwd", "rmsnorm_bwd", "rmsnorm_bwd_noalloc", "layernorm_fwd", "layernorm_bwd",
                 "rmsnorm_rope_fwd", "rmsnorm_rope_bwd", "layernorm_gelu_fwd", "layernorm_gelu_bwd",
                 "rope_interleaved_apply", "rope_table_1d", "rope_table_3d",
                 "nr_bwd_workspace_bytes", "nr_status_str", "nr_last_hip_error", "nr_tune",
@@ -208,6 +208,15 @@ def test_rejected_calls_return_status(lib):
     assert L.nr_stream_mix(FAKE, 0x80000, FAKE + 32, 64, 0, None) == NR_ERR_ALIAS
     assert L.nr_stream_mix(FAKE, 0x80000, 0x80000, 64, 1, None) == NR_ERR_ALIAS
     assert L.nr_stream_mix(None, None, None, 0, 1, None) == NR_OK
+    # the no-allocation backward: a shape whose partial rows exceed its
+    # 16 MiB scratch array (2048 rows of 65536: 33.5 MB) is refused before
+    # anything else; a shape needing no scratch (no dw, short rows) goes
+    # straight to rmsnorm_bwd's checks
+    X = 1 << 24
+    assert nr.nr_bwd_workspace_bytes(2048, 65536, 0) > 16 << 20
+    assert L.rmsnorm_bwd_noalloc(BF16, FAKE, X, None, FAKE, 1 << 30, FAKE, 2048, 65536, 0,
+                                 None) == NR_ERR_WORKSPACE
+    assert L.rmsnorm_bwd_noalloc(7, FAKE, X, None, FAKE, 1 << 25, None, 4, 8, 0, None) == NR_ERR_DTYPE
     # long rows need the workspace even without a column gradient
     X2, DX2, WS2 = 1 << 24, 1 << 25, 1 << 26
     assert L.rmsnorm_bwd(BF16, FAKE, X2, None, FAKE, DX2, None, 4, 20000, 0, None, 0, None) == NR_ERR_WORKSPACE
