@@ -117,3 +117,52 @@ def test_bound_is_far_tighter_than_the_magnitude_sum(case):
     S = np.abs(case["y"]) @ np.abs(case["W"]).T
     assert np.median(case["extra"] / (2.0 ** -8 * S)) < 0.2
     assert np.median(case["extra"] / np.abs(case["R"])) < 0.025
+
+
+# ---- LayerNorm -> linear composition -----------------------------------------
+
+def test_ln_linear_brute_force_tiny():
+    x, g, b, W = _x((3, 6), 21, 2.0) + 0.5, _x(6, 22, 0.1) + 1.0, _x(6, 23, 0.1), _x((4, 6), 24)
+    out, mu, rs = oracle.layernorm_linear(x, g, b, W, eps=1e-5)
+    for m in range(3):
+        row = [float(v) for v in x[m]]
+        mean = sum(row) / 6
+        var = sum((v - mean) ** 2 for v in row) / 6
+        r = 1.0 / (var + 1e-5) ** 0.5
+        assert abs(mu[m] - mean) <= 1e-15 * (abs(mean) + 1) and abs(rs[m] - r) <= 1e-14 * r
+        for n in range(4):
+            terms = [((row[k] - mean) * r * float(g[k]) + float(b[k])) * float(W[n, k]) for k in range(6)]
+            assert abs(out[m, n] - sum(terms)) <= 1e-13 * sum(abs(t) for t in terms)
+
+
+def test_ln_linear_identity_weight_is_layernorm():
+    x, g, b = _x((5, 16), 25), _x(16, 26, 0.1) + 1, _x(16, 27, 0.1)
+    out, mu, rs = oracle.layernorm_linear(x, g, b, torch.eye(16, dtype=torch.float64), 1e-5)
+    y, mu2, rs2 = oracle.layernorm_fwd(x, g, b, 1e-5)
+    assert np.array_equal(out, y) and np.array_equal(mu, mu2) and np.array_equal(rs, rs2)
+
+
+def test_ln_linear_is_linear_in_W_and_shift_invariant():
+    x, g, b = _x((6, 8), 28), _x(8, 29, 0.2) + 1, _x(8, 30, 0.1)
+    W1, W2 = _x((3, 8), 31), _x((3, 8), 32)
+    a, _, _ = oracle.layernorm_linear(x, g, b, W1)
+    c2, _, _ = oracle.layernorm_linear(x, g, b, W2)
+    c, _, _ = oracle.layernorm_linear(x, g, b, 3.0 * W1 - W2)
+    np.testing.assert_allclose(c, 3.0 * a - c2, rtol=1e-12, atol=1e-12)
+    # a constant added to every element of a row leaves the normalised row,
+    # so the output, unchanged
+    s, _, _ = oracle.layernorm_linear(x + 7.25, g, b, W1)
+    np.testing.assert_allclose(s, a, rtol=1e-9, atol=1e-9)
+
+
+def test_ln_linear_constant_rows_give_the_bias_through_W():
+    x = torch.full((3, 16), 0.75, dtype=torch.float64)
+    g, b, W = _x(16, 33, 0.1) + 1, _x(16, 34, 0.1), _x((5, 16), 35)
+    out, _, _ = oracle.layernorm_linear(x, g, b, W, 1e-5)
+    y, _, _ = oracle.layernorm_fwd(x, g, b, 1e-5)
+    assert np.array_equal(y, np.broadcast_to(b.numpy(), y.shape))  # the normalised row is 0
+    expect = b.numpy() @ W.numpy().T  # (the matrix product may add in another order)
+    np.testing.assert_allclose(out, np.broadcast_to(expect, out.shape), rtol=1e-14, atol=1e-15)
+    # no gamma / beta: gamma 1, beta 0 (a constant row then gives exactly 0)
+    out0, _, _ = oracle.layernorm_linear(x, None, None, W, 1e-5)
+    assert np.array_equal(out0, np.zeros_like(out0))
