@@ -71,7 +71,7 @@ def source_hash(workload=None):
     counter summaries taken on other sources are not reused.  The folded
     RMSNorm->linear kernel has a source file of its own (plus the two shared
     headers); the row and RoPE kernels are built from everything else."""
-    gemm = workload is not None and workload.startswith("rms_linear")
+    gemm = workload is not None and workload.startswith(("rms_linear", "ln_linear"))
     hsh = hashlib.sha256()
     for f in sorted(os.listdir(CSRC)):
         if not f.endswith((".hip", ".hpp")):
@@ -229,7 +229,7 @@ def build_ops(name, dev):
         # one call: the norm weight folded into W (a 52 MB pass), then the
         # GEMM kernel; the call's time, fold included, is charged to the GEMM
         ops = [
-            ("rmsnorm_linear_fwd", "rmsnorm_linear_tile256_kernel",
+            ("rmsnorm_linear_fwd", "norm_linear_tile256_kernel[rms]",
              lambda: nr.rmsnorm_linear_fwd(x, w, W, 1e-6, out=out, inv_rms=r, workspace=ws),
              2 * m * k + 2 * n * k + 2 * k + 2 * m * n + 4 * m),
         ]
@@ -239,6 +239,34 @@ def build_ops(name, dev):
                     unfused=dict(fns=[lambda: nr.rmsnorm_fwd(x, w, 1e-6, y=y, inv_rms=r),
                                       lambda: torch.matmul(y, W.t(), out=out)],
                                  what="rmsnorm_fwd, then torch.matmul (the vendor GEMM) on y"))
+    elif name == "ln_linear_65536x5120x5120":
+        # LayerNorm folded into the following linear layer (a 5120 -> 5120
+        # projection of the long-sequence activation, with the affine
+        # LayerNorm parameters): matrix-core bound
+        inp = workloads.norm_inputs("longseq_65536x5120")
+        lnp = workloads.norm_inputs("ln_affine_15360x5120")
+        m, k = inp["x"].shape
+        n = 5120
+        x, gm, bt = g(inp["x"]), g(lnp["w"]), g(lnp["b"])
+        W = workloads.normal((n, k), 4243, torch.bfloat16, std=k ** -0.5).to(dev)
+        out = torch.empty(m, n, dtype=torch.bfloat16, device=dev)
+        mu, rs = (torch.empty(m, dtype=torch.float32, device=dev) for _ in range(2))
+        ws = torch.empty(max(1, nr.nr_layernorm_linear_workspace_bytes(m, n, k, True)),
+                         dtype=torch.uint8, device=dev)
+        # one call: row statistics, the fold (a 52 MB pass) and the GEMM; the
+        # call's whole time is charged to the GEMM
+        ops = [
+            ("layernorm_linear_fwd", "norm_linear_tile256_kernel[ln]",
+             lambda: nr.layernorm_linear_fwd(x, gm, bt, W, 1e-5, out=out, mean=mu, rstd=rs,
+                                             workspace=ws),
+             2 * m * k + 2 * n * k + 4 * k + 2 * m * n + 8 * m),
+        ]
+        y = torch.empty_like(x)
+        desc = dict(workload=name, rows=m, hidden=k, out_features=n, io_dtype="bf16",
+                    flops_per_step=2 * m * n * k, weight="W ~ N(0, 1/K), seed 4243",
+                    unfused=dict(fns=[lambda: nr.layernorm_fwd(x, gm, bt, 1e-5, y=y, mean=mu, rstd=rs),
+                                      lambda: torch.matmul(y, W.t(), out=out)],
+                                 what="layernorm_fwd, then torch.matmul (the vendor GEMM) on y"))
     else:
         raise SystemExit(f"unknown workload {name}")
     return ops, desc
@@ -521,7 +549,7 @@ def main():
     ap.add_argument("--workload", default="longseq_65536x5120",
                     choices=["longseq_65536x5120", "longseq_fused_65536x5120", "rms_gemma_3840x5120",
                              "ln_affine_15360x5120", "ln_gelu_15360x5120", "rope3d_15360x40x128",
-                             "rms_linear_65536x5120x5120"])
+                             "rms_linear_65536x5120x5120", "ln_linear_65536x5120x5120"])
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-configs", action="store_true",

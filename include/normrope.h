@@ -271,9 +271,11 @@ nr_status_t layernorm_gelu_bwd(nr_dtype_t dt, const void* dout, const void* x,
 
 /*
  * rmsnorm_linear_fwd -- RMSNorm folded into the linear layer that consumes
- * it (the write-up's fusion of element-wise work into its neighbours, Helios
- * 性能优化全解析, 内核一 FlashNorm: the normalised row never makes a round trip
- * through memory):
+ * it: the norm -> linear fusion of "HY-Motion 1.0性能优化" (section 3.1
+ * 算子融合与计算图优化: the normalisation merged with the following matrix
+ * multiplication, so the intermediate is neither stored nor re-read) and of
+ * "Janus-Pro-7B模型推理加速实战" (section 4.1 融合的LayerNorm与线性层内核),
+ * with the RMSNorm of Helios 性能优化全解析, 内核一 FlashNorm as the norm:
  *   r_m = 1/sqrt(mean_k x[m][k]^2 + eps)            -> inv_rms [M] (or NULL)
  *   out[m][n] = r_m sum_k x[m][k] w'_k W[n][k]      -> out [M][N]
  * i.e. out = rmsnorm_fwd(x, w_norm) W^T with W [N][K] row-major (the layout
@@ -298,6 +300,45 @@ nr_status_t rmsnorm_linear_fwd(nr_dtype_t dt, const void* x, const void* w_norm,
                                int64_t M, int64_t N, int64_t K, float eps,
                                int gemma_offset, void* workspace,
                                size_t workspace_bytes, void* stream);
+
+/*
+ * layernorm_linear_fwd -- LayerNorm folded into the linear layer that
+ * consumes it ("HY-Motion 1.0性能优化", section 3.1 算子融合与计算图优化:
+ * LayerNorm's mean and variance merged with the following matrix
+ * multiplication, so the normalised activation is neither stored nor
+ * re-read; "Janus-Pro-7B模型推理加速实战", section 4.1
+ * 融合的LayerNorm与线性层内核):
+ *   mu_m = mean_k x[m][k], r_m = 1/sqrt(mean_k (x[m][k] - mu_m)^2 + eps)
+ *                                             -> mean, rstd [M] (or NULL)
+ *   out[m][n] = sum_k ((x[m][k] - mu_m) r_m gamma_k + beta_k) W[n][k]
+ *                                             -> out [M][N]
+ * i.e. out = layernorm_fwd(x, gamma, beta) W^T with W [N][K] row-major;
+ * gamma NULL -> 1, beta NULL -> 0.  bf16 only (NR_BF16).  It is evaluated
+ * as r_m (sum_k x[m][k] Wf[n][k] - mu_m c_n) + d_n: x enters the bf16
+ * matrix cores exactly, Wf = gamma_k W[n][k] rounded once to bf16,
+ * c_n = sum_k Wf[n][k] and d_n = sum_k beta_k W[n][k] in fp32, fp32
+ * accumulation, out rounded once.  (The mean is removed after the product:
+ * for rows whose mean is large against their spread, the fp32 accumulation
+ * of the uncentred product bounds the accuracy.)  Forward only.
+ * Shapes: K a multiple of 64 (at most 65536), N a multiple of 256 (at most
+ * 2^22), any M; x, W, out, gamma and beta 16-byte aligned (else
+ * NR_ERR_SHAPE); out may not overlap x or W.
+ * Workspace: nr_layernorm_linear_workspace_bytes(M, N, K, gamma != NULL)
+ * bytes, 16-byte aligned and apart from every operand (else
+ * NR_ERR_WORKSPACE / NR_ERR_ALIAS); it takes the row statistics when mean
+ * or rstd is NULL, the column terms and the folded weight.  Its contents on
+ * return are unspecified.
+ */
+nr_status_t layernorm_linear_fwd(nr_dtype_t dt, const void* x, const void* gamma,
+                                 const void* beta, const void* W, void* out,
+                                 float* mean, float* rstd, int64_t M, int64_t N,
+                                 int64_t K, float eps, void* workspace,
+                                 size_t workspace_bytes, void* stream);
+
+/* Workspace bytes layernorm_linear_fwd needs at this shape (has_gamma: a
+ * gamma will be passed); 0 for a shape it does not take.  Host only. */
+size_t nr_layernorm_linear_workspace_bytes(int64_t M, int64_t N, int64_t K,
+                                           int has_gamma);
 
 /* Workspace bytes rmsnorm_linear_fwd may need at this shape (has_weight: a
  * norm weight is passed): on the large-tile path ceil(4 M / 256) 256 for

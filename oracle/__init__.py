@@ -273,8 +273,8 @@ def rmsnorm_linear(x, w, W, eps=1e-6, gemma=False):
 
 def layernorm_linear(x, gamma, beta, W, eps=1e-5):
     """D3 followed by the linear layer y @ W^T, in float64 with no rounding in
-    between (the LayerNorm fused with the linear layer after it, HY-Motion
-    1.0 page, 3.1 算子融合与计算图优化); W is [N, K].  Returns
+    between (the LayerNorm fused with the linear layer after it,
+    "HY-Motion 1.0性能优化", 3.1 算子融合与计算图优化); W is [N, K].  Returns
     (out [rows, N], mean [rows], rstd [rows])."""
     y, mu, rs = layernorm_fwd(x, gamma, beta, eps)
     Wd = W.detach().cpu().double().numpy() if isinstance(W, torch.Tensor) else np.asarray(W, np.float64)

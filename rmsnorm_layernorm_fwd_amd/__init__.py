@@ -22,7 +22,8 @@ __all__ = [
     "rmsnorm_rope_fwd", "rmsnorm_rope_bwd", "layernorm_gelu_fwd", "layernorm_gelu_bwd",
     "rope_interleaved_apply", "rope_table_1d", "rope_table_3d", "nr_bwd_workspace_bytes",
     "nr_status_str", "nr_tune", "nr_norm_n_max", "nr_stream_copy", "nr_stream_mix", "rmsnorm_linear_fwd",
-    "rmsnorm_linear_fold_weight", "nr_rmsnorm_linear_workspace_bytes",
+    "rmsnorm_linear_fold_weight", "nr_rmsnorm_linear_workspace_bytes", "layernorm_linear_fwd",
+    "nr_layernorm_linear_workspace_bytes",
     "library_path",
 ]
 
@@ -87,6 +88,8 @@ def _lib():
             "rmsnorm_linear_fwd": [i32, vp, vp, vp, vp, vp, i64, i64, i64, f32, i32, vp, sz, vp],
             "nr_rmsnorm_linear_workspace_bytes": [i64, i64, i64, i32],
             "rmsnorm_linear_fold_weight": [i32, vp, vp, vp, i64, i64, i32, vp],
+            "layernorm_linear_fwd": [i32, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, f32, vp, sz, vp],
+            "nr_layernorm_linear_workspace_bytes": [i64, i64, i64, i32],
         }
         for name, args in sig.items():
             fn = getattr(L, name)
@@ -94,6 +97,7 @@ def _lib():
             fn.restype = i32
         L.nr_bwd_workspace_bytes.restype = sz
         L.nr_rmsnorm_linear_workspace_bytes.restype = sz
+        L.nr_layernorm_linear_workspace_bytes.restype = sz
         L.nr_status_str.restype = ctypes.c_char_p
         L.nr_norm_n_max.restype = i64
         _L = L
@@ -462,6 +466,44 @@ def rmsnorm_linear_fold_weight(w_norm, W, gemma_offset=False, out=None):
     _run("rmsnorm_linear_fold_weight", W,
          NR_BF16, _ptr(w_norm), _ptr(W), _ptr(out), n, k, int(bool(gemma_offset)))
     return out
+
+
+def layernorm_linear_fwd(x, gamma, beta, W, eps=1e-5, out=None, mean=None, rstd=None,
+                         want_stats=True, workspace=None):
+    """out = layernorm(x, gamma, beta) @ W.T with the norm folded into the
+    GEMM (bf16; W [N, K] as a linear layer stores it, N % 256 == 0);
+    returns (out, mean, rstd)."""
+    _dev("x", x, torch.bfloat16)
+    rows, k = _rows_n(x)
+    _dev("W", W, torch.bfloat16, device=x.device)
+    if W.dim() != 2 or W.shape[1] != k:
+        raise ValueError(f"W must be [N, {k}]")
+    n = W.shape[0]
+    _dev("gamma", gamma, torch.bfloat16, (k,), device=x.device)
+    _dev("beta", beta, torch.bfloat16, (k,), device=x.device)
+    if out is None:
+        out = torch.empty(x.shape[:-1] + (n,), dtype=torch.bfloat16, device=x.device)
+    _dev("out", out, torch.bfloat16, x.shape[:-1] + (n,), device=x.device)
+    if want_stats:
+        if mean is None:
+            mean = torch.empty(x.shape[:-1], dtype=torch.float32, device=x.device)
+        if rstd is None:
+            rstd = torch.empty(x.shape[:-1], dtype=torch.float32, device=x.device)
+    _dev("mean", mean, torch.float32, x.shape[:-1], device=x.device)
+    _dev("rstd", rstd, torch.float32, x.shape[:-1], device=x.device)
+    wsb = nr_layernorm_linear_workspace_bytes(rows, n, k, gamma is not None)
+    if workspace is None and wsb > 0:
+        workspace = torch.empty(wsb, dtype=torch.uint8, device=x.device)
+    _dev("workspace", workspace, device=x.device)
+    _run("layernorm_linear_fwd", x,
+         NR_BF16, _ptr(x), _ptr(gamma), _ptr(beta), _ptr(W), _ptr(out), _ptr(mean), _ptr(rstd),
+         rows, n, k, float(eps), _ptr(workspace),
+         0 if workspace is None else workspace.numel() * workspace.element_size())
+    return out, mean, rstd
+
+
+def nr_layernorm_linear_workspace_bytes(m, n, k, has_gamma) -> int:
+    return int(_lib().nr_layernorm_linear_workspace_bytes(m, n, k, int(bool(has_gamma))))
 
 
 def nr_rmsnorm_linear_workspace_bytes(m, n, k, has_weight) -> int:

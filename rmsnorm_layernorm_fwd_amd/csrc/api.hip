@@ -427,7 +427,8 @@ nr_status_t norm_bwd_common(bool ln, nr_dtype_t dt, const void* dy, const void* 
     // reduction over zero partials writes the zeros (a kernel, not a memset,
     // so the call stays safe to record into a graph).
     if (!want_cols) return NR_OK;
-    return hip_status(nr::launch_colreduce(nullptr, 0, 0, static_cast<int>(n), o0, o1, st));
+    return hip_status(
+        nr::launch_colreduce(nullptr, 0, 0, static_cast<int>(n), o0, o1, st));
   }
   if (dy == nullptr || x == nullptr || dx == nullptr || rstat == nullptr ||
       (ln && mean == nullptr))
@@ -564,7 +565,8 @@ nr_status_t rmsnorm_rope_bwd(nr_dtype_t dt, const void* dout, const void* x, con
   const hipStream_t st = static_cast<hipStream_t>(stream);
   if (rows == 0) {
     if (dw == nullptr) return NR_OK;
-    return hip_status(nr::launch_colreduce(nullptr, 0, 0, static_cast<int>(n), dw, nullptr, st));
+    return hip_status(
+        nr::launch_colreduce(nullptr, 0, 0, static_cast<int>(n), dw, nullptr, st));
   }
   if (dout == nullptr || x == nullptr || dx == nullptr || inv_rms == nullptr) return NR_ERR_NULLPTR;
   bool vec_tab;
@@ -722,6 +724,46 @@ nr_status_t rmsnorm_linear_fwd(nr_dtype_t dt, const void* x, const void* w_norm,
                                               static_cast<int>(M), static_cast<int>(N),
                                               static_cast<int>(K), eps, gemma_offset ? 1.0f : 0.0f,
                                               tile, static_cast<hipStream_t>(stream)));
+}
+
+size_t nr_layernorm_linear_workspace_bytes(int64_t M, int64_t N, int64_t K, int has_gamma) {
+  if (M <= 0 || M > INT32_MAX || N <= 0 || K <= 0 || N > (int64_t{1} << 22) || K > 65536) return 0;
+  return nr::layernorm_linear_ws_bytes(M, N, K, has_gamma != 0);
+}
+
+nr_status_t layernorm_linear_fwd(nr_dtype_t dt, const void* x, const void* gamma, const void* beta,
+                                 const void* W, void* out, float* mean, float* rstd, int64_t M,
+                                 int64_t N, int64_t K, float eps, void* workspace,
+                                 size_t workspace_bytes, void* stream) {
+  if (dt != NR_BF16) return NR_ERR_DTYPE;  // the bf16 matrix cores only
+  if (M < 0 || M > INT32_MAX || N < 256 || N % 256 != 0 || K < 64 || K % 64 != 0)
+    return NR_ERR_SHAPE;
+  if (K > 65536 || N > (int64_t{1} << 22)) return NR_ERR_UNSUPPORTED_N;
+  if (M == 0) return NR_OK;
+  if (x == nullptr || W == nullptr || out == nullptr) return NR_ERR_NULLPTR;
+  if (!aligned16(x) || !aligned16(W) || !aligned16(out) ||
+      (gamma != nullptr && !aligned16(gamma)) || (beta != nullptr && !aligned16(beta)))
+    return NR_ERR_SHAPE;
+  if (M > INT64_MAX / K / 2 || M > INT64_MAX / N / 2) return NR_ERR_SHAPE;
+  if (((M + 255) / 256) * (N / 256) > INT32_MAX) return NR_ERR_SHAPE;
+  const size_t xb = static_cast<size_t>(M * K) * 2, wb = static_cast<size_t>(N * K) * 2,
+               ob = static_cast<size_t>(M * N) * 2, rb = static_cast<size_t>(M) * 4,
+               vb = static_cast<size_t>(K) * 2;
+  if (bad_overlap(out, ob, x, xb) || out == x || bad_overlap(out, ob, W, wb) || out == W)
+    return NR_ERR_ALIAS;
+  const size_t need = nr::layernorm_linear_ws_bytes(M, N, K, gamma != nullptr);
+  if (workspace == nullptr || workspace_bytes < need || !aligned16(workspace))
+    return NR_ERR_WORKSPACE;
+  const void* ops[] = {x, W, out, gamma, beta, mean, rstd};
+  const size_t opb[] = {xb, wb, ob, vb, vb, rb, rb};
+  for (int i = 0; i < 7; ++i)
+    if (ops[i] == workspace || bad_overlap(workspace, need, ops[i], opb[i])) return NR_ERR_ALIAS;
+  if (mean != nullptr && rstd != nullptr && (mean == rstd || bad_overlap(mean, rb, rstd, rb)))
+    return NR_ERR_ALIAS;
+  return hip_status(nr::launch_layernorm_linear(x, gamma, beta, W, out, mean, rstd, workspace,
+                                                static_cast<int>(M), static_cast<int>(N),
+                                                static_cast<int>(K), eps,
+                                                static_cast<hipStream_t>(stream)));
 }
 
 nr_status_t rmsnorm_linear_fold_weight(nr_dtype_t dt, const void* w_norm, const void* W,

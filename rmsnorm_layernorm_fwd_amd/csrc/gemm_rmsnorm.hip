@@ -1,5 +1,6 @@
-// gemm_rmsnorm.hip -- RMSNorm folded into the following linear layer:
-// out = RMSNorm(x) W^T, with the normalised activation never written to HBM.
+// gemm_rmsnorm.hip -- RMSNorm (or LayerNorm) folded into the following
+// linear layer: out = Norm(x) W^T, with the normalised activation never
+// written to HBM.
 //
 // The pages fuse element-wise work into its neighbours to save memory round
 // trips (Helios 性能优化全解析, 内核一 FlashNorm and the closing advice to
@@ -309,15 +310,22 @@ __device__ __forceinline__ void big_step(const lds_char* __restrict__ cur, lds_c
   __syncthreads();
 }
 
+// LN: the LayerNorm form of the epilogue, out = r_m (acc - mu_m c_n) + d_n
+// (mu, c, d as described at launch_layernorm_linear); otherwise
+// out = r_m acc.
+template <bool LN>
 __global__ void __launch_bounds__(kBigThreads)
-rmsnorm_linear_tile256_kernel(const bf16* __restrict__ x, const bf16* __restrict__ W,
-                              bf16* __restrict__ out, const float* __restrict__ rin, int M, int N,
-                              int K, int tiles_m, int tiles_n) {
+norm_linear_tile256_kernel(const bf16* __restrict__ x, const bf16* __restrict__ W,
+                           bf16* __restrict__ out, const float* __restrict__ rin,
+                           const float* __restrict__ mu, const float* __restrict__ cn,
+                           const float* __restrict__ dn, int M, int N, int K, int tiles_m,
+                           int tiles_n) {
   // two LDS stages as separate arrays: the loads into one and the operand
   // reads of the other are then provably disjoint
   __shared__ __align__(1024) char st0[kBigStage];
   __shared__ __align__(1024) char st1[kBigStage];
   __shared__ float rrow[kBig];
+  __shared__ float mrow[LN ? kBig : 1], ccol[LN ? kBig : 1], dcol[LN ? kBig : 1];
 
   // tile order: XCD (workgroup id mod 8) takes a contiguous run of tile
   // numbers; numbers go through groups of kGroupM row tiles, column-major
@@ -343,6 +351,13 @@ rmsnorm_linear_tile256_kernel(const bf16* __restrict__ x, const bf16* __restrict
   c.v1 = lr * K * 2 + 16 * (pc ^ lr ^ 1);
   c.K = K;
   if (t < kBig) rrow[t] = t < xrows ? rin[m0 + t] : 0.0f;
+  if constexpr (LN) {
+    if (t < kBig) {
+      mrow[t] = t < xrows ? mu[m0 + t] : 0.0f;
+      ccol[t] = cn[n0 + t];
+      dcol[t] = dn != nullptr ? dn[n0 + t] : 0.0f;
+    }
+  }
 
   // operand reads: lane l takes A row (and B column) l % 32 of each 32-tile,
   // k chunk 2 ks + l / 32 of the step, at physical chunk ^ swz(row)
@@ -393,8 +408,16 @@ rmsnorm_linear_tile256_kernel(const bf16* __restrict__ x, const bf16* __restrict
         for (int e = 0; e < 16; e += 2) {
           const int rl = i * 32 + 8 * (e / 4) + 4 * h + (e % 4);
           const int cc = wn_ * 64 + j * 32 + fr;
-          const uint32_t p = pack_bf16x2(acc[i][j][e] * rrow[wm * 128 + rl],
-                                         acc[i][j][e + 1] * rrow[wm * 128 + rl + 1]);
+          const int r0 = wm * 128 + rl;
+          float v0, v1;
+          if constexpr (LN) {
+            v0 = fmaf(acc[i][j][e] - mrow[r0] * ccol[cc], rrow[r0], dcol[cc]);
+            v1 = fmaf(acc[i][j][e + 1] - mrow[r0 + 1] * ccol[cc], rrow[r0 + 1], dcol[cc]);
+          } else {
+            v0 = acc[i][j][e] * rrow[r0];
+            v1 = acc[i][j][e + 1] * rrow[r0 + 1];
+          }
+          const uint32_t p = pack_bf16x2(v0, v1);
           const int s0 = ((rl >> 2) & 1) << 2, s1 = (((rl + 1) >> 2) & 1) << 2;
           Cs[rl * kBig + (((cc >> 3) ^ s0) << 3) + (cc & 7)] = static_cast<uint16_t>(p & 0xffffu);
           Cs[(rl + 1) * kBig + (((cc >> 3) ^ s1) << 3) + (cc & 7)] = static_cast<uint16_t>(p >> 16);
@@ -430,6 +453,84 @@ row_inv_rms_kernel(const bf16* __restrict__ x, float* __restrict__ r, int M, int
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) s += __shfl_xor(s, o);
   if (lane == 0) r[row] = rsqrtf(s / static_cast<float>(K) + eps);
+}
+
+// Row statistics of the LayerNorm form: mean_m and rstd_m = 1/sqrt(var_m +
+// eps) with the biased variance, one wave per row, fp32; the variance is a
+// second pass over the row (centred squares; the row is re-read from cache).
+__global__ void __launch_bounds__(256)
+row_mean_rstd_kernel(const bf16* __restrict__ x, float* __restrict__ mean,
+                     float* __restrict__ rstd, int M, int K, float eps) {
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+  if (row >= M) return;
+  const rsrc_t xr = make_rsrc(x + static_cast<int64_t>(row) * K, static_cast<uint32_t>(K) * 2u);
+  float s = 0.0f;
+  for (int c = lane; c < K / 8; c += 64) {
+    float f[8];
+    unpack<bf16>(__builtin_amdgcn_raw_buffer_load_b128(xr, c * 16, 0, 0), f);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) s += f[e];
+  }
+  const float mu = wave_sum(s) / static_cast<float>(K);
+  float q = 0.0f;
+  for (int c = lane; c < K / 8; c += 64) {
+    float f[8];
+    unpack<bf16>(__builtin_amdgcn_raw_buffer_load_b128(xr, c * 16, 0, kStream), f);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float d = f[e] - mu;
+      q = fmaf(d, d, q);
+    }
+  }
+  const float r = rsqrtf(wave_sum(q) / static_cast<float>(K) + eps);
+  if (lane == 0) {
+    mean[row] = mu;
+    rstd[row] = r;
+  }
+}
+
+// Per output column n of the LayerNorm form, one wave per row of W:
+//   Wf[n][k] = bf16(gamma_k W[n][k])     (written when gamma is given)
+//   c_n = sum_k Wf[n][k]                 (the weight the matrix cores use)
+//   d_n = sum_k beta_k W[n][k]           (0 without beta)
+// fp32 sums, each lane over its chunks in order, then the wave sum.
+__global__ void __launch_bounds__(256)
+fold_ln_weight_kernel(const bf16* __restrict__ gamma, const bf16* __restrict__ beta,
+                      const bf16* __restrict__ W, bf16* __restrict__ Wf, float* __restrict__ cn,
+                      float* __restrict__ dn, int N, int K) {
+  const int n = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+  if (n >= N) return;
+  const int64_t row = static_cast<int64_t>(n) * K;
+  float c = 0.0f, d = 0.0f;
+  for (int k8 = lane; k8 < K / 8; k8 += 64) {
+    float w[8], g[8], b[8];
+    unpack<bf16>(*reinterpret_cast<const u32x4*>(W + row + 8 * k8), w);
+    if (gamma != nullptr) {
+      unpack<bf16>(*reinterpret_cast<const u32x4*>(gamma + 8 * k8), g);
+      float f[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) f[e] = w[e] * g[e];
+      const u32x4 packed = pack<bf16>(f);
+      *reinterpret_cast<u32x4*>(Wf + row + 8 * k8) = packed;
+      unpack<bf16>(packed, f);  // the rounded weight, as the matrix cores see it
+#pragma unroll
+      for (int e = 0; e < 8; ++e) c += f[e];
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) c += w[e];
+    }
+    if (beta != nullptr) {
+      unpack<bf16>(*reinterpret_cast<const u32x4*>(beta + 8 * k8), b);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) d = fmaf(b[e], w[e], d);
+    }
+  }
+  c = wave_sum(c);
+  d = wave_sum(d);
+  if (lane == 0) {
+    cn[n] = c;
+    dn[n] = d;
+  }
 }
 
 // W_folded[n][k] = bf16(W[n][k] (w_k + w_add)), 8 elements per lane.
@@ -490,11 +591,46 @@ hipError_t launch_rmsnorm_linear(const void* x, const void* wn, const void* W, v
     Wop = wfold;
   }
   const int tiles_m = (M + kBig - 1) / kBig, tiles_n = N / kBig;
-  hipLaunchKernelGGL(rmsnorm_linear_tile256_kernel,
+  hipLaunchKernelGGL(norm_linear_tile256_kernel<false>,
                      dim3(static_cast<unsigned>(static_cast<int64_t>(tiles_m) * tiles_n)),
                      dim3(kBigThreads), 0, st, static_cast<const bf16*>(x),
-                     static_cast<const bf16*>(Wop), static_cast<bf16*>(out), r, M, N, K, tiles_m,
-                     tiles_n);
+                     static_cast<const bf16*>(Wop), static_cast<bf16*>(out), r, nullptr, nullptr,
+                     nullptr, M, N, K, tiles_m, tiles_n);
+  return hipGetLastError();
+}
+
+// LayerNorm folded into the linear layer:
+//   out[m][n] = sum_k ((x[m][k] - mu_m) r_m gamma_k + beta_k) W[n][k]
+//             = r_m (sum_k x[m][k] Wf[n][k] - mu_m c_n) + d_n
+// with Wf = bf16(gamma W), c_n = sum_k Wf[n][k] (so that the centring is
+// exact relative to the weight the matrix cores use) and d_n = sum_k beta_k
+// W[n][k].  The row statistics go to mean / rstd (or the workspace), the
+// column terms and the folded weight to the workspace; then the same
+// 256 x 256 matrix-core kernel with the LayerNorm epilogue.
+hipError_t launch_layernorm_linear(const void* x, const void* gamma, const void* beta,
+                                   const void* W, void* out, float* mean, float* rstd, void* ws,
+                                   int M, int N, int K, float eps, hipStream_t st) {
+  char* p = static_cast<char*>(ws);
+  float* mu = mean != nullptr ? mean : reinterpret_cast<float*>(p);
+  p += linear_rows_bytes(M);
+  float* rs = rstd != nullptr ? rstd : reinterpret_cast<float*>(p);
+  p += linear_rows_bytes(M);
+  float* cn = reinterpret_cast<float*>(p);
+  p += linear_rows_bytes(N);
+  float* dn = reinterpret_cast<float*>(p);
+  p += linear_rows_bytes(N);
+  bf16* wf = reinterpret_cast<bf16*>(p);
+  hipLaunchKernelGGL(row_mean_rstd_kernel, dim3(static_cast<unsigned>((M + 3) / 4)), dim3(256), 0,
+                     st, static_cast<const bf16*>(x), mu, rs, M, K, eps);
+  hipLaunchKernelGGL(fold_ln_weight_kernel, dim3(static_cast<unsigned>((N + 3) / 4)), dim3(256), 0,
+                     st, static_cast<const bf16*>(gamma), static_cast<const bf16*>(beta),
+                     static_cast<const bf16*>(W), wf, cn, dn, N, K);
+  const bf16* Wop = gamma != nullptr ? wf : static_cast<const bf16*>(W);
+  const int tiles_m = (M + kBig - 1) / kBig, tiles_n = N / kBig;
+  hipLaunchKernelGGL(norm_linear_tile256_kernel<true>,
+                     dim3(static_cast<unsigned>(static_cast<int64_t>(tiles_m) * tiles_n)),
+                     dim3(kBigThreads), 0, st, static_cast<const bf16*>(x), Wop,
+                     static_cast<bf16*>(out), rs, mu, cn, dn, M, N, K, tiles_m, tiles_n);
   return hipGetLastError();
 }
 

@@ -100,6 +100,17 @@ inline size_t linear_rows_bytes(int64_t M) { return static_cast<size_t>((M * 4 +
 hipError_t launch_rmsnorm_linear(const void* x, const void* wn, const void* W, void* out,
                                  float* inv_rms, void* ws, int M, int N, int K, float eps,
                                  float w_add, int tile, hipStream_t st);
+// LayerNorm -> linear on the 256 x 256 tile (N % 256 == 0); workspace:
+// layernorm_linear_ws_bytes(M, N, K, gamma != nullptr) bytes: mean, rstd
+// (used when the caller's pointers are null), c_n, d_n, each padded to 256
+// bytes, then the folded weight (N K bf16) when gamma is given
+inline size_t layernorm_linear_ws_bytes(int64_t M, int64_t N, int64_t K, bool has_gamma) {
+  return 2 * linear_rows_bytes(M) + 2 * linear_rows_bytes(N) +
+         (has_gamma ? static_cast<size_t>(N * K) * 2 : 0);
+}
+hipError_t launch_layernorm_linear(const void* x, const void* gamma, const void* beta,
+                                   const void* W, void* out, float* mean, float* rstd, void* ws,
+                                   int M, int N, int K, float eps, hipStream_t st);
 // Wf[n][k] = bf16(W[n][k] (wn[k] + w_add)); N K % 8 == 0, 16-byte aligned
 hipError_t launch_fold_norm_weight(const void* wn, const void* W, void* Wf, int64_t N, int K,
                                    float w_add, hipStream_t st);

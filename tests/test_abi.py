@@ -39,7 +39,8 @@ def test_header_functions_exported(lib):
                 "rope_interleaved_apply", "rope_table_1d", "rope_table_3d",
                 "nr_bwd_workspace_bytes", "nr_status_str", "nr_last_hip_error", "nr_tune",
                 "nr_norm_n_max", "nr_stream_copy", "nr_stream_mix", "rmsnorm_linear_fwd",
-                "rmsnorm_linear_fold_weight", "nr_rmsnorm_linear_workspace_bytes"}
+                "rmsnorm_linear_fold_weight", "nr_rmsnorm_linear_workspace_bytes",
+                "layernorm_linear_fwd", "nr_layernorm_linear_workspace_bytes"}
     assert expected <= set(names), names
     out = subprocess.run(["nm", "-D", "--defined-only", nr.library_path()],
                          capture_output=True, text=True, check=True).stdout
@@ -187,6 +188,25 @@ def test_rejected_calls_return_status(lib):
         assert lin(BF16, XA, None, WA, OA, None, 4, 384, 64, 1e-6, 0, None, 0, None) == NR_ERR_SHAPE
     finally:
         L.nr_tune(b"gemm_tile", 0)
+    # LayerNorm -> linear: bf16, N % 256, K % 64, pointers, alignment,
+    # workspace size / alignment / overlap
+    ll = L.layernorm_linear_fwd
+    lw = nr.nr_layernorm_linear_workspace_bytes(4, 256, 64, True)
+    assert lw == 2 * 256 + 2 * 1024 + 256 * 64 * 2
+    assert nr.nr_layernorm_linear_workspace_bytes(4, 256, 64, False) == 2 * 256 + 2 * 1024
+    WS = 1 << 34
+    args = lambda m, n, k: (m, n, k, 1e-5)
+    assert ll(F32, XA, None, None, WA, OA, None, None, *args(4, 256, 64), WS, lw, None) == NR_ERR_DTYPE
+    assert ll(BF16, XA, None, None, WA, OA, None, None, *args(4, 128, 64), WS, lw, None) == NR_ERR_SHAPE
+    assert ll(BF16, XA, None, None, WA, OA, None, None, *args(4, 256, 72), WS, lw, None) == NR_ERR_SHAPE
+    assert ll(BF16, None, None, None, WA, OA, None, None, *args(4, 256, 64), WS, lw, None) == NR_ERR_NULLPTR
+    assert ll(BF16, XA, XA + 2, None, WA, OA, None, None, *args(4, 256, 64), WS, lw, None) == NR_ERR_SHAPE
+    assert ll(BF16, XA, None, None, WA, XA + 64, None, None, *args(4, 256, 64), WS, lw, None) == NR_ERR_ALIAS
+    assert ll(BF16, XA, FAKE, None, WA, OA, None, None, *args(4, 256, 64), None, 0, None) == NR_ERR_WORKSPACE
+    assert ll(BF16, XA, FAKE, None, WA, OA, None, None, *args(4, 256, 64), WS, lw - 16, None) == NR_ERR_WORKSPACE
+    assert ll(BF16, XA, FAKE, None, WA, OA, None, None, *args(4, 256, 64), WS + 8, lw, None) == NR_ERR_WORKSPACE
+    assert ll(BF16, XA, FAKE, None, WA, OA, None, None, *args(4, 256, 64), WA + 512, lw, None) == NR_ERR_ALIAS
+    assert ll(BF16, None, None, None, None, None, None, None, *args(0, 256, 64), None, 0, None) == NR_OK
     # the standalone fold: bf16, K % 8, pointers, alignment, partial overlap
     fold = L.rmsnorm_linear_fold_weight
     assert fold(F32, XA, WA, OA, 16, 64, 0, None) == NR_ERR_DTYPE

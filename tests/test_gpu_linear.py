@@ -173,3 +173,75 @@ def test_rmsnorm_linear_matches_unfused_closely():
     extra = linear_extra(R, y64, W.cpu(), folded=True)
     check("fused", out.cpu(), R, "bf16", s=0.0, extra=extra)
     check("unfused", ref.cpu(), R, "bf16", s=0.0, extra=extra)
+
+
+# ---- LayerNorm -> linear (layernorm_linear_fwd) -------------------------------
+#
+# Against the oracle's fp64 LayerNorm followed by the fp64 product, within
+# tolerance.ln_linear_extra (derived from the folded weight's rounding, the
+# fp32 sums of the product and of the column terms, and the statistics).
+
+from tolerance import ln_linear_extra  # noqa: E402
+
+
+def run_ln_case(tag, m, n, k, seed, affine=("g", "b"), mean=0.5, std=2.0, rows=None):
+    print(f"[case] {tag}: layernorm->linear M={m} N={n} K={k} affine={affine}", flush=True)
+    x = workloads.normal((m, k), seed, torch.bfloat16, mean=mean, std=std)
+    W = workloads.normal((n, k), seed + 1, torch.bfloat16, std=k ** -0.5)
+    g = workloads.normal((k,), seed + 2, torch.bfloat16, mean=1.0, std=0.1) if "g" in affine else None
+    b = workloads.normal((k,), seed + 3, torch.bfloat16, std=0.1) if "b" in affine else None
+    dv = lambda t: None if t is None else t.to(DEV)
+    out, mu, rs = nr.layernorm_linear_fwd(x.to(DEV), dv(g), dv(b), W.to(DEV), 1e-5)
+    torch.cuda.synchronize()
+    sel = np.arange(m) if rows is None else rows
+    R, rmu, rrs = oracle.layernorm_linear(x[sel], g, b, W, 1e-5)
+    idx = torch.as_tensor(sel, device=DEV)
+    extra = ln_linear_extra(R, x[sel], rmu, rrs, g, b, W)
+    worst = check(f"{tag} out", out[idx].cpu(), R, "bf16", s=0.0, extra=extra)
+    x64 = x[sel].double().numpy()
+    check(f"{tag} mean", mu[idx].cpu(), rmu, "stat", s=np.sqrt(np.mean(x64 * x64, axis=1)))
+    check(f"{tag} rstd", rs[idx].cpu(), rrs, "stat", s=0.0)
+    print(f"[case] {tag}: worst error / bound {worst:.3f}", flush=True)
+
+
+@pytest.mark.parametrize("m,n,k,affine", [
+    (1, 256, 64, ("g", "b")), (130, 256, 128, ()), (257, 512, 320, ("g",)),
+    (1000, 1280, 5120, ("g", "b")), (4096, 768, 5120, ("b",)),
+])
+def test_layernorm_linear_cases(m, n, k, affine):
+    run_ln_case(f"ln {m}x{n}x{k}", m, n, k, 9600 + m + n + k, affine)
+
+
+def test_layernorm_linear_large_mean_rows():
+    # rows whose mean is four times their spread: the mean is removed after
+    # the product, so the bound carries the uncentred magnitude sum
+    run_ln_case("ln large mean", 600, 512, 2048, 9610, mean=4.0, std=1.0)
+
+
+def test_layernorm_linear_widest_n_and_longest_k():
+    run_ln_case("ln widest N", 300, 1 << 22, 64, 9620, rows=np.array([0, 1, 255, 256, 299]))
+    run_ln_case("ln longest K", 300, 256, 65536, 9630, rows=np.array([0, 1, 100, 255, 256, 299]))
+
+
+def test_layernorm_linear_long_sequence_sampled():
+    m, n, k = 65536, 5120, 5120
+    rng = np.random.default_rng(9640)
+    rows = np.unique(np.concatenate([rng.choice(m, 48, replace=False), [0, 255, 256, m - 1]]))
+    run_ln_case("ln longseq", m, n, k, 9640, rows=rows)
+
+
+def test_layernorm_linear_stats_to_workspace_and_reuse():
+    # without caller statistics the workspace takes them; a caller workspace
+    # serves repeated calls with identical results
+    print("[case] ln->linear: statistics in the workspace, workspace reused", flush=True)
+    m, n, k = 700, 512, 1024
+    x = workloads.normal((m, k), 9650, torch.bfloat16, mean=0.5, std=2.0).to(DEV)
+    W = workloads.normal((n, k), 9651, torch.bfloat16, std=k ** -0.5).to(DEV)
+    g = workloads.normal((k,), 9652, torch.bfloat16, mean=1.0, std=0.1).to(DEV)
+    b = workloads.normal((k,), 9653, torch.bfloat16, std=0.1).to(DEV)
+    ws = torch.empty(nr.nr_layernorm_linear_workspace_bytes(m, n, k, True), dtype=torch.uint8,
+                     device=DEV)
+    a, mu, rs = nr.layernorm_linear_fwd(x, g, b, W, workspace=ws)
+    c, _, _ = nr.layernorm_linear_fwd(x, g, b, W, want_stats=False, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(a, c)

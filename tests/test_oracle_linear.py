@@ -166,3 +166,57 @@ def test_ln_linear_constant_rows_give_the_bias_through_W():
     # no gamma / beta: gamma 1, beta 0 (a constant row then gives exactly 0)
     out0, _, _ = oracle.layernorm_linear(x, None, None, W, 1e-5)
     assert np.array_equal(out0, np.zeros_like(out0))
+
+
+# ---- the GPU test's bound for the fused LayerNorm -> linear output bites ---
+
+from tolerance import ln_linear_extra  # noqa: E402
+
+
+@pytest.fixture(scope="module")
+def ln_case():
+    m, n, k = 48, 96, 1024
+    rng = np.random.default_rng(4712)
+    bf = lambda a: torch.from_numpy(a.astype(np.float32)).to(torch.bfloat16)
+    x = bf(0.5 + 2.0 * rng.standard_normal((m, k)))
+    g = bf(1.0 + 0.1 * rng.standard_normal(k))
+    b = bf(0.1 * rng.standard_normal(k))
+    W = bf(rng.standard_normal((n, k)) / np.sqrt(k))
+    R, mu, rs = oracle.layernorm_linear(x, g, b, W, 1e-5)
+    extra = ln_linear_extra(R, x, mu, rs, g, b, W)
+    xd, gd, bd, Wd = (t.double().numpy() for t in (x, g, b, W))
+    return dict(R=R, mu=mu, rs=rs, extra=extra, x=xd, g=gd, b=bd, W=Wd, k=k)
+
+
+def _ln_kernel_like(c, Wf=None, drop_mean=False, drop_beta=False):
+    # the epilogue form: fp32 x . Wf, c_n = sum Wf, d_n = sum beta W
+    Wf = _bf16(c["W"] * c["g"][None, :]) if Wf is None else Wf
+    acc = (c["x"].astype(np.float32) @ Wf.astype(np.float32).T).astype(np.float64)
+    cn = Wf.astype(np.float32).sum(axis=1).astype(np.float64)
+    dn = (c["W"].astype(np.float32) @ c["b"].astype(np.float32)).astype(np.float64)
+    mu = 0.0 if drop_mean else c["mu"][:, None]
+    d = 0.0 if drop_beta else dn[None, :]
+    return _bf16(c["rs"][:, None] * (acc - mu * cn[None, :]) + d)
+
+
+def test_ln_bound_admits_the_kernels_arithmetic(ln_case):
+    check("emulated LN-linear", _ln_kernel_like(ln_case), ln_case["R"], "bf16", s=0.0,
+          extra=ln_case["extra"])
+
+
+@pytest.mark.parametrize("mistake", ["dropped K step", "mean not removed", "bias dropped",
+                                     "coarser fold"])
+def test_ln_bound_rejects_mistakes(ln_case, mistake):
+    c = ln_case
+    if mistake == "dropped K step":
+        k0 = 16 * 9
+        xc = (c["x"] - c["mu"][:, None]) * c["rs"][:, None] * c["g"][None, :] + c["b"][None, :]
+        bad = _bf16(c["R"] - xc[:, k0:k0 + 16] @ c["W"][:, k0:k0 + 16].T)
+    elif mistake == "mean not removed":
+        bad = _ln_kernel_like(c, drop_mean=True)
+    elif mistake == "bias dropped":
+        bad = _ln_kernel_like(c, drop_beta=True)
+    else:
+        bad = _ln_kernel_like(c, Wf=_round_sig(c["W"] * c["g"][None, :], 4))
+    with pytest.raises(AssertionError, match="outside the bound"):
+        check(mistake, bad, c["R"], "bf16", s=0.0, extra=c["extra"])

@@ -131,3 +131,39 @@ def linear_extra(R, y, W, folded):
     if folded:
         extra = extra + LIN_C1 * 2.0 ** -9 * np.sqrt((y * y) @ (Wd * Wd).T)
     return extra
+
+
+def ln_linear_extra(R, x, mean, rstd, gamma, beta, W):
+    """Allowance beyond one bf16 ulp for an output of LayerNorm folded into
+    the following linear layer, evaluated on the matrix cores as
+    r_m (sum_k x[m][k] Wf[n][k] - mu_m c_n) + d_n with Wf = bf16(gamma W),
+    c_n = sum_k Wf[n][k], d_n = sum_k beta_k W[n][k] (fp32 sums).  mean and
+    rstd are the oracle's fp64 statistics.  With g = gamma (1 when none):
+      * the folded weight's one rounding: LIN_C1 2^-9 sqrt(sum_k p_k^2),
+        p_k = (x_k - mu) r g_k W[n][k] (0 without gamma: W enters exactly);
+      * the fp32 sums, LIN_C2 sqrt(K) 2^-24 times the magnitude sum of what
+        each adds: r sum_k |x_k g_k W[n][k]| (the product, of the uncentred
+        x), r |mu| sum_k |g_k W[n][k]| (c_n), sum_k |beta_k W[n][k]| (d_n),
+        plus a few fp32 roundings of those terms in the epilogue;
+      * the statistics, held to 1e-5 by their own checks: 1e-5 |R - d| from
+        r, and 1e-5 rms(x) r |c_n| from the mean.
+    """
+    x, Wd = to64(x), to64(W)
+    K = Wd.shape[1]
+    mu, r = to64(mean)[:, None], to64(rstd)[:, None]
+    g = np.ones(K) if gamma is None else to64(gamma)
+    b = np.zeros(K) if beta is None else to64(beta)
+    gW = np.abs(Wd * g[None, :])
+    Sx = np.abs(x) @ gW.T
+    Sc = gW.sum(axis=1)[None, :]
+    Sd = (np.abs(Wd) @ np.abs(b))[None, :]
+    d = (Wd @ b)[None, :]
+    c = (Wd * g[None, :]).sum(axis=1)[None, :]
+    sums = r * Sx + r * np.abs(mu) * Sc + Sd
+    extra = (LIN_C2 * np.sqrt(K) + 4.0) * 2.0 ** -24 * sums
+    extra = extra + 1e-5 * (np.abs(R) + np.abs(d))
+    extra = extra + 1e-5 * np.sqrt(np.mean(x * x, axis=1, keepdims=True)) * r * np.abs(c)
+    if gamma is not None:
+        xc = (x - mu) * r * g[None, :]
+        extra = extra + LIN_C1 * 2.0 ** -9 * np.sqrt((xc * xc) @ (Wd * Wd).T)
+    return extra
