@@ -155,23 +155,22 @@ bool fwd_grid_ok(int64_t rows, const FwdPlan& pl) {
 // Backward launch shape.
 //   K, W: as few chunks per lane as lets at most 16 waves cover the row
 //     (5120 bf16: K = 1, W = 10).
-//   D (rows per batch) and PF (batches loaded ahead): the largest that fit
-//     the 128-VGPR budget of a 1024-thread workgroup without spilling.
-//     RMSNorm with one chunk per lane takes D = 2 (aligned rows), PF = 2;
-//     LayerNorm, which also carries the dbeta accumulators, D = 1, PF = 1.
-//     LayerNorm + GeLU spends far more ALU time per row (the activation's
-//     derivative), so it loads two batches ahead (PF = 2) to keep HBM busy
-//     meanwhile.
+//   D (rows per batch) and PF (batches loaded ahead): by default the
+//     largest that fit the 128-VGPR budget of a 1024-thread workgroup
+//     without spilling (RMSNorm with one chunk per lane: D = 2 on aligned
+//     rows, PF = 2; LayerNorm, which also carries the dbeta accumulators:
+//     D = 1, PF = 1), and the measured shapes below for the rows of 5120
+//     bf16 the workloads use.
 //   P (workgroups): each handles about rows/P rows, dealt out round robin.
 //     At least 8 rows per workgroup keep the fp32 partial rows small next
 //     to the row traffic (under 9% extra at 16-bit storage, under 2% once
 //     the cap below applies: 65536 rows).  Short batches want every CU busy
 //     more than they want fewer partial rows: 3840 rows of 5120 bf16 took
-//     25 us on 256 workgroups against 28 us on 240.  At most 256 (plain RMSNorm, D = 2; LayerNorm +
-//     GeLU, whose 104 VGPRs leave room for one 10-wave workgroup per CU) or
-//     512 (LayerNorm and the fused RMSNorm + RoPE, D = 1): on MI355X's 256
-//     CUs that is one or two resident workgroups per CU; more gave a second,
-//     partial round of workgroups and measured slower.
+//     25 us on 256 workgroups against 28 us on 240.  At most 256, or 512
+//     where two workgroups of the shape fit a CU (LayerNorm and the fused
+//     RMSNorm + RoPE with one or two batches ahead): on MI355X's 256 CUs
+//     one or two resident workgroups per CU; more gave a second, partial
+//     round of workgroups and measured slower.
 //   P depends on the row count and the operator only, so the summation order
 //   and the workspace size are the same on every device.
 void bwd_grid(int64_t rows, bool two_per_cu, int64_t* P_out, int64_t* rpb_out) {
@@ -207,12 +206,14 @@ nr_status_t plan_bwd(nr_dtype_t dt, bool ln, int64_t rows, int64_t n, bool align
   // 15360 x 5118 bf16)
   int D = (!ln && !rope && K == 1 && aligned) ? 2 : 1;
   int PF = ((!ln || gelu) && K == 1) ? 2 : 1;
-  // LayerNorm, and the fused RMSNorm + RoPE backward, on rows of one chunk
-  // per lane and at most 10 waves: one workgroup per CU with three batches
-  // in flight (65536 x 5120 bf16: LayerNorm 347 -> 333 us against two
-  // workgroups per CU with one batch each, RMSNorm + RoPE 343 -> 336 us
-  // against two per CU with two batches each)
-  if (((ln && !gelu) || rope) && K == 1 && (need + K - 1) / K <= 10) PF = 3;
+  // LayerNorm (with or without GeLU), and the fused RMSNorm + RoPE
+  // backward, on rows of one chunk per lane and at most 10 waves: one
+  // workgroup per CU with three batches in flight (65536 x 5120 bf16:
+  // LayerNorm 347 -> 333 us against two workgroups per CU with one batch
+  // each, RMSNorm + RoPE 343 -> 336 us against two per CU with two batches
+  // each; 15360 x 5120 bf16 LayerNorm + GeLU 116.8 -> 113.9 us against two
+  // batches ahead, 146 us with two workgroups per CU)
+  if ((ln || rope) && K == 1 && (need + K - 1) / K <= 10) PF = 3;
   // Plain RMSNorm on aligned rows of 8..10 chunk slots (4096..5120 bf16):
   //   batches of 16384 rows or more: two chunks per lane on half the waves
   //     (5120 bf16: 5 waves), one row per batch, two batches ahead -- fewer
