@@ -459,16 +459,13 @@ def cold_op_times(ops, rounds, dev):
     return res
 
 
-def time_steps(ops, steps, warmup):
+def warm_up(ops, warmup):
     """W warm-up steps, continued (untimed) until at least 0.5 s of steps
-    have run (short steps otherwise start timing before the GPU's clocks
-    have settled: the first ~20 fused-backward launches on a fresh process
-    ran ~15% slower), then exactly `steps` steps timed with HIP events on the
-    launch stream, one pair around each operation.  Returns (warm-up steps
-    run, ms per step, per-operation figures)."""
+    have run: short steps otherwise start timing before the GPU's clocks
+    have settled (the first ~20 fused-backward launches on a fresh process
+    ran ~15% slower).  Returns the number of steps run."""
     import torch
 
-    stream = torch.cuda.current_stream()
     t0, done = time.perf_counter(), 0
     while done < warmup or time.perf_counter() - t0 < 0.5:
         for _, _, fn, _ in ops:
@@ -477,21 +474,41 @@ def time_steps(ops, steps, warmup):
         if done >= warmup:
             torch.cuda.synchronize()
     torch.cuda.synchronize()
+    return done
+
+
+def time_steps(ops, steps, warmup, only=None):
+    """Warm-up (warm_up), then exactly `steps` steps timed with HIP events on
+    the launch stream.  An event pair brackets every operation, or, with
+    `only`, just the launches of that kernel (each pair costs a few
+    microseconds of queue time, so the headline steps carry only the pairs
+    the roofline needs).  Returns (warm-up steps run, ms per step, figures
+    of the bracketed operations)."""
+    import torch
+
+    stream = torch.cuda.current_stream()
+    done = warm_up(ops, warmup) if warmup > 0 else 0
+    timed = [only is None or kname == only for _, kname, _, _ in ops]
     ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in ops] for _ in range(steps)]
+           if timed[i] else None for i in range(len(ops))] for _ in range(steps)]
     t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t_start.record(stream)
     for s in range(steps):
         for i, (_, _, fn, _) in enumerate(ops):
-            ev[s][i][0].record(stream)
-            fn()
-            ev[s][i][1].record(stream)
+            if timed[i]:
+                ev[s][i][0].record(stream)
+                fn()
+                ev[s][i][1].record(stream)
+            else:
+                fn()
     t_end.record(stream)
     torch.cuda.synchronize()
     ms_per_step = t_start.elapsed_time(t_end) / steps
     per_op = {}
     for i, (label, kname, _, b) in enumerate(ops):
+        if not timed[i]:
+            continue
         times = [ev[s][i][0].elapsed_time(ev[s][i][1]) for s in range(steps)]
         mean = sum(times) / len(times)
         std = (sum((t - mean) ** 2 for t in times) / len(times)) ** 0.5
@@ -500,6 +517,21 @@ def time_steps(ops, steps, warmup):
                              gbs=round(b / (mean * 1e-3) / 1e9, 1),
                              frac_of_peak=round(b / (mean * 1e-3) / 1e9 / PEAK_GBS, 4))
     return done, ms_per_step, per_op
+
+
+def dominant_kernel(ops, per_op):
+    """The kernel (one instantiation, one shape) with the largest share of
+    the step's time; a backward call's two kernels (rows, column sum) count
+    as one "kernel" ("a+b"), since events around the call time the pair."""
+    kern = {}
+    for label, kname, _, b in ops:
+        k = kern.setdefault(kname, dict(launches=0, bytes=0, ms=0.0, ops=[]))
+        k["launches"] += 1
+        k["bytes"] += b
+        k["ms"] += per_op[label]["ms_mean"]
+        k["ops"].append(label)
+    name = max(kern, key=lambda k: kern[k]["ms"])
+    return name, kern[name]
 
 
 # the other configurations the 80%-of-peak bar applies to, measured in the
@@ -579,27 +611,21 @@ def main():
 
     ops, desc = build_ops(args.workload, dev)
     step_bytes = sum(b for _, _, _, b in ops)
-    done, ms_per_step, per_op = time_steps(ops, args.steps, args.warmup)
-    # dominant kernel: the kernel (one instantiation, one shape) with the
-    # largest share of the step's time, its per-launch figures averaged over
-    # all its launches in the step.  A backward is one call that launches
-    # two kernels (the rows, then the column reduction): events around the
-    # call time the pair, so the pair counts as one "kernel" ("a+b")
-    kern = {}
-    for label, kname, _, b in ops:
-        k = kern.setdefault(kname, dict(launches=0, bytes=0, ms=0.0, ops=[]))
-        k["launches"] += 1
-        k["bytes"] += b
-        k["ms"] += per_op[label]["ms_mean"]
-        k["ops"].append(label)
-    dname = max(kern, key=lambda k: kern[k]["ms"])
-    dk = kern[dname]
-    bpl, mspl = dk["bytes"] / dk["launches"], dk["ms"] / dk["launches"]
+    # untimed calibration: an event pair around every operation gives the
+    # per-operation figures ("ops") and the dominant kernel
+    done, _, per_op = time_steps(ops, args.steps, args.warmup)
+    dname, dk = dominant_kernel(ops, per_op)
+    # the timed region: exactly K steps, event pairs only around the
+    # dominant kernel's launches (for the roofline)
+    _, ms_per_step, dom_ops = time_steps(ops, args.steps, 0, only=dname)
+    bpl = dk["bytes"] / dk["launches"]
+    mspl = sum(v["ms_mean"] for v in dom_ops.values()) / len(dom_ops)
     achieved = bpl / (mspl * 1e-3) / 1e9
     roofline = dict(bound="hbm", achieved=round(achieved, 1), peak=PEAK_GBS, unit="GB/s",
                     frac=round(achieved / PEAK_GBS, 4), traffic=read_traffic(dname, args.workload),
                     kernel=dname, ops=dk["ops"], bytes_per_launch=int(bpl),
-                    ms_per_launch=round(mspl, 5), share_of_step=round(dk["ms"] / ms_per_step, 3))
+                    ms_per_launch=round(mspl, 5),
+                    share_of_step=round(mspl * dk["launches"] / ms_per_step, 3))
     unfused = desc.pop("unfused", None)
     if "flops_per_step" in desc:
         # a contraction: the matrix cores' bf16 dense peak bounds it
@@ -634,6 +660,8 @@ def main():
         "ceiling": ceiling,
         "mix_ceilings": mixes,
         "ops": per_op,
+        "ops_note": ("per-operation figures from an untimed pass of K steps with an event pair "
+                     "around every operation, run just before the timed steps"),
         "ops_cold": cold,
     }
     if not args.no_configs and args.workload == "longseq_65536x5120":

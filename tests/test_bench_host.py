@@ -50,3 +50,13 @@ def test_operation_mix():
     assert bench.op_mix("layernorm_gelu_bwd") == "2R1W"
     assert bench.op_mix("rmsnorm_fwd") == "1R1W"
     assert bench.op_mix("rope_inverse") == "1R1W"
+
+
+def test_dominant_kernel_counts_launches_and_pairs():
+    import bench
+    ops = [("a", "k1", None, 10), ("b", "k2+k3", None, 30), ("c", "k1", None, 10)]
+    per_op = {"a": dict(ms_mean=1.0), "b": dict(ms_mean=1.5), "c": dict(ms_mean=1.0)}
+    name, k = bench.dominant_kernel(ops, per_op)
+    assert name == "k1" and k["launches"] == 2 and k["bytes"] == 20 and k["ops"] == ["a", "c"]
+    per_op["b"]["ms_mean"] = 2.5
+    assert bench.dominant_kernel(ops, per_op)[0] == "k2+k3"
