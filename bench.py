@@ -540,13 +540,16 @@ GATED = ("rms_gemma_3840x5120", "ln_affine_15360x5120", "rope3d_15360x40x128")
 
 
 def config_summary(name, steps, warmup, cold_rounds, dev):
-    """One gated configuration, timed the same way as the headline workload
-    (warm, within steps) and alone with the caches flushed."""
+    """One gated configuration, timed the same way as the headline workload:
+    per operation in a pass with an event pair around each, the step over
+    steps run back to back, and each operation alone with the caches
+    flushed."""
     import torch
 
     ops, desc = build_ops(name, dev)
     step_bytes = sum(b for _, _, _, b in ops)
-    _, ms, per_op = time_steps(ops, steps, warmup)
+    _, _, per_op = time_steps(ops, steps, warmup)  # per operation, an event pair around each
+    _, ms, _ = time_steps(ops, steps, 0, only="")  # the step, operations back to back
     cold = cold_op_times(ops, cold_rounds, dev) if cold_rounds > 0 else None
     out = dict(step_bytes=step_bytes, ms_per_step=round(ms, 5),
                gbs=round(step_bytes / (ms * 1e-3) / 1e9, 1),

@@ -28,7 +28,11 @@
  *     take the 128-bit load path; other shapes take an element-wise path in
  *     the same kernels.  (The linear-layer calls need 16-byte alignment.)
  *   - An output may be the very same buffer as an input of the same shape
- *     (in place, e.g. y == x, dx == dy); partial overlap is not allowed.
+ *     (in place: y == x, dx == dy or dx == x); no other output, and no
+ *     workspace, may share a byte with any operand of the call (weights, row
+ *     statistics, tables, column gradients included), else NR_ERR_ALIAS.
+ *     The backward kernels read the row statistics through the scalar cache,
+ *     which writes to other buffers do not update.
  *   - Backward results are bitwise reproducible: for a given shape every
  *     summation order is fixed (no atomics), whatever the device.
  *   - Thread safety: calls may be made from several host threads; the only

@@ -73,6 +73,66 @@ bool bad_overlap(const void* a, size_t na, const void* b, size_t nb) {
   return a0 < b0 + nb && b0 < a0 + na;
 }
 
+// Two byte ranges share at least one byte (ranges that coincide included).
+// Range ends saturate, so a size past the address space cannot wrap.
+bool any_overlap(const void* a, size_t na, const void* b, size_t nb) {
+  if (a == nullptr || b == nullptr || na == 0 || nb == 0) return false;
+  const uintptr_t a0 = reinterpret_cast<uintptr_t>(a), b0 = reinterpret_cast<uintptr_t>(b);
+  const uintptr_t a1 = na > UINTPTR_MAX - a0 ? UINTPTR_MAX : a0 + na;
+  const uintptr_t b1 = nb > UINTPTR_MAX - b0 ? UINTPTR_MAX : b0 + nb;
+  return a0 < b1 && b0 < a1;
+}
+
+// The forward's outputs against its inputs, x against y excepted (in place
+// is the caller's choice, checked by the caller): y and the row statistics
+// are written while x, the weights and the tables are read.
+bool fwd_buffers_disjoint(nr_dtype_t dt, int64_t rows, int64_t n, const void* x, const void* w,
+                          const void* beta, const void* y, const float* s0, const float* s1,
+                          const float* cos_tab = nullptr, const float* sin_tab = nullptr,
+                          size_t tab_bytes = 0) {
+  const size_t bytes = static_cast<size_t>(rows * n) * elem_bytes(dt);
+  const size_t wb = static_cast<size_t>(n) * elem_bytes(dt);
+  const size_t sb = static_cast<size_t>(rows) * sizeof(float);
+  struct Range { const void* p; size_t n; };
+  const Range read[] = {{x, bytes}, {w, wb}, {beta, wb}, {cos_tab, tab_bytes}, {sin_tab, tab_bytes}};
+  const Range written[] = {{y, bytes}, {s0, sb}, {s1, sb}};
+  for (int i = 0; i < 3; ++i) {
+    for (int j = (i == 0 ? 1 : 0); j < 5; ++j)
+      if (any_overlap(written[i].p, written[i].n, read[j].p, read[j].n)) return false;
+    for (int j = i + 1; j < 3; ++j)
+      if (any_overlap(written[i].p, written[i].n, written[j].p, written[j].n)) return false;
+  }
+  return true;
+}
+
+// The backward's buffers beyond dx against dy and x (checked by the caller):
+// dx, the column gradients and the workspace are written while every other
+// operand is read, so none of them may share a byte with another operand.
+// (The row statistics are read through the scalar cache, which the writes to
+// dx would not update.)
+bool bwd_buffers_disjoint(nr_dtype_t dt, int64_t rows, int64_t n, const void* dy, const void* x,
+                          const void* w, const void* beta, const float* mean, const float* rstat,
+                          const void* dx, const float* o0, const float* o1, const void* workspace,
+                          size_t workspace_bytes, const float* cos_tab = nullptr,
+                          const float* sin_tab = nullptr, size_t tab_bytes = 0) {
+  const size_t bytes = static_cast<size_t>(rows * n) * elem_bytes(dt);
+  const size_t wb = static_cast<size_t>(n) * elem_bytes(dt);
+  const size_t sb = static_cast<size_t>(rows) * sizeof(float);
+  const size_t cb = static_cast<size_t>(n) * sizeof(float);
+  struct Range { const void* p; size_t n; };
+  const Range read[] = {{dy, bytes}, {x, bytes}, {w, wb}, {beta, wb}, {mean, sb}, {rstat, sb},
+                        {cos_tab, tab_bytes}, {sin_tab, tab_bytes}};
+  const Range written[] = {{dx, bytes}, {o0, cb}, {o1, cb}, {workspace, workspace_bytes}};
+  for (int i = 0; i < 4; ++i) {
+    // dx may coincide with dy or x (in place): those pairs are the caller's
+    for (int j = (i == 0 ? 2 : 0); j < 8; ++j)
+      if (any_overlap(written[i].p, written[i].n, read[j].p, read[j].n)) return false;
+    for (int j = i + 1; j < 4; ++j)
+      if (any_overlap(written[i].p, written[i].n, written[j].p, written[j].n)) return false;
+  }
+  return true;
+}
+
 nr_status_t check_dtype(nr_dtype_t dt) {
   return (dt == NR_F32 || dt == NR_BF16 || dt == NR_F16) ? NR_OK : NR_ERR_DTYPE;
 }
@@ -271,7 +331,7 @@ bool rope_vectors_disjoint(int64_t batch, int64_t tokens, int64_t heads, int64_t
 }
 
 nr_status_t plan_rope(nr_dtype_t dt, int64_t heads, int64_t head_dim, bool aligned,
-                      RopePlan* pl) {
+                      int64_t vectors, RopePlan* pl) {
   const int E = aligned ? vec_elems(dt) : 2;
   const int64_t cph = head_dim / E;
   const int64_t nchunk = heads * cph;
@@ -279,8 +339,12 @@ nr_status_t plan_rope(nr_dtype_t dt, int64_t heads, int64_t head_dim, bool align
   // lane each (a 40 x 128 bf16 token: 640 chunks, 3 waves of 4): against
   // one wave of 10 chunks per token that measured 6.3 -> 6.45-6.5 TB/s on
   // 65536 such tokens and 6.0 -> 6.4 TB/s on 15360, i.e. the streaming-copy
-  // ceiling.  Very long tokens keep at most 64 waves and loop.
-  int groups = static_cast<int>(std::min<int64_t>((nchunk + 255) / 256, 64));
+  // ceiling.  Batches of fewer than 32768 token vectors take about 2
+  // chunks per lane on more waves (40 x 128 bf16: 5 waves of 2; 15360
+  // tokens 50.2 -> 49.3 us; at 65536 tokens the 4-chunk shape stays ahead).
+  // Very long tokens keep at most 64 waves and loop.
+  const int64_t per_wave = vectors < 32768 ? 128 : 256;
+  int groups = static_cast<int>(std::min<int64_t>((nchunk + per_wave - 1) / per_wave, 64));
   if (tune(ROPE_GROUPS) > 0) groups = tune(ROPE_GROUPS);
   int K = pick_at_least((nchunk + 64 * groups - 1) / (64 * groups), kRopeK, 7);
   if (K == 0) K = 10;  // several passes over the heads
@@ -354,6 +418,7 @@ nr_status_t rmsnorm_fwd(nr_dtype_t dt, const void* x, const void* w, void* y, fl
   if (x == nullptr || y == nullptr) return NR_ERR_NULLPTR;
   const size_t bytes = static_cast<size_t>(rows * n) * elem_bytes(dt);
   if (bad_overlap(y, bytes, x, bytes)) return NR_ERR_ALIAS;
+  if (!fwd_buffers_disjoint(dt, rows, n, x, w, nullptr, y, inv_rms, nullptr)) return NR_ERR_ALIAS;
   const bool aligned = (n % vec_elems(dt)) == 0 && aligned16(x) && aligned16(y) &&
                        (w == nullptr || aligned16(w));
   FwdPlan pl;
@@ -374,6 +439,7 @@ nr_status_t layernorm_fwd(nr_dtype_t dt, const void* x, const void* gamma, const
   if (x == nullptr || y == nullptr) return NR_ERR_NULLPTR;
   const size_t bytes = static_cast<size_t>(rows * n) * elem_bytes(dt);
   if (bad_overlap(y, bytes, x, bytes)) return NR_ERR_ALIAS;
+  if (!fwd_buffers_disjoint(dt, rows, n, x, gamma, beta, y, mean, rstd)) return NR_ERR_ALIAS;
   const bool aligned = (n % vec_elems(dt)) == 0 && aligned16(x) && aligned16(y) &&
                        (gamma == nullptr || aligned16(gamma)) &&
                        (beta == nullptr || aligned16(beta));
@@ -436,6 +502,9 @@ nr_status_t norm_bwd_common(bool ln, nr_dtype_t dt, const void* dy, const void* 
     return NR_ERR_NULLPTR;
   const size_t bytes = static_cast<size_t>(rows * n) * elem_bytes(dt);
   if (bad_overlap(dx, bytes, dy, bytes) || bad_overlap(dx, bytes, x, bytes)) return NR_ERR_ALIAS;
+  if (!bwd_buffers_disjoint(dt, rows, n, dy, x, w, beta, mean, rstat, dx, o0, o1, workspace,
+                            workspace_bytes))
+    return NR_ERR_ALIAS;
   const bool aligned = (n % vec_elems(dt)) == 0 && aligned16(dy) && aligned16(x) &&
                        aligned16(dx) && (w == nullptr || aligned16(w)) &&
                        (beta == nullptr || aligned16(beta));
@@ -491,6 +560,7 @@ nr_status_t layernorm_gelu_fwd(nr_dtype_t dt, const void* x, const void* gamma, 
   if (x == nullptr || y == nullptr) return NR_ERR_NULLPTR;
   const size_t bytes = static_cast<size_t>(rows * n) * elem_bytes(dt);
   if (bad_overlap(y, bytes, x, bytes)) return NR_ERR_ALIAS;
+  if (!fwd_buffers_disjoint(dt, rows, n, x, gamma, beta, y, mean, rstd)) return NR_ERR_ALIAS;
   const bool aligned = (n % vec_elems(dt)) == 0 && aligned16(x) && aligned16(y) &&
                        (gamma == nullptr || aligned16(gamma)) &&
                        (beta == nullptr || aligned16(beta));
@@ -542,6 +612,11 @@ nr_status_t rmsnorm_rope_fwd(nr_dtype_t dt, const void* x, const void* w, void* 
     return s;
   const size_t bytes = static_cast<size_t>(rows * n) * elem_bytes(dt);
   if (bad_overlap(y, bytes, x, bytes)) return NR_ERR_ALIAS;
+  const size_t tab_bytes =
+      static_cast<size_t>((rows + rows_per_token - 1) / rows_per_token) * (head_dim / 2) * 4;
+  if (!fwd_buffers_disjoint(dt, rows, n, x, w, nullptr, y, inv_rms, nullptr, cos_tab, sin_tab,
+                            tab_bytes))
+    return NR_ERR_ALIAS;
   const bool aligned = vec_tab && (n % vec_elems(dt)) == 0 && aligned16(x) && aligned16(y) &&
                        (w == nullptr || aligned16(w));
   FwdPlan pl;
@@ -575,6 +650,12 @@ nr_status_t rmsnorm_rope_bwd(nr_dtype_t dt, const void* dout, const void* x, con
     return s;
   const size_t bytes = static_cast<size_t>(rows * n) * elem_bytes(dt);
   if (bad_overlap(dx, bytes, dout, bytes) || bad_overlap(dx, bytes, x, bytes)) return NR_ERR_ALIAS;
+  // the tables: head_dim / 2 angles per token
+  const size_t tab_bytes =
+      static_cast<size_t>((rows + rows_per_token - 1) / rows_per_token) * (head_dim / 2) * 4;
+  if (!bwd_buffers_disjoint(dt, rows, n, dout, x, w, nullptr, nullptr, inv_rms, dx, dw, nullptr,
+                            workspace, workspace_bytes, cos_tab, sin_tab, tab_bytes))
+    return NR_ERR_ALIAS;
   const bool aligned = vec_tab && (n % vec_elems(dt)) == 0 && aligned16(dout) && aligned16(x) &&
                        aligned16(dx) && (w == nullptr || aligned16(w));
   const nr::RopeArgs ra{cos_tab, sin_tab, static_cast<int>(head_dim), rows_per_token};
@@ -626,7 +707,7 @@ nr_status_t rope_interleaved_apply(nr_dtype_t dt, void* x, const float* cos_tab,
                        stride_head % v == 0 && aligned16(x) && aligned16(cos_tab) &&
                        aligned16(sin_tab);
   RopePlan pl;
-  if ((s = plan_rope(dt, heads, head_dim, aligned, &pl)) != NR_OK) return s;
+  if ((s = plan_rope(dt, heads, head_dim, aligned, batch * tokens, &pl)) != NR_OK) return s;
   // `groups` waves per token, waves_per_block waves per workgroup: the grid
   // must fit the hardware's 2^31 - 1 workgroups
   if (batch * tokens > INT64_MAX / 64 ||

@@ -47,7 +47,25 @@ struct RowBatch {
   float tc[D * TS][Vec<T>::N / 2], ts[D * TS][Vec<T>::N / 2];
 };
 
-template <typename T, int K, int D, bool VEC, bool LN, bool ROPE, int TS>
+// A batch's row statistics as scalar loads (into SGPRs: each is uniform over
+// the workgroup).  They are read-only for the kernel's whole run, which is
+// what the constant address space asserts.  Rows past the end take 0 and load
+// nothing.
+template <typename T, int K, int D, bool LN, int TS>
+__device__ __forceinline__ void load_stats(RowBatch<T, K, D, TS>& b, int64_t base, int64_t rows,
+                                           const float* mean, const float* rstat) {
+  using cfloat = const __attribute__((address_space(4))) float;
+#pragma unroll
+  for (int d = 0; d < D; ++d) {
+    const int64_t row = base + d;
+    const bool okr = row < rows;
+    b.rs[d] = okr ? ((cfloat*)rstat)[row] : 0.0f;
+    b.mu[d] = (LN && okr) ? ((cfloat*)mean)[row] : 0.0f;
+  }
+}
+
+// SSTAT: the statistics are left to load_stats, issued later.
+template <typename T, int K, int D, bool VEC, bool LN, bool ROPE, int TS, bool SSTAT>
 __device__ __forceinline__ void load_batch(RowBatch<T, K, D, TS>& b, int64_t base,
                                            int64_t rows, const T* x, const T* dy,
                                            const float* mean, const float* rstat, int n, int t,
@@ -67,8 +85,10 @@ __device__ __forceinline__ void load_batch(RowBatch<T, K, D, TS>& b, int64_t bas
       b.x[d * K + k] = ld_chunk<T, VEC, kStream>(xr, t + k * nthr);
       b.g[d * K + k] = ld_chunk<T, VEC, kStream>(gr, t + k * nthr);
     }
-    b.rs[d] = okr ? rstat[row] : 0.0f;
-    b.mu[d] = (LN && okr) ? mean[row] : 0.0f;
+    if constexpr (!SSTAT) {
+      b.rs[d] = okr ? rstat[row] : 0.0f;
+      b.mu[d] = (LN && okr) ? mean[row] : 0.0f;
+    }
     if constexpr (ROPE) {
       // the token's table rows; this lane's chunks sit at fixed offsets in
       // their heads (see the forward)
@@ -115,7 +135,14 @@ __device__ __forceinline__ void dy_chunk(const RowBatch<T, K, D, TS>& b, int i,
 // EPI == kEpiGelu (LayerNorm): the upstream gradient is that of
 // gelu(xhat gamma + beta); the pre-activation is recomputed from the cached
 // statistics and dy = dout * gelu'(pre-activation).
-template <typename T, int K, int D, bool VEC, bool LN, bool ROPE, int EPI, int TS>
+// late(): with SSTAT, issues the scalar statistics loads of a batch loaded
+// ahead, once this batch's sums are complete.  Scalar loads complete out of
+// order, so every wait for one (and for an LDS access: they share a counter)
+// waits for all; issued here, after the sums' LDS read has been waited for,
+// they have the rest of this batch and the next batch's first pass before
+// the next such wait.
+template <typename T, int K, int D, bool VEC, bool LN, bool ROPE, int EPI, int TS, bool SSTAT,
+          typename F>
 __device__ __forceinline__ void process_batch(RowBatch<T, K, D, TS>& b, int64_t base,
                                               int64_t rows, T* dx, int n, int t, int nthr, int W,
                                               int wave, int lane, float inv_n,
@@ -124,7 +151,7 @@ __device__ __forceinline__ void process_batch(RowBatch<T, K, D, TS>& b, int64_t 
                                               const u32x4 (&wpk)[K], const u32x4 (&bpk)[K],
                                               float w_add, float (&acc1)[K][Vec<T>::N],
                                               float (&acc2)[K][Vec<T>::N],
-                                              float (*red)[16], int& parity) {
+                                              float (*red)[16], int& parity, F&& late) {
   constexpr int E = Vec<T>::N;
   constexpr int NS = LN ? 2 : 1;  // row sums per row
   // per-lane partial row sums, and the column partials.  Elements past n
@@ -197,13 +224,29 @@ __device__ __forceinline__ void process_batch(RowBatch<T, K, D, TS>& b, int64_t 
       for (int i = 0; i < NS * D; ++i) rp[i][wave] = s[i];
     }
     __syncthreads();
+    // The GeLU backward, whose activation arithmetic already stands between
+    // a batch's loads and its barrier, adds the W wave sums with one LDS read
+    // and a 16-lane tree (15360 x 5120 bf16: 110.1 -> 102.9 us).  The others
+    // keep the in-order loop over the slots: measured against the tree on
+    // one MI355X, the RMSNorm and LayerNorm backward at 65536 x 5120 bf16
+    // ran 3-6% slower with it (329.6 -> 338.9 and 325.0 -> 343.5 us) and the
+    // forwards no faster.
 #pragma unroll
     for (int i = 0; i < NS * D; ++i) {
-      float tot = 0.0f;
-      for (int q = 0; q < W; ++q) tot += rp[i][q];
-      s[i] = tot;
+      if constexpr (EPI == kEpiGelu) {
+        s[i] = slot_sum16(rp[i], 0, W);
+      } else {
+        float tot = 0.0f;
+        for (int q = 0; q < W; ++q) tot += rp[i][q];
+        s[i] = tot;
+      }
     }
     parity ^= 1;  // the other buffer next batch: no second barrier needed
+  }
+  if constexpr (SSTAT) {
+    // the asm needs the finished sum, and memory operations cannot cross it
+    asm volatile("" ::"s"(s[0]) : "memory");
+    late();
   }
 
   const uint32_t rbytes = static_cast<uint32_t>(n) * sizeof(T);
@@ -322,19 +365,34 @@ norm_bwd_rows(const T* dy, const T* x, const T* w, const T* beta, const float* m
   // PF batches are loaded ahead of the one being reduced; PF + 1 register
   // buffers are used in turn (the loop is unrolled over them, so no register
   // copy ever waits on a load in flight).
+  //
+  // The row statistics of the LayerNorm (with or without GeLU) and RoPE
+  // backward come in through scalar loads (SSTAT), which frees their VGPRs in
+  // every buffer.  Measured on MI355X (bf16, rows of 5120): LayerNorm + GeLU
+  // at 15360 rows 103 -> 94 us, RMSNorm + RoPE at 65536 rows 349 -> 324 us,
+  // LayerNorm 85.4 -> 82.5 us at 15360 rows and level at 65536; the plain
+  // RMSNorm backward ran about 1% slower with them and keeps vector loads.
+  constexpr bool SSTAT = LN || ROPE;
   RowBatch<T, K, D, TS> buf[PF + 1];
 #pragma unroll
-  for (int i = 0; i < PF; ++i)
-    load_batch<T, K, D, VEC, LN, ROPE, TS>(buf[i], base + i * step, rows, x, dy, mean, rstat, n, t,
-                                       nthr, ra);
+  for (int i = 0; i < PF; ++i) {
+    load_batch<T, K, D, VEC, LN, ROPE, TS, SSTAT>(buf[i], base + i * step, rows, x, dy, mean, rstat,
+                                                  n, t, nthr, ra);
+    if constexpr (SSTAT) load_stats<T, K, D, LN, TS>(buf[i], base + i * step, rows, mean, rstat);
+  }
   while (true) {
 #pragma unroll
     for (int i = 0; i <= PF; ++i) {
       if (base >= rows) goto done;
-      load_batch<T, K, D, VEC, LN, ROPE, TS>(buf[(i + PF) % (PF + 1)], base + PF * step, rows, x, dy,
-                                         mean, rstat, n, t, nthr, ra);
-      process_batch<T, K, D, VEC, LN, ROPE, EPI, TS>(buf[i], base, rows, dx, n, t, nthr, W, wave, lane,
-                                                 inv_n, wv, bv, wpk, bpk, w_add_packed, acc1, acc2, red, parity);
+      RowBatch<T, K, D, TS>& ahead = buf[(i + PF) % (PF + 1)];
+      const int64_t abase = base + PF * step;
+      load_batch<T, K, D, VEC, LN, ROPE, TS, SSTAT>(ahead, abase, rows, x, dy, mean, rstat, n, t,
+                                                    nthr, ra);
+      process_batch<T, K, D, VEC, LN, ROPE, EPI, TS, SSTAT>(
+          buf[i], base, rows, dx, n, t, nthr, W, wave, lane, inv_n, wv, bv, wpk, bpk, w_add_packed,
+          acc1, acc2, red, parity, [&] {
+            if constexpr (SSTAT) load_stats<T, K, D, LN, TS>(ahead, abase, rows, mean, rstat);
+          });
       base += step;
     }
   }

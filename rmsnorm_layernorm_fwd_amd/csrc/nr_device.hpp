@@ -356,6 +356,24 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
+// Sum of the slots [lo, hi) of a 16-float LDS line that the waves of a
+// workgroup have filled (one slot per wave), returned as a uniform value.
+// One LDS read per lane, whatever the number of waves: lane i of each
+// 16-lane row reads slot i, slots outside [lo, hi) (another row group's, or
+// never written) are replaced by 0, and the row's first four butterfly steps
+// of wave_sum add the 16 in a fixed tree; every wave that asks gets the same
+// bits.
+__device__ __forceinline__ float slot_sum16(const float* line, int lo, int hi) {
+  const int i = threadIdx.x & 15;
+  float v = line[i];
+  v = (i >= lo && i < hi) ? v : 0.0f;
+  v += dpp<0xB1>(v);   // quad_perm [1,0,3,2]
+  v += dpp<0x4E>(v);   // quad_perm [2,3,0,1]
+  v += dpp<0x141>(v);  // row_half_mirror
+  v += dpp<0x140>(v);  // row_mirror
+  return __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(v)));
+}
+
 // Sum of v over the W waves of a row group (W == 1: a pure wave reduction).
 // red: LDS scratch of at least blockDim/64 floats, used once per call site;
 // wave sums meet there and are added in wave order.

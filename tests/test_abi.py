@@ -146,12 +146,29 @@ def test_rejected_calls_return_status(lib):
     assert L.rmsnorm_bwd(BF16, FAKE, 0x90000, None, FAKE, FAKE + 16, None, 4, 8, 0, None, 0, None) == NR_ERR_ALIAS
     assert L.rope_interleaved_apply(BF16, FAKE, FAKE, FAKE, 1, 4, 2, 8, 64, 16, 4, 0, None) == NR_ERR_ALIAS
     # workspace missing, short or misaligned when a column gradient is wanted
+    # (64 x 256 fp32 rows: dy at FAKE, x, dx 64 KiB each; statistics, dw,
+    # dbeta and the workspace in ranges of their own)
+    R, MU, DW, DB, WS = 0xC0000, 0xC8000, 0xD0000, 0xD8000, 0xE0000
     need = nr.nr_bwd_workspace_bytes(64, 256, 0)
-    assert L.rmsnorm_bwd(F32, FAKE, 0x90000, None, FAKE, 0xA0000, FAKE, 64, 256, 0, None, 0, None) == NR_ERR_WORKSPACE
-    assert L.rmsnorm_bwd(F32, FAKE, 0x90000, None, FAKE, 0xA0000, FAKE, 64, 256, 0, 0xB0000, need - 4, None) == NR_ERR_WORKSPACE
-    assert L.rmsnorm_bwd(F32, FAKE, 0x90000, None, FAKE, 0xA0000, FAKE, 64, 256, 0, 0xB0004, need, None) == NR_ERR_WORKSPACE
+    assert L.rmsnorm_bwd(F32, FAKE, 0x90000, None, R, 0xA0000, DW, 64, 256, 0, None, 0, None) == NR_ERR_WORKSPACE
+    assert L.rmsnorm_bwd(F32, FAKE, 0x90000, None, R, 0xA0000, DW, 64, 256, 0, WS, need - 4, None) == NR_ERR_WORKSPACE
+    assert L.rmsnorm_bwd(F32, FAKE, 0x90000, None, R, 0xA0000, DW, 64, 256, 0, WS + 4, need, None) == NR_ERR_WORKSPACE
     need_ln = nr.nr_bwd_workspace_bytes(64, 256, 1)
-    assert L.layernorm_bwd(F32, FAKE, 0x90000, None, FAKE, FAKE, 0xA0000, None, FAKE, 64, 256, 0xB0000, need_ln - 1, None) == NR_ERR_WORKSPACE
+    assert L.layernorm_bwd(F32, FAKE, 0x90000, None, MU, R, 0xA0000, None, DB, 64, 256, WS, need_ln - 1, None) == NR_ERR_WORKSPACE
+    # every other output and the workspace share no byte with any operand:
+    # dx over the statistics or the weight, a column gradient over dy, over
+    # the workspace or over the other one, the workspace over x
+    assert L.rmsnorm_bwd(F32, FAKE, 0x90000, None, 0xA0000 + 256, 0xA0000, DW, 64, 256, 0, WS, need, None) == NR_ERR_ALIAS
+    assert L.rmsnorm_bwd(F32, FAKE, 0x90000, 0xA0000 + 512, R, 0xA0000, DW, 64, 256, 0, WS, need, None) == NR_ERR_ALIAS
+    assert L.rmsnorm_bwd(F32, FAKE, 0x90000, None, R, 0xA0000, FAKE + 64, 64, 256, 0, WS, need, None) == NR_ERR_ALIAS
+    assert L.rmsnorm_bwd(F32, FAKE, 0x90000, None, R, 0xA0000, WS + 16, 64, 256, 0, WS, need, None) == NR_ERR_ALIAS
+    assert L.rmsnorm_bwd(F32, FAKE, 0x90000, None, R, 0xA0000, DW, 64, 256, 0, 0x90000 + 1024, need, None) == NR_ERR_ALIAS
+    assert L.layernorm_bwd(F32, FAKE, 0x90000, None, MU, R, 0xA0000, DB, DB + 512, 64, 256, WS, need_ln, None) == NR_ERR_ALIAS
+    # the forward: y over the weight, the statistics over x or over each other
+    assert L.rmsnorm_fwd(F32, FAKE, 0xA0000 + 1024, 0xA0000, None, 64, 256, 1e-6, 0, None) == NR_ERR_ALIAS
+    assert L.rmsnorm_fwd(F32, FAKE, None, 0xA0000, FAKE + 4, 64, 256, 1e-6, 0, None) == NR_ERR_ALIAS
+    assert L.layernorm_fwd(F32, FAKE, None, None, 0xA0000, R, R + 128, 64, 256, 1e-5, None) == NR_ERR_ALIAS
+    assert L.layernorm_gelu_fwd(F32, FAKE, 0xA0000 + 64, None, 0xA0000, R, MU, 64, 256, 1e-5, None) == NR_ERR_ALIAS
     # grids beyond the hardware's 2^31 - 1 workgroups are refused, not truncated
     FAR = 1 << 40
     assert L.rmsnorm_fwd(BF16, FAKE, None, FAR, None, 1 << 33, 1, 1e-6, 0, None) == NR_ERR_SHAPE
@@ -238,9 +255,9 @@ def test_rejected_calls_return_status(lib):
                                  None) == NR_ERR_WORKSPACE
     assert L.rmsnorm_bwd_noalloc(7, FAKE, X, None, FAKE, 1 << 25, None, 4, 8, 0, None) == NR_ERR_DTYPE
     # long rows need the workspace even without a column gradient
-    X2, DX2, WS2 = 1 << 24, 1 << 25, 1 << 26
-    assert L.rmsnorm_bwd(BF16, FAKE, X2, None, FAKE, DX2, None, 4, 20000, 0, None, 0, None) == NR_ERR_WORKSPACE
-    assert L.layernorm_bwd(F32, FAKE, X2, None, FAKE, FAKE, DX2, None, None, 4, 20000, WS2, 31, None) == NR_ERR_WORKSPACE
+    X2, DX2, WS2, R2 = 1 << 24, 1 << 25, 1 << 26, 1 << 27
+    assert L.rmsnorm_bwd(BF16, FAKE, X2, None, R2, DX2, None, 4, 20000, 0, None, 0, None) == NR_ERR_WORKSPACE
+    assert L.layernorm_bwd(F32, FAKE, X2, None, R2 + 4096, R2, DX2, None, None, 4, 20000, WS2, 31, None) == NR_ERR_WORKSPACE
     # a forced launch shape that cannot cover the row
     assert L.nr_tune(b"fwd_k", 1) == NR_OK
     try:
