@@ -456,30 +456,62 @@ row_inv_rms_kernel(const bf16* __restrict__ x, float* __restrict__ r, int M, int
 }
 
 // Row statistics of the LayerNorm form: mean_m and rstd_m = 1/sqrt(var_m +
-// eps) with the biased variance, one wave per row, fp32; the variance is a
-// second pass over the row (centred squares; the row is re-read from cache).
+// eps) with the biased variance, one wave per row, fp32.  The variance is
+// the mean of the centred squares, a second pass over the row: with
+// CPL > 0 over the row kept in registers (CPL 16-byte chunks per lane, rows
+// of up to 512 CPL elements: one read of x from HBM), with CPL == 0 over
+// the row read again (longer rows; the second read mostly misses the cache).
+template <int CPL>
 __global__ void __launch_bounds__(256)
 row_mean_rstd_kernel(const bf16* __restrict__ x, float* __restrict__ mean,
                      float* __restrict__ rstd, int M, int K, float eps) {
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
   if (row >= M) return;
+  const int chunks = K / 8;
   const rsrc_t xr = make_rsrc(x + static_cast<int64_t>(row) * K, static_cast<uint32_t>(K) * 2u);
-  float s = 0.0f;
-  for (int c = lane; c < K / 8; c += 64) {
-    float f[8];
-    unpack<bf16>(__builtin_amdgcn_raw_buffer_load_b128(xr, c * 16, 0, 0), f);
+  float s = 0.0f, q = 0.0f, mu;
+  if constexpr (CPL > 0) {
+    // chunks past the row read as 0 (buffer range) and are left out of the
+    // centred squares
+    u32x4 v[CPL];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) s += f[e];
-  }
-  const float mu = wave_sum(s) / static_cast<float>(K);
-  float q = 0.0f;
-  for (int c = lane; c < K / 8; c += 64) {
-    float f[8];
-    unpack<bf16>(__builtin_amdgcn_raw_buffer_load_b128(xr, c * 16, 0, kStream), f);
+    for (int i = 0; i < CPL; ++i)
+      v[i] = __builtin_amdgcn_raw_buffer_load_b128(xr, (lane + 64 * i) * 16, 0, kStream);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const float d = f[e] - mu;
-      q = fmaf(d, d, q);
+    for (int i = 0; i < CPL; ++i) {
+      float f[8];
+      unpack<bf16>(v[i], f);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) s += f[e];
+    }
+    mu = wave_sum(s) / static_cast<float>(K);
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) {
+      if (lane + 64 * i >= chunks) break;
+      float f[8];
+      unpack<bf16>(v[i], f);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float d = f[e] - mu;
+        q = fmaf(d, d, q);
+      }
+    }
+  } else {
+    for (int c = lane; c < chunks; c += 64) {
+      float f[8];
+      unpack<bf16>(__builtin_amdgcn_raw_buffer_load_b128(xr, c * 16, 0, 0), f);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) s += f[e];
+    }
+    mu = wave_sum(s) / static_cast<float>(K);
+    for (int c = lane; c < chunks; c += 64) {
+      float f[8];
+      unpack<bf16>(__builtin_amdgcn_raw_buffer_load_b128(xr, c * 16, 0, kStream), f);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float d = f[e] - mu;
+        q = fmaf(d, d, q);
+      }
     }
   }
   const float r = rsqrtf(wave_sum(q) / static_cast<float>(K) + eps);
@@ -620,8 +652,15 @@ hipError_t launch_layernorm_linear(const void* x, const void* gamma, const void*
   float* dn = reinterpret_cast<float*>(p);
   p += linear_rows_bytes(N);
   bf16* wf = reinterpret_cast<bf16*>(p);
-  hipLaunchKernelGGL(row_mean_rstd_kernel, dim3(static_cast<unsigned>((M + 3) / 4)), dim3(256), 0,
-                     st, static_cast<const bf16*>(x), mu, rs, M, K, eps);
+  // the row in registers when it fits 4, 10 or 16 chunks per lane (the
+  // fewest that cover it), else read twice
+  const int cpl = (K / 8 + 63) / 64;
+  auto stats = cpl <= 4    ? row_mean_rstd_kernel<4>
+               : cpl <= 10 ? row_mean_rstd_kernel<10>
+               : cpl <= 16 ? row_mean_rstd_kernel<16>
+                           : row_mean_rstd_kernel<0>;
+  hipLaunchKernelGGL(stats, dim3(static_cast<unsigned>((M + 3) / 4)), dim3(256), 0, st,
+                     static_cast<const bf16*>(x), mu, rs, M, K, eps);
   hipLaunchKernelGGL(fold_ln_weight_kernel, dim3(static_cast<unsigned>((N + 3) / 4)), dim3(256), 0,
                      st, static_cast<const bf16*>(gamma), static_cast<const bf16*>(beta),
                      static_cast<const bf16*>(W), wf, cn, dn, N, K);

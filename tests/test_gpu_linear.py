@@ -207,6 +207,9 @@ def run_ln_case(tag, m, n, k, seed, affine=("g", "b"), mean=0.5, std=2.0, rows=N
 @pytest.mark.parametrize("m,n,k,affine", [
     (1, 256, 64, ("g", "b")), (130, 256, 128, ()), (257, 512, 320, ("g",)),
     (1000, 1280, 5120, ("g", "b")), (4096, 768, 5120, ("b",)),
+    # rows held in 10 and 16 chunks per lane by the statistics pass, and past
+    # that (read twice; K = 65536 below)
+    (200, 256, 3072, ()), (70, 256, 8192, ("g", "b")), (33, 256, 8256, ("g",)),
 ])
 def test_layernorm_linear_cases(m, n, k, affine):
     run_ln_case(f"ln {m}x{n}x{k}", m, n, k, 9600 + m + n + k, affine)
