@@ -78,6 +78,8 @@ __device__ __forceinline__ void fwd_finish_rows(u32x4 (&xa)[J * K], u32x4 (&wa)[
   constexpr int E = Vec<T>::N;
   const uint32_t rbytes = static_cast<uint32_t>(n) * sizeof(T);
   const float fn = static_cast<float>(n);
+  // without a weight its loads returned 0, and 0 + 1 is the weight 1
+  const float wadd = (w != nullptr) ? w_add : 1.0f;
   float mean[J], r[J];
   if constexpr (LN) {
     float s[J];
@@ -94,21 +96,38 @@ __device__ __forceinline__ void fwd_finish_rows(u32x4 (&xa)[J * K], u32x4 (&wa)[
     }
     group_sum_n<J>(s, W, wave, g, red0);
     reload_barrier<J * K>(xa);
-    // second pass over the registers, not over HBM: squared deviations
+    // second pass over the registers, not over HBM: squared deviations.
+    // The slots past n (read as 0) are left out; when the row fills every
+    // slot of the row group exactly (5120 bf16 on 2 waves of 5 chunks) no
+    // slot is masked, a uniform branch.
     float q[J];
+    const bool full = nthr * K * E == n;
 #pragma unroll
     for (int j = 0; j < J; ++j) {
       mean[j] = s[j] / fn;
       q[j] = 0.0f;
+      if (full) {
 #pragma unroll
-      for (int k = 0; k < K; ++k) {
-        const int c = t + k * nthr;
-        float v[E];
-        unpack<T>(xa[j * K + k], v);
+        for (int k = 0; k < K; ++k) {
+          float v[E];
+          unpack<T>(xa[j * K + k], v);
 #pragma unroll
-        for (int e = 0; e < E; ++e) {
-          const float d = (c * E + e < n) ? v[e] - mean[j] : 0.0f;
-          q[j] = fmaf(d, d, q[j]);
+          for (int e = 0; e < E; ++e) {
+            const float d = v[e] - mean[j];
+            q[j] = fmaf(d, d, q[j]);
+          }
+        }
+      } else {
+#pragma unroll
+        for (int k = 0; k < K; ++k) {
+          const int c = t + k * nthr;
+          float v[E];
+          unpack<T>(xa[j * K + k], v);
+#pragma unroll
+          for (int e = 0; e < E; ++e) {
+            const float d = (c * E + e < n) ? v[e] - mean[j] : 0.0f;
+            q[j] = fmaf(d, d, q[j]);
+          }
         }
       }
     }
@@ -163,7 +182,7 @@ __device__ __forceinline__ void fwd_finish_rows(u32x4 (&xa)[J * K], u32x4 (&wa)[
       if constexpr (LN) unpack<T>(ba[k], bv);
 #pragma unroll
       for (int e = 0; e < E; ++e) {
-        const float ww = (w != nullptr) ? wv[e] + w_add : 1.0f;
+        const float ww = wv[e] + wadd;
         if constexpr (LN) {
           o[e] = fmaf((v[e] - mean[j]) * r[j], ww, bv[e]);
           if constexpr (EPI == kEpiGelu) o[e] = gelu_tanh(o[e]);
