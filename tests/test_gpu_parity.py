@@ -367,19 +367,29 @@ def test_empty_batch():
     assert torch.all(dw == 0) and torch.all(dg == 0) and torch.all(db == 0)
 
 
-@pytest.mark.parametrize("kind", ["rms", "ln"])
+@pytest.mark.parametrize("kind", ["rms", "ln", "ln_gelu", "rms_rope"])
 def test_backward_bitwise_deterministic(kind):
+    # every backward, the fused ones included (the GeLU one adds its wave
+    # sums in a DPP tree, the LayerNorm, GeLU and RoPE ones read their row
+    # statistics through scalar loads): bit-identical results on repeat
     inp = workloads.norm_inputs("rms_gemma_3840x5120")
     x, w, dy = g(inp["x"]), g(inp["w"]), g(inp["dy"])
     say(f"{kind} bwd determinism 3840x5120")
+    ct, st = nr.rope_table_1d(x.shape[0], 128, 0, 10000.0, device=DEV)
     outs = []
     for _ in range(2):
         if kind == "rms":
             _, r = nr.rmsnorm_fwd(x, w, gemma_offset=True)
             outs.append(nr.rmsnorm_bwd(dy, x, w, r, gemma_offset=True))
-        else:
+        elif kind == "ln":
             _, mu, rs = nr.layernorm_fwd(x, w, w)
             outs.append(nr.layernorm_bwd(dy, x, w, mu, rs))
+        elif kind == "ln_gelu":
+            _, mu, rs = nr.layernorm_gelu_fwd(x, w, w)
+            outs.append(nr.layernorm_gelu_bwd(dy, x, w, w, mu, rs))
+        else:
+            _, r = nr.rmsnorm_rope_fwd(x, w, ct, st, 128)
+            outs.append(nr.rmsnorm_rope_bwd(dy, x, w, r, ct, st, 128))
     torch.cuda.synchronize()
     for a, b in zip(outs[0], outs[1]):
         assert torch.equal(a, b)
