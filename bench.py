@@ -392,16 +392,16 @@ def stream_ceiling(dev, reps=10):
                 frac_of_peak=round(2 * nbytes / (ms * 1e-3) / 1e9 / PEAK_GBS, 4))
 
 
-def mix_ceilings(dev, reps=10):
+def mix_ceilings(dev, reps=10, nbytes=65536 * 5120 * 2):
     """Practical ceilings of the three read/write mixes of the path, over
-    operands of one long-sequence activation (65536 x 5120 bf16 each):
-    one stream read and one written (copy: the forwards and RoPE), two read
-    and one written (the backwards), two read and none written."""
+    operands of nbytes each (by default one long-sequence activation,
+    65536 x 5120 bf16): one stream read and one written (copy: the forwards
+    and RoPE), two read and one written (the backwards), two read and none
+    written."""
     import torch
 
     import rmsnorm_layernorm_fwd_amd as nr
 
-    nbytes = 65536 * 5120 * 2
     a = torch.full((nbytes // 4,), 0x01020304, dtype=torch.int32, device=dev)
     b = torch.full_like(a, 0x10203040)
     c = torch.empty_like(a)
@@ -551,11 +551,20 @@ def config_summary(name, steps, warmup, cold_rounds, dev):
     _, _, per_op = time_steps(ops, steps, warmup)  # per operation, an event pair around each
     _, ms, _ = time_steps(ops, steps, 0, only="")  # the step, operations back to back
     cold = cold_op_times(ops, cold_rounds, dev) if cold_rounds > 0 else None
+    # the mix probes over operands of this configuration's activation size
+    # (a forward or RoPE operation moves about two of them), warm like the
+    # operations they are set against
+    act = min(b for lab, _, _, b in ops if op_mix(lab) == "1R1W") // 2 // 4096 * 4096
+    mixes = mix_ceilings(dev, nbytes=act)
     out = dict(step_bytes=step_bytes, ms_per_step=round(ms, 5),
                gbs=round(step_bytes / (ms * 1e-3) / 1e9, 1),
                frac_of_peak=round(step_bytes / (ms * 1e-3) / 1e9 / PEAK_GBS, 4),
+               mix_ceilings={k: dict(gbs=v["gbs"], bytes_per_launch=v["bytes_per_launch"])
+                             for k, v in mixes.items()},
                ops={k: dict(gbs=v["gbs"], frac_of_peak=v["frac_of_peak"], ms_mean=v["ms_mean"],
-                            bytes=v["bytes"]) for k, v in per_op.items()},
+                            bytes=v["bytes"],
+                            frac_of_mix_ceiling=round(v["gbs"] / mixes[op_mix(k)]["gbs"], 4))
+                    for k, v in per_op.items()},
                ops_cold=None if cold is None else
                {k: dict(gbs=v["gbs"], frac_of_peak=v["frac_of_peak"], ms_mean=v["ms_mean"])
                 for k, v in cold.items()})
