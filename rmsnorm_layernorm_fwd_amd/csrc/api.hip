@@ -727,6 +727,8 @@ nr_status_t rope_table_1d(float* cos_tab, float* sin_tab, int64_t tokens, int64_
   if (tokens == 0) return NR_OK;
   if (tokens > INT64_MAX / head_dim) return NR_ERR_SHAPE;
   if (cos_tab == nullptr || sin_tab == nullptr) return NR_ERR_NULLPTR;
+  const size_t tb = static_cast<size_t>(tokens * (head_dim / 2)) * sizeof(float);
+  if (any_overlap(cos_tab, tb, sin_tab, tb)) return NR_ERR_ALIAS;
   return hip_status(nr::launch_rope_table_1d(cos_tab, sin_tab, tokens, static_cast<int>(head_dim),
                                              pos0, theta, static_cast<hipStream_t>(stream)));
 }
@@ -742,6 +744,9 @@ nr_status_t rope_table_3d(float* cos_tab, float* sin_tab, int64_t frames, int64_
   if (height > INT64_MAX / width || frames > INT64_MAX / (height * width) / (1 << 20))
     return NR_ERR_SHAPE;
   if (cos_tab == nullptr || sin_tab == nullptr) return NR_ERR_NULLPTR;
+  const size_t tb =
+      static_cast<size_t>(frames * height * width * (pairs_t + pairs_h + pairs_w)) * sizeof(float);
+  if (any_overlap(cos_tab, tb, sin_tab, tb)) return NR_ERR_ALIAS;
   return hip_status(nr::launch_rope_table_3d(
       cos_tab, sin_tab, frames, height, width, static_cast<int>(pairs_t),
       static_cast<int>(pairs_h), static_cast<int>(pairs_w), theta,
