@@ -699,6 +699,21 @@ nr_status_t rope_interleaved_apply(nr_dtype_t dt, void* x, const float* cos_tab,
                              stride_head))
     return NR_ERR_ALIAS;
   if (x == nullptr || cos_tab == nullptr || sin_tab == nullptr) return NR_ERR_NULLPTR;
+  // x is rewritten while the tables are read: its extent (saturating) may not
+  // share a byte with either table (head_dim / 2 fp32 angles per token)
+  {
+    int64_t ext = head_dim;  // elements from x to one past its last element
+    const int64_t cnt[3] = {batch - 1, tokens - 1, heads - 1};
+    const int64_t str[3] = {stride_batch, stride_token, stride_head};
+    for (int i = 0; i < 3; ++i) {
+      if (str[i] > 0 && cnt[i] > (INT64_MAX - ext) / str[i]) ext = INT64_MAX;
+      else if (ext != INT64_MAX) ext += cnt[i] * str[i];
+    }
+    const int64_t e = elem_bytes(dt);
+    const size_t xb = ext > INT64_MAX / e ? SIZE_MAX : static_cast<size_t>(ext * e);
+    const size_t tb = static_cast<size_t>(tokens) * static_cast<size_t>(head_dim / 2) * 4u;
+    if (any_overlap(x, xb, cos_tab, tb) || any_overlap(x, xb, sin_tab, tb)) return NR_ERR_ALIAS;
+  }
   // a token's heads are addressed with 32-bit byte offsets from the token start
   const int64_t span = ((heads - 1) * stride_head + head_dim) * elem_bytes(dt);
   if (stride_head > (int64_t{1} << 30) || span >= (int64_t{1} << 30)) return NR_ERR_UNSUPPORTED_N;

@@ -138,6 +138,9 @@ def test_rejected_calls_return_status(lib):
     assert L.rope_table_3d(FAKE, FAKE, 2, 3, 4, 0, 2, 2, 1e4, None) == NR_ERR_SHAPE
     # the two tables of a builder may not share bytes
     assert L.rope_table_1d(FAKE, FAKE + 32, 4, 8, 0, 1e4, None) == NR_ERR_ALIAS  # 64-byte tables
+    # RoPE: x (rewritten in place) may not overlap its tables
+    assert L.rope_interleaved_apply(F32, FAKE, FAKE + 64, 0x90000, 1, 4, 2, 8, 64, 16, 8, 0, None) == NR_ERR_ALIAS
+    assert L.rope_interleaved_apply(F32, FAKE, 0x90000, FAKE + 200, 1, 4, 2, 8, 64, 16, 8, 0, None) == NR_ERR_ALIAS
     assert L.rope_table_3d(FAKE, FAKE + 64, 2, 3, 4, 2, 2, 2, 1e4, None) == NR_ERR_ALIAS
     assert L.rmsnorm_fwd(F16, FAKE, None, None, None, 4, 8, 1e-6, 0, None) == NR_ERR_NULLPTR
     # row length beyond the on-chip limit
