@@ -77,3 +77,34 @@ def test_calls_run_on_the_tensors_device_with_its_stream():
     ry, rr = oracle.rmsnorm_fwd(x.cpu(), w.cpu(), 1e-6)
     check("side stream y", y.cpu(), ry, "bf16")
     check("side stream inv_rms", r.cpu(), rr, "stat", s=0.0)
+
+
+def test_overlapping_buffers_refused_by_the_library():
+    # buffers the binding accepts (right dtype, shape, device) but that share
+    # bytes with another operand: the library refuses them (NR_ERR_ALIAS)
+    # before queuing anything, and the outputs keep their contents
+    print("[case] binding: overlapping buffers", flush=True)
+    x, w = _inputs(rows=8, n=256, dtype=torch.float32)
+    dy = torch.randn_like(x)
+    y, r = nr.rmsnorm_fwd(x, w)
+    torch.cuda.synchronize()
+    # the column gradient inside dy's storage
+    dw_view = dy.view(-1)[:256]
+    before = dy.clone()
+    with pytest.raises(nr.NormRopeError):
+        nr.rmsnorm_bwd(dy, x, w, r, dw=dw_view)
+    torch.cuda.synchronize()
+    assert torch.equal(dy, before)
+    # the row statistics inside the output of the forward
+    y2 = torch.full_like(x, 7.0)
+    with pytest.raises(nr.NormRopeError):
+        nr.rmsnorm_fwd(x, w, y=y2, inv_rms=y2.view(-1)[:8])
+    torch.cuda.synchronize()
+    assert torch.all(y2 == 7.0)
+    # RoPE tables inside the tensor they rotate
+    q = torch.randn(1, 4, 2, 8, device=DEV)
+    qc = q.clone()
+    with pytest.raises(nr.NormRopeError):
+        nr.rope_interleaved_apply(q, q.view(-1)[:16].view(4, 4), q.view(-1)[16:32].view(4, 4))
+    torch.cuda.synchronize()
+    assert torch.equal(q, qc)
