@@ -28,6 +28,7 @@ namespace nr {
 
 constexpr int kSplitLanes = 256;  // pass B: 4 waves per workgroup
 constexpr int kSplitK = 2;        // pass B: chunks per lane (slice = 512 chunks)
+static_assert(kSplitLanes * kSplitK == kLongSliceChunks, "the host sizes P by this slice width");
 
 // cos / sin of the pairs in chunk c of a row whose table row is at cr / sr
 template <typename T, bool VEC>

@@ -47,13 +47,22 @@ struct RopeArgs {
 };
 
 // Rows of at least kLongRowMin elements take the two-pass backward
-// (norm_bwd_long.hpp).  Its pass B uses long_bwd_groups(rows) row groups:
-// a function of the row count only, so the summation order and the
-// workspace size do not depend on the device.
+// (norm_bwd_long.hpp).  Its pass B runs P row groups times S column slices
+// of kLongSliceChunks 16-byte chunks, with P = min(ceil(rows / 16),
+// max(1, 256 / S)): about one workgroup per CU.  Fewer, longer row streams
+// measured fastest (bf16 LayerNorm backward of 4096 rows of 65536: 447 us
+// at 256 workgroups, 460 at 512, 499 at 2048); past one per CU the extra
+// streams only add open DRAM pages.  P is a function of the shape and the
+// element size alone, so the summation order does not depend on the device.
 constexpr int64_t kLongRowMin = 16385;
-inline int64_t long_bwd_groups(int64_t rows) {
+constexpr int kLongSliceChunks = 512;
+inline int64_t long_bwd_groups(int64_t rows, int64_t n, int elem_bytes) {
+  const int64_t chunks = (n * elem_bytes + 15) / 16;
+  const int64_t slices = (chunks + kLongSliceChunks - 1) / kLongSliceChunks;
+  int64_t cap = 256 / slices;
+  if (cap < 1) cap = 1;
   int64_t p = (rows + 15) / 16;
-  if (p > 128) p = 128;
+  if (p > cap) p = cap;
   return p < 1 ? 1 : p;
 }
 
@@ -83,8 +92,11 @@ hipError_t launch_norm_fwd(bool ln, int dt, const FwdPlan& pl, const void* x, co
 hipError_t launch_norm_bwd(bool ln, int dt, const BwdPlan& pl, const void* dy, const void* x,
                            const void* w, const float* mean, const float* rstat, void* dx,
                            float* part, int64_t rows, int n, float w_add, hipStream_t st);
+// slices: 1..16 row slices of the P partial rows, summed in order (16 for
+// the short-row backward; the long-row one, with few partial rows and
+// n/64 >= 256 column workgroups, takes about P/4)
 hipError_t launch_colreduce(const float* part, int64_t part_stride, int P, int n, float* out0,
-                            float* out1, hipStream_t st);
+                            float* out1, hipStream_t st, int slices = 16);
 hipError_t launch_rope(int dt, const RopePlan& pl, void* x, const float* cos_tab,
                        const float* sin_tab, int64_t batch, int64_t tokens, int heads,
                        int head_dim, int64_t sb, int64_t st_, int64_t sh, float sign,

@@ -79,11 +79,15 @@ def test_workspace_bytes():
     assert nr.nr_bwd_workspace_bytes(17, 8, 0) == 3 * 8 * 4
     assert nr.nr_bwd_workspace_bytes(65536, 5120, 2) == 512 * 5120 * 4  # fused RMSNorm + RoPE
     assert nr.nr_bwd_workspace_bytes(64, 8, 3) == 0
-    # rows of more than 16384 elements: ceil(rows / 16) (at most 128) partial
-    # rows, then two fp32 terms per row
+    # rows of more than 16384 elements: ceil(rows / 16) partial rows, at most
+    # 256 / S where S = ceil(n / 4096) column slices of a 2-byte row (the
+    # largest count of the storage types), then two fp32 terms per row
     assert nr.nr_bwd_workspace_bytes(100, 20000, 1) == 7 * 20000 * 4 * 2 + 100 * 8
     assert nr.nr_bwd_workspace_bytes(100, 20000, 0) == 7 * 20000 * 4 + 100 * 8
-    assert nr.nr_bwd_workspace_bytes(4096, 32768, 2) == 128 * 32768 * 4 + 4096 * 8
+    assert nr.nr_bwd_workspace_bytes(8192, 20480, 0) == 51 * 20480 * 4 + 8192 * 8
+    assert nr.nr_bwd_workspace_bytes(4096, 32768, 2) == 32 * 32768 * 4 + 4096 * 8
+    assert nr.nr_bwd_workspace_bytes(4096, 65536, 1) == 2 * 16 * 65536 * 4 + 4096 * 8
+    assert nr.nr_bwd_workspace_bytes(160, 65536, 1) == 2 * 10 * 65536 * 4 + 160 * 8
 
 
 def test_linear_workspace_bytes():
@@ -251,13 +255,13 @@ def test_rejected_calls_return_status(lib):
     assert L.nr_stream_mix(FAKE, 0x80000, FAKE + 32, 64, 0, None) == NR_ERR_ALIAS
     assert L.nr_stream_mix(FAKE, 0x80000, 0x80000, 64, 1, None) == NR_ERR_ALIAS
     assert L.nr_stream_mix(None, None, None, 0, 1, None) == NR_OK
-    # the no-allocation backward: a shape whose partial rows exceed its
-    # 16 MiB scratch array (2048 rows of 65536: 33.5 MB) is refused before
-    # anything else; a shape needing no scratch (no dw, short rows) goes
-    # straight to rmsnorm_bwd's checks
+    # the no-allocation backward: a shape whose workspace exceeds its 16 MiB
+    # scratch array (2^21 rows of 65536: 4 MiB of partial rows and 16 MiB of
+    # row terms) is refused before anything else; a shape needing no scratch
+    # (no dw, short rows) goes straight to rmsnorm_bwd's checks
     X = 1 << 24
-    assert nr.nr_bwd_workspace_bytes(2048, 65536, 0) > 16 << 20
-    assert L.rmsnorm_bwd_noalloc(BF16, FAKE, X, None, FAKE, 1 << 30, FAKE, 2048, 65536, 0,
+    assert nr.nr_bwd_workspace_bytes(1 << 21, 65536, 0) > 16 << 20
+    assert L.rmsnorm_bwd_noalloc(BF16, FAKE, X, None, FAKE, 1 << 30, FAKE, 1 << 21, 65536, 0,
                                  None) == NR_ERR_WORKSPACE
     assert L.rmsnorm_bwd_noalloc(7, FAKE, X, None, FAKE, 1 << 25, None, 4, 8, 0, None) == NR_ERR_DTYPE
     # long rows need the workspace even without a column gradient
