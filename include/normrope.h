@@ -108,6 +108,9 @@ nr_status_t rmsnorm_fwd(nr_dtype_t dt, const void* x, const void* w, void* y,
  *   reduction first, then dx and the column partials by column slices) and
  *   keep two fp32 terms per row in the workspace, so for them it is
  *   required even when dw is NULL; otherwise it may be NULL when dw is.
+ *   Exception: bf16 / fp16 rows of up to 32768 elements with dy, x, dx and
+ *   w 16-byte aligned and n a multiple of 8 take one pass here (not in
+ *   rmsnorm_rope_bwd or the LayerNorm backwards).
  *   The workspace is scratch: its content on entry does not matter and is
  *   overwritten.
  */
@@ -123,8 +126,9 @@ nr_status_t rmsnorm_bwd(nr_dtype_t dt, const void* dy, const void* x,
  * workspace arguments.  The partial rows go to a scratch array the library
  * holds in device memory, one copy per GPU, for as long as it is loaded.
  * Its limit is NR_NOALLOC_SCRATCH_BYTES: a call whose
- * nr_bwd_workspace_bytes(rows, n, 0) exceeds it (only rows longer than
- * 16384 elements can) returns NR_ERR_WORKSPACE and queues nothing.
+ * nr_bwd_workspace_bytes(rows, n, 0) exceeds it (only batches of millions
+ * of rows longer than 16384 elements can) returns NR_ERR_WORKSPACE and
+ * queues nothing.
  * The call allocates nothing.  Its first call on a device looks the array's
  * address up on that device (outside any graph capture, so make one call
  * before capturing); a failed lookup returns NR_ERR_HIP.
@@ -133,7 +137,7 @@ nr_status_t rmsnorm_bwd(nr_dtype_t dt, const void* dy, const void* x,
  * race on it and must not be made.  Nothing in the array needs to start at
  * zero; it keeps the last call's contents.
  */
-#define NR_NOALLOC_SCRATCH_BYTES (16u << 20)
+#define NR_NOALLOC_SCRATCH_BYTES (32u << 20)
 nr_status_t rmsnorm_bwd_noalloc(nr_dtype_t dt, const void* dy, const void* x,
                                 const void* w, const float* inv_rms, void* dx,
                                 float* dw, int64_t rows, int64_t n,

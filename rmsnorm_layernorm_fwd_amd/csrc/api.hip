@@ -233,8 +233,9 @@ bool fwd_grid_ok(int64_t rows, const FwdPlan& pl) {
 //     round of workgroups and measured slower.
 //   P depends on the row count and the operator only, so the summation order
 //   and the workspace size are the same on every device.
-void bwd_grid(int64_t rows, bool two_per_cu, int64_t* P_out, int64_t* rpb_out) {
-  const int64_t rows_min = tune(BWD_ROWS_MIN) > 0 ? tune(BWD_ROWS_MIN) : 8;
+void bwd_grid(int64_t rows, bool two_per_cu, int64_t* P_out, int64_t* rpb_out,
+              int64_t rows_min_default = 8) {
+  const int64_t rows_min = tune(BWD_ROWS_MIN) > 0 ? tune(BWD_ROWS_MIN) : rows_min_default;
   const int64_t pcap = tune(BWD_P) > 0 ? tune(BWD_P) : (two_per_cu ? 512 : 256);
   int64_t P = tune(BWD_P) > 0 ? pcap : (rows + rows_min - 1) / rows_min;
   if (P > pcap) P = pcap;
@@ -303,9 +304,23 @@ nr_status_t plan_bwd(nr_dtype_t dt, bool ln, int64_t rows, int64_t n, bool align
   if (static_cast<int64_t>(64) * W * K < nchunk) return NR_ERR_SHAPE;
   // two resident workgroups per CU only when two of them fit: 2 W waves
   // over the CU's 4 SIMDs at the kernels' ~76-100 VGPRs allow W <= 10
+  // Plain RMSNorm on aligned 16-bit rows of 16385..32768 elements (32
+  // elements a lane, up to 16 waves): one pass, dW accumulated in LDS, one
+  // batch ahead.  Against the two passes (bf16): 4096 x 32768 222 -> 149 us
+  // (5.4 TB/s), 16384 x 32768 852 -> 584 us, 4096 x 20480 148 -> 96 us,
+  // 8192 x 16392 267 -> 154 us; 256 x 32768 level.
+  const bool lacc = !ln && !rope && !gelu && aligned && E == 8 && n >= nr::kLongRowMin &&
+                    n <= nr::kRmsOnePassMax;
+  if (lacc) {
+    if (K * E != 32 || W > 16) return NR_ERR_SHAPE;
+    D = 1;
+    PF = 1;
+  }
+  // (its rows are 32-64 KiB: one row per workgroup at least, where short
+  // rows take eight; 256 x 32768 bf16: 40.9 us on 32 workgroups of 8 rows)
   int64_t P, rpb;
-  bwd_grid(rows, ((ln && !gelu) || rope) && W <= 10 && PF <= 2, &P, &rpb);
-  *pl = BwdPlan{W, K, D, static_cast<int>(P), PF, rpb, aligned};
+  bwd_grid(rows, ((ln && !gelu) || rope) && W <= 10 && PF <= 2, &P, &rpb, lacc ? 1 : 8);
+  *pl = BwdPlan{W, K, D, static_cast<int>(P), PF, rpb, aligned, lacc};
   return NR_OK;
 }
 
@@ -399,15 +414,23 @@ nr_status_t nr_tune(const char* key, int value) {
 
 size_t nr_bwd_workspace_bytes(int64_t rows, int64_t n, int op) {
   if (rows <= 0 || n < 1 || op < 0 || op > 2) return 0;
-  if (n >= nr::kLongRowMin) {  // two passes: partial rows, then two fp32 terms per row
+  int64_t P, rpb;
+  bwd_grid(rows, op != 0, &P, &rpb, op == 0 && n >= nr::kLongRowMin ? 1 : 8);
+  const size_t one_pass =
+      static_cast<size_t>(P) * static_cast<size_t>(n) * sizeof(float) * (op == 1 ? 2u : 1u);
+  if (nr::bwd_two_pass(op == 0, n)) {  // partial rows, then two fp32 terms per row
     // sized for 2-byte elements, whose shorter rows give the largest P
-    const int64_t P = nr::long_bwd_groups(rows, n, 2);
-    return static_cast<size_t>(P) * static_cast<size_t>(n) * sizeof(float) * (op == 1 ? 2u : 1u) +
+    const int64_t PL = nr::long_bwd_groups(rows, n, 2);
+    return static_cast<size_t>(PL) * static_cast<size_t>(n) * sizeof(float) * (op == 1 ? 2u : 1u) +
            static_cast<size_t>(rows) * 2u * sizeof(float);
   }
-  int64_t P, rpb;
-  bwd_grid(rows, op != 0, &P, &rpb);
-  return static_cast<size_t>(P) * static_cast<size_t>(n) * sizeof(float) * (op == 1 ? 2u : 1u);
+  if (n < nr::kLongRowMin) return one_pass;
+  // plain RMSNorm of 16385..32768 elements: one pass for aligned 16-bit
+  // rows, two for the others; the larger of the two sizes
+  const int64_t PL = nr::long_bwd_groups(rows, n, 2);
+  const size_t two_pass = static_cast<size_t>(PL) * static_cast<size_t>(n) * sizeof(float) +
+                          static_cast<size_t>(rows) * 2u * sizeof(float);
+  return one_pass > two_pass ? one_pass : two_pass;
 }
 
 nr_status_t rmsnorm_fwd(nr_dtype_t dt, const void* x, const void* w, void* y, float* inv_rms,
@@ -513,7 +536,7 @@ nr_status_t norm_bwd_common(bool ln, nr_dtype_t dt, const void* dy, const void* 
   const bool aligned = (n % vec_elems(dt)) == 0 && aligned16(dy) && aligned16(x) &&
                        aligned16(dx) && (w == nullptr || aligned16(w)) &&
                        (beta == nullptr || aligned16(beta));
-  if (n >= nr::kLongRowMin) {
+  if (nr::bwd_two_pass(!ln && !gelu && aligned && vec_elems(dt) == 8, n)) {
     const nr::RopeArgs none{nullptr, nullptr, 2, 1};
     return bwd_long(dt, ln, gelu ? 2 : 0, aligned, dy, x, w, beta, mean, rstat, dx, o0, o1, rows,
                     n, w_add, none, workspace, workspace_bytes, st);
@@ -664,7 +687,7 @@ nr_status_t rmsnorm_rope_bwd(nr_dtype_t dt, const void* dout, const void* x, con
   const bool aligned = vec_tab && (n % vec_elems(dt)) == 0 && aligned16(dout) && aligned16(x) &&
                        aligned16(dx) && (w == nullptr || aligned16(w));
   const nr::RopeArgs ra{cos_tab, sin_tab, static_cast<int>(head_dim), rows_per_token};
-  if (n >= nr::kLongRowMin)
+  if (nr::bwd_two_pass(false, n))
     return bwd_long(dt, false, 1, aligned, dout, x, w, nullptr, nullptr, inv_rms, dx, dw, nullptr,
                     rows, n, gemma_offset ? 1.0f : 0.0f, ra, workspace, workspace_bytes, st);
   BwdPlan pl;

@@ -48,7 +48,7 @@ nr_status_t rmsnorm_bwd_noalloc(nr_dtype_t dt, const void* dy, const void* x, co
                                 int64_t n, int gemma_offset, void* stream) {
   // the same checks as rmsnorm_bwd run there; only the scratch size is
   // checked here, before the (one-time) symbol lookup
-  const bool long_rows = n > 16384;
+  const bool long_rows = n >= nr::kLongRowMin;  // may take two passes, which need it without dw
   const bool needs = dw != nullptr || long_rows;
   const size_t need = needs ? nr_bwd_workspace_bytes(rows, n, 0) : 0;
   if (need > NR_NOALLOC_SCRATCH_BYTES) return NR_ERR_WORKSPACE;

@@ -142,7 +142,7 @@ __device__ __forceinline__ void dy_chunk(const RowBatch<T, K, D, TS>& b, int i,
 // they have the rest of this batch and the next batch's first pass before
 // the next such wait.
 template <typename T, int K, int D, bool VEC, bool LN, bool ROPE, int EPI, int TS, bool SSTAT,
-          typename F>
+          bool LACC, typename F>
 __device__ __forceinline__ void process_batch(RowBatch<T, K, D, TS>& b, int64_t base,
                                               int64_t rows, T* dx, int n, int t, int nthr, int W,
                                               int wave, int lane, float inv_n,
@@ -151,7 +151,8 @@ __device__ __forceinline__ void process_batch(RowBatch<T, K, D, TS>& b, int64_t 
                                               const u32x4 (&wpk)[K], const u32x4 (&bpk)[K],
                                               float w_add, float (&acc1)[K][Vec<T>::N],
                                               float (&acc2)[K][Vec<T>::N],
-                                              float (*red)[16], int& parity, F&& late) {
+                                              float4* lacc, float (*red)[16], int& parity,
+                                              F&& late) {
   constexpr int E = Vec<T>::N;
   constexpr int NS = LN ? 2 : 1;  // row sums per row
   // per-lane partial row sums, and the column partials.  Elements past n
@@ -168,6 +169,9 @@ __device__ __forceinline__ void process_batch(RowBatch<T, K, D, TS>& b, int64_t 
   // 1024-thread kernel within its 128 VGPRs, where it spilled before.
   constexpr int GD = EPI == kEpiGelu ? D * K : 0;
   constexpr bool LEAN = EPI == kEpiGelu && K > 1;
+  // LACC (RMSNorm rows of 16385..32768 elements): the weight stays packed as
+  // for LEAN, and dW is accumulated in LDS, in the second pass
+  constexpr bool PACKW = LEAN || LACC;
   float gdd[GD > 0 ? GD : 1][E], gxh[(GD > 0 && !LEAN) ? GD : 1][E];
 #pragma unroll
   for (int d = 0; d < D; ++d) {
@@ -177,17 +181,20 @@ __device__ __forceinline__ void process_batch(RowBatch<T, K, D, TS>& b, int64_t 
       float xv[E], dv[E], wl[E], bl[E];
       unpack<T>(b.x[d * K + k], xv);
       dy_chunk<T, K, D, ROPE, TS>(b, d * K + k, dv);
-      if constexpr (LEAN) {
-        u32x4 wq[1] = {wpk[k]}, bq[1] = {bpk[k]};
+      if constexpr (PACKW) {
+        u32x4 wq[1] = {wpk[k]};
         reload_barrier<1>(wq);
-        reload_barrier<1>(bq);
         unpack<T>(wq[0], wl);
+      }
+      if constexpr (LEAN) {
+        u32x4 bq[1] = {bpk[k]};
+        reload_barrier<1>(bq);
         unpack<T>(bq[0], bl);
       }
 #pragma unroll
       for (int e = 0; e < E; ++e) {
         const float xh = (xv[e] - b.mu[d]) * b.rs[d];
-        const float wk = LEAN ? wl[e] + w_add : wv[k][e];
+        const float wk = PACKW ? wl[e] + w_add : wv[k][e];
         float dd = dv[e];
         if constexpr (EPI == kEpiGelu)
           dd *= gelu_tanh_grad(fmaf(xh, wk, LEAN ? bl[e] : bv[k][e]));
@@ -203,7 +210,7 @@ __device__ __forceinline__ void process_batch(RowBatch<T, K, D, TS>& b, int64_t 
         } else {
           s1 = fmaf(gg, xh, s1);
         }
-        acc1[k][e] = fmaf(dd, xh, acc1[k][e]);
+        if constexpr (!LACC) acc1[k][e] = fmaf(dd, xh, acc1[k][e]);
       }
     }
     s[NS * d] = s1;
@@ -262,9 +269,14 @@ __device__ __forceinline__ void process_batch(RowBatch<T, K, D, TS>& b, int64_t 
     const float k1 = -b.rs[d] * c1, k2 = -b.rs[d] * c2;
 #pragma unroll
     for (int k = 0; k < K; ++k) {
-      float xv[E], dv[E], o[E];
+      float xv[E], dv[E], o[E], wl[E], xhv[E];
       if constexpr (EPI != kEpiGelu || LEAN) unpack<T>(b.x[d * K + k], xv);
       if constexpr (EPI != kEpiGelu) dy_chunk<T, K, D, ROPE, TS>(b, d * K + k, dv);
+      if constexpr (LACC) {
+        u32x4 wq[1] = {wpk[k]};
+        reload_barrier<1>(wq);
+        unpack<T>(wq[0], wl);
+      }
 #pragma unroll
       for (int e = 0; e < E; ++e) {
         float xh, gg;
@@ -272,9 +284,10 @@ __device__ __forceinline__ void process_batch(RowBatch<T, K, D, TS>& b, int64_t 
           gg = gdd[d * K + k][e];
           xh = LEAN ? (xv[e] - b.mu[d]) * b.rs[d] : gxh[d * K + k][e];
         } else {
-          gg = dv[e] * wv[k][e];
+          gg = dv[e] * (LACC ? wl[e] + w_add : wv[k][e]);
           xh = (xv[e] - b.mu[d]) * b.rs[d];
         }
+        xhv[e] = xh;
         if constexpr (LN) {
           o[e] = fmaf(b.rs[d], gg, fmaf(xh, k2, k1));
         } else {
@@ -282,6 +295,20 @@ __device__ __forceinline__ void process_batch(RowBatch<T, K, D, TS>& b, int64_t 
         }
       }
       st_chunk<T, VEC, kNormStore>(dr, t + k * nthr, pack<T>(o));
+      if constexpr (LACC) {
+        // this lane's own slots (no other lane touches them): the same fma,
+        // in the same row order, as the register accumulators would take
+        float4* slot = lacc + (k * (E / 4)) * 1024 + t;
+#pragma unroll
+        for (int q = 0; q < E / 4; ++q) {
+          float4 a = slot[q * 1024];
+          a.x = fmaf(dv[4 * q + 0], xhv[4 * q + 0], a.x);
+          a.y = fmaf(dv[4 * q + 1], xhv[4 * q + 1], a.y);
+          a.z = fmaf(dv[4 * q + 2], xhv[4 * q + 2], a.z);
+          a.w = fmaf(dv[4 * q + 3], xhv[4 * q + 3], a.w);
+          slot[q * 1024] = a;
+        }
+      }
     }
   }
 }
@@ -291,8 +318,12 @@ __device__ __forceinline__ void process_batch(RowBatch<T, K, D, TS>& b, int64_t 
 // most 10 waves, i.e. one workgroup per CU, which leaves up to 168.
 // SHARED (RoPE, more than one chunk per lane): one set of table angles per
 // row, valid when the lane stride of the row is a multiple of the head size.
+// LACC (plain RMSNorm, aligned 16-bit rows, 4 chunks = 32 elements per lane,
+// one row per batch, one batch ahead): the 32 fp32 dW accumulators of each
+// lane live in 128 KiB of LDS, one workgroup per CU, where in registers they
+// spilled; rows of 16385..32768 elements then take one pass instead of two.
 template <typename T, int K, int D, int PF, bool VEC, bool LN, int EPI, int LB = 1024,
-          bool SHARED = false>
+          bool SHARED = false, bool LACC = false>
 __global__ void __launch_bounds__(LB)
 norm_bwd_rows(const T* dy, const T* x, const T* w, const T* beta, const float* mean,
               const float* rstat, T* dx, float* part, int64_t part_stride, int64_t rows, int n,
@@ -314,6 +345,11 @@ norm_bwd_rows(const T* dy, const T* x, const T* w, const T* beta, const float* m
   // backward with more than one chunk per lane, kept packed (ones packed
   // where there is no weight, the offset applied where it is widened)
   constexpr bool LEAN = EPI == kEpiGelu && K > 1;
+  static_assert(!LACC || (!LN && EPI == kEpiNone && D == 1 && PF == 1 && K * E == 32 &&
+                          LB == 1024 && VEC),
+                "LDS accumulators: plain aligned RMSNorm, 32 elements a lane, one batch ahead");
+  constexpr int LQ = K * E / 4;  // float4 accumulator slots per lane
+  __shared__ float4 lacc[LACC ? LQ * 1024 : 1];
   float wv[K][E];
   u32x4 wpk[K];
   const float w_add_packed = (w != nullptr) ? w_add : 0.0f;
@@ -322,7 +358,7 @@ norm_bwd_rows(const T* dy, const T* x, const T* w, const T* beta, const float* m
 #pragma unroll
     for (int k = 0; k < K; ++k) {
       wpk[k] = ld_chunk<T, VEC>(wr, t + k * nthr);
-      if constexpr (LEAN) {
+      if constexpr (LEAN || LACC) {
         if (w == nullptr) {
           float one[E];
 #pragma unroll
@@ -358,6 +394,10 @@ norm_bwd_rows(const T* dy, const T* x, const T* w, const T* beta, const float* m
       acc1[k][e] = 0.0f;
       acc2[k][e] = 0.0f;
     }
+  if constexpr (LACC) {
+#pragma unroll
+    for (int q = 0; q < LQ; ++q) lacc[q * 1024 + t] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+  }
 
   int parity = 0;
   const int64_t step = static_cast<int64_t>(gridDim.x) * D;
@@ -388,9 +428,9 @@ norm_bwd_rows(const T* dy, const T* x, const T* w, const T* beta, const float* m
       const int64_t abase = base + PF * step;
       load_batch<T, K, D, VEC, LN, ROPE, TS, SSTAT>(ahead, abase, rows, x, dy, mean, rstat, n, t,
                                                     nthr, ra);
-      process_batch<T, K, D, VEC, LN, ROPE, EPI, TS, SSTAT>(
+      process_batch<T, K, D, VEC, LN, ROPE, EPI, TS, SSTAT, LACC>(
           buf[i], base, rows, dx, n, t, nthr, W, wave, lane, inv_n, wv, bv, wpk, bpk, w_add_packed,
-          acc1, acc2, red, parity, [&] {
+          acc1, acc2, lacc, red, parity, [&] {
             if constexpr (SSTAT) load_stats<T, K, D, LN, TS>(ahead, abase, rows, mean, rstat);
           });
       base += step;
@@ -409,6 +449,13 @@ done:
       const int c = t + k * nthr;
 #pragma unroll
       for (int q = 0; q < E / 4; ++q) {
+        if constexpr (LACC) {
+          const float4 a = lacc[(k * (E / 4) + q) * 1024 + t];
+          acc1[k][4 * q + 0] = a.x;
+          acc1[k][4 * q + 1] = a.y;
+          acc1[k][4 * q + 2] = a.z;
+          acc1[k][4 * q + 3] = a.w;
+        }
         if constexpr (VEC) {
           // whole 16-byte groups of 4 columns (n is a multiple of 4 here)
           u32x4 v1, v2;
@@ -445,6 +492,14 @@ hipError_t launch_bwd_kd(const BwdPlan& pl, const void* dy, const void* x, const
       kern = pl.PF == 3 ? norm_bwd_rows<T, K, D, 3, A, LN, EP, 640>
                         : norm_bwd_rows<T, K, D, 4, A, LN, EP, 640>;
     }
+  }
+  if constexpr (!LN && EP == kEpiNone && D == 1 && K == 4 && Vec<T>::N == 8 && A) {
+    if (pl.lacc) {
+      if (pl.PF != 1 || pl.W > 16) return hipErrorInvalidValue;
+      kern = norm_bwd_rows<T, K, D, 1, A, LN, EP, 1024, false, true>;
+    }
+  } else {
+    if (pl.lacc) return hipErrorInvalidValue;
   }
   // RoPE with several chunks per lane: when a lane's chunks sit at the same
   // offset in their heads, one set of angles per row (the two-chunk kernel

@@ -25,6 +25,7 @@ struct BwdPlan {
   int W, K, D, P, PF;
   int64_t rows_per_block;
   bool aligned;
+  bool lacc;  // dW accumulators in LDS (plain RMSNorm, 32 elements a lane)
 };
 
 // RoPE: `groups` waves per token, each taking K chunks per lane per pass
@@ -56,6 +57,14 @@ struct RopeArgs {
 // element size alone, so the summation order does not depend on the device.
 constexpr int64_t kLongRowMin = 16385;
 constexpr int kLongSliceChunks = 512;
+// The plain RMSNorm backward of 16-byte-aligned 16-bit rows keeps one pass
+// up to 32768 elements, its dW accumulators in LDS (norm_bwd.hpp; for fp32
+// or element-wise rows the same kernel spilled).  Every other backward takes
+// two passes from kLongRowMin on.
+constexpr int64_t kRmsOnePassMax = 32768;
+inline bool bwd_two_pass(bool rms_one_pass_ok, int64_t n) {
+  return n >= kLongRowMin && (!rms_one_pass_ok || n > kRmsOnePassMax);
+}
 inline int64_t long_bwd_groups(int64_t rows, int64_t n, int elem_bytes) {
   const int64_t chunks = (n * elem_bytes + 15) / 16;
   const int64_t slices = (chunks + kLongSliceChunks - 1) / kLongSliceChunks;

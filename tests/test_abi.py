@@ -79,13 +79,19 @@ def test_workspace_bytes():
     assert nr.nr_bwd_workspace_bytes(17, 8, 0) == 3 * 8 * 4
     assert nr.nr_bwd_workspace_bytes(65536, 5120, 2) == 512 * 5120 * 4  # fused RMSNorm + RoPE
     assert nr.nr_bwd_workspace_bytes(64, 8, 3) == 0
-    # rows of more than 16384 elements: ceil(rows / 16) partial rows, at most
-    # 256 / S where S = ceil(n / 4096) column slices of a 2-byte row (the
-    # largest count of the storage types), then two fp32 terms per row
+    # rows of more than 16384 elements (two passes): ceil(rows / 16) partial
+    # rows, at most 256 / S where S = ceil(n / 4096) column slices of a 2-byte
+    # row (the largest count of the storage types), then two fp32 terms per row
     assert nr.nr_bwd_workspace_bytes(100, 20000, 1) == 7 * 20000 * 4 * 2 + 100 * 8
-    assert nr.nr_bwd_workspace_bytes(100, 20000, 0) == 7 * 20000 * 4 + 100 * 8
-    assert nr.nr_bwd_workspace_bytes(8192, 20480, 0) == 51 * 20480 * 4 + 8192 * 8
     assert nr.nr_bwd_workspace_bytes(4096, 32768, 2) == 32 * 32768 * 4 + 4096 * 8
+    assert nr.nr_bwd_workspace_bytes(100, 40000, 0) == 7 * 40000 * 4 + 100 * 8
+    # plain RMSNorm of 16385..32768 elements: one pass for aligned 16-bit rows
+    # (the short-row partial rows), two for the others; the larger size
+    assert nr.nr_bwd_workspace_bytes(100, 20000, 0) == 100 * 20000 * 4  # a row a workgroup
+    assert nr.nr_bwd_workspace_bytes(8192, 20480, 0) == 256 * 20480 * 4
+    assert nr.nr_bwd_workspace_bytes(512, 32768, 0) == 256 * 32768 * 4
+    assert nr.nr_bwd_workspace_bytes(300, 32768, 0) == 150 * 32768 * 4  # 2 rows each
+    assert nr.nr_bwd_workspace_bytes(1, 32768, 0) == 32768 * 4 + 8  # the two-pass size
     assert nr.nr_bwd_workspace_bytes(4096, 65536, 1) == 2 * 16 * 65536 * 4 + 4096 * 8
     assert nr.nr_bwd_workspace_bytes(160, 65536, 1) == 2 * 10 * 65536 * 4 + 160 * 8
 
@@ -255,18 +261,23 @@ def test_rejected_calls_return_status(lib):
     assert L.nr_stream_mix(FAKE, 0x80000, FAKE + 32, 64, 0, None) == NR_ERR_ALIAS
     assert L.nr_stream_mix(FAKE, 0x80000, 0x80000, 64, 1, None) == NR_ERR_ALIAS
     assert L.nr_stream_mix(None, None, None, 0, 1, None) == NR_OK
-    # the no-allocation backward: a shape whose workspace exceeds its 16 MiB
-    # scratch array (2^21 rows of 65536: 4 MiB of partial rows and 16 MiB of
+    # the no-allocation backward: a shape whose workspace exceeds its 32 MiB
+    # scratch array (2^22 rows of 65536: 4 MiB of partial rows and 32 MiB of
     # row terms) is refused before anything else; a shape needing no scratch
     # (no dw, short rows) goes straight to rmsnorm_bwd's checks
     X = 1 << 24
-    assert nr.nr_bwd_workspace_bytes(1 << 21, 65536, 0) > 16 << 20
-    assert L.rmsnorm_bwd_noalloc(BF16, FAKE, X, None, FAKE, 1 << 30, FAKE, 1 << 21, 65536, 0,
+    assert nr.nr_bwd_workspace_bytes(1 << 22, 65536, 0) > 32 << 20
+    assert nr.nr_bwd_workspace_bytes(1 << 20, 32768, 0) <= 32 << 20  # the one pass fits
+    assert L.rmsnorm_bwd_noalloc(BF16, FAKE, X, None, FAKE, 1 << 30, FAKE, 1 << 22, 65536, 0,
                                  None) == NR_ERR_WORKSPACE
     assert L.rmsnorm_bwd_noalloc(7, FAKE, X, None, FAKE, 1 << 25, None, 4, 8, 0, None) == NR_ERR_DTYPE
-    # long rows need the workspace even without a column gradient
+    # rows that take two passes need the workspace even without a column
+    # gradient: bf16 past 32768 elements, or past 16384 when not a multiple
+    # of 8 (element-wise), fp32 past 16384
     X2, DX2, WS2, R2 = 1 << 24, 1 << 25, 1 << 26, 1 << 27
-    assert L.rmsnorm_bwd(BF16, FAKE, X2, None, R2, DX2, None, 4, 20000, 0, None, 0, None) == NR_ERR_WORKSPACE
+    assert L.rmsnorm_bwd(BF16, FAKE, X2, None, R2, DX2, None, 4, 40000, 0, None, 0, None) == NR_ERR_WORKSPACE
+    assert L.rmsnorm_bwd(BF16, FAKE, X2, None, R2, DX2, None, 4, 20001, 0, None, 0, None) == NR_ERR_WORKSPACE
+    assert L.rmsnorm_bwd(F32, FAKE, X2, None, R2, DX2, None, 4, 20000, 0, None, 0, None) == NR_ERR_WORKSPACE
     assert L.layernorm_bwd(F32, FAKE, X2, None, R2 + 4096, R2, DX2, None, None, 4, 20000, WS2, 31, None) == NR_ERR_WORKSPACE
     # a forced launch shape that cannot cover the row
     assert L.nr_tune(b"fwd_k", 1) == NR_OK

@@ -280,8 +280,12 @@ NORM_EDGES = [
     # IEEE fp16 storage
     (7, 40, torch.float16), (33, 1000, torch.float16), (65, 5120, torch.float16),
     (5, 4097, torch.float16), (2, 65536, torch.float16),
-    # rows past 16384 elements: the two-pass backward (aligned and element-wise)
+    # rows past 16384 elements: RMSNorm's one-pass backward with its dW
+    # accumulators in LDS (aligned 16-bit rows up to 32768: 20480, 16392 and
+    # 32768, the last two with many rows per workgroup), and the two-pass
+    # backward (element-wise 17001, fp32 24576, LayerNorm throughout)
     (37, 20480, torch.bfloat16), (5, 17001, torch.float16), (9, 24576, torch.float32),
+    (300, 16392, torch.float16), (600, 32768, torch.bfloat16),
 ]
 
 
@@ -395,9 +399,11 @@ def test_backward_bitwise_deterministic(kind):
         assert torch.equal(a, b)
 
 
-@pytest.mark.parametrize("kind", ["rms", "ln"])
-def test_long_row_backward_deterministic_and_without_column_gradients(kind):
-    rows, n = 300, 20480  # two-pass backward; 19 row groups
+@pytest.mark.parametrize("kind,n", [("rms", 20480), ("rms", 40960), ("ln", 20480)])
+def test_long_row_backward_deterministic_and_without_column_gradients(kind, n):
+    # RMSNorm 20480: one pass, dW in LDS (38 workgroups of 8 rows); RMSNorm
+    # 40960 and LayerNorm: two passes (19 row groups)
+    rows = 300
     x = workloads.normal((rows, n), 6100, torch.bfloat16)
     w = workloads.normal((n,), 6101, torch.bfloat16, mean=1.0, std=0.1)
     dy = workloads.normal((rows, n), 6102, torch.bfloat16)

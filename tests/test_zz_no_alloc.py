@@ -59,8 +59,9 @@ def test_noalloc_without_dw_and_empty_batch():
 
 
 def test_noalloc_long_rows_twice_second_smaller():
-    # rows over 16384 elements: the two-pass backward, whose partial rows and
-    # row terms both live in the scratch array (a workspace beyond the array,
-    # over 1.5 M such rows, is refused on the host: the ABI test covers it)
+    # rows over 16384 elements: the two-pass backward (65536), whose partial
+    # rows and row terms both live in the scratch array, then the one-pass
+    # backward with its accumulators in LDS (20000 bf16); a workspace beyond
+    # the array, millions of such rows, is refused on the host (ABI test)
     one_call(512, 65536, 7400, False)
     one_call(100, 20000, 7500, True)
