@@ -188,6 +188,13 @@ nr_status_t plan_fwd(nr_dtype_t dt, int64_t rows, int64_t n, bool aligned, FwdPl
     K = pick_at_least((need + 1) / 2, kFwdK, 6);
     if (K <= 5) J = 2;  // one weight load serves two rows
     R = J == 1 ? 2 : 1;
+    // Plain RMSNorm on a batch that sixteen-row workgroups cover in one round
+    // of about one workgroup per CU (3584..4096 rows on 256 CUs): eight row
+    // groups per workgroup, so the whole batch is dispatched as ~240
+    // workgroups instead of ~1900 (3840 x 5120 bf16: 14.1-14.3 -> 13.1-13.4 us
+    // on two MI355X boxes; LayerNorm and LayerNorm + GeLU measured level or
+    // slower with it, and larger batches slower).
+    if (op == kFwdRms && J == 2 && rows >= 3584 && rows <= 4096) R = 8;
   } else {
     W = static_cast<int>((need + 7) / 8);
     K = pick_at_least((need + W - 1) / W, kFwdK, 6);  // K <= 8 when W > 1
