@@ -286,6 +286,9 @@ NORM_EDGES = [
     # backward (element-wise 17001, fp32 24576, LayerNorm throughout)
     (37, 20480, torch.bfloat16), (5, 17001, torch.float16), (9, 24576, torch.float32),
     (300, 16392, torch.float16), (600, 32768, torch.bfloat16),
+    # batches of 3584..4096 rows, where the RMSNorm forward packs eight row
+    # groups (16 rows) into a workgroup; a partial last workgroup included
+    (4095, 4104, torch.bfloat16), (3584, 2560, torch.float32), (3601, 5000, torch.float16),
 ]
 
 
