@@ -550,6 +550,18 @@ nr_status_t norm_bwd_common(bool ln, nr_dtype_t dt, const void* dy, const void* 
   }
   BwdPlan pl;
   if ((s = plan_bwd(dt, ln, rows, n, aligned, &pl, false, gelu)) != NR_OK) return s;
+  // LayerNorm + GeLU on 16-bit rows of 2560 or 5120: 10 elements a lane on
+  // n / 640 waves, which load the CU's four SIMDs evenly (the one-chunk
+  // layout puts 10 waves on them 3/3/2/2).  The 4-wave form (2560) takes two
+  // workgroups per CU once the batch gives each one 16 rows (15360 x 2560
+  // bf16: 63 -> 51 us against one per CU; at 3840 rows, 8 rows each, 23 -> 26
+  // us); the 8-wave form keeps the usual count (95 against 93 us with two)
+  const bool pair = gelu && nr::ln_gelu_pair_fits(dt, n, aligned);
+  if (pair && n / 640 == 4) {
+    int64_t P2, rpb2;
+    bwd_grid(rows, true, &P2, &rpb2, 16);
+    pl.P = static_cast<int>(P2);
+  }
   float* part = nullptr;
   if (want_cols) {
     const size_t need = static_cast<size_t>(pl.P) * n * sizeof(float) * (ln ? 2 : 1);
@@ -557,10 +569,13 @@ nr_status_t norm_bwd_common(bool ln, nr_dtype_t dt, const void* dy, const void* 
       return NR_ERR_WORKSPACE;
     part = static_cast<float*>(workspace);
   }
-  const hipError_t e = gelu ? nr::launch_ln_gelu_bwd(dt, pl, dy, x, w, beta, mean, rstat, dx, part,
-                                                      rows, static_cast<int>(n), st)
-                            : nr::launch_norm_bwd(ln, dt, pl, dy, x, w, mean, rstat, dx, part, rows,
-                                                  static_cast<int>(n), w_add, st);
+  const hipError_t e =
+      pair ? nr::launch_ln_gelu_bwd_pair(dt, pl.P, dy, x, w, beta, mean, rstat, dx, part, rows,
+                                         static_cast<int>(n), st)
+      : gelu ? nr::launch_ln_gelu_bwd(dt, pl, dy, x, w, beta, mean, rstat, dx, part, rows,
+                                      static_cast<int>(n), st)
+             : nr::launch_norm_bwd(ln, dt, pl, dy, x, w, mean, rstat, dx, part, rows,
+                                   static_cast<int>(n), w_add, st);
   if ((s = hip_status(e)) != NR_OK) return s;
   if (want_cols)
     return hip_status(nr::launch_colreduce(part, static_cast<int64_t>(pl.P) * n, pl.P,

@@ -95,6 +95,13 @@ hipError_t launch_ln_gelu_bwd(int dt, const BwdPlan& pl, const void* dout, const
                               const void* gamma, const void* beta, const float* mean,
                               const float* rstd, void* dx, float* part, int64_t rows, int n,
                               hipStream_t st);
+// LayerNorm + GeLU backward, stage 1, on 16-bit rows of 640 W elements (W =
+// 4 or 8) with 10 elements a lane: W waves, the same number on every SIMD.
+bool ln_gelu_pair_fits(int dt, int64_t n, bool aligned);
+hipError_t launch_ln_gelu_bwd_pair(int dt, int P, const void* dout, const void* x,
+                                   const void* gamma, const void* beta, const float* mean,
+                                   const float* rstd, void* dx, float* part, int64_t rows, int n,
+                                   hipStream_t st);
 hipError_t launch_norm_fwd(bool ln, int dt, const FwdPlan& pl, const void* x, const void* w,
                            const void* b, void* y, float* s0, float* s1, int64_t rows, int n,
                            float eps, float w_add, hipStream_t st);

@@ -176,6 +176,10 @@ def test_ln_gelu_full_size():
     (40, 520, torch.bfloat16, True, "unaligned"), (3, 32768, torch.float32, True, "packed"),
     (45, 5120, torch.float16, True, "packed"), (6, 1003, torch.float16, True, "packed"),
     (7, 20480, torch.bfloat16, True, "packed"), (5, 17003, torch.bfloat16, True, "unaligned"),
+    # 16-bit rows of 2560 and 5120: the backward's 10-elements-a-lane layout
+    (300, 2560, torch.bfloat16, True, "packed"), (513, 5120, torch.bfloat16, False, "packed"),
+    (77, 2560, torch.float16, True, "packed"), (1, 5120, torch.bfloat16, True, "packed"),
+    (31, 2560, torch.bfloat16, True, "unaligned"), (8200, 2560, torch.bfloat16, True, "packed"),
 ])
 def test_ln_gelu_edges(rows, n, dtype, affine, layout):
     seed = 8000 + rows * 3 + n
