@@ -194,7 +194,7 @@ def build_ops(name, dev):
         ops = [
             ("layernorm_gelu_fwd", "norm_fwd[ln+gelu]",
              lambda: nr.layernorm_gelu_fwd(x, gm, bt, 1e-5, y=y, mean=mu, rstd=rs), ln_fwd_bytes(m, n)),
-            ("layernorm_gelu_bwd", "norm_bwd_rows[ln+gelu]+colreduce",
+            ("layernorm_gelu_bwd", "ln_gelu_bwd_pair+colreduce",
              lambda: nr.layernorm_gelu_bwd(dy, x, gm, bt, mu, rs, dx=dx, dgamma=dg, dbeta=db, workspace=ws),
              ln_bwd_bytes(m, n) + 2 * n),
         ]

@@ -89,6 +89,8 @@ __device__ __forceinline__ void load_row_stats(PairBatch& b, int64_t row, int64_
   b.mu = ok ? ((cfloat*)mean)[row] : 0.0f;
 }
 
+}  // namespace
+
 template <typename T, int PF>
 __global__ void __launch_bounds__(512)
 ln_gelu_bwd_pair(const T* dy, const T* x, const T* gamma, const T* beta, const float* mean,
@@ -227,8 +229,6 @@ done:
     __builtin_amdgcn_raw_buffer_store_b64(q2, p2, p4, 0, 0);
   }
 }
-
-}  // namespace
 
 bool ln_gelu_pair_fits(int dt, int64_t n, bool aligned) {
   return dt != 0 && aligned && n % 640 == 0 && (n / 640) % 4 == 0 && n / 640 <= 8;
