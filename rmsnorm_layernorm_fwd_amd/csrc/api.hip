@@ -219,6 +219,14 @@ bool fwd_grid_ok(int64_t rows, const FwdPlan& pl) {
   return (rows + per - 1) / per <= INT32_MAX;
 }
 
+// Resident workgroups per CU wanted for a backward whose row takes W waves
+// (about ten waves a CU, at most four workgroups).
+int narrow_per_cu(int64_t W) {
+  if (W >= 6) return 1;
+  const int64_t k = 10 / W;
+  return static_cast<int>(k > 4 ? 4 : k);
+}
+
 // Backward launch shape.
 //   K, W: as few chunks per lane as lets at most 16 waves cover the row
 //     (5120 bf16: K = 1, W = 10).
@@ -238,12 +246,19 @@ bool fwd_grid_ok(int64_t rows, const FwdPlan& pl) {
 //     RMSNorm + RoPE with one or two batches ahead): on MI355X's 256 CUs
 //     one or two resident workgroups per CU; more gave a second, partial
 //     round of workgroups and measured slower.
-//   P depends on the row count and the operator only, so the summation order
-//   and the workspace size are the same on every device.
-void bwd_grid(int64_t rows, bool two_per_cu, int64_t* P_out, int64_t* rpb_out,
+//   Narrow rows, whose row takes few waves, leave a CU with little in flight
+//   at one or two workgroups: there the cap is 256 times narrow_per_cu
+//   (LayerNorm from 5 waves a row down, RMSNorm from 4; 15360 rows of bf16:
+//   LayerNorm 2560 wide 72 -> 50 us on 512 workgroups, 1280 wide 56 -> 32 us
+//   on 768, RMSNorm 1280 wide 38 -> 26 us on 768; RMSNorm 2560 wide measured
+//   7% faster on 512 at 15360 rows but 4% slower at 65536, and keeps 256).
+//   P depends on the shape (row count, width, element size) and the operator
+//   only, so the summation order and the workspace size are the same on every
+//   device.
+void bwd_grid(int64_t rows, int per_cu, int64_t* P_out, int64_t* rpb_out,
               int64_t rows_min_default = 8) {
   const int64_t rows_min = tune(BWD_ROWS_MIN) > 0 ? tune(BWD_ROWS_MIN) : rows_min_default;
-  const int64_t pcap = tune(BWD_P) > 0 ? tune(BWD_P) : (two_per_cu ? 512 : 256);
+  const int64_t pcap = tune(BWD_P) > 0 ? tune(BWD_P) : 256 * static_cast<int64_t>(per_cu);
   int64_t P = tune(BWD_P) > 0 ? pcap : (rows + rows_min - 1) / rows_min;
   if (P > pcap) P = pcap;
   if (P > rows) P = rows;
@@ -326,7 +341,12 @@ nr_status_t plan_bwd(nr_dtype_t dt, bool ln, int64_t rows, int64_t n, bool align
   // (its rows are 32-64 KiB: one row per workgroup at least, where short
   // rows take eight; 256 x 32768 bf16: 40.9 us on 32 workgroups of 8 rows)
   int64_t P, rpb;
-  bwd_grid(rows, ((ln && !gelu) || rope) && W <= 10 && PF <= 2, &P, &rpb, lacc ? 1 : 8);
+  int per_cu = (((ln && !gelu) || rope) && W <= 10 && PF <= 2) ? 2 : 1;
+  if (!rope && !lacc && K == 1 && (ln ? W <= 5 : W <= 4)) {
+    const int nw = narrow_per_cu(W);
+    if (nw > per_cu) per_cu = nw;
+  }
+  bwd_grid(rows, per_cu, &P, &rpb, lacc ? 1 : 8);
   *pl = BwdPlan{W, K, D, static_cast<int>(P), PF, rpb, aligned, lacc};
   return NR_OK;
 }
@@ -422,7 +442,15 @@ nr_status_t nr_tune(const char* key, int value) {
 size_t nr_bwd_workspace_bytes(int64_t rows, int64_t n, int op) {
   if (rows <= 0 || n < 1 || op < 0 || op > 2) return 0;
   int64_t P, rpb;
-  bwd_grid(rows, op != 0, &P, &rpb, op == 0 && n >= nr::kLongRowMin ? 1 : 8);
+  // the most workgroups any dtype can take: 16-bit rows have the fewest
+  // waves (one 8-element chunk a lane), so the most workgroups per CU
+  int per_cu = op != 0 ? 2 : 1;
+  const int64_t w16 = ((n + 7) / 8 + 63) / 64;
+  if (op != 2 && (op == 1 ? w16 <= 5 : w16 <= 4)) {
+    const int nw = narrow_per_cu(w16);
+    if (nw > per_cu) per_cu = nw;
+  }
+  bwd_grid(rows, per_cu, &P, &rpb, op == 0 && n >= nr::kLongRowMin ? 1 : 8);
   const size_t one_pass =
       static_cast<size_t>(P) * static_cast<size_t>(n) * sizeof(float) * (op == 1 ? 2u : 1u);
   if (nr::bwd_two_pass(op == 0, n)) {  // partial rows, then two fp32 terms per row
@@ -559,7 +587,7 @@ nr_status_t norm_bwd_common(bool ln, nr_dtype_t dt, const void* dy, const void* 
   const bool pair = gelu && nr::ln_gelu_pair_fits(dt, n, aligned);
   if (pair && n / 640 == 4) {
     int64_t P2, rpb2;
-    bwd_grid(rows, true, &P2, &rpb2, 16);
+    bwd_grid(rows, 2, &P2, &rpb2, 16);
     pl.P = static_cast<int>(P2);
   }
   float* part = nullptr;

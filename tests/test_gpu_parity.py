@@ -289,6 +289,8 @@ NORM_EDGES = [
     # batches of 3584..4096 rows, where the RMSNorm forward packs eight row
     # groups (16 rows) into a workgroup; a partial last workgroup included
     (4095, 4104, torch.bfloat16), (3584, 2560, torch.float32), (3601, 5000, torch.float16),
+    # narrow rows on many rows: two to four backward workgroups per CU
+    (15000, 1280, torch.bfloat16), (9001, 2560, torch.float16), (8200, 2048, torch.bfloat16),
 ]
 
 
