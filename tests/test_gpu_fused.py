@@ -188,3 +188,16 @@ def test_ln_gelu_edges(rows, n, dtype, affine, layout):
     bt = workloads.normal((n,), seed + 2, dtype, std=0.5) if affine else None
     dout = workloads.normal((rows, n), seed + 3, dtype)
     check_ln_gelu(f"ln+gelu edge {rows}x{n}", x, gm, bt, dout, layout=layout)
+
+
+@pytest.mark.parametrize("which,n", [("gamma", 5120), ("beta", 5120), ("gamma", 2560), ("beta", 2560)])
+def test_ln_gelu_one_affine_parameter(which, n):
+    # gamma without beta and beta without gamma, on the widths whose backward
+    # takes 10 elements a lane (a missing gamma is 1, a missing beta 0)
+    rows = 129
+    seed = 8800 + n + (which == "beta")
+    x = workloads.normal((rows, n), seed, torch.bfloat16, mean=0.5, std=2.0)
+    gm = workloads.normal((n,), seed + 1, torch.bfloat16, mean=1.0, std=0.1) if which == "gamma" else None
+    bt = workloads.normal((n,), seed + 2, torch.bfloat16, std=0.5) if which == "beta" else None
+    dout = workloads.normal((rows, n), seed + 3, torch.bfloat16)
+    check_ln_gelu(f"ln+gelu {which} only {rows}x{n}", x, gm, bt, dout)
