@@ -78,6 +78,19 @@ def test_workspace_bytes():
     # 17 rows: 3 workgroups of at most 6 rows
     assert nr.nr_bwd_workspace_bytes(17, 8, 0) == 3 * 8 * 4
     assert nr.nr_bwd_workspace_bytes(65536, 5120, 2) == 512 * 5120 * 4  # fused RMSNorm + RoPE
+    # narrow rows (few waves a row, counted for 16-bit rows): up to 256 x
+    # floor(10 / W) workgroups, at most 4 per CU -- LayerNorm from 5 waves a
+    # row down (2560: W = 5, two per CU), RMSNorm from 4 (2048: W = 4, two;
+    # 1280: W = 3, three); RMSNorm at 2560 keeps one, the RoPE one is unchanged
+    assert nr.nr_bwd_workspace_bytes(65536, 2560, 1) == 2 * 512 * 2560 * 4
+    assert nr.nr_bwd_workspace_bytes(65536, 2560, 0) == 256 * 2560 * 4
+    assert nr.nr_bwd_workspace_bytes(65536, 2048, 0) == 512 * 2048 * 4
+    # (768 allowed; 86 rows each, so 763 with none empty)
+    assert nr.nr_bwd_workspace_bytes(65536, 1280, 0) == 763 * 1280 * 4
+    assert nr.nr_bwd_workspace_bytes(65536, 1280, 1) == 2 * 763 * 1280 * 4
+    assert nr.nr_bwd_workspace_bytes(65536, 512, 1) == 2 * 1024 * 512 * 4
+    assert nr.nr_bwd_workspace_bytes(65536, 1280, 2) == 512 * 1280 * 4
+    assert nr.nr_bwd_workspace_bytes(15000, 1280, 0) == 750 * 1280 * 4  # 20 rows each
     assert nr.nr_bwd_workspace_bytes(64, 8, 3) == 0
     # rows of more than 16384 elements (two passes): ceil(rows / 16) partial
     # rows, at most 256 / S where S = ceil(n / 4096) column slices of a 2-byte
