@@ -91,6 +91,10 @@ def test_workspace_bytes():
     assert nr.nr_bwd_workspace_bytes(65536, 512, 1) == 2 * 1024 * 512 * 4
     assert nr.nr_bwd_workspace_bytes(65536, 1280, 2) == 512 * 1280 * 4
     assert nr.nr_bwd_workspace_bytes(15000, 1280, 0) == 750 * 1280 * 4  # 20 rows each
+    # rows of at most 32 chunks (a per-head norm) take up to eight a CU
+    assert nr.nr_bwd_workspace_bytes(65536, 256, 0) == 2048 * 256 * 4
+    assert nr.nr_bwd_workspace_bytes(65536, 128, 1) == 2 * 2048 * 128 * 4
+    assert nr.nr_bwd_workspace_bytes(65536, 264, 0) == 1024 * 264 * 4  # 33 chunks
     assert nr.nr_bwd_workspace_bytes(64, 8, 3) == 0
     # rows of more than 16384 elements (two passes): ceil(rows / 16) partial
     # rows, at most 256 / S where S = ceil(n / 4096) column slices of a 2-byte
@@ -200,7 +204,7 @@ def test_rejected_calls_return_status(lib):
     assert L.layernorm_gelu_fwd(F32, FAKE, 0xA0000 + 64, None, 0xA0000, R, MU, 64, 256, 1e-5, None) == NR_ERR_ALIAS
     # grids beyond the hardware's 2^31 - 1 workgroups are refused, not truncated
     FAR = 1 << 40
-    assert L.rmsnorm_fwd(BF16, FAKE, None, FAR, None, 1 << 33, 1, 1e-6, 0, None) == NR_ERR_SHAPE
+    assert L.rmsnorm_fwd(BF16, FAKE, None, FAR, None, 1 << 34, 1, 1e-6, 0, None) == NR_ERR_SHAPE
     assert L.rope_interleaved_apply(BF16, FAKE, FAR, FAR + (1 << 36), 1, 1 << 33, 1, 2, 2, 2, 2, 0,
                                     None) == NR_ERR_SHAPE
     # RMSNorm -> linear: bf16 only, K % 64, N % 128, pointers, alignment, overlap

@@ -291,6 +291,9 @@ NORM_EDGES = [
     (4095, 4104, torch.bfloat16), (3584, 2560, torch.float32), (3601, 5000, torch.float16),
     # narrow rows on many rows: two to four backward workgroups per CU
     (15000, 1280, torch.bfloat16), (9001, 2560, torch.float16), (8200, 2048, torch.bfloat16),
+    # per-head-sized rows on many rows: two rows a wave forward, up to eight
+    # backward workgroups per CU
+    (40003, 128, torch.bfloat16), (20000, 256, torch.float32), (17000, 256, torch.float16),
 ]
 
 
