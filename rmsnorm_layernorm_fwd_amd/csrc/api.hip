@@ -25,10 +25,10 @@ using nr::RopePlan;
 // ---- tuning overrides ---------------------------------------------------
 
 enum TuneKey { FWD_W, FWD_K, FWD_R, FWD_J, BWD_W, BWD_K, BWD_D, BWD_P, BWD_ROWS_MIN, BWD_PF,
-               ROPE_K, ROPE_WPB, ROPE_GROUPS, GEMM_TILE, NKEYS };
+               ROPE_K, ROPE_WPB, ROPE_GROUPS, GEMM_TILE, FWD_PACK, NKEYS };
 const char* const kTuneNames[NKEYS] = {"fwd_w", "fwd_k", "fwd_r", "fwd_j", "bwd_w", "bwd_k",
                                        "bwd_d", "bwd_p", "bwd_rows_min", "bwd_pf", "rope_k",
-                                       "rope_wpb", "rope_groups", "gemm_tile"};
+                                       "rope_wpb", "rope_groups", "gemm_tile", "fwd_pack"};
 std::atomic<int> g_tune[NKEYS];
 
 int tune(TuneKey k) { return g_tune[k].load(std::memory_order_relaxed); }
@@ -165,6 +165,18 @@ nr_status_t plan_fwd(nr_dtype_t dt, int64_t rows, int64_t n, bool aligned, FwdPl
   // against the two-wave shape; 3840 rows: RMSNorm 15.5 -> 14.8 us the other
   // way round).  Longer rows: up to 8 chunks per lane and as many waves as
   // needed.
+  // Aligned rows of at most 32 chunks (256 16-bit or 128 fp32 elements, e.g.
+  // a per-head q/k norm): 64 / S rows side by side in a wave, S lanes each,
+  // so no lane idles (norm_fwd_packed).  fwd_pack = 1 keeps the wave-per-row
+  // kernels; 4..32 forces S.
+  if (aligned && nchunk <= 32 && tune(FWD_PACK) != 1) {
+    int S = 4;
+    while (S < nchunk) S *= 2;
+    if (tune(FWD_PACK) > 1) S = tune(FWD_PACK);
+    if ((S != 4 && S != 8 && S != 16 && S != 32) || S < nchunk) return NR_ERR_SHAPE;
+    *pl = FwdPlan{1, 1, 1, 1, aligned, S};
+    return NR_OK;
+  }
   int W, K, J = 1, R;
   if (need <= 4) {
     W = 1;
@@ -218,7 +230,7 @@ nr_status_t plan_fwd(nr_dtype_t dt, int64_t rows, int64_t n, bool aligned, FwdPl
 // The forward launches one workgroup per J*R rows: the grid must fit the
 // hardware's 2^31 - 1 workgroups.
 bool fwd_grid_ok(int64_t rows, const FwdPlan& pl) {
-  const int64_t per = static_cast<int64_t>(pl.J) * pl.R;
+  const int64_t per = pl.S > 0 ? nr::fwd_packed_rows_per_block(pl.S) : static_cast<int64_t>(pl.J) * pl.R;
   return (rows + per - 1) / per <= INT32_MAX;
 }
 

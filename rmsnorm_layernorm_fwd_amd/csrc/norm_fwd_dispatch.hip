@@ -27,6 +27,8 @@ hipError_t launch_norm_fwd(bool ln, int dt, const FwdPlan& pl, const void* x, co
                            const void* b, void* y, float* s0, float* s1, int64_t rows, int n,
                            float eps, float w_add, hipStream_t st) {
   const RopeArgs none{nullptr, nullptr, 2, 1};
+  if (pl.S > 0)
+    return launch_fwd_packed(dt, ln, kEpiNone, pl, x, w, b, y, s0, s1, rows, n, eps, w_add, none, st);
   return by_dtype(dt, [&](auto tag) {
     using T = decltype(tag);
     return ln ? launch_fwd_t<T, true, kEpiNone>(pl, x, w, b, y, s0, s1, rows, n, eps, w_add, none, st)
@@ -37,6 +39,9 @@ hipError_t launch_norm_fwd(bool ln, int dt, const FwdPlan& pl, const void* x, co
 hipError_t launch_rms_rope_fwd(int dt, const FwdPlan& pl, const void* x, const void* w, void* y,
                                float* inv_rms, const RopeArgs& ra, int64_t rows, int n, float eps,
                                float w_add, hipStream_t st) {
+  if (pl.S > 0)
+    return launch_fwd_packed(dt, false, kEpiRope, pl, x, w, nullptr, y, inv_rms, nullptr, rows, n,
+                             eps, w_add, ra, st);
   return by_dtype(dt, [&](auto tag) {
     using T = decltype(tag);
     return launch_fwd_t<T, false, kEpiRope>(pl, x, w, nullptr, y, inv_rms, nullptr, rows, n, eps,
@@ -48,6 +53,9 @@ hipError_t launch_ln_gelu_fwd(int dt, const FwdPlan& pl, const void* x, const vo
                               const void* beta, void* y, float* mean, float* rstd, int64_t rows,
                               int n, float eps, hipStream_t st) {
   const RopeArgs none{nullptr, nullptr, 2, 1};
+  if (pl.S > 0)
+    return launch_fwd_packed(dt, true, kEpiGelu, pl, x, gamma, beta, y, mean, rstd, rows, n, eps,
+                             0.0f, none, st);
   return by_dtype(dt, [&](auto tag) {
     using T = decltype(tag);
     return launch_fwd_t<T, true, kEpiGelu>(pl, x, gamma, beta, y, mean, rstd, rows, n, eps, 0.0f,

@@ -17,6 +17,7 @@ constexpr int kF16 = 2;   // matches NR_F16
 struct FwdPlan {
   int W, K, R, J;
   bool aligned;
+  int S = 0;  // > 0: rows of at most S chunks, S lanes each (norm_fwd_packed)
 };
 
 // Backward stage 1: P workgroups of W waves, D rows per batch, K chunks per
@@ -102,6 +103,13 @@ hipError_t launch_ln_gelu_bwd_pair(int dt, int P, const void* dout, const void* 
                                    const void* gamma, const void* beta, const float* mean,
                                    const float* rstd, void* dx, float* part, int64_t rows, int n,
                                    hipStream_t st);
+// Rows of at most pl.S whole chunks, 64 / pl.S of them side by side in a
+// wave (pl.S = 4, 8, 16 or 32; aligned rows only); epi as the row kernels.
+int fwd_packed_rows_per_block(int S);
+hipError_t launch_fwd_packed(int dt, bool ln, int epi, const FwdPlan& pl, const void* x,
+                             const void* w, const void* b, void* y, float* s0, float* s1,
+                             int64_t rows, int n, float eps, float w_add, const RopeArgs& ra,
+                             hipStream_t st);
 hipError_t launch_norm_fwd(bool ln, int dt, const FwdPlan& pl, const void* x, const void* w,
                            const void* b, void* y, float* s0, float* s1, int64_t rows, int n,
                            float eps, float w_add, hipStream_t st);

@@ -317,6 +317,72 @@ def test_ln_edges(rows, n, dtype):
     check_ln_full(f"ln edge {rows}x{n}", x, gm, bt, dy, 1e-5)
 
 
+# Forwards of aligned rows of at most 32 16-byte chunks put 64 / S rows side
+# by side in a wave, S lanes each.  Each lane width, forced, on ragged batches
+# (a partial last wave and workgroup), rows that leave lanes of their S idle,
+# and every operator and epilogue of the forward, against the oracle.
+PACKED = [
+    # (S, rows, n, dtype)
+    (4, 1037, 24, torch.bfloat16), (4, 3, 16, torch.float32), (8, 1001, 64, torch.bfloat16),
+    (8, 517, 28, torch.float32), (16, 1039, 120, torch.float16), (16, 2050, 128, torch.bfloat16),
+    (32, 1, 256, torch.bfloat16), (32, 777, 200, torch.bfloat16), (32, 1030, 128, torch.float32),
+    (32, 300, 64, torch.bfloat16),  # 8 chunks on 32 lanes
+]
+
+
+class forced_pack:
+    def __init__(self, s):
+        self.s = s
+
+    def __enter__(self):
+        nr.nr_tune("fwd_pack", self.s)
+
+    def __exit__(self, *a):
+        nr.nr_tune("fwd_pack", 0)
+
+
+@pytest.mark.parametrize("S,rows,n,dtype", PACKED)
+@pytest.mark.parametrize("op", ["rms", "rms_gemma", "ln", "ln_gelu", "rms_rope"])
+def test_packed_rows_forward(S, rows, n, dtype, op):
+    seed = 9100 + S * 13 + rows + n
+    say(f"packed forward S={S} {rows}x{n} {dtype} {op}")
+    x = workloads.normal((rows, n), seed, dtype, mean=0.5 if op.startswith("ln") else 0.0, std=2.0)
+    gemma = op == "rms_gemma"
+    w = workloads.normal((n,), seed + 1, dtype, mean=0.0 if gemma else 1.0, std=0.1)
+    k = out_kind(dtype)
+    with forced_pack(S):
+        if op in ("rms", "rms_gemma"):
+            y, r = nr.rmsnorm_fwd(g(x), g(w), eps=1e-6, gemma_offset=gemma)
+            torch.cuda.synchronize()
+            ry, rr = oracle.rmsnorm_fwd(x, w, 1e-6, gemma)
+            check(f"S={S} y", y.reshape(-1, n), ry, k)
+            check(f"S={S} inv_rms", r.reshape(-1), rr, "stat", s=0.0)
+        elif op == "rms_rope":
+            hd = n if n % 16 else n // 2  # per-head rows, or two heads a row
+            rpt = 2 if hd == n else 1
+            ang = oracle.rope_angles_1d(-(-rows // rpt), hd, 5, 10000.0)
+            ct = torch.from_numpy(np.cos(ang)).float().to("cuda")
+            st = torch.from_numpy(np.sin(ang)).float().to("cuda")
+            y, r = nr.rmsnorm_rope_fwd(g(x), g(w), ct, st, hd, rpt, 1e-6, False)
+            torch.cuda.synchronize()
+            ry, rr = oracle.rmsnorm_rope_fwd(x, w, ang, hd, rpt, 1e-6, False)
+            check(f"S={S} y", y, ry, k)
+            check(f"S={S} inv_rms", r, rr, "stat", s=0.0)
+        else:
+            bt = workloads.normal((n,), seed + 2, dtype, std=0.5)
+            x64 = to64(x).reshape(-1, n)
+            if op == "ln":
+                y, mu, rs = nr.layernorm_fwd(g(x), g(w), g(bt), eps=1e-5)
+                ry, rmu, rrs = oracle.layernorm_fwd(x, w, bt, 1e-5)
+            else:
+                y, mu, rs = nr.layernorm_gelu_fwd(g(x), g(w), g(bt), 1e-5)
+                ry, rmu, rrs = oracle.layernorm_gelu_fwd(x, w, bt, 1e-5)
+            torch.cuda.synchronize()
+            check(f"S={S} y", y.reshape(-1, n), ry, k)
+            check(f"S={S} mean", mu.reshape(-1), rmu, "stat", s=np.sqrt(np.mean(x64 * x64, axis=1)))
+            check(f"S={S} rstd", rs.reshape(-1), rrs, "stat", s=0.0)
+
+
 def test_non_affine_and_constant_rows():
     x = workloads.normal((40, 96), 4001, torch.bfloat16)
     dy = workloads.normal((40, 96), 4002, torch.bfloat16)
