@@ -25,10 +25,11 @@ using nr::RopePlan;
 // ---- tuning overrides ---------------------------------------------------
 
 enum TuneKey { FWD_W, FWD_K, FWD_R, FWD_J, BWD_W, BWD_K, BWD_D, BWD_P, BWD_ROWS_MIN, BWD_PF,
-               ROPE_K, ROPE_WPB, ROPE_GROUPS, GEMM_TILE, FWD_PACK, NKEYS };
+               ROPE_K, ROPE_WPB, ROPE_GROUPS, GEMM_TILE, FWD_PACK, BWD_PACK, NKEYS };
 const char* const kTuneNames[NKEYS] = {"fwd_w", "fwd_k", "fwd_r", "fwd_j", "bwd_w", "bwd_k",
                                        "bwd_d", "bwd_p", "bwd_rows_min", "bwd_pf", "rope_k",
-                                       "rope_wpb", "rope_groups", "gemm_tile", "fwd_pack"};
+                                       "rope_wpb", "rope_groups", "gemm_tile", "fwd_pack",
+                                       "bwd_pack"};
 std::atomic<int> g_tune[NKEYS];
 
 int tune(TuneKey k) { return g_tune[k].load(std::memory_order_relaxed); }
@@ -232,6 +233,28 @@ nr_status_t plan_fwd(nr_dtype_t dt, int64_t rows, int64_t n, bool aligned, FwdPl
 bool fwd_grid_ok(int64_t rows, const FwdPlan& pl) {
   const int64_t per = pl.S > 0 ? nr::fwd_packed_rows_per_block(pl.S) : static_cast<int64_t>(pl.J) * pl.R;
   return (rows + per - 1) / per <= INT32_MAX;
+}
+
+// Backward of aligned rows of at most 32 chunks: the lanes per row S of the
+// packed kernel (0: the row kernels), and its workgroup count, at least one
+// batch per wave and at most the row kernels' count, which sizes the
+// workspace.  bwd_pack = 1 keeps the row kernels; 4..32 forces S.
+nr_status_t plan_bwd_packed(nr_dtype_t dt, int64_t rows, int64_t n, bool aligned, BwdPlan* pl,
+                            int* S_out) {
+  *S_out = 0;
+  const int64_t nchunk = n / vec_elems(dt);
+  if (!aligned || nchunk > 32 || tune(BWD_PACK) == 1) return NR_OK;
+  int S = 4;
+  while (S < nchunk) S *= 2;
+  if (tune(BWD_PACK) > 1) S = tune(BWD_PACK);
+  if ((S != 4 && S != 8 && S != 16 && S != 32) || S < nchunk) return NR_ERR_SHAPE;
+  const int64_t rw = nr::bwd_packed_rows_per_wave(S);
+  int64_t P = ((rows + rw - 1) / rw + 3) / 4;
+  if (P > pl->P) P = pl->P;
+  if (P < 1) P = 1;
+  pl->P = static_cast<int>(P);
+  *S_out = S;
+  return NR_OK;
 }
 
 // Resident workgroups per CU wanted for a backward whose row takes W waves
@@ -603,6 +626,8 @@ nr_status_t norm_bwd_common(bool ln, nr_dtype_t dt, const void* dy, const void* 
   // workgroups per CU once the batch gives each one 16 rows (15360 x 2560
   // bf16: 63 -> 51 us against one per CU; at 3840 rows, 8 rows each, 23 -> 26
   // us); the 8-wave form keeps the usual count (95 against 93 us with two)
+  int S = 0;
+  if (!gelu && (s = plan_bwd_packed(dt, rows, n, aligned, &pl, &S)) != NR_OK) return s;
   const bool pair = gelu && nr::ln_gelu_pair_fits(dt, n, aligned);
   if (pair && n / 640 == 4) {
     int64_t P2, rpb2;
@@ -616,8 +641,11 @@ nr_status_t norm_bwd_common(bool ln, nr_dtype_t dt, const void* dy, const void* 
       return NR_ERR_WORKSPACE;
     part = static_cast<float*>(workspace);
   }
+  const nr::RopeArgs none{nullptr, nullptr, 2, 1};
   const hipError_t e =
-      pair ? nr::launch_ln_gelu_bwd_pair(dt, pl.P, dy, x, w, beta, mean, rstat, dx, part, rows,
+      S > 0 ? nr::launch_bwd_packed(dt, ln, false, S, pl.P, dy, x, w, mean, rstat, dx, part, rows,
+                                    static_cast<int>(n), w_add, none, st)
+      : pair ? nr::launch_ln_gelu_bwd_pair(dt, pl.P, dy, x, w, beta, mean, rstat, dx, part, rows,
                                          static_cast<int>(n), st)
       : gelu ? nr::launch_ln_gelu_bwd(dt, pl, dy, x, w, beta, mean, rstat, dx, part, rows,
                                       static_cast<int>(n), st)
@@ -761,6 +789,8 @@ nr_status_t rmsnorm_rope_bwd(nr_dtype_t dt, const void* dout, const void* x, con
                     rows, n, gemma_offset ? 1.0f : 0.0f, ra, workspace, workspace_bytes, st);
   BwdPlan pl;
   if ((s = plan_bwd(dt, false, rows, n, aligned, &pl, true)) != NR_OK) return s;
+  int S = 0;
+  if ((s = plan_bwd_packed(dt, rows, n, aligned, &pl, &S)) != NR_OK) return s;
   float* part = nullptr;
   if (dw != nullptr) {
     const size_t need = static_cast<size_t>(pl.P) * n * sizeof(float);
@@ -768,9 +798,13 @@ nr_status_t rmsnorm_rope_bwd(nr_dtype_t dt, const void* dout, const void* x, con
       return NR_ERR_WORKSPACE;
     part = static_cast<float*>(workspace);
   }
-  if ((s = hip_status(nr::launch_rms_rope_bwd(dt, pl, dout, x, w, inv_rms, ra, dx, part, rows,
-                                              static_cast<int>(n), gemma_offset ? 1.0f : 0.0f,
-                                              st))) != NR_OK)
+  if ((s = hip_status(
+           S > 0 ? nr::launch_bwd_packed(dt, false, true, S, pl.P, dout, x, w, nullptr, inv_rms, dx,
+                                         part, rows, static_cast<int>(n),
+                                         gemma_offset ? 1.0f : 0.0f, ra, st)
+                 : nr::launch_rms_rope_bwd(dt, pl, dout, x, w, inv_rms, ra, dx, part, rows,
+                                           static_cast<int>(n), gemma_offset ? 1.0f : 0.0f,
+                                           st))) != NR_OK)
     return s;
   if (dw != nullptr)
     return hip_status(nr::launch_colreduce(part, static_cast<int64_t>(pl.P) * n, pl.P,

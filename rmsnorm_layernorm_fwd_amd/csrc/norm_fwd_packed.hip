@@ -32,23 +32,6 @@ namespace {
 
 constexpr int PJ = NR_PACK_J;  // row groups a wave loads at once
 
-// Sum over the S consecutive lanes (S a power of two, 4..32) that hold one
-// row; lanes that hold disjoint partial sums are added pairwise.
-template <int S>
-__device__ __forceinline__ float lane_group_sum(float v) {
-  v += dpp<0xB1>(v);  // quad_perm [1,0,3,2]
-  v += dpp<0x4E>(v);  // quad_perm [2,3,0,1]
-  if constexpr (S >= 8) v += dpp<0x141>(v);  // row_half_mirror: the other quad
-  if constexpr (S >= 16) v += dpp<0x140>(v);  // row_mirror: the other half-row
-  if constexpr (S >= 32) {
-    // rows 0 <-> 1 and 2 <-> 3 of the wave
-    const uint32_t u = __float_as_uint(v);
-    auto p = __builtin_amdgcn_permlane16_swap(u, u, false, false);
-    v = __uint_as_float(p[0]) + __uint_as_float(p[1]);
-  }
-  return v;
-}
-
 }  // namespace
 
 template <typename T, int S, bool LN, int EPI>

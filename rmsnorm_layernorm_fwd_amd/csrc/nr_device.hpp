@@ -356,6 +356,23 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
+// Sum over the S consecutive lanes (S a power of two, 4..32) that hold one
+// row; lanes that hold disjoint partial sums are added pairwise.
+template <int S>
+__device__ __forceinline__ float lane_group_sum(float v) {
+  v += dpp<0xB1>(v);  // quad_perm [1,0,3,2]
+  v += dpp<0x4E>(v);  // quad_perm [2,3,0,1]
+  if constexpr (S >= 8) v += dpp<0x141>(v);  // row_half_mirror: the other quad
+  if constexpr (S >= 16) v += dpp<0x140>(v);  // row_mirror: the other half-row
+  if constexpr (S >= 32) {
+    // rows 0 <-> 1 and 2 <-> 3 of the wave
+    const uint32_t u = __float_as_uint(v);
+    auto p = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    v = __uint_as_float(p[0]) + __uint_as_float(p[1]);
+  }
+  return v;
+}
+
 // Sum of the slots [lo, hi) of a 16-float LDS line that the waves of a
 // workgroup have filled (one slot per wave), returned as a uniform value.
 // One LDS read per lane, whatever the number of waves: lane i of each

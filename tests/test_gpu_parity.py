@@ -383,6 +383,48 @@ def test_packed_rows_forward(S, rows, n, dtype, op):
             check(f"S={S} rstd", rs.reshape(-1), rrs, "stat", s=0.0)
 
 
+class forced_bwd_pack(forced_pack):
+    def __enter__(self):
+        nr.nr_tune("bwd_pack", self.s)
+
+    def __exit__(self, *a):
+        nr.nr_tune("bwd_pack", 0)
+
+
+@pytest.mark.parametrize("S,rows,n,dtype", PACKED)
+@pytest.mark.parametrize("op", ["rms", "rms_gemma", "rms_no_weight", "ln", "rms_rope"])
+def test_packed_rows_backward(S, rows, n, dtype, op):
+    """The backward's packed form (S lanes a row, column sums through LDS and
+    the column reduction), each lane width forced, against the oracle."""
+    seed = 9500 + S * 13 + rows + n
+    say(f"packed backward S={S} {rows}x{n} {dtype} {op}")
+    x = workloads.normal((rows, n), seed, dtype, mean=0.5 if op == "ln" else 0.0, std=2.0)
+    gemma = op == "rms_gemma"
+    w = workloads.normal((n,), seed + 1, dtype, mean=0.0 if gemma else 1.0, std=0.1)
+    dy = workloads.normal((rows, n), seed + 2, dtype)
+    with forced_bwd_pack(S):
+        if op == "ln":
+            bt = workloads.normal((n,), seed + 3, dtype, std=0.5)
+            check_ln_full(f"S={S}", x, w, bt, dy, 1e-5)
+        elif op == "rms_rope":
+            hd = n if n % 16 else n // 2
+            rpt = 2 if hd == n else 1
+            ang = oracle.rope_angles_1d(-(-rows // rpt), hd, 5, 10000.0)
+            ct = torch.from_numpy(np.cos(ang)).float().to("cuda")
+            st = torch.from_numpy(np.sin(ang)).float().to("cuda")
+            y, r = nr.rmsnorm_rope_fwd(g(x), g(w), ct, st, hd, rpt, 1e-6, False)
+            dx, dw = nr.rmsnorm_rope_bwd(g(dy), g(x), g(w), r, ct, st, hd, rpt, False)
+            torch.cuda.synchronize()
+            rdx, rdw = oracle.rmsnorm_rope_bwd(dy, x, w, ang, hd, rpt, 1e-6, False)
+            _, rr = oracle.rmsnorm_rope_fwd(x, w, ang, hd, rpt, 1e-6, False)
+            dy64 = oracle.rope_apply(dy.reshape(1, rows, n // hd, hd),
+                                     ang[np.arange(rows) // rpt], inverse=True).reshape(rows, n)
+            check(f"S={S} dx", dx, rdx, out_kind(dtype), s=grad_scale(rr, dy64, w, False))
+            check(f"S={S} dw", dw, rdw, "col")
+        else:
+            check_rms_full(f"S={S}", x, None if op == "rms_no_weight" else w, dy, 1e-6, gemma)
+
+
 def test_non_affine_and_constant_rows():
     x = workloads.normal((40, 96), 4001, torch.bfloat16)
     dy = workloads.normal((40, 96), 4002, torch.bfloat16)
