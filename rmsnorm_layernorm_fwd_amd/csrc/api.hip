@@ -248,8 +248,15 @@ nr_status_t plan_bwd_packed(nr_dtype_t dt, int64_t rows, int64_t n, bool aligned
   while (S < nchunk) S *= 2;
   if (tune(BWD_PACK) > 1) S = tune(BWD_PACK);
   if ((S != 4 && S != 8 && S != 16 && S != 32) || S < nchunk) return NR_ERR_SHAPE;
+  // at most five workgroups per CU (what ~100 VGPRs a lane leave resident),
+  // the batches spread evenly over the rounds of the waves: 65536 x 256 bf16
+  // RMSNorm 23.7 -> 21.2 us against 2048 workgroups of one batch a wave;
+  // level (within 3%) at 655360..2621440 rows of 128 and 256
   const int64_t rw = nr::bwd_packed_rows_per_wave(S);
-  int64_t P = ((rows + rw - 1) / rw + 3) / 4;
+  const int64_t nb = (rows + rw - 1) / rw;
+  const int64_t cap = pl->P < 1280 ? pl->P : 1280;
+  const int64_t rounds = (nb + 4 * cap - 1) / (4 * cap);
+  int64_t P = (nb + 4 * rounds - 1) / (4 * rounds);
   if (P > pl->P) P = pl->P;
   if (P < 1) P = 1;
   pl->P = static_cast<int>(P);
