@@ -395,6 +395,10 @@ nr_status_t plan_bwd(nr_dtype_t dt, bool ln, int64_t rows, int64_t n, bool align
     const int nw = narrow_per_cu(W, nchunk);
     if (nw > per_cu) per_cu = nw;
   }
+  // RoPE rows of at most 32 16-bit chunks (a per-head q/k norm): up to five
+  // a CU, as the packed backward of the plain norms takes (65536 tokens x 40
+  // heads x 128 bf16: 450 -> 348 us against 512 workgroups)
+  if (rope && (n + 7) / 8 <= 32) per_cu = 5;
   bwd_grid(rows, per_cu, &P, &rpb, lacc ? 1 : 8);
   *pl = BwdPlan{W, K, D, static_cast<int>(P), PF, rpb, aligned, lacc};
   return NR_OK;
@@ -499,6 +503,7 @@ size_t nr_bwd_workspace_bytes(int64_t rows, int64_t n, int op) {
     const int nw = narrow_per_cu(w16, (n + 7) / 8);
     if (nw > per_cu) per_cu = nw;
   }
+  if (op == 2 && (n + 7) / 8 <= 32) per_cu = 5;
   bwd_grid(rows, per_cu, &P, &rpb, op == 0 && n >= nr::kLongRowMin ? 1 : 8);
   const size_t one_pass =
       static_cast<size_t>(P) * static_cast<size_t>(n) * sizeof(float) * (op == 1 ? 2u : 1u);

@@ -95,6 +95,10 @@ def test_workspace_bytes():
     assert nr.nr_bwd_workspace_bytes(65536, 256, 0) == 2048 * 256 * 4
     assert nr.nr_bwd_workspace_bytes(65536, 128, 1) == 2 * 2048 * 128 * 4
     assert nr.nr_bwd_workspace_bytes(65536, 264, 0) == 1024 * 264 * 4  # 33 chunks
+    # RMSNorm -> RoPE on such rows (per-head): up to five a CU
+    assert nr.nr_bwd_workspace_bytes(2621440, 128, 2) == 1280 * 128 * 4
+    assert nr.nr_bwd_workspace_bytes(4000, 256, 2) == 500 * 256 * 4  # 8 rows each
+    assert nr.nr_bwd_workspace_bytes(65536, 264, 2) == 512 * 264 * 4
     assert nr.nr_bwd_workspace_bytes(64, 8, 3) == 0
     # rows of more than 16384 elements (two passes): ceil(rows / 16) partial
     # rows, at most 256 / S where S = ceil(n / 4096) column slices of a 2-byte

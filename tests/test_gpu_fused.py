@@ -71,6 +71,11 @@ CASES = [
     (23, 100, 96, 1, torch.bfloat16, False, "packed"),    # 9600 wide: 5120 % 96 != 0
     (21, 160, 128, 1, torch.bfloat16, False, "packed"),   # 20480 wide: two-pass backward
     (9, 170, 102, 1, torch.float32, True, "packed"),      # 17340 wide, element-wise tables
+    # per-head rows (a q/k norm): the packed kernels, on enough rows for the
+    # backward's full workgroup count, and the wave-per-row kernels unaligned
+    (90001, 1, 128, 40, torch.bfloat16, False, "packed"),
+    (20000, 1, 64, 8, torch.float16, True, "packed"),
+    (3001, 1, 128, 8, torch.bfloat16, False, "unaligned"),
 ]
 
 
