@@ -41,6 +41,13 @@ def test_noalloc_matches_workspace_call_twice_second_smaller():
     one_call(1000, 3000, 7200, True)
 
 
+def test_noalloc_per_head_rows_twice_second_smaller():
+    # rows of at most 32 chunks: the packed backward's partial rows in the
+    # scratch array (up to 1280 of them), then a smaller batch of wider rows
+    one_call(90000, 128, 7300, False)
+    one_call(5000, 256, 7400, True)
+
+
 def test_noalloc_without_dw_and_empty_batch():
     print("[case] rmsnorm_bwd_noalloc without dw; empty batch", flush=True)
     x = workloads.normal((300, 640), 7300, torch.bfloat16).to(DEV)
