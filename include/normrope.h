@@ -390,7 +390,7 @@ int nr_last_hip_error(void);
  * "rope_groups", "gemm_tile" (1: 128 x 128 outputs per workgroup, 2: 256 x
  * 256), "fwd_pack" (forwards of aligned rows of at most 32 16-byte chunks:
  * 1 one wave per row, 4/8/16/32 that many lanes per row), "bwd_pack" (the
- * same for the backwards of RMSNorm, LayerNorm and RMSNorm + RoPE).  A key whose forced value
+ * same for the backwards).  A key whose forced value
  * does not fit a call's shape makes that call return NR_ERR_SHAPE.
  * Returns NR_ERR_TUNE for an unknown key or a negative value.  Host only.
  */

@@ -235,8 +235,8 @@ bool fwd_grid_ok(int64_t rows, const FwdPlan& pl) {
   return (rows + per - 1) / per <= INT32_MAX;
 }
 
-// Backward of aligned rows of at most 32 chunks: the lanes per row S of the
-// packed kernel (0: the row kernels), and its workgroup count, at least one
+// Backward of aligned rows of at most 32 chunks (every operator): the lanes
+// per row S of the packed kernel (0: the row kernels), and its workgroup count, at least one
 // batch per wave and at most the row kernels' count, which sizes the
 // workspace.  bwd_pack = 1 keeps the row kernels; 4..32 forces S.
 nr_status_t plan_bwd_packed(nr_dtype_t dt, int64_t rows, int64_t n, bool aligned, BwdPlan* pl,
@@ -639,7 +639,7 @@ nr_status_t norm_bwd_common(bool ln, nr_dtype_t dt, const void* dy, const void* 
   // bf16: 63 -> 51 us against one per CU; at 3840 rows, 8 rows each, 23 -> 26
   // us); the 8-wave form keeps the usual count (95 against 93 us with two)
   int S = 0;
-  if (!gelu && (s = plan_bwd_packed(dt, rows, n, aligned, &pl, &S)) != NR_OK) return s;
+  if ((s = plan_bwd_packed(dt, rows, n, aligned, &pl, &S)) != NR_OK) return s;
   const bool pair = gelu && nr::ln_gelu_pair_fits(dt, n, aligned);
   if (pair && n / 640 == 4) {
     int64_t P2, rpb2;
@@ -655,8 +655,9 @@ nr_status_t norm_bwd_common(bool ln, nr_dtype_t dt, const void* dy, const void* 
   }
   const nr::RopeArgs none{nullptr, nullptr, 2, 1};
   const hipError_t e =
-      S > 0 ? nr::launch_bwd_packed(dt, ln, false, S, pl.P, dy, x, w, mean, rstat, dx, part, rows,
-                                    static_cast<int>(n), w_add, none, st)
+      S > 0 ? nr::launch_bwd_packed(dt, ln, gelu ? 2 : 0, S, pl.P, dy, x, w,
+                                    beta, mean, rstat, dx, part, rows, static_cast<int>(n), w_add,
+                                    none, st)
       : pair ? nr::launch_ln_gelu_bwd_pair(dt, pl.P, dy, x, w, beta, mean, rstat, dx, part, rows,
                                          static_cast<int>(n), st)
       : gelu ? nr::launch_ln_gelu_bwd(dt, pl, dy, x, w, beta, mean, rstat, dx, part, rows,
@@ -811,8 +812,8 @@ nr_status_t rmsnorm_rope_bwd(nr_dtype_t dt, const void* dout, const void* x, con
     part = static_cast<float*>(workspace);
   }
   if ((s = hip_status(
-           S > 0 ? nr::launch_bwd_packed(dt, false, true, S, pl.P, dout, x, w, nullptr, inv_rms, dx,
-                                         part, rows, static_cast<int>(n),
+           S > 0 ? nr::launch_bwd_packed(dt, false, 1, S, pl.P, dout, x, w, nullptr,
+                                         nullptr, inv_rms, dx, part, rows, static_cast<int>(n),
                                          gemma_offset ? 1.0f : 0.0f, ra, st)
                  : nr::launch_rms_rope_bwd(dt, pl, dout, x, w, inv_rms, ra, dx, part, rows,
                                            static_cast<int>(n), gemma_offset ? 1.0f : 0.0f,

@@ -7,7 +7,9 @@
 // mean(g x^)) and LayerNorm's dx = r (g - mean(g) - x^ mean(g x^)); the
 // weight gradients are column sums over the rows, dw = sum dy x^ (and
 // dbeta = sum dy).  After RoPE the incoming gradient is first rotated back
-// by the token's angles.  fp32 arithmetic, one rounding per output.
+// by the token's angles; after LayerNorm + tanh-GeLU (LLM层的优化算子,
+// 编写定制融合算子) it is first multiplied by the activation's derivative at
+// x^ gamma + beta.  fp32 arithmetic, one rounding per output.
 //
 // Mapping as the packed forward (norm_fwd_packed.hip): a row of at most 32
 // whole 16-byte chunks takes S lanes of a wave, 64 / S rows side by side and
@@ -32,15 +34,18 @@ constexpr int PJB = NR_PACK_BWD_J;  // row groups a wave loads per batch
 
 }  // namespace
 
-template <typename T, int S, bool LN, bool ROPE>
+template <typename T, int S, bool LN, int EPI>
 __global__ __launch_bounds__(256) void norm_bwd_packed(
     const T* __restrict__ dy, const T* __restrict__ x, const T* __restrict__ w,
-    const float* __restrict__ mean, const float* __restrict__ rstat, T* __restrict__ dx,
+    const T* __restrict__ b, const float* __restrict__ mean, const float* __restrict__ rstat, T* __restrict__ dx,
     float* __restrict__ part, int64_t rows, int n, float w_add, RopeArgs ra) {
   constexpr int E = Vec<T>::N;
   constexpr int L = 64 / S;      // rows side by side in a wave
   constexpr int RW = PJB * L;    // rows per batch of a wave
   constexpr int NA = LN ? 2 : 1;  // column sums per element
+  constexpr bool ROPE = EPI == kEpiRope;
+  constexpr bool GELU = EPI == kEpiGelu;
+  constexpr bool PRE = ROPE || GELU;  // the incoming gradient transformed first
   __shared__ float red[NA * 256 * E];
   const int lane = static_cast<int>(threadIdx.x) & 63;
   const int wave = static_cast<int>(threadIdx.x) >> 6;
@@ -57,6 +62,11 @@ __global__ __launch_bounds__(256) void norm_bwd_packed(
     const float wadd = (w != nullptr) ? w_add : 1.0f;
 #pragma unroll
     for (int e = 0; e < E; ++e) wv[e] += wadd;
+  }
+  float bv[GELU ? E : 1];
+  if constexpr (GELU) {
+    const rsrc_t br = make_rsrc(b, b != nullptr ? rb : 0u);
+    unpack<T>(ld_chunk<T, true>(br, c), bv);
   }
   float acc[NA][E];
 #pragma unroll
@@ -91,8 +101,20 @@ __global__ __launch_bounds__(256) void norm_bwd_packed(
       rs[j] = ld_f32(rr, (j * L + slot) * 4);
       mu[j] = LN ? ld_f32(mr, (j * L + slot) * 4) : 0.0f;
     }
-    // RoPE: the incoming gradient rotated back by its token's angles
-    float dr[ROPE ? PJB : 1][E];
+    // RoPE: the incoming gradient rotated back by its token's angles; GeLU:
+    // times the derivative at the pre-activation
+    float dr[PRE ? PJB : 1][E];
+    if constexpr (GELU) {
+#pragma unroll
+      for (int j = 0; j < PJB; ++j) {
+        float xv[E];
+        unpack<T>(xa[j], xv);
+        unpack<T>(da[j], dr[j]);
+#pragma unroll
+        for (int e = 0; e < E; ++e)
+          dr[j][e] *= gelu_tanh_grad(fmaf((xv[e] - mu[j]) * rs[j], wv[e], bv[e]));
+      }
+    }
     if constexpr (ROPE) {
       constexpr int PP = E / 2;
       const int64_t tok0 = base / ra.rows_per_token;
@@ -118,7 +140,7 @@ __global__ __launch_bounds__(256) void norm_bwd_packed(
     for (int j = 0; j < PJB; ++j) {
       float xv[E], dv[E];
       unpack<T>(xa[j], xv);
-      if constexpr (ROPE) {
+      if constexpr (PRE) {
 #pragma unroll
         for (int e = 0; e < E; ++e) dv[e] = dr[j][e];
       } else {
@@ -146,12 +168,12 @@ __global__ __launch_bounds__(256) void norm_bwd_packed(
     // widen the packed chunks again after the sums rather than keep their
     // fp32 copies alive across them
     reload_barrier<PJB>(xa);
-    if constexpr (!ROPE) reload_barrier<PJB>(da);
+    if constexpr (!PRE) reload_barrier<PJB>(da);
 #pragma unroll
     for (int j = 0; j < PJB; ++j) {
       float xv[E], dv[E], o[E];
       unpack<T>(xa[j], xv);
-      if constexpr (ROPE) {
+      if constexpr (PRE) {
 #pragma unroll
         for (int e = 0; e < E; ++e) dv[e] = dr[j][e];
       } else {
@@ -199,27 +221,27 @@ __global__ __launch_bounds__(256) void norm_bwd_packed(
 
 namespace {
 
-template <typename T, int S, bool LN, bool ROPE>
+template <typename T, int S, bool LN, int EPI>
 hipError_t launch_bwd_packed_s(int P, const void* dy, const void* x, const void* w,
-                               const float* mean, const float* rstat, void* dx, float* part,
+                               const void* b, const float* mean, const float* rstat, void* dx, float* part,
                                int64_t rows, int n, float w_add, const RopeArgs& ra,
                                hipStream_t st) {
-  hipLaunchKernelGGL((norm_bwd_packed<T, S, LN, ROPE>), dim3(P), dim3(256), 0, st,
+  hipLaunchKernelGGL((norm_bwd_packed<T, S, LN, EPI>), dim3(P), dim3(256), 0, st,
                      static_cast<const T*>(dy), static_cast<const T*>(x),
-                     static_cast<const T*>(w), mean, rstat, static_cast<T*>(dx), part, rows, n,
+                     static_cast<const T*>(w), static_cast<const T*>(b), mean, rstat, static_cast<T*>(dx), part, rows, n,
                      w_add, ra);
   return hipGetLastError();
 }
 
-template <typename T, bool LN, bool ROPE>
+template <typename T, bool LN, int EPI>
 hipError_t launch_bwd_packed_t(int S, int P, const void* dy, const void* x, const void* w,
-                               const float* mean, const float* rstat, void* dx, float* part,
+                               const void* b, const float* mean, const float* rstat, void* dx, float* part,
                                int64_t rows, int n, float w_add, const RopeArgs& ra,
                                hipStream_t st) {
   switch (S) {
 #define NR_CASE(SS)                                                                              \
   case SS:                                                                                       \
-    return launch_bwd_packed_s<T, SS, LN, ROPE>(P, dy, x, w, mean, rstat, dx, part, rows, n,    \
+    return launch_bwd_packed_s<T, SS, LN, EPI>(P, dy, x, w, b, mean, rstat, dx, part, rows, n,  \
                                                 w_add, ra, st);
     NR_CASE(4) NR_CASE(8) NR_CASE(16) NR_CASE(32)
 #undef NR_CASE
@@ -231,21 +253,26 @@ hipError_t launch_bwd_packed_t(int S, int P, const void* dy, const void* x, cons
 
 int bwd_packed_rows_per_wave(int S) { return PJB * (64 / S); }
 
-hipError_t launch_bwd_packed(int dt, bool ln, bool rope, int S, int P, const void* dy,
-                             const void* x, const void* w, const float* mean, const float* rstat,
-                             void* dx, float* part, int64_t rows, int n, float w_add,
-                             const RopeArgs& ra, hipStream_t st) {
-  // whole 16-byte chunks only, at most S of them a row
-  if (P < 1 || n > S * (dt == 0 ? 4 : 8) || (ln && rope)) return hipErrorInvalidValue;
+hipError_t launch_bwd_packed(int dt, bool ln, int epi, int S, int P, const void* dy,
+                             const void* x, const void* w, const void* b, const float* mean,
+                             const float* rstat, void* dx, float* part, int64_t rows, int n,
+                             float w_add, const RopeArgs& ra, hipStream_t st) {
+  // whole 16-byte chunks only, at most S of them a row; RoPE after RMSNorm,
+  // GeLU after LayerNorm
+  if (P < 1 || n > S * (dt == 0 ? 4 : 8) || (epi == kEpiRope && ln) || (epi == kEpiGelu && !ln))
+    return hipErrorInvalidValue;
   return by_dtype(dt, [&](auto tag) {
     using T = decltype(tag);
-    if (rope)
-      return launch_bwd_packed_t<T, false, true>(S, P, dy, x, w, mean, rstat, dx, part, rows, n,
-                                                 w_add, ra, st);
-    return ln ? launch_bwd_packed_t<T, true, false>(S, P, dy, x, w, mean, rstat, dx, part, rows, n,
-                                                    w_add, ra, st)
-              : launch_bwd_packed_t<T, false, false>(S, P, dy, x, w, mean, rstat, dx, part, rows,
-                                                     n, w_add, ra, st);
+    if (epi == kEpiRope)
+      return launch_bwd_packed_t<T, false, kEpiRope>(S, P, dy, x, w, b, mean, rstat, dx, part,
+                                                     rows, n, w_add, ra, st);
+    if (epi == kEpiGelu)
+      return launch_bwd_packed_t<T, true, kEpiGelu>(S, P, dy, x, w, b, mean, rstat, dx, part,
+                                                    rows, n, w_add, ra, st);
+    return ln ? launch_bwd_packed_t<T, true, kEpiNone>(S, P, dy, x, w, b, mean, rstat, dx, part,
+                                                       rows, n, w_add, ra, st)
+              : launch_bwd_packed_t<T, false, kEpiNone>(S, P, dy, x, w, b, mean, rstat, dx, part,
+                                                        rows, n, w_add, ra, st);
   });
 }
 

@@ -114,10 +114,11 @@ hipError_t launch_fwd_packed(int dt, bool ln, int epi, const FwdPlan& pl, const 
 // 64 / S rows side by side in a wave; P workgroups of four waves take the
 // batches of bwd_packed_rows_per_wave(S) rows round-robin.
 int bwd_packed_rows_per_wave(int S);
-hipError_t launch_bwd_packed(int dt, bool ln, bool rope, int S, int P, const void* dy,
-                             const void* x, const void* w, const float* mean, const float* rstat,
-                             void* dx, float* part, int64_t rows, int n, float w_add,
-                             const RopeArgs& ra, hipStream_t st);
+// epi: kEpiNone, kEpiRope (RMSNorm) or kEpiGelu (LayerNorm; b = beta).
+hipError_t launch_bwd_packed(int dt, bool ln, int epi, int S, int P, const void* dy,
+                             const void* x, const void* w, const void* b, const float* mean,
+                             const float* rstat, void* dx, float* part, int64_t rows, int n,
+                             float w_add, const RopeArgs& ra, hipStream_t st);
 hipError_t launch_norm_fwd(bool ln, int dt, const FwdPlan& pl, const void* x, const void* w,
                            const void* b, void* y, float* s0, float* s1, int64_t rows, int n,
                            float eps, float w_add, hipStream_t st);

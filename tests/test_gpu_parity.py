@@ -392,13 +392,13 @@ class forced_bwd_pack(forced_pack):
 
 
 @pytest.mark.parametrize("S,rows,n,dtype", PACKED)
-@pytest.mark.parametrize("op", ["rms", "rms_gemma", "rms_no_weight", "ln", "rms_rope"])
+@pytest.mark.parametrize("op", ["rms", "rms_gemma", "rms_no_weight", "ln", "rms_rope", "ln_gelu"])
 def test_packed_rows_backward(S, rows, n, dtype, op):
     """The backward's packed form (S lanes a row, column sums through LDS and
     the column reduction), each lane width forced, against the oracle."""
     seed = 9500 + S * 13 + rows + n
     say(f"packed backward S={S} {rows}x{n} {dtype} {op}")
-    x = workloads.normal((rows, n), seed, dtype, mean=0.5 if op == "ln" else 0.0, std=2.0)
+    x = workloads.normal((rows, n), seed, dtype, mean=0.5 if op.startswith("ln") else 0.0, std=2.0)
     gemma = op == "rms_gemma"
     w = workloads.normal((n,), seed + 1, dtype, mean=0.0 if gemma else 1.0, std=0.1)
     dy = workloads.normal((rows, n), seed + 2, dtype)
@@ -406,6 +406,17 @@ def test_packed_rows_backward(S, rows, n, dtype, op):
         if op == "ln":
             bt = workloads.normal((n,), seed + 3, dtype, std=0.5)
             check_ln_full(f"S={S}", x, w, bt, dy, 1e-5)
+        elif op == "ln_gelu":
+            bt = workloads.normal((n,), seed + 3, dtype, std=0.5)
+            _, mu, rs = nr.layernorm_gelu_fwd(g(x), g(w), g(bt), 1e-5)
+            dx, dg, db = nr.layernorm_gelu_bwd(g(dy), g(x), g(w), g(bt), mu, rs)
+            torch.cuda.synchronize()
+            rdx, rdg, rdb = oracle.layernorm_gelu_bwd(dy, x, w, bt, 1e-5)
+            _, _, rrs = oracle.layernorm_gelu_fwd(x, w, bt, 1e-5)
+            # |gelu'| stays below 1.13
+            check(f"S={S} dx", dx, rdx, out_kind(dtype), s=1.13 * grad_scale(rrs, dy, w))
+            check(f"S={S} dgamma", dg, rdg, "col")
+            check(f"S={S} dbeta", db, rdb, "col")
         elif op == "rms_rope":
             hd = n if n % 16 else n // 2
             rpt = 2 if hd == n else 1
